@@ -1,0 +1,190 @@
+"""Benchmark of the chunkwise gated delta-rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step = one gdn_chunk_fwd call over the whole workload (gate scan, Gram tiles,
+triangular solve, WY factors, state pass and output for every chunk of every
+chain), on inputs already resident in HBM.  The default workload is the
+Sykra-shaped layer (B=8, T=2048, H=12, d=64, chunk 64, bf16 q/k/v).  To keep
+the 256 MB Infinity Cache from serving a step's inputs, the timed loop cycles
+through enough independent copies of the inputs (>= 1 GiB in total) that each
+step reads data not touched for several steps.
+
+Prints ONE JSON line on stdout.  `value` is tokens/s (B*T tokens per step) from
+the wall time of the K timed steps; `roofline.achieved` is the kernel's
+algorithmic bytes per launch divided by its average launch duration, measured
+with HIP events on the stream the kernel runs on.  `cpu_baseline` times the
+fp64 CPU oracle on the host cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "tokens/sec gated-delta chunk fwd (H=12,d=64,T=2048,C=64); % of roofline"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["linear_attention_sequence_gated_amd/csrc/chunk_fwd.hip",
+                  "linear_attention_sequence_gated_amd/csrc/gdn_device.hpp"]
+
+
+def algorithmic_bytes(w, with_s0: bool) -> int:
+    """Bytes the method must move per call: q, k, v, alpha, beta, o, S0 (if given), S_final."""
+    eb = {"bf16": 2, "f32": 4, "c64": 8}[w.dtype]
+    sb = 8 if w.dtype == "c64" else 4
+    tok = w.B * w.T * w.H
+    b = tok * (2 * w.dk + 2 * w.dv) * eb + tok * 2 * 4 + w.B * w.H * w.dk * w.dv * sb
+    if with_s0:
+        b += w.B * w.H * w.dk * w.dv * sb
+    return b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"chunk_fwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, w, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on the host over the full workload."""
+    import oracle
+    q, k, v = (np.asarray(inp[x], dtype=np.float64) for x in ("q", "k", "v"))
+    a, b = np.asarray(inp["alpha"], np.float64), np.asarray(inp["beta"], np.float64)
+    s0 = None if inp.get("S0") is None else np.asarray(inp["S0"], np.float64)
+    threads = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    used = threads
+    while True:
+        _, _, used = oracle.recurrent_fwd(q, k, v, a, b, s0, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    tokens = w.B * w.T * reps
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"whole workload ({w.B}x{w.T} tokens x {w.H} heads, fp64 C token loop, OpenMP over "
+                      f"{w.B * w.H} chains) repeated {reps}x in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sykra_layer_bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to cycle (0 = enough for >= 1 GiB)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (chains are independent, so a "
+              f"multi-GPU run would shard batch x heads with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_sequence_gated_amd as gdn
+    from gdn_inputs import WORKLOADS, gen_workload
+
+    w = WORKLOADS[args.workload]
+    if w.kind != "chunk":
+        raise SystemExit(f"{args.workload} is not a chunked-forward workload")
+    gdn.load()
+    dev = torch.device("cuda:0")
+    inp = gen_workload(w)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
+    wbytes = algorithmic_bytes(w, inp["S0"] is not None)
+    ncopies = args.copies or max(2, int(np.ceil((1 << 30) / wbytes)))
+
+    def upload():
+        d = {x: torch.from_numpy(inp[x]).to(dev) for x in ("q", "k", "v", "alpha", "beta")}
+        for x in ("q", "k", "v"):
+            d[x] = d[x].to(tdt)
+        d["S0"] = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
+        d["out"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=dev)
+        d["S"] = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.complex64 if w.dtype == "c64" else torch.float32,
+                             device=dev)
+        return d
+
+    sets = [upload() for _ in range(ncopies)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % ncopies]
+        gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], out=d["out"], S_final=d["S"],
+                      stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(kern_ms))
+
+    tokens = w.B * w.T
+    value = tokens * args.steps / wall
+    achieved = wbytes / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": METRIC if args.workload == "sykra_layer_bf16" else f"tokens/sec gated-delta chunk fwd ({w.name})",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; unit-norm q/k, N(0,1) v, sigmoid beta, exp(-softplus) alpha)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "S0": inp["S0"] is not None, "input_copies_cycled": ncopies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": wbytes, "kernel_avg_ms": avg_ms,
+                     "kernel_min_ms": float(np.min(kern_ms)), "kernel": "gdn::chunk_fwd_kernel"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * gdn.h -- C ABI of libgdn, the MI355X (gfx950) gated delta-rule library.
+ *
+ * The method: per head, a d_k x d_v associative state S is carried over the
+ * sequence and updated by a gated delta rule,
+ *
+ *     S_t = alpha_t (I - beta_t k_t kread_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T qread_t,
+ *
+ * where kread = k, qread = q for real data and kread = conj(k), qread = conj(q)
+ * for complex data.  References for each piece:
+ *   - rank-one delta write with a keyed readout and residual error:
+ *     DeltaPhase README, section 2 "Complex Phase Matrix Delta Memory";
+ *   - the data-dependent forget gate alpha_t: Sykra 0.3.3 README,
+ *     "Architectural Highlights" (data-dependent forget gating); the gate
+ *     scales the whole updated state (Gated DeltaNet ordering, named in the
+ *     DeltaPhase lineage list);
+ *   - beta in (0, 2) as the extended Householder range: DeltaPhase README,
+ *     section 1 "Extended Householder Beta Range";
+ *   - the chunkwise-parallel evaluation (WY / unit triangular transform) that
+ *     gdn_chunk_fwd implements: Sykra README, "Architectural Highlights"
+ *     (chunkwise parallel training), DeltaPhase README, section 1 "Fast
+ *     Triangular Solve", and section 5 (log-space factorisation of the decay);
+ *   - the O(d^2) single-token step of gdn_recurrent_step: Sykra README,
+ *     "Computational Complexity" table (inference step time O(d^2), fixed state).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers (memory the caller allocated on the
+ *     current HIP device), except where stated.  The library allocates
+ *     nothing and keeps no state besides a cached device-property query.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream) and the call returns without synchronising.
+ *   - Argument errors are reported synchronously, before anything is
+ *     launched, and no output is touched.  A launch failure returns
+ *     GDN_ERR_HIP.  Faults during execution surface at the caller's next
+ *     synchronisation of the stream.  No C++ exception crosses this ABI.
+ *   - Calls are thread-safe.  Two calls that write the same buffers must be
+ *     ordered by the caller.
+ *   - Element types: `dtype` selects the storage of q, k, v and out:
+ *       GDN_F32  float32, GDN_BF16 bfloat16, GDN_C64 complex64 (interleaved
+ *       re, im float32).  alpha and beta are always float32.  States (S0,
+ *       S_final, S) are float32, or complex64 when dtype == GDN_C64.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Preconditions not checked on the device (violations give undefined,
+ *     typically non-finite, results): 0 < alpha <= 1, 0 <= beta <= 2, finite
+ *     inputs.  Inputs and outputs must not overlap, except that S_final may
+ *     equal S0.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  GDN_ERR_SHAPE = 2,       /* a size is negative or the total is too large   */
+  GDN_ERR_DTYPE = 3,       /* dtype is not one of GDN_F32, GDN_BF16, GDN_C64 */
+  GDN_ERR_UNSUPPORTED = 4, /* valid but not supported (chunk, head dims)     */
+  GDN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned              */
+  GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required     */
+  GDN_ERR_HIP = 7          /* the HIP runtime reported an error on launch    */
+};
+
+/* Element types (the `dtype` argument). */
+enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_C64 = 2 };
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes; 0 means the
+ * call may pass workspace = NULL.  Returns 0 also for unsupported arguments
+ * (gdn_chunk_fwd then reports the error).
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/*
+ * Chunkwise-parallel forward of the gated delta rule over whole sequences.
+ *
+ *   q, k      [B, T, H, dk]  dtype          queries and keys (row-major, d fastest)
+ *   v         [B, T, H, dv]  dtype          values
+ *   alpha     [B, T, H]      float32        forget gate, 0 < alpha <= 1
+ *   beta      [B, T, H]      float32        write strength, 0 <= beta <= 2
+ *   S0        [B, H, dk, dv] state type     initial state (row = key dim); NULL -> zeros
+ *   chunk                                    chunk length C; 64 is supported
+ *   out       [B, T, H, dv]  dtype          o_t for every token
+ *   S_final   [B, H, dk, dv] state type     state after token T-1; NULL -> not written;
+ *                                            may be the same buffer as S0
+ *   workspace, workspace_bytes               device scratch, at least
+ *                                            gdn_chunk_fwd_workspace_bytes(...) bytes
+ *   stream                                   hipStream_t to enqueue on
+ *
+ * Supported: chunk == 64; dk == dv in {64, 128} for GDN_F32 / GDN_BF16;
+ * dk == dv == 32 for GDN_C64.  Any T >= 0 (T % 64 != 0 is handled exactly:
+ * the tail chunk is shorter).  B == 0, H == 0 or T == 0 with S_final given
+ * copies S0 (or zeros) into S_final.
+ *
+ * Arithmetic: bf16 inputs are multiplied on bf16 matrix cores with fp32
+ * accumulation; the state is carried in fp32.  fp32 and complex64 inputs use
+ * fp32 matrix cores throughout.
+ */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                  const void *S0, int chunk, void *out, void *S_final, int B, int T, int H, int dk,
+                  int dv, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One single-token decode step on N independent states, in place.
+ *
+ *   q, k   [N, dk] dtype;  v [N, dv] dtype;  alpha, beta [N] float32
+ *   S      [N, dk, dv] state type, read and overwritten with the new state
+ *   out    [N, dv] dtype, o = S_new^T qread
+ *
+ * Supported: dk == dv == 64 or 128 for GDN_F32 / GDN_BF16; 32 for GDN_C64.
+ * N == 0 is a no-op.  The state is read once and written once.
+ */
+int gdn_recurrent_step(const void *q, const void *k, const void *v, const float *alpha,
+                       const float *beta, void *S, void *out, int N, int dk, int dv, int dtype,
+                       void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gdn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

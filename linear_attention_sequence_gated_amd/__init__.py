@@ -1,0 +1,7 @@
+"""MI355X-native gated delta rule: chunkwise forward and single-token decode.
+
+The compute path is libgdn.so (hand-written HIP kernels for gfx950 behind the C
+ABI of include/gdn.h); this package is its thin ctypes binding.
+"""
+from .gdn import (GDN_BF16, GDN_C64, GDN_F32, GdnError, chunk_fwd, gdn_chunk_fwd,  # noqa: F401
+                  gdn_chunk_fwd_workspace_bytes, gdn_recurrent_step, gdn_status_str, load, recurrent_step)

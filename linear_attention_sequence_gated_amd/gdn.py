@@ -1,0 +1,165 @@
+"""ctypes binding of libgdn (include/gdn.h).
+
+The raw entry points keep the C names and take integer device addresses:
+``gdn_chunk_fwd``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
+``gdn_status_str``.  ``chunk_fwd`` and ``recurrent_step`` are conveniences for
+torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
+``data_ptr()`` and the current HIP stream, and raise on a non-OK status.  Every
+step of the computation runs in the HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3
+GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
+GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
+
+EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_str")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(gdn_status_str(status))
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libgdn.so (built by ``python -m linear_attention_sequence_gated_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m linear_attention_sequence_gated_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [ci] * 7
+    lib.gdn_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.gdn_chunk_fwd.restype = ci
+    lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
+    lib.gdn_recurrent_step.restype = ci
+    lib.gdn_status_str.argtypes = [ci]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ raw C ABI
+def gdn_status_str(status: int) -> str:
+    return load().gdn_status_str(int(status)).decode()
+
+
+def gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype) -> int:
+    return int(load().gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype))
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype,
+                  workspace, workspace_bytes, stream) -> int:
+    return int(load().gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype,
+                                    workspace, workspace_bytes, stream))
+
+
+def gdn_recurrent_step(q, k, v, alpha, beta, S, out, N, dk, dv, dtype, stream) -> int:
+    return int(load().gdn_recurrent_step(q, k, v, alpha, beta, S, out, N, dk, dv, dtype, stream))
+
+
+# ------------------------------------------------------------- torch helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    if t.dtype == torch.complex64:
+        return GDN_C64
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16, float32 or complex64")
+
+
+def _state_dtype(code: int):
+    import torch
+    return torch.complex64 if code == GDN_C64 else torch.float32
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def chunk_fwd(q, k, v, alpha, beta, S0=None, chunk: int = 64, out=None, S_final=None, stream=None):
+    """Chunked forward on device tensors.  q, k [B,T,H,dk]; v [B,T,H,dv]; alpha, beta [B,T,H] fp32.
+
+    Returns (out [B,T,H,dv], S_final [B,H,dk,dv]).
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd: tensors must live on a HIP device")
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    sdt = _state_dtype(code)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), sdt, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, T, H, dv), q.dtype, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=sdt, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), sdt, dev)
+    ws_bytes = gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    s = gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), chunk, _ptr(out),
+                      _ptr(S_final), B, T, H, dk, dv, code, _ptr(ws), ws_bytes, st)
+    if s != GDN_OK:
+        raise GdnError(s)
+    return out, S_final
+
+
+def recurrent_step(q, k, v, alpha, beta, S, out=None, stream=None):
+    """One decode step, in place on S [N,dk,dv].  q, k [N,dk]; v [N,dv]; alpha, beta [N].  Returns out [N,dv]."""
+    import torch
+    N, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("recurrent_step: tensors must live on a HIP device")
+    _check(k, "k", (N, dk), q.dtype, dev)
+    _check(v, "v", (N, dv), q.dtype, dev)
+    _check(alpha, "alpha", (N,), torch.float32, dev)
+    _check(beta, "beta", (N,), torch.float32, dev)
+    _check(S, "S", (N, dk, dv), _state_dtype(code), dev)
+    if out is None:
+        out = torch.empty((N, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (N, dv), q.dtype, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    s = gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(out), N, dk, dv,
+                           code, st)
+    if s != GDN_OK:
+        raise GdnError(s)
+    return out

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every symbol include/gdn.h declares, and rejects
+bad arguments before launching anything.  CPU only: no call here reaches a kernel
+(every call either fails validation or has nothing to do)."""
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_gated_amd as gdn
+from linear_attention_sequence_gated_amd import gdn as raw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000  # a 16-byte aligned fake address; validation rejects before any use
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = gdn.load()
+    names = declared_functions()
+    assert set(names) == set(raw.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert gdn.gdn_status_str(s).startswith("GDN_")
+    assert "unknown" in gdn.gdn_status_str(99)
+
+
+def chunk(**kw):
+    args = dict(q=A, k=A, v=A, alpha=A, beta=A, S0=None, chunk=64, out=A, S_final=A, B=2, T=128, H=3, dk=64,
+                dv=64, dtype=gdn.GDN_BF16, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return gdn.gdn_chunk_fwd(**args)
+
+
+def step(**kw):
+    args = dict(q=A, k=A, v=A, alpha=A, beta=A, S=A, out=A, N=16, dk=64, dv=64, dtype=gdn.GDN_BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_recurrent_step(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), raw.GDN_ERR_DTYPE),
+    (dict(dtype=-1), raw.GDN_ERR_DTYPE),
+    (dict(B=-1), raw.GDN_ERR_SHAPE),
+    (dict(T=-5), raw.GDN_ERR_SHAPE),
+    (dict(dk=0), raw.GDN_ERR_SHAPE),
+    (dict(B=1 << 20, T=1 << 20, H=1 << 10), raw.GDN_ERR_SHAPE),
+    (dict(chunk=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=96, dv=96), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=64, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_F32, dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=64, dv=64), raw.GDN_ERR_UNSUPPORTED),
+    (dict(q=None), raw.GDN_ERR_NULL),
+    (dict(alpha=None), raw.GDN_ERR_NULL),
+    (dict(out=None), raw.GDN_ERR_NULL),
+    (dict(k=A + 8), raw.GDN_ERR_ALIGN),
+    (dict(S0=A + 4), raw.GDN_ERR_ALIGN),
+    (dict(S_final=A + 2), raw.GDN_ERR_ALIGN),
+])
+def test_chunk_argument_errors(kw, status):
+    assert chunk(**kw) == status
+
+
+def test_chunk_empty_is_noop():
+    # no chains: nothing to launch, even with NULL inputs
+    assert chunk(B=0, q=None, k=None, v=None, alpha=None, beta=None, out=None, S_final=None) == raw.GDN_OK
+    assert chunk(H=0) == raw.GDN_OK
+
+
+def test_workspace_query():
+    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), raw.GDN_ERR_DTYPE),
+    (dict(N=-1), raw.GDN_ERR_SHAPE),
+    (dict(dk=48, dv=48), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),
+    (dict(S=None), raw.GDN_ERR_NULL),
+    (dict(v=None), raw.GDN_ERR_NULL),
+    (dict(out=A + 8), raw.GDN_ERR_ALIGN),
+])
+def test_step_argument_errors(kw, status):
+    assert step(**kw) == status
+
+
+def test_step_empty_is_noop():
+    assert step(N=0, q=None, S=None) == raw.GDN_OK
+
+
+def test_torch_helper_rejects_bad_shapes_on_cpu():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host tensors are refused before any HIP call
+        gdn.chunk_fwd(q, q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
+    with pytest.raises(TypeError):
+        gdn.chunk_fwd(q.to(torch.float16), q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
+    with pytest.raises(ValueError):
+        gdn.recurrent_step(q[0, 0], q[0, 0], q[0, 0], torch.zeros(1), torch.zeros(1), torch.zeros(1, 64, 64))

@@ -1,0 +1,155 @@
+"""Chunked forward on the GPU (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from gdn_inputs import WORKLOADS, gen_chunk, gen_workload
+from gpu_util import (TOL, assert_close, chain_rel_errors, down, note, oracle_chunk, run_chunk, take_chains,
+                      torch_dev, up)
+
+pytestmark = pytest.mark.gpu
+
+# (name, dtype, B, T, H, d, extra generator args).  Sizes span several chunks and
+# a ragged tail; the oracle finishes each in well under a second.
+SMALL = [
+    ("f32_single_head_full", "f32", 1, 256, 1, 64, {}),
+    ("f32_tail_s0", "f32", 2, 200, 3, 64, dict(s0_var=0.1)),
+    ("bf16_d64_tail", "bf16", 2, 300, 3, 64, {}),
+    ("bf16_d64_s0", "bf16", 1, 129, 2, 64, dict(s0_var=0.01)),
+    ("bf16_d128_s0", "bf16", 1, 200, 2, 128, dict(s0_var=0.01, alpha_mu=-5.0)),
+    ("bf16_d128_tail", "bf16", 2, 77, 1, 128, {}),
+    ("c64_tail", "c64", 2, 200, 2, 32, dict(beta_scale=2.0)),
+    ("c64_s0", "c64", 1, 130, 1, 32, dict(beta_scale=2.0, s0_var=0.5)),
+]
+
+
+@pytest.mark.parametrize("name,dtype,B,T,H,d,extra", SMALL, ids=[s[0] for s in SMALL])
+def test_chunk_small(name, dtype, B, T, H, d, extra):
+    torch_dev()
+    inp = gen_chunk(B, T, H, d, d, dtype=dtype, seed=100 + len(name), **extra)
+    note(f"chunk {name} B={B} T={T} H={H} d={d}")
+    o, S = run_chunk(inp, dtype)
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close(name, dtype, o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("c64", 32)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 191])
+def test_chunk_lengths(dtype, d, T):
+    torch_dev()
+    inp = gen_chunk(2, T, 2, d, d, dtype=dtype, seed=7 + T, s0_var=0.1,
+                    beta_scale=2.0 if dtype == "c64" else 1.0)
+    note(f"chunk lengths dtype={dtype} d={d} T={T}")
+    o, S = run_chunk(inp, dtype)
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close(f"len{T}_{dtype}_{d}", dtype, o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("c64", 32)])
+def test_chunk_empty_sequence_copies_state(dtype, d):
+    torch = torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    inp = gen_chunk(2, 0, 3, d, d, dtype=dtype, seed=3, s0_var=1.0)
+    note(f"chunk T=0 dtype={dtype}")
+    sd = torch.complex64 if dtype == "c64" else torch.float32
+    q = torch.empty((2, 0, 3, d), dtype={"f32": torch.float32, "bf16": torch.bfloat16, "c64": torch.complex64}[dtype],
+                    device="cuda")
+    a = torch.empty((2, 0, 3), dtype=torch.float32, device="cuda")
+    s0 = up(inp["S0"], "f32")
+    _, S = gdn.chunk_fwd(q, q, q, a, a, s0)
+    assert np.array_equal(down(S), inp["S0"])
+    _, S = gdn.chunk_fwd(q, q, q, a, a, None)
+    assert down(S).dtype == (np.complex64 if sd == torch.complex64 else np.float32)
+    assert not down(S).any()
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("c64", 32)])
+def test_chunk_state_in_place(dtype, d):
+    """S_final may alias S0."""
+    torch_dev()
+    inp = gen_chunk(1, 150, 2, d, d, dtype=dtype, seed=31, s0_var=0.1)
+    note(f"chunk in-place state dtype={dtype}")
+    o, S = run_chunk(inp, dtype, S_final_alias=True)
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close(f"alias_{dtype}", dtype, o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("c64", 32)])
+def test_chunk_repeated_keys(dtype, d):
+    """Associative-recall structure: a small key set written over and over."""
+    torch_dev()
+    rng = np.random.default_rng(5)
+    inp = gen_chunk(2, 320, 2, d, d, dtype=dtype, seed=41, beta_scale=2.0 if dtype == "c64" else 1.0)
+    idx = rng.integers(0, 16, size=320)
+    inp["k"] = np.ascontiguousarray(inp["k"][:, :16][:, idx])  # token t reuses key idx[t]
+    inp["q"] = np.ascontiguousarray(inp["k"][:, rng.permutation(320)])
+    note(f"chunk repeated keys dtype={dtype}")
+    o, S = run_chunk(inp, dtype)
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close(f"repeat_{dtype}", dtype, o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("c64", 32)])
+def test_chunk_reflection_keeps_norm(dtype, d):
+    """beta = 2, alpha = 1, v = 0: Householder reflections keep ||S||_F; matches the oracle too."""
+    torch_dev()
+    inp = gen_chunk(1, 200, 2, d, d, dtype=dtype, seed=51, s0_var=1.0)
+    inp["beta"][:] = 2.0
+    inp["alpha"][:] = 1.0
+    inp["v"][:] = 0
+    note(f"chunk reflection dtype={dtype}")
+    o, S = run_chunk(inp, dtype)
+    n0 = np.linalg.norm(inp["S0"].reshape(2, -1).astype(np.complex128), axis=1)
+    n1 = np.linalg.norm(S.reshape(2, -1).astype(np.complex128), axis=1)
+    assert np.allclose(n0, n1, rtol=1e-4), (n0, n1)
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close(f"reflect_{dtype}", dtype, o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("c64", 32)])
+def test_chunk_split_invariance(dtype, d):
+    """Two calls chained through S_final -> S0 agree with one call."""
+    torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    inp = gen_chunk(1, 256, 2, d, d, dtype=dtype, seed=61, s0_var=0.1)
+    note(f"chunk split dtype={dtype}")
+    o, S = run_chunk(inp, dtype)
+    first = {k_: (v_[:, :128] if k_ in ("q", "k", "v", "alpha", "beta") else v_) for k_, v_ in inp.items()}
+    o1, S1 = run_chunk(first, dtype)
+    second = {k_: (v_[:, 128:] if k_ in ("q", "k", "v", "alpha", "beta") else v_) for k_, v_ in inp.items()}
+    second["S0"] = S1
+    o2, S2 = run_chunk(second, dtype)
+    eo, es = chain_rel_errors(np.concatenate([o1, o2], axis=1), S2, o, S)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+def test_chunk_deterministic():
+    torch_dev()
+    inp = gen_chunk(2, 300, 3, 64, 64, dtype="bf16", seed=71)
+    note("chunk determinism bf16 d64")
+    o1, S1 = run_chunk(inp, "bf16")
+    o2, S2 = run_chunk(inp, "bf16")
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = [("sykra_layer_bf16", [(0, 0), (3, 7), (7, 11), (5, 2)]),
+        ("long_context_bf16", [(0, 0), (1, 15)]),
+        ("deltaphase_c64", [(0, 0), (2, 5), (3, 7)]),
+        ("single_head_f32", [(0, 0)])]
+
+
+@pytest.mark.parametrize("wname,chains", FULL, ids=[f[0] for f in FULL])
+def test_chunk_full_size_sampled_chains(wname, chains):
+    """The workload at its full size, in the launch configuration the benchmark times;
+    a sample of chains is recomputed by the oracle (chains are independent)."""
+    torch_dev()
+    w = WORKLOADS[wname]
+    inp = gen_workload(w)
+    note(f"chunk full size {wname}")
+    o, S = run_chunk(inp, w.dtype)
+    sub = take_chains(inp, chains)
+    o_ref, S_ref = oracle_chunk(sub)
+    o_s = np.stack([o[b, :, h] for b, h in chains], axis=1)[None]
+    S_s = np.stack([S[b, h] for b, h in chains])[None]
+    assert_close(f"full_{wname}", w.dtype, o_s, S_s, o_ref, S_ref)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
