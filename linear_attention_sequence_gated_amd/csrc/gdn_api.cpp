@@ -75,6 +75,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::ChunkArgs a{q, k, v, alpha, beta, S0, out, S_final, B, T, H, dk, dv, dtype, stream};
+  // The pipelined bf16 kernel addresses one batch row of q/k/v/out with 32-bit
+  // buffer offsets; larger rows use the fused kernel.
+  const bool pipe_fits = (long long)T * H * (dk > dv ? dk : dv) * 2 < (1LL << 31);
+  if (dtype == GDN_BF16 && pipe_fits) return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

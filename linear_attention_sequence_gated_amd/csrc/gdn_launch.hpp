@@ -31,7 +31,8 @@ struct StepArgs {
   void* stream;
 };
 
-hipError_t launch_chunk_fwd(const ChunkArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, every dtype
+hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only
 hipError_t launch_recurrent_step(const StepArgs& a);
 
 }  // namespace gdn
