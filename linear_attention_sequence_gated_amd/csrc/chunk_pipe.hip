@@ -20,7 +20,7 @@
 //     which is the same algebra as Ut = U - W S with U = T diag(beta) V,
 //     W = T diag(beta)(Kr * gamma).  Every intermediate stays in MFMA
 //     accumulators and is fed back as the next product's operand.
-//   * Decay factors above the diagonal blocks are products of a per-row and a
+//   * Decay factors below the diagonal blocks are products of a per-row and a
 //     per-column factor, each <= 1 (exp(g_r - g_m) exp(g_m - g_s) with m the
 //     first row of the row block), so only the diagonal blocks need per-element
 //     exponentials, masked before the exponential.
@@ -28,6 +28,10 @@
 //     are read with ds_read_b64_tr_b16 straight from the row-major tiles.
 //   * Global traffic uses buffer loads/stores whose range check implements the
 //     ragged tail (rows >= T read as zero and are never written).
+//   * The chunk loop is unrolled by two so that every LDS address is a per-lane
+//     base plus a compile-time offset.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -36,6 +40,7 @@ namespace pipe {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
+template <int V> using ic = std::integral_constant<int, V>;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
@@ -43,28 +48,68 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ bf16x4 as_bf16x4(short4_t s) { return __builtin_bit_cast(bf16x4, s); }
+// Barrier between pipeline phases: waits for this wave's LDS traffic only (so
+// global prefetches stay in flight) and stops the scheduler from moving any
+// instruction across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-// Four consecutive bf16 at p (8-byte aligned LDS).
 __device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
 // Transposed sub-block of a row-major bf16 LDS matrix M (row stride ld):
-// lane (g, c) receives M[row0 + 4g + j][col + c], j = 0..3.
-__device__ __forceinline__ bf16x4 ld4_tr(const __bf16* M, int ld, int row0, int col) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
-  const __bf16* p = M + (row0 + 4 * g + (i >> 2)) * ld + col + 4 * (i & 3);
-  return as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
+// lane (g, c) receives M[row0 + 4g + j][col + c], j = 0..3.  `p` must be the
+// lane's address &M[row0 + 4g + (c >> 2)][col + 4 (c & 3)].
+__device__ __forceinline__ bf16x4 ld4_tr(const __bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// fp32 -> bf16 (round to nearest even), converted in pairs (one v_cvt_pk_bf16_f32 each).
 __device__ __forceinline__ bf16x4 cvt4(const f32x4& a) {
-  bf16x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = (__bf16)a[j];
-  return r;
+  const bf16x2 lo = __builtin_convertvector(f32x2{a[0], a[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector(f32x2{a[2], a[3]}, bf16x2);
+  return bf16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-__device__ __forceinline__ f32x4 mfma(const bf16x4& a0, const bf16x4& a1, const bf16x4& b0, const bf16x4& b1,
-                                      const f32x4& c) {
+// Keeps the loads issued above it from being moved below it.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Barrier for waves that only read LDS in the current buffer: no wait on their
+// own outstanding LDS reads, so operand loads stay in flight across it.
+__device__ __forceinline__ void reader_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts within
+// rows of 16, then the row totals are broadcast into the following rows.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  auto shr = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                 0xf, 0xf, true));
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});  // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});  // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});  // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});  // row_shr:8
+  // row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// c += [a0 a1] [b0; b1]  (two 16-wide k sub-blocks, one 16x16x32 issue)
+__device__ __forceinline__ f32x4 mma2(const bf16x4& a0, const bf16x4& a1, const bf16x4& b0, const bf16x4& b1,
+                                     const f32x4& c) {
   bf16x8 a, b;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -83,30 +128,34 @@ __device__ __forceinline__ bf16x4 z4() {
   return z;
 }
 
-__device__ __forceinline__ float bcast_quad(float x, int q) {
-  // quad_perm [q, q, q, q]
-  switch (q) {
-    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x00, 0xf, 0xf, false));
-    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55, 0xf, 0xf, false));
-    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xAA, 0xf, 0xf, false));
-    default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xFF, 0xf, 0xf, false));
-  }
+// c += a b  (one 16-wide k sub-block).  Only used where c comes from VALU code
+// or is zero: a 16x16x16 issue that reads as its accumulator the result of a
+// 16x16x32 issue was observed to be scheduled without the wait states that
+// mixed-shape dependency needs, so such chains use 16x16x32 with a zero half.
+__device__ __forceinline__ f32x4 mma1(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int Q> __device__ __forceinline__ float bcast_quad(float x) {
+  constexpr int ctrl = Q * 0x55;  // quad_perm [Q, Q, Q, Q]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
 }
 
 __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <int DK> struct Cfg {
-  static constexpr int NV = 64;                 // value columns per workgroup
+  static constexpr int NV = 64;  // value columns per workgroup
   static constexpr int NDT = DK / 16, NKP = DK / 32;
   static constexpr int LDK = DK + 8, LDV = NV + 8, LD16 = 16 + 8;
-  // element offsets (bf16) of the double-buffered raw tiles and hand-off tiles
+  // bf16 element offsets: double-buffered raw tiles and hand-off tiles
   static constexpr int szK = 64 * LDK, szV = 64 * LDV;
   static constexpr int oRK = 0, oRQ = szK, oRV = 2 * szK, szRaw = 2 * szK + szV;
-  static constexpr int szTri = 10 * 16 * LD16, szTd = 4 * 16 * LD16;
+  static constexpr int szTile = 16 * LD16, szTri = 10 * szTile, szTd = 4 * szTile;
   static constexpr int oHA = 0, oHP = szTri, oHT = 2 * szTri, szHand = 2 * szTri + szTd;
+  static constexpr int oRaw0 = 0, oHand0 = 2 * szRaw;
   static constexpr int nBf = 2 * szRaw + 2 * szHand;
   static constexpr int fBase = ((nBf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
-  // fp32 region (floats): gates[2] = beta, beta*gamma, gamma, lambda (64 each) + gamma_C (pad 4)
+  // fp32 region (floats): gates[2] = beta, beta*gamma, gamma, lambda (64 each) + gamma_C (padded)
   static constexpr int szGate = 4 * 64 + 4;
   static constexpr int fGate = 0;
   // producer-only: per-token g2, beta, rowf (64 each) and colf for row blocks 1..3 (3 x 64)
@@ -117,7 +166,7 @@ template <int DK> struct Cfg {
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   // global geometry
-  static constexpr int UPRK = DK * 2 / 16, UPRV = NV * 2 / 16;   // 16-byte units per row
+  static constexpr int UPRK = DK * 2 / 16, UPRV = NV * 2 / 16;  // 16-byte units per row
   static constexpr int NUK = 64 * UPRK / 256, NUV = 64 * UPRV / 256;
 };
 
@@ -142,10 +191,6 @@ __global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __rest
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
   const int nchunks = (T + 63) >> 6;
 
-  auto raw = [&](int buf) { return sb + buf * Cf::szRaw; };
-  auto hand = [&](int buf) { return sb + 2 * Cf::szRaw + buf * Cf::szHand; };
-  auto gate = [&](int buf) { return sf + Cf::fGate + buf * Cf::szGate; };
-
   if (w >= 4) {
     // ======================================================== PRODUCERS
     const int pt = tid - 256, pw = w - 4;
@@ -156,19 +201,21 @@ __global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __rest
         make_rsrc(vg + tokbase * DV + dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)h * DV + dv0) * 2));
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(alpha + tokbase, (uint32_t)(((size_t)T * H - h) * 4));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + tokbase, (uint32_t)(((size_t)T * H - h) * 4));
-    const int rowK = H * DK * 2, rowV = H * DV * 2;  // bytes between tokens
+    const int rowK = H * DK * 2, rowV = H * DV * 2;  // bytes between consecutive tokens
     uint4 pk[Cf::NUK], pq[Cf::NUK], pv[Cf::NUV];
     float pa = 1.f, pb = 0.f;
-    int vofK[Cf::NUK], vofV[Cf::NUV];
+    int vofK[Cf::NUK], vofV[Cf::NUV], ldsK[Cf::NUK], ldsV[Cf::NUV];
 #pragma unroll
     for (int u = 0; u < Cf::NUK; ++u) {
-      const int unit = pt + 256 * u;
-      vofK[u] = (unit / Cf::UPRK) * rowK + (unit % Cf::UPRK) * 16;
+      const int unit = pt + 256 * u, row = unit / Cf::UPRK, cu = unit % Cf::UPRK;
+      vofK[u] = row * rowK + cu * 16;
+      ldsK[u] = row * LDK + cu * 8;
     }
 #pragma unroll
     for (int u = 0; u < Cf::NUV; ++u) {
-      const int unit = pt + 256 * u;
-      vofV[u] = (unit / Cf::UPRV) * rowV + (unit % Cf::UPRV) * 16;
+      const int unit = pt + 256 * u, row = unit / Cf::UPRV, cu = unit % Cf::UPRV;
+      vofV[u] = row * rowV + cu * 16;
+      ldsV[u] = row * LDV + cu * 8;
     }
     auto prefetch = [&](int n) {
       const int c0 = n * 64;
@@ -182,106 +229,84 @@ __global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __rest
         pv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofV[u], c0 * rowV, 0));
       pa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
       pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
-      if (c0 + l >= T) pa = 1.f;  // padding token: alpha = 1 (beta reads as 0)
     };
 
-    // Stage chunk n (from the prefetch registers) into raw buffer n & 1, run the
-    // gate scan, publish gates for the consumers and decay factors for the Gram.
-    auto stage = [&](int n) {
-      __bf16* R = raw(n & 1);
+    // Stage chunk n (prefetched registers) into raw buffer BUF, run the gate
+    // scan, publish gates for the consumers and decay factors for the Gram.
+    auto stage = [&](auto bufc, int n) {
+      constexpr int BUF = decltype(bufc)::value;
+      __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
 #pragma unroll
       for (int u = 0; u < Cf::NUK; ++u) {
-        const int unit = pt + 256 * u, row = unit / Cf::UPRK, col = (unit % Cf::UPRK) * 8;
-        *reinterpret_cast<uint4*>(R + Cf::oRK + row * LDK + col) = pk[u];
-        *reinterpret_cast<uint4*>(R + Cf::oRQ + row * LDK + col) = pq[u];
+        *reinterpret_cast<uint4*>(R + Cf::oRK + ldsK[u]) = pk[u];
+        *reinterpret_cast<uint4*>(R + Cf::oRQ + ldsK[u]) = pq[u];
       }
 #pragma unroll
-      for (int u = 0; u < Cf::NUV; ++u) {
-        const int unit = pt + 256 * u, row = unit / Cf::UPRV, col = (unit % Cf::UPRV) * 8;
-        *reinterpret_cast<uint4*>(R + Cf::oRV + row * LDV + col) = pv[u];
-      }
+      for (int u = 0; u < Cf::NUV; ++u) *reinterpret_cast<uint4*>(R + Cf::oRV + ldsV[u]) = pv[u];
       if (pw == 0) {
-        float x = log2f(pa);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off, 64);
-          if (l >= off) x += y;
-        }
+        const float a = (n * 64 + l < T) ? pa : 1.f;  // padding token: alpha = 1 (beta reads as 0)
+        const float x = wave_prefix_sum(__builtin_amdgcn_logf(a));
         const float g63 = __shfl(x, 63, 64);
         const float gblk = __shfl(x, l & ~15, 64);
-        const float gam = exp2f(x);
-        float* G = gate(n & 1);
+        const float gam = __builtin_amdgcn_exp2f(x);
+        float* G = sf + Cf::fGate + BUF * Cf::szGate;
         G[l] = pb;
         G[64 + l] = pb * gam;
         G[128 + l] = gam;
-        G[192 + l] = exp2f(g63 - x);
+        G[192 + l] = __builtin_amdgcn_exp2f(g63 - x);
         if (l == 63) G[256] = gam;
         float* PG = sf + Cf::fPG;
         PG[l] = x;
         PG[64 + l] = pb;
-        PG[128 + l] = exp2f(x - gblk);
+        PG[128 + l] = __builtin_amdgcn_exp2f(x - gblk);
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
           const float gi = __shfl(x, 16 * i, 64);
-          PG[128 + 64 * i + l] = exp2f(l < 16 * i ? gi - x : -INFINITY);
+          PG[128 + 64 * i + l] = __builtin_amdgcn_exp2f(l < 16 * i ? gi - x : -INFINITY);
         }
       }
     };
 
-    // Gram tiles, decay, and the inverse of this wave's diagonal block for chunk n.
-    auto gram = [&](int n) {
-      const __bf16* R = raw(n & 1);
-      __bf16* Hd = hand(n & 1);
-      const float* PG = sf + Cf::fPG;
-      float* DS = sf + Cf::fDS + pw * Cf::szDS;
-      auto tile = [&](int ti, int tj) {
-        f32x4 aG = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
+    float* const DS = sf + Cf::fDS + pw * Cf::szDS;
+    // Operands of one Gram tile: K rows of the column block (A operand) and the
+    // K and Q rows of the row block (B operands), NKP k-pairs each.
+    struct TileOps {
+      bf16x4 a[NKP][2], k[NKP][2], q[NKP][2];
+    };
+    auto load_tile = [&](const __bf16* R, int ti, int tj, TileOps& o) {
 #pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-          const bf16x4 a0 = ld4(R + Cf::oRK + (16 * tj + c) * LDK + 32 * p + 4 * g);
-          const bf16x4 a1 = ld4(R + Cf::oRK + (16 * tj + c) * LDK + 32 * p + 16 + 4 * g);
-          const bf16x4 k0 = ld4(R + Cf::oRK + (16 * ti + c) * LDK + 32 * p + 4 * g);
-          const bf16x4 k1 = ld4(R + Cf::oRK + (16 * ti + c) * LDK + 32 * p + 16 + 4 * g);
-          const bf16x4 q0 = ld4(R + Cf::oRQ + (16 * ti + c) * LDK + 32 * p + 4 * g);
-          const bf16x4 q1 = ld4(R + Cf::oRQ + (16 * ti + c) * LDK + 32 * p + 16 + 4 * g);
-          aG = mfma(a0, a1, k0, k1, aG);  // [s][r] = k_s . k_r
-          aP = mfma(a0, a1, q0, q1, aP);  // [s][r] = k_s . q_r
-        }
-        const int r = 16 * ti + c;
-        f32x4 va, vp;
-        if (ti != tj) {
-          const float rf = PG[128 + r], nb = -PG[64 + r] * rf;
-          const f32x4 cf = *reinterpret_cast<const f32x4*>(PG + 128 + 64 * ti + 16 * tj + 4 * g);
+      for (int p = 0; p < NKP; ++p) {
+        const __bf16* ra_ = R + Cf::oRK + (16 * tj + c) * LDK + 32 * p + 4 * g;
+        const __bf16* rk_ = R + Cf::oRK + (16 * ti + c) * LDK + 32 * p + 4 * g;
+        const __bf16* rq_ = R + Cf::oRQ + (16 * ti + c) * LDK + 32 * p + 4 * g;
+        o.a[p][0] = ld4(ra_);
+        o.a[p][1] = ld4(ra_ + 16);
+        o.k[p][0] = ld4(rk_);
+        o.k[p][1] = ld4(rk_ + 16);
+        o.q[p][0] = ld4(rq_);
+        o.q[p][1] = ld4(rq_ + 16);
+      }
+    };
+    // accumulators [s][r] = k_s . k_r and k_s . q_r of one tile
+    auto tile_mma = [&](const TileOps& o, f32x4& aG, f32x4& aP) {
+      aG = zero4();
+      aP = zero4();
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            va[j] = aG[j] * (nb * cf[j]);
-            vp[j] = aP[j] * (rf * cf[j]);
-          }
-        } else {
-          const float gr = PG[r], br = PG[64 + r];
-          const f32x4 gs = *reinterpret_cast<const f32x4*>(PG + 16 * tj + 4 * g);
-          f32x4 ad;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int s = 16 * tj + 4 * g + j;
-            const float gm = exp2f(r >= s ? gr - gs[j] : -INFINITY);
-            ad[j] = r > s ? br * gm * aG[j] : 0.f;
-            va[j] = -ad[j];
-            vp[j] = gm * aP[j];
-          }
-          *reinterpret_cast<f32x4*>(DS + c * 20 + 4 * g) = ad;
-        }
-        *reinterpret_cast<bf16x4*>(Hd + Cf::oHA + tri(ti, tj) * 16 * LD16 + c * LD16 + 4 * g) = cvt4(va);
-        *reinterpret_cast<bf16x4*>(Hd + Cf::oHP + tri(ti, tj) * 16 * LD16 + c * LD16 + 4 * g) = cvt4(vp);
-      };
-      tile(pw, pw);
-      if (pw == 0) { tile(1, 0); tile(2, 0); }
-      if (pw == 1) { tile(2, 1); tile(3, 0); }
-      if (pw == 2) tile(3, 1);
-      if (pw == 3) tile(3, 2);
-      // (I + A_pw,pw)^{-1} by forward substitution: lane (q = l & 3, cc = l >> 2)
-      // owns column cc, rows 4k + q.  Once row s is final its value is broadcast
-      // inside the quad and subtracted from every later row.
+      for (int p = 0; p < NKP; ++p) {
+        aG = mma2(o.a[p][0], o.a[p][1], o.k[p][0], o.k[p][1], aG);
+        aP = mma2(o.a[p][0], o.a[p][1], o.q[p][0], o.q[p][1], aP);
+      }
+    };
+    auto store_tile = [&](__bf16* Hd, int t, const f32x4& va, const f32x4& vp) {
+      *reinterpret_cast<bf16x4*>(Hd + Cf::oHA + t * Cf::szTile + c * LD16 + 4 * g) = cvt4(va);
+      *reinterpret_cast<bf16x4*>(Hd + Cf::oHP + t * Cf::szTile + c * LD16 + 4 * g) = cvt4(vp);
+    };
+
+    // (I + A_pw,pw)^{-1} by forward substitution.  Lane (q = l & 3, cc = l >> 2)
+    // owns column cc and rows 4k + q; once row s is final its value is
+    // broadcast inside the quad and subtracted from every later row.
+    auto solve = [&](__bf16* Hd) {
+      __bf16* Td = Hd + Cf::oHT + pw * Cf::szTile;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int q = l & 3, cc = l >> 2;
       float a[4][16], t[4];
@@ -295,35 +320,101 @@ __global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __rest
         }
         t[k] = (4 * k + q == cc) ? 1.f : 0.f;
       }
-#pragma unroll
-      for (int s = 0; s < 15; ++s) {
-        const float ts = bcast_quad(t[s >> 2], s & 3);
+      auto step = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        const float ts = bcast_quad<s & 3>(t[s >> 2]);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           if (4 * k + 3 > s) t[k] -= a[k][s] * ts;  // a[k][s] = 0 unless row 4k+q > s
-      }
-      __bf16* Td = Hd + Cf::oHT + pw * 16 * LD16;
+      };
+      step(ic<0>{}); step(ic<1>{}); step(ic<2>{}); step(ic<3>{}); step(ic<4>{});
+      step(ic<5>{}); step(ic<6>{}); step(ic<7>{}); step(ic<8>{}); step(ic<9>{});
+      step(ic<10>{}); step(ic<11>{}); step(ic<12>{}); step(ic<13>{}); step(ic<14>{});
 #pragma unroll
       for (int k = 0; k < 4; ++k) Td[(4 * k + q) * LD16 + cc] = (__bf16)t[k];
+    };
+
+    // Tiles of this wave: its diagonal tile (pw, pw) and two tiles below the
+    // diagonal.  The six sub-diagonal tiles are split two per wave over waves
+    // 0..2; wave 3 recomputes wave 2's pair and does not store it, so every
+    // wave runs the same straight-line code.
+    const int o1i = pw == 0 ? 1 : pw == 1 ? 2 : 3, o1j = pw == 0 ? 0 : pw == 1 ? 1 : 2;
+    const int o2i = pw == 0 ? 2 : 3, o2j = pw == 0 ? 0 : pw == 1 ? 0 : 1;
+    const bool storeOff = pw < 3;
+    auto gram = [&](auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
+      __bf16* Hd = sb + Cf::oHand0 + BUF * Cf::szHand;
+      const float* PG = sf + Cf::fPG;
+      TileOps od, o1, o2;
+      load_tile(R, pw, pw, od);
+      load_tile(R, o1i, o1j, o1);
+      load_tile(R, o2i, o2j, o2);
+      // decay factors: diagonal tile (g2 and beta of row r, g2 of columns s) and
+      // the row / column factors of the two sub-diagonal tiles
+      const int rd = 16 * pw + c, r1 = 16 * o1i + c, r2 = 16 * o2i + c;
+      const float gr = PG[rd], br = PG[64 + rd];
+      const f32x4 gs = *reinterpret_cast<const f32x4*>(PG + 16 * pw + 4 * g);
+      const float rf1 = PG[128 + r1], nb1 = -PG[64 + r1] * rf1;
+      const float rf2 = PG[128 + r2], nb2 = -PG[64 + r2] * rf2;
+      const f32x4 cf1 = *reinterpret_cast<const f32x4*>(PG + 128 + 64 * o1i + 16 * o1j + 4 * g);
+      const f32x4 cf2 = *reinterpret_cast<const f32x4*>(PG + 128 + 64 * o2i + 16 * o2j + 4 * g);
+      issue_fence();
+      f32x4 gD, pD, g1, p1, g2, p2;
+      tile_mma(od, gD, pD);
+      tile_mma(o1, g1, p1);
+      tile_mma(o2, g2, p2);
+      // diagonal tile: per-element decay, masked before the exponential
+      f32x4 ad, va, vp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = 16 * pw + 4 * g + j;
+        const float gm = __builtin_amdgcn_exp2f(rd >= s ? gr - gs[j] : -INFINITY);
+        ad[j] = rd > s ? br * gm * gD[j] : 0.f;
+        va[j] = -ad[j];
+        vp[j] = gm * pD[j];
+      }
+      *reinterpret_cast<f32x4*>(DS + c * 20 + 4 * g) = ad;
+      store_tile(Hd, tri(pw, pw), va, vp);
+      // sub-diagonal tiles: decay = row factor x column factor
+      f32x4 va1, vp1, va2, vp2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        va1[j] = g1[j] * (nb1 * cf1[j]);
+        vp1[j] = p1[j] * (rf1 * cf1[j]);
+        va2[j] = g2[j] * (nb2 * cf2[j]);
+        vp2[j] = p2[j] * (rf2 * cf2[j]);
+      }
+      if (storeOff) {
+        store_tile(Hd, tri(o1i, o1j), va1, vp1);
+        store_tile(Hd, tri(o2i, o2j), va2, vp2);
+      }
+      solve(Hd);
     };
 
     // prologue: chunk 0 staged and solved before the consumers start
     if (nchunks > 0) {
       prefetch(0);
-      stage(0);
+      stage(ic<0>{}, 0);
       if (nchunks > 1) prefetch(1);
     }
-    lds_barrier();
-    if (nchunks > 0) gram(0);
-    lds_barrier();
-    for (int n = 0; n < nchunks; ++n) {
+    phase_barrier();
+    if (nchunks > 0) gram(ic<0>{});
+    phase_barrier();
+    // iteration n: stage / solve chunk n+1 into buffer (n+1) & 1
+    // iteration n: stage / solve chunk n+1 into buffer (n+1) & 1
+    auto iter = [&](auto nbufc, int n) {
       if (n + 1 < nchunks) {
-        stage(n + 1);
+        stage(nbufc, n + 1);
         if (n + 2 < nchunks) prefetch(n + 2);
       }
-      lds_barrier();
-      if (n + 1 < nchunks) gram(n + 1);
-      lds_barrier();
+      phase_barrier();
+      if (n + 1 < nchunks) gram(nbufc);
+      phase_barrier();
+    };
+    for (int n = 0; n < nchunks; n += 2) {
+      iter(ic<1>{}, n);
+      if (n + 1 < nchunks) iter(ic<0>{}, n + 1);
     }
   } else {
     // ======================================================== CONSUMERS
@@ -335,116 +426,156 @@ __global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __rest
       for (int j = 0; j < 4; ++j)
         S[d][j] = S0g ? S0g[((size_t)chain * DK + 16 * d + 4 * g + j) * DV + col] : 0.f;
 
+    // Output: lane (g, c) of wave w writes token c of each 16-token block,
+    // value columns 16w + 4g .. 16w + 4g + 3 (one 8-byte store).
     const size_t obase = ((size_t)b * T * H + h) * DV + dv0;
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(outg + obase, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)h * DV + dv0) * 2));
     const int rowO = H * DV * 2;
-    const int vofO = 4 * g * rowO + (16 * w + c) * 2;
+    const int vofO = c * rowO + (16 * w + 4 * g) * 2;
+    // per-lane LDS element offsets (relative to a raw / hand-off buffer)
+    const int offRow = c * LDK + 4 * g;                                  // row c, k sub-block 4g
+    const int offTrK = (4 * g + (c >> 2)) * LDK + 4 * (c & 3);           // transposed K reads
+    const int offTrV = (4 * g + (c >> 2)) * LDV + 16 * w + 4 * (c & 3);  // transposed V reads
+    const int offT16 = c * LD16 + 4 * g;                                 // 16x16 hand-off tiles
 
-    lds_barrier();  // prologue: chunk 0 staged
-    lds_barrier();  // prologue: chunk 0 Gram and diagonal inverses ready
-    for (int n = 0; n < nchunks; ++n) {
-      const int buf = n & 1;
-      const __bf16* R = raw(buf);
-      const __bf16* Hd = hand(buf);
-      const float* G = gate(buf);
-      // ---- phase 1: Ut = (I + A)^{-1}(diag(beta) V - diag(beta gamma) K S); state update
+    auto body = [&](auto bufc, int n) {
+      constexpr int BUF = decltype(bufc)::value;
+      const __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
+      const __bf16* Hd = sb + Cf::oHand0 + BUF * Cf::szHand;
+      const float* G = sf + Cf::fGate + BUF * Cf::szGate;
+      auto Atile = [&](int i, int j) { return ld4(Hd + Cf::oHA + tri(i, j) * Cf::szTile + offT16); };
+      auto Ptile = [&](int i, int j) { return ld4(Hd + Cf::oHP + tri(i, j) * Cf::szTile + offT16); };
+      // ---- phase 1: Ut = (I + A)^{-1}(diag(beta) V - diag(beta gamma) K S); state update.
+      // Operand loads for the whole phase are issued first.
+      bf16x4 kr[4][NKP][2], vv[4], Am[6], Tm[4];
+      f32x4 bt[4], bg[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) {
+          const __bf16* pr = R + Cf::oRK + 16 * i * LDK + 32 * p + offRow;
+          kr[i][p][0] = ld4(pr);
+          kr[i][p][1] = ld4(pr + 16);
+        }
+        vv[i] = ld4_tr(R + Cf::oRV + 16 * i * LDV + offTrV);
+        bt[i] = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
+        bg[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
+        Tm[i] = ld4(Hd + Cf::oHT + i * Cf::szTile + offT16);
+      }
+      Am[0] = Atile(1, 0); Am[1] = Atile(2, 0); Am[2] = Atile(2, 1);
+      Am[3] = Atile(3, 0); Am[4] = Atile(3, 1); Am[5] = Atile(3, 2);
+      issue_fence();
       bf16x4 sfr[NDT];
 #pragma unroll
       for (int d = 0; d < NDT; ++d) sfr[d] = cvt4(S[d]);
+      f32x4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = zero4();
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) acc[i] = mma2(kr[i][p][0], kr[i][p][1], sfr[2 * p], sfr[2 * p + 1], acc[i]);
+      }
+      // operands of the state update, in flight during the substitution
+      bf16x4 kt[NDT][4];
+      f32x4 lm[4];
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) {
+        const __bf16* pk = R + Cf::oRK + 16 * d + offTrK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kt[d][i] = ld4_tr(pk + 16 * i * LDK);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lm[i] = *reinterpret_cast<const f32x4*>(G + 192 + 16 * i + 4 * g);
+      const float gC = G[256];
+      issue_fence();
       f32x4 X[4];
       bf16x4 Xf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-          const bf16x4 a0 = ld4(R + Cf::oRK + (16 * i + c) * LDK + 32 * p + 4 * g);
-          const bf16x4 a1 = ld4(R + Cf::oRK + (16 * i + c) * LDK + 32 * p + 16 + 4 * g);
-          acc = mfma(a0, a1, sfr[2 * p], sfr[2 * p + 1], acc);
-        }
-        const bf16x4 vv = ld4_tr(R + Cf::oRV, LDV, 16 * i, 16 * w);
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
-        const f32x4 bg = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
         f32x4 y;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = bt[j] * (float)vv[j] - bg[j] * acc[j];
+        for (int j = 0; j < 4; ++j) y[j] = bt[i][j] * (float)vv[i][j] - bg[i][j] * acc[i][j];
         // y -= sum_{i' < i} A_{i i'} X_{i'}   (the hand-off holds -A)
-        if (i == 1) y = mfma(ld4(Hd + Cf::oHA + tri(1, 0) * 16 * LD16 + c * LD16 + 4 * g), z4(), Xf[0], z4(), y);
-        if (i == 2)
-          y = mfma(ld4(Hd + Cf::oHA + tri(2, 0) * 16 * LD16 + c * LD16 + 4 * g),
-                   ld4(Hd + Cf::oHA + tri(2, 1) * 16 * LD16 + c * LD16 + 4 * g), Xf[0], Xf[1], y);
+        if (i == 1) y = mma1(Am[0], Xf[0], y);
+        if (i == 2) y = mma2(Am[1], Am[2], Xf[0], Xf[1], y);
         if (i == 3) {
-          y = mfma(ld4(Hd + Cf::oHA + tri(3, 0) * 16 * LD16 + c * LD16 + 4 * g),
-                   ld4(Hd + Cf::oHA + tri(3, 1) * 16 * LD16 + c * LD16 + 4 * g), Xf[0], Xf[1], y);
-          y = mfma(ld4(Hd + Cf::oHA + tri(3, 2) * 16 * LD16 + c * LD16 + 4 * g), z4(), Xf[2], z4(), y);
+          y = mma2(Am[3], Am[4], Xf[0], Xf[1], y);
+          y = mma2(Am[5], z4(), Xf[2], z4(), y);
         }
-        X[i] = mfma(ld4(Hd + Cf::oHT + i * 16 * LD16 + c * LD16 + 4 * g), z4(), cvt4(y), z4(),
-                    f32x4{0.f, 0.f, 0.f, 0.f});
+        X[i] = mma1(Tm[i], cvt4(y), zero4());
         Xf[i] = cvt4(X[i]);
       }
       // S <- gamma_C S + K^T diag(lambda) Ut
       bf16x4 XL[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 lm = *reinterpret_cast<const f32x4*>(G + 192 + 16 * i + 4 * g);
         f32x4 t;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = X[i][j] * lm[j];
+        for (int j = 0; j < 4; ++j) t[j] = X[i][j] * lm[i][j];
         XL[i] = cvt4(t);
       }
-      const float gC = G[256];
+      // operands of the output, in flight during the state update
+      bf16x4 qr[4][NKP][2], Pm[10];
+      float gm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) {
+          const __bf16* pr = R + Cf::oRQ + 16 * i * LDK + 32 * p + offRow;
+          qr[i][p][0] = ld4(pr);
+          qr[i][p][1] = ld4(pr + 16);
+        }
+        gm[i] = G[128 + 16 * i + c];  // gamma of token 16i + c
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) Pm[tri(i, j)] = Ptile(i, j);
+      issue_fence();
 #pragma unroll
       for (int d = 0; d < NDT; ++d) {
-        f32x4 s = S[d];
+        f32x4 sd = S[d];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[j] *= gC;
-        s = mfma(ld4_tr(R + Cf::oRK, LDK, 0, 16 * d), ld4_tr(R + Cf::oRK, LDK, 16, 16 * d), XL[0], XL[1], s);
-        s = mfma(ld4_tr(R + Cf::oRK, LDK, 32, 16 * d), ld4_tr(R + Cf::oRK, LDK, 48, 16 * d), XL[2], XL[3], s);
-        S[d] = s;
+        for (int j = 0; j < 4; ++j) sd[j] *= gC;
+        sd = mma2(kt[d][0], kt[d][1], XL[0], XL[1], sd);
+        sd = mma2(kt[d][2], kt[d][3], XL[2], XL[3], sd);
+        S[d] = sd;
       }
-      lds_barrier();
-      // ---- phase 2: O = diag(gamma) Q S + P Ut
+      reader_barrier();
+      // ---- phase 2: output, computed transposed so each lane holds four
+      // consecutive value columns of one token:
+      //   O_i^T = S^T Q_i^T diag(gamma_i) + sum_{i' <= i} Ut_{i'}^T P_{i i'}^T.
+      // S^T and Ut^T in A-operand layout are exactly the accumulator layouts of
+      // S and Ut; Q_i^T and P^T in B-operand layout are row-major reads.
       const int c0 = n * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        f32x4 o = zero4();
 #pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-          const bf16x4 a0 = ld4(R + Cf::oRQ + (16 * i + c) * LDK + 32 * p + 4 * g);
-          const bf16x4 a1 = ld4(R + Cf::oRQ + (16 * i + c) * LDK + 32 * p + 16 + 4 * g);
-          o = mfma(a0, a1, sfr[2 * p], sfr[2 * p + 1], o);
-        }
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(G + 128 + 16 * i + 4 * g);
+        for (int p = 0; p < NKP; ++p) o = mma2(sfr[2 * p], sfr[2 * p + 1], qr[i][p][0], qr[i][p][1], o);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= gm[j];
-        const __bf16* Pi = Hd + Cf::oHP;
-        if (i == 0) o = mfma(ld4(Pi + tri(0, 0) * 16 * LD16 + c * LD16 + 4 * g), z4(), Xf[0], z4(), o);
-        if (i == 1)
-          o = mfma(ld4(Pi + tri(1, 0) * 16 * LD16 + c * LD16 + 4 * g), ld4(Pi + tri(1, 1) * 16 * LD16 + c * LD16 + 4 * g),
-                   Xf[0], Xf[1], o);
+        for (int j = 0; j < 4; ++j) o[j] *= gm[i];
+        if (i == 0) o = mma1(Xf[0], Pm[tri(0, 0)], o);
+        if (i == 1) o = mma2(Xf[0], Xf[1], Pm[tri(1, 0)], Pm[tri(1, 1)], o);
         if (i == 2) {
-          o = mfma(ld4(Pi + tri(2, 0) * 16 * LD16 + c * LD16 + 4 * g), ld4(Pi + tri(2, 1) * 16 * LD16 + c * LD16 + 4 * g),
-                   Xf[0], Xf[1], o);
-          o = mfma(ld4(Pi + tri(2, 2) * 16 * LD16 + c * LD16 + 4 * g), z4(), Xf[2], z4(), o);
+          o = mma2(Xf[0], Xf[1], Pm[tri(2, 0)], Pm[tri(2, 1)], o);
+          o = mma2(Xf[2], z4(), Pm[tri(2, 2)], z4(), o);
         }
         if (i == 3) {
-          o = mfma(ld4(Pi + tri(3, 0) * 16 * LD16 + c * LD16 + 4 * g), ld4(Pi + tri(3, 1) * 16 * LD16 + c * LD16 + 4 * g),
-                   Xf[0], Xf[1], o);
-          o = mfma(ld4(Pi + tri(3, 2) * 16 * LD16 + c * LD16 + 4 * g), ld4(Pi + tri(3, 3) * 16 * LD16 + c * LD16 + 4 * g),
-                   Xf[2], Xf[3], o);
+          o = mma2(Xf[0], Xf[1], Pm[tri(3, 0)], Pm[tri(3, 1)], o);
+          o = mma2(Xf[2], Xf[3], Pm[tri(3, 2)], Pm[tri(3, 3)], o);
         }
-        // Extract the four 16-bit results from the packed dwords with explicit
-        // shifts (element extraction from a bf16 vector followed by a 16-bit
-        // bit cast was observed to drop the upper halves).
-        const uint2 ob = __builtin_bit_cast(uint2, cvt4(o));
-        const unsigned short h16[4] = {(unsigned short)(ob.x & 0xffffu), (unsigned short)(ob.x >> 16),
-                                       (unsigned short)(ob.y & 0xffffu), (unsigned short)(ob.y >> 16)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          __builtin_amdgcn_raw_buffer_store_b16(h16[j], ro, vofO, (c0 + 16 * i + j) * rowO, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(o)), ro, vofO, (c0 + 16 * i) * rowO, 0);
       }
-      lds_barrier();
+      phase_barrier();
+    };
+
+    phase_barrier();  // prologue: chunk 0 staged
+    phase_barrier();  // prologue: chunk 0 Gram and diagonal inverses ready
+    for (int n = 0; n < nchunks; n += 2) {
+      body(ic<0>{}, n);
+      if (n + 1 < nchunks) body(ic<1>{}, n + 1);
     }
     if (Sfg) {
 #pragma unroll
