@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "tokens/sec gated-delta chunk fwd (H=12,d=64,T=2048,C=64); % of roofline"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["linear_attention_sequence_gated_amd/csrc/chunk_fwd.hip",
+                  "linear_attention_sequence_gated_amd/csrc/chunk_pipe.hip",
                   "linear_attention_sequence_gated_amd/csrc/gdn_device.hpp"]
 
 
@@ -57,10 +58,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"chunk_fwd_{workload}_traffic.md")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -69,6 +70,13 @@ def measured_traffic(workload: str):
     if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
         return None
     return float(m_b.group(1))
+
+
+def decode_bytes(w) -> int:
+    """Bytes one decode step must move: S read and written (fp32), q, k, v, o (bf16), alpha, beta."""
+    eb = {"bf16": 2, "f32": 4, "c64": 8}[w.dtype]
+    sb = 8 if w.dtype == "c64" else 4
+    return w.N * (2 * w.dk * w.dv * sb + (2 * w.dk + 2 * w.dv) * eb + 2 * 4)
 
 
 def cpu_baseline(inp, w, budget_s: float = 12.0):
@@ -84,12 +92,43 @@ def cpu_baseline(inp, w, budget_s: float = 12.0):
         _, _, used = oracle.recurrent_fwd(q, k, v, a, b, s0, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
+        if el >= budget_s or reps >= 400:
             break
     tokens = w.B * w.T * reps
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"whole workload ({w.B}x{w.T} tokens x {w.H} heads, fp64 C token loop, OpenMP over "
                       f"{w.B * w.H} chains) repeated {reps}x in {el:.1f} s"}
+
+
+def summarize(path: str) -> None:
+    """Print a markdown summary of rocprofv3 CSV output under `path` (kernel stats and/or
+    FETCH_SIZE / WRITE_SIZE counters, scaled by the copy kernel recorded in the same run)."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        print(f"kernel stats ({os.path.relpath(f, path)}):\n")
+        print("| kernel | calls | avg us | min us | max us | total % |")
+        print("|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(f)):
+            name = r["Name"]
+            short = name if len(name) < 70 else name[:67] + "..."
+            print(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                  f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+        print()
+    counters = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    for f in counters:
+        per = {}
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
+        print(f"counters ({os.path.relpath(f, path)}), mean per dispatch:\n")
+        print("| kernel | counter | dispatches | mean per dispatch |")
+        print("|---|---|---|---|")
+        for (k, cn), vals in sorted(per.items()):
+            short = k if len(k) < 70 else k[:67] + "..."
+            print(f"| {short} | {cn} | {len(vals)} | {np.mean(vals):.1f} |")
+        print()
 
 
 def main():
@@ -100,7 +139,13 @@ def main():
     ap.add_argument("--workload", default="sykra_layer_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copies", type=int, default=0, help="input copies to cycle (0 = enough for >= 1 GiB)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--summarize", metavar="DIR", help="summarise rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (chains are independent, so a "
@@ -113,10 +158,10 @@ def main():
     from gdn_inputs import WORKLOADS, gen_workload
 
     w = WORKLOADS[args.workload]
-    if w.kind != "chunk":
-        raise SystemExit(f"{args.workload} is not a chunked-forward workload")
     gdn.load()
     dev = torch.device("cuda:0")
+    if w.kind == "decode":
+        return bench_decode(args, w, dev)
     inp = gen_workload(w)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
     wbytes = algorithmic_bytes(w, inp["S0"] is not None)
@@ -160,7 +205,10 @@ def main():
     tokens = w.B * w.T
     value = tokens * args.steps / wall
     achieved = wbytes / (avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    # The library takes the pipelined kernel for bf16 whenever a chain's row offsets fit 32 bits.
+    pipe = w.dtype == "bf16" and w.T * w.H * max(w.dk, w.dv) * 2 < 2 ** 31
+    kernel = "chunk_pipe_kernel" if pipe else "chunk_fwd_kernel"
+    traffic = measured_traffic(kernel, args.workload)
     result = {
         "metric": METRIC if args.workload == "sykra_layer_bf16" else f"tokens/sec gated-delta chunk fwd ({w.name})",
         "value": value,
@@ -179,10 +227,82 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": wbytes, "kernel_avg_ms": avg_ms,
-                     "kernel_min_ms": float(np.min(kern_ms)), "kernel": "gdn::chunk_fwd_kernel"},
+                     "kernel_min_ms": float(np.min(kern_ms)),
+                     "kernel": ("gdn::pipe::" if pipe else "gdn::") + kernel},
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(inp, w)
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+    print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(dev):
+    """A plain device-to-device copy of 256 MiB, five times: its FETCH_SIZE / WRITE_SIZE
+    counters give the scale between counter units and bytes on this machine."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def bench_decode(args, w, dev):
+    """One step = one gdn_recurrent_step over all N states (one token each).  The timed loop
+    cycles through independent state sets (>= 1 GiB in total) so a step's state is not
+    served from the Infinity Cache."""
+    import torch
+
+    import linear_attention_sequence_gated_amd as gdn
+    from gdn_inputs import gen_decode_workload
+    inp = gen_decode_workload(w, steps=8)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
+    sbytes = decode_bytes(w)
+    state_bytes = inp["S"].nbytes
+    ncopies = args.copies or max(2, int(np.ceil((1 << 30) / state_bytes)))
+    S = [torch.from_numpy(inp["S"]).to(dev) for _ in range(ncopies)]
+    toks = []
+    for t in range(inp["q"].shape[0]):
+        d = {x: torch.from_numpy(inp[x][t]).to(dev) for x in ("q", "k", "v", "alpha", "beta")}
+        for x in ("q", "k", "v"):
+            d[x] = d[x].to(tdt)
+        toks.append(d)
+    out = torch.empty((w.N, w.dv), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = toks[i % len(toks)]
+        gdn.recurrent_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S[i % ncopies], out=out,
+                           stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+    avg_ms = float(np.mean(kern_ms))
+    achieved = sbytes / (avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"state-steps/sec gated-delta decode step ({w.name})", "value": w.N * args.steps / wall,
+        "unit": "state-steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "N": w.N, "dk": w.dk, "dv": w.dv, "state_copies_cycled": ncopies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": sbytes,
+                     "kernel_avg_ms": avg_ms, "kernel_min_ms": float(np.min(kern_ms)), "kernel": "gdn::decode_kernel"},
+    }
     print(json.dumps(result), flush=True)
 
 
