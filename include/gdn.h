@@ -93,8 +93,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
  *                                            gdn_chunk_fwd_workspace_bytes(...) bytes
  *   stream                                   hipStream_t to enqueue on
  *
- * Supported: chunk == 64; dk == dv in {64, 128} for GDN_F32 / GDN_BF16;
- * dk == dv == 32 for GDN_C64.  Any T >= 0 (T % 64 != 0 is handled exactly:
+ * Supported: chunk == 64; dk == dv in {64, 128} for GDN_BF16; dk == dv == 64
+ * for GDN_F32; dk == dv == 32 for GDN_C64.  Any T >= 0 (T % 64 != 0 is handled exactly:
  * the tail chunk is shorter).  B == 0, H == 0 or T == 0 with S_final given
  * copies S0 (or zeros) into S_final.
  *
