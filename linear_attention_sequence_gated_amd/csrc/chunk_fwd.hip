@@ -150,7 +150,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
   const int b = chain / H, h = chain % H;
   const int dv0 = slice * NV;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+  // w is made explicitly uniform so that branches on it are scalar branches:
+  // matrix-core instructions do not honour the exec mask.
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
 
   // ------------------------------------------------------------ prefetch
   uint4 pk[Cf::NUK], pq[Cf::NUK], pv[Cf::NUV];
@@ -501,9 +503,8 @@ template <int DT, int DK, int NV>
 static hipError_t launch_fused(const ChunkArgs& a) {
   const int nslices = a.dv / NV;
   const long nblk = (long)a.B * a.H * nslices;
-  hipLaunchKernelGGL((chunk_fwd_kernel<DT, DK, NV>), dim3((unsigned)nblk), dim3(256), 0, (hipStream_t)a.stream, a.q, a.k,
-                     a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
-  return hipGetLastError();
+  return launch_kernel(chunk_fwd_kernel<DT, DK, NV>, dim3((unsigned)nblk), dim3(256), (hipStream_t)a.stream, a.q, a.k,
+                       a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {

@@ -4,32 +4,44 @@
 // Same method as the fused kernel (chunkwise WY / UT transform of the gated
 // delta rule: Sykra 0.3.3 README, "Architectural Highlights"; DeltaPhase README,
 // section 1 "Fast Triangular Solve" and section 5 "Exact Chunkwise-Parallel
-// Scan"), reorganised so that no wave stalls on another's latency:
+// Scan"), organised so that the three limited resources of a CU -- LDS
+// bandwidth, vector-ALU issue (a wave64 instruction occupies its SIMD for four
+// cycles) and matrix-core issue -- are spread over the four SIMDs.
 //
-//   * 8 waves per workgroup (one workgroup per (batch, head, 64 value columns)).
-//     Waves 4..7 are PRODUCERS: for chunk n+1 they stage the raw q/k/v tiles
-//     into LDS, run the log-space gate scan, form the Gram tiles of K Kr^T and
-//     K Qr^T on MFMA, apply the decay, and invert the four 16x16 diagonal blocks
-//     of (I + A).  Waves 0..3 are CONSUMERS: each owns 16 value columns of the
-//     state and runs the sequential part for chunk n.  Two barriers per chunk.
-//   * The consumer never forms W or U.  With S the state at the chunk start,
-//       R  = diag(beta) V - diag(beta gamma) Kr S,
-//       Ut = (I + A)^{-1} R                (block forward substitution),
-//       O  = diag(gamma) Qr S + P Ut,
-//       S <- gamma_C S + K^T diag(lambda) Ut,   lambda_t = exp(g_C - g_t),
-//     which is the same algebra as Ut = U - W S with U = T diag(beta) V,
-//     W = T diag(beta)(Kr * gamma).  Every intermediate stays in MFMA
-//     accumulators and is fed back as the next product's operand.
-//   * Decay factors below the diagonal blocks are products of a per-row and a
-//     per-column factor, each <= 1 (exp(g_r - g_m) exp(g_m - g_s) with m the
-//     first row of the row block), so only the diagonal blocks need per-element
-//     exponentials, masked before the exponential.
-//   * Transposed operands (K^T for the state update, V in accumulator layout)
-//     are read with ds_read_b64_tr_b16 straight from the row-major tiles.
-//   * Global traffic uses buffer loads/stores whose range check implements the
-//     ragged tail (rows >= T read as zero and are never written).
-//   * The chunk loop is unrolled by two so that every LDS address is a per-lane
-//     base plus a compile-time offset.
+// One workgroup of 7 waves per (batch, head, 32 value columns), so a head's
+// columns are spread over two CUs; one barrier per chunk.  While the two
+// CONSUMER waves run chunk n out of LDS buffer n & 1, the five PRODUCER waves
+// fill buffer (n + 1) & 1 for chunk n + 1 from registers loaded from HBM two
+// chunks ahead:
+//
+//   wave 0, 1   consumers: 16 value columns each (one MFMA tile).
+//   wave 2, 3   Gram waves for row blocks {0,1} / {2,3}: K and Q straight from
+//               HBM in MFMA operand layout (published to LDS for the consumers),
+//               tiles (i,i), (i+1,i), (i+1,i+1) of Q K^T and the sub-diagonal
+//               tile of K K^T, and the inverse of diagonal block i.
+//   wave 4, 5   Gram waves for row block i = 2 / 3: tiles (i,0), (i,1) of
+//               K K^T and Q K^T, and the inverse of diagonal block 1 / 3.
+//   wave 6      the V tile, gamma and lambda.
+//
+// With S the state at the chunk start, g the within-chunk prefix sum of
+// log alpha, gamma_r = exp(g_r), lambda_r = exp(g_C - g_r), Gamma_rs =
+// exp(g_r - g_s) (r >= s), Gt = strict_lower(K K^T * Gamma) and T_ii =
+// (I + diag(beta_i) Gt_ii)^{-1}, block row i of
+// Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S) is
+//     Ut_i = T_ii diag(beta_i) (V_i - gamma_i * (K S)_i - sum_{j<i} Gt_ij Ut_j),
+// so beta only enters through the producer-built factors T_ii diag(beta_i);
+//     O  = gamma * (Q S) + lower(Q K^T * Gamma) Ut,
+//     S <- gamma_C S + K^T (lambda * Ut).
+// Diagonal blocks are inverted by row-owner forward substitution: lane (g, c)
+// owns row c of the inverse and each finished row is broadcast along the
+// 16-lane rows with DPP row_newbcast.
+//
+// Global traffic uses buffer loads/stores whose range check implements the
+// ragged tail (rows >= T read as zero and are never written).  Decay factors
+// are exp(g_r - g_s) with r >= s only (masked before the exponential), so no
+// factor above one is ever formed.  Packed bf16 values are handled as 32-bit
+// words throughout (two values per word), which keeps every conversion a
+// paired v_cvt_pk_bf16_f32.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -40,53 +52,49 @@ namespace pipe {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;  // four bf16
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // eight bf16
 template <int V> using ic = std::integral_constant<int, V>;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
+constexpr int kPipeThreads = 7 * 64;     // waves: 2 consumers, 4 Gram, 1 V
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
-// Barrier between pipeline phases: waits for this wave's LDS traffic only (so
+// Barrier between pipeline stages: waits for this wave's LDS traffic only (so
 // global prefetches stay in flight) and stops the scheduler from moving any
 // instruction across it.
-__device__ __forceinline__ void phase_barrier() {
+__device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+// Keeps the loads issued above it from being moved below it.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ u32x2 ld4(const __bf16* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Transposed sub-block of a row-major bf16 LDS matrix M (row stride ld):
 // lane (g, c) receives M[row0 + 4g + j][col + c], j = 0..3.  `p` must be the
 // lane's address &M[row0 + 4g + (c >> 2)][col + 4 (c & 3)].
-__device__ __forceinline__ bf16x4 ld4_tr(const __bf16* p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
+__device__ __forceinline__ u32x2 ld4_tr(const __bf16* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
 }
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-
-// fp32 -> bf16 (round to nearest even), converted in pairs (one v_cvt_pk_bf16_f32 each).
-__device__ __forceinline__ bf16x4 cvt4(const f32x4& a) {
-  const bf16x2 lo = __builtin_convertvector(f32x2{a[0], a[1]}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector(f32x2{a[2], a[3]}, bf16x2);
-  return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+// fp32 -> bf16 (round to nearest even), two values per v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned cvt2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+__device__ __forceinline__ u32x2 cvt4(const f32x4& a) { return u32x2{cvt2(a[0], a[1]), cvt2(a[2], a[3])}; }
 
-// Keeps the loads issued above it from being moved below it.
-__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
-
-// Barrier for waves that only read LDS in the current buffer: no wait on their
-// own outstanding LDS reads, so operand loads stay in flight across it.
-__device__ __forceinline__ void reader_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// bf16 halves of a 32-bit word as fp32.
+__device__ __forceinline__ float lo_f(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float hi_f(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts within
 // rows of 16, then the row totals are broadcast into the following rows.
@@ -95,512 +103,1077 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
                                                                  0xf, 0xf, true));
   };
-  x += shr(x, std::integral_constant<int, 0x111>{});  // row_shr:1
-  x += shr(x, std::integral_constant<int, 0x112>{});  // row_shr:2
-  x += shr(x, std::integral_constant<int, 0x114>{});  // row_shr:4
-  x += shr(x, std::integral_constant<int, 0x118>{});  // row_shr:8
+  x += shr(x, ic<0x111>{});  // row_shr:1
+  x += shr(x, ic<0x112>{});  // row_shr:2
+  x += shr(x, ic<0x114>{});  // row_shr:4
+  x += shr(x, ic<0x118>{});  // row_shr:8
   // row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
   return x;
 }
 
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// c += [a0 a1] [b0; b1]  (two 16-wide k sub-blocks, one 16x16x32 issue)
-__device__ __forceinline__ f32x4 mma2(const bf16x4& a0, const bf16x4& a1, const bf16x4& b0, const bf16x4& b1,
-                                     const f32x4& c) {
-  bf16x8 a, b;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a[j] = a0[j];
-    a[4 + j] = a1[j];
-    b[j] = b0[j];
-    b[4 + j] = b1[j];
-  }
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// Value of lane M of this lane's row of 16 (DPP row_newbcast:M; every lane
+// has a valid source, so no old value is needed).
+template <int M> __device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + M, 0xf, 0xf, true));
 }
 
-__device__ __forceinline__ bf16x4 z4() {
-  bf16x4 z;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) z[j] = (__bf16)0.0f;
-  return z;
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ u32x2 z4() { return u32x2{0u, 0u}; }
+
+// c += a b over one 32-wide k block (operands straight from 16-byte loads).
+__device__ __forceinline__ f32x4 mma32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// c += [a0 a1] [b0; b1]  (two 16-wide k sub-blocks, one 16x16x32 issue)
+__device__ __forceinline__ f32x4 mma2(const u32x2& a0, const u32x2& a1, const u32x2& b0, const u32x2& b1,
+                                     const f32x4& c) {
+  return mma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, u32x4{b0[0], b0[1], b1[0], b1[1]}, c);
 }
 
 // c += a b  (one 16-wide k sub-block).  Only used where c comes from VALU code
 // or is zero: a 16x16x16 issue that reads as its accumulator the result of a
 // 16x16x32 issue was observed to be scheduled without the wait states that
 // mixed-shape dependency needs, so such chains use 16x16x32 with a zero half.
-__device__ __forceinline__ f32x4 mma1(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma1(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), c,
+                                                   0, 0, 0);
 }
 
-template <int Q> __device__ __forceinline__ float bcast_quad(float x) {
-  constexpr int ctrl = Q * 0x55;  // quad_perm [Q, Q, Q, Q]
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
-}
-
-__host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
+__host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }   // i >= j
+__host__ __device__ constexpr int stri(int i, int j) { return i * (i - 1) / 2 + j; }  // i > j
 
 template <int DK> struct Cfg {
-  static constexpr int NV = 64;  // value columns per workgroup
+  static constexpr int NV = 32;  // value columns per workgroup
+  static constexpr int NT = NV / 32;  // 16-column tiles per consumer wave (two consumer waves)
   static constexpr int NDT = DK / 16, NKP = DK / 32;
   static constexpr int LDK = DK + 8, LDV = NV + 8, LD16 = 16 + 8;
-  // bf16 element offsets: double-buffered raw tiles and hand-off tiles
-  static constexpr int szK = 64 * LDK, szV = 64 * LDV;
-  static constexpr int oRK = 0, oRQ = szK, oRV = 2 * szK, szRaw = 2 * szK + szV;
-  static constexpr int szTile = 16 * LD16, szTri = 10 * szTile, szTd = 4 * szTile;
-  static constexpr int oHA = 0, oHP = szTri, oHT = 2 * szTri, szHand = 2 * szTri + szTd;
-  static constexpr int oRaw0 = 0, oHand0 = 2 * szRaw;
-  static constexpr int nBf = 2 * szRaw + 2 * szHand;
-  static constexpr int fBase = ((nBf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
-  // fp32 region (floats): gates[2] = beta, beta*gamma, gamma, lambda (64 each) + gamma_C (padded)
-  static constexpr int szGate = 4 * 64 + 4;
-  static constexpr int fGate = 0;
-  // producer-only: per-token g2, beta, rowf (64 each) and colf for row blocks 1..3 (3 x 64)
-  static constexpr int fPG = 2 * szGate, szPG = 6 * 64;
-  // producer diagonal-block scratch (fp32 16 x 20 per producer wave)
-  static constexpr int fDS = fPG + szPG, szDS = 16 * 20;
+  // bf16 element offsets inside one of the two stage buffers
+  static constexpr int szTile = 16 * LD16;
+  static constexpr int oK = 0, oQ = 64 * LDK, oV = 2 * 64 * LDK;
+  static constexpr int oNG = oV + 64 * LDV;     // -Gt, the six sub-diagonal tiles
+  static constexpr int oTP = oNG + 6 * szTile;  // T_ii diag(beta_i), four tiles
+  static constexpr int oP = oTP + 4 * szTile;   // P, ten lower tiles
+  static constexpr int szBuf = oP + 10 * szTile;
+  static constexpr int fBase = ((2 * szBuf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
+  // fp32 region (floats): per stage buffer gamma[64], lambda[64], gamma_C;
+  // then one private gate table (g, beta per token) and one 16 x 20 block
+  // scratch per Gram wave.
+  static constexpr int szGate = 132, fGate = 0;
+  static constexpr int fPGT = 2 * szGate, szPGT = 128;
+  static constexpr int fDS = fPGT + 4 * szPGT, szDS = 16 * 20;
   static constexpr int nF = fDS + 4 * szDS;
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  // global geometry
-  static constexpr int UPRK = DK * 2 / 16, UPRV = NV * 2 / 16;  // 16-byte units per row
-  static constexpr int NUK = 64 * UPRK / 256, NUV = 64 * UPRV / 256;
 };
 
+struct Ctx {
+  const __bf16* qg;
+  const __bf16* kg;
+  const __bf16* vg;
+  const float* alpha;
+  const float* beta;
+  const float* S0g;
+  __bf16* outg;
+  float* Sfg;
+  int T, H, DV, b, h, chain, dv0, nchunks;
+};
+
+// ---------------------------------------------------------------- producers
+// Per-token gates of chunk c0: g (log2 units, inclusive prefix of log2 alpha)
+// in lane l, written with beta to the wave's private table.
+__device__ __forceinline__ float gate_scan(float pa, float pb, int c0, int T, int l, float* PGT) {
+  const float a = (c0 + l < T) ? pa : 1.f;  // padding token: alpha = 1 (beta reads as 0)
+  const float x = wave_prefix_sum(__builtin_amdgcn_logf(a));
+  PGT[l] = x;
+  PGT[64 + l] = pb;
+  return x;
+}
+
+// Decay factors of diagonal block i: lane (g, c) gets Gamma[r][s] for r = 16i + c,
+// s = 16i + 4g + j, masked to 0 for s > r before the exponential.
+__device__ __forceinline__ f32x4 diag_gamma(const float* PGT, int i, int g, int c) {
+  const float gr = PGT[16 * i + c];
+  const f32x4 gs = *reinterpret_cast<const f32x4*>(PGT + 16 * i + 4 * g);
+  f32x4 gm;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gm[j] = __builtin_amdgcn_exp2f(c >= 4 * g + j ? gr - gs[j] : -INFINITY);
+  return gm;
+}
+
+// One forward-substitution step m for the four columns a lane owns:
+// t_j += row_bcast<m>(t_j) * a_m, fused into one DPP instruction per column.
+#define GDN_INV_STEP(M, A)                                                               \
+  "v_fmac_f32_dpp %0, %0, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
+  "v_fmac_f32_dpp %1, %1, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
+  "v_fmac_f32_dpp %2, %2, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
+  "v_fmac_f32_dpp %3, %3, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"
+
+// T_ii diag(beta_i) for diagonal block i.  G is its Gram accumulator (lane
+// (g, c) holds k_s . k_r, r = 16i + c, s = 16i + 4g + j; K K^T is symmetric, so
+// it is also row c of the block) and gm its decay factors.  (I + A)^{-1} with
+// A = diag(beta) Gt_ii strictly lower is found by forward substitution: lane
+// (g, c) owns row c, and once row m is final it is broadcast along each row of
+// 16 lanes (DPP row_newbcast) and added, scaled by -A[c][m], to every later row.
+// The four column chains are interleaved, so each DPP source was written three
+// instructions earlier (two wait states are required); the leading s_nop covers
+// the instructions before the block.
 template <int DK>
-__global__ __launch_bounds__(512, 1) void chunk_pipe_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
+__device__ __forceinline__ void diag_inverse(const f32x4& G, const f32x4& gm, const float* PGT, float* ds, int i,
+                                             int g, int c, __bf16* dst) {
+  const float br = PGT[64 + 16 * i + c];
+  f32x4 na;  // -A[c][4g + j]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) na[j] = c > 4 * g + j ? -br * gm[j] * G[j] : 0.f;
+  *reinterpret_cast<f32x4*>(ds + c * 20 + 4 * g) = na;
+  float a[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ds + c * 20 + 4 * q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
+  }
+  float t0 = c == 4 * g ? 1.f : 0.f, t1 = c == 4 * g + 1 ? 1.f : 0.f;
+  float t2 = c == 4 * g + 2 ? 1.f : 0.f, t3 = c == 4 * g + 3 ? 1.f : 0.f;
+  asm volatile("s_nop 1\n"
+               GDN_INV_STEP(0, 4) GDN_INV_STEP(1, 5) GDN_INV_STEP(2, 6) GDN_INV_STEP(3, 7) GDN_INV_STEP(4, 8)
+               GDN_INV_STEP(5, 9) GDN_INV_STEP(6, 10) GDN_INV_STEP(7, 11) GDN_INV_STEP(8, 12) GDN_INV_STEP(9, 13)
+               GDN_INV_STEP(10, 14) GDN_INV_STEP(11, 15) GDN_INV_STEP(12, 16) GDN_INV_STEP(13, 17)
+               GDN_INV_STEP(14, 18)
+               : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3)
+               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+                 "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
+  const f32x4 bs = *reinterpret_cast<const f32x4*>(PGT + 64 + 16 * i + 4 * g);
+  const f32x4 t{t0 * bs[0], t1 * bs[1], t2 * bs[2], t3 * bs[3]};
+  *reinterpret_cast<u32x2*>(dst + c * Cfg<DK>::LD16 + 4 * g) = cvt4(t);
+}
+#undef GDN_INV_STEP
+
+// Decayed Gram tile (row block i, column block j < i, so every r > s):
+// -Gt from the K K^T accumulator and P from the Q K^T accumulator.
+template <int DK>
+__device__ __forceinline__ void offdiag_tiles(const f32x4& G, const f32x4& P, const float* PGT, int i, int j, int g,
+                                              int c, __bf16* R) {
+  using Cf = Cfg<DK>;
+  const float gr = PGT[16 * i + c];
+  const f32x4 gs = *reinterpret_cast<const f32x4*>(PGT + 16 * j + 4 * g);
+  f32x4 ng, pv;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float gm = __builtin_amdgcn_exp2f(gr - gs[jj]);
+    ng[jj] = -gm * G[jj];
+    pv[jj] = gm * P[jj];
+  }
+  *reinterpret_cast<u32x2*>(R + Cf::oNG + stri(i, j) * Cf::szTile + c * Cf::LD16 + 4 * g) = cvt4(ng);
+  *reinterpret_cast<u32x2*>(R + Cf::oP + tri(i, j) * Cf::szTile + c * Cf::LD16 + 4 * g) = cvt4(pv);
+}
+
+// Decayed diagonal tile of P (gm from diag_gamma, zero above the diagonal).
+template <int DK>
+__device__ __forceinline__ void diag_p_tile(const f32x4& P, const f32x4& gm, int i, int g, int c, __bf16* R) {
+  using Cf = Cfg<DK>;
+  const f32x4 pv{gm[0] * P[0], gm[1] * P[1], gm[2] * P[2], gm[3] * P[3]};
+  *reinterpret_cast<u32x2*>(R + Cf::oP + tri(i, i) * Cf::szTile + c * Cf::LD16 + 4 * g) = cvt4(pv);
+}
+
+// One pipelined producer role: loads for chunk n + 2 are issued before chunk
+// n + 1 is processed; register set and stage buffer are chosen by parity.
+template <class Load, class Process>
+__device__ __forceinline__ void producer_loop(int nch, Load&& load, Process&& process) {
+  if (nch > 0) load(ic<0>{}, 0);
+  if (nch > 1) load(ic<1>{}, 1);
+  if (nch > 0) process(ic<0>{}, 0);
+  stage_barrier();
+  auto iter = [&](auto pc, int n) {
+    constexpr int par = decltype(pc)::value;
+    if (n + 2 < nch) load(ic<par>{}, n + 2);
+    issue_fence();
+    if (n + 1 < nch) process(ic<par ^ 1>{}, n + 1);
+    stage_barrier();
+  };
+  for (int n = 0; n < nch; n += 2) {
+    iter(ic<0>{}, n);
+    if (n + 1 < nch) iter(ic<1>{}, n + 1);
+  }
+}
+
+// Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).
+template <int DK>
+__device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, int l) {
+  using Cf = Cfg<DK>;
+  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
+  const int wi = b0 >> 1;
+  float* const PGT = sf + Cf::fPGT + wi * Cf::szPGT;
+  float* const DS = sf + Cf::fDS + wi * Cf::szDS;
+  const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const uint32_t spanK = (uint32_t)((size_t)T * H * DK * 2 - (size_t)x.h * DK * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
+  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
+  const int rowK = H * DK * 2;
+  int vofs[2][NKP];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) vofs[e][p] = (16 * (b0 + e) + c) * rowK + 64 * p + 16 * g;
+
+  struct Set {
+    u32x4 k[2][NKP], q[2][NKP];
+    float a, b;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = n * 64;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        st[s].k[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofs[e][p], c0 * rowK, 0));
+        st[s].q[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofs[e][p], c0 * rowK, 0));
+      }
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;  // register set == stage buffer == n & 1
+    const Set& S = st[s];
+    __bf16* const R = sb + s * Cf::szBuf;
+    // K and Q rows of both blocks, for the consumers
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
+        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
+      }
+    gate_scan(S.a, S.b, n * 64, T, l, PGT);
+    // accumulator [s][r]: s from the A operand (column block), r from the B
+    // operand (row block)
+    f32x4 Gd = zero4(), Go = zero4(), P0 = zero4(), P1 = zero4(), Po = zero4();
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      Gd = mma32(S.k[0][p], S.k[0][p], Gd);
+      P0 = mma32(S.k[0][p], S.q[0][p], P0);
+      Go = mma32(S.k[0][p], S.k[1][p], Go);
+      Po = mma32(S.k[0][p], S.q[1][p], Po);
+      P1 = mma32(S.k[1][p], S.q[1][p], P1);
+    }
+    offdiag_tiles<DK>(Go, Po, PGT, b0 + 1, b0, g, c, R);
+    const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
+    diag_p_tile<DK>(P0, gm0, b0, g, c, R);
+    diag_p_tile<DK>(P1, gm1, b0 + 1, g, c, R);
+    diag_inverse<DK>(Gd, gm0, PGT, DS, b0, g, c, R + Cf::oTP + b0 * Cf::szTile);
+  };
+  producer_loop(x.nchunks, load, process);
+}
+
+// Waves 4 and 5: row block i = 2 / 3 below the first two column blocks, tiles
+// (i, 0) and (i, 1), and the inverse of diagonal block 1 / 3.
+template <int DK>
+__device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, int l) {
+  using Cf = Cfg<DK>;
+  constexpr int NKP = Cf::NKP;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
+  float* const PGT = sf + Cf::fPGT + i * Cf::szPGT;  // tables 2 and 3
+  float* const DS = sf + Cf::fDS + i * Cf::szDS;
+  const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
+  const int id = i == 2 ? 1 : 3;  // diagonal block inverted here
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const uint32_t spanK = (uint32_t)((size_t)T * H * DK * 2 - (size_t)x.h * DK * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
+  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
+  const int rowK = H * DK * 2;
+  int vof0[NKP], vof1[NKP], vofi[NKP];
+#pragma unroll
+  for (int p = 0; p < NKP; ++p) {
+    vof0[p] = c * rowK + 64 * p + 16 * g;
+    vof1[p] = (16 + c) * rowK + 64 * p + 16 * g;
+    vofi[p] = (16 * i + c) * rowK + 64 * p + 16 * g;
+  }
+  struct Set {
+    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
+    float a, b;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = n * 64;
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      st[s].k0[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof0[p], c0 * rowK, 0));
+      st[s].k1[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof1[p], c0 * rowK, 0));
+      st[s].ki[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofi[p], c0 * rowK, 0));
+      st[s].qi[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofi[p], c0 * rowK, 0));
+    }
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    const Set& S = st[s];
+    __bf16* const R = sb + s * Cf::szBuf;
+    gate_scan(S.a, S.b, n * 64, T, l, PGT);
+    f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4(), Gd = zero4();
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      G0 = mma32(S.k0[p], S.ki[p], G0);
+      P0 = mma32(S.k0[p], S.qi[p], P0);
+      G1 = mma32(S.k1[p], S.ki[p], G1);
+      P1 = mma32(S.k1[p], S.qi[p], P1);
+      const u32x4 kd = id == 1 ? S.k1[p] : S.ki[p];  // uniform choice
+      Gd = mma32(kd, kd, Gd);
+    }
+    offdiag_tiles<DK>(G0, P0, PGT, i, 0, g, c, R);
+    offdiag_tiles<DK>(G1, P1, PGT, i, 1, g, c, R);
+    diag_inverse<DK>(Gd, diag_gamma(PGT, id, g, c), PGT, DS, id, g, c, R + Cf::oTP + id * Cf::szTile);
+  };
+  producer_loop(x.nchunks, load, process);
+}
+
+// Wave 6: the 64 x 32 V tile of the chunk, and gamma, lambda and gamma_C.
+template <int DK>
+__device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
+  using Cf = Cfg<DK>;
+  constexpr int LDV = Cf::LDV;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
+  const int H = x.H, T = x.T, DV = x.DV;
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(x.vg + tokbase * DV + x.dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, (uint32_t)(((size_t)T * H - x.h) * 4));
+  const int rowV = H * DV * 2;
+  int vof[4], lof[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
+    vof[u] = row * rowV + cu * 16;
+    lof[u] = row * LDV + cu * 8;
+  }
+  struct Set {
+    u32x4 v[4];
+    float a;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = n * 64;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    __bf16* const R = sb + s * Cf::szBuf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
+    const float a = (n * 64 + l < T) ? st[s].a : 1.f;
+    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
+    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
+    float* G = sf + Cf::fGate + s * Cf::szGate;
+    G[l] = __builtin_amdgcn_exp2f(xg);
+    G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
+    if (l == 63) G[128] = __builtin_amdgcn_exp2f(gC);
+  };
+  producer_loop(x.nchunks, load, process);
+}
+
+// ---------------------------------------------------------------- consumers
+// A consumer wave owns value columns 16 NT w .. 16 NT (w + 1) - 1 of the
+// workgroup's slice, as NT 16-column tiles t.  The state lives in MFMA
+// accumulators: S[t][d] holds rows 16d + 4g + j of column 16t + c.
+template <int DK>
+struct Consumer {
+  using Cf = Cfg<DK>;
+  static constexpr int NDT = Cf::NDT, NKP = Cf::NKP, LDK = Cf::LDK, LDV = Cf::LDV, LD16 = Cf::LD16, NT = Cf::NT;
+  f32x4 S[NT][NDT];
+  int g, c, w, rowO, vofO, offRow, offTrK, offTrV, offT16;
+  __amdgpu_buffer_rsrc_t ro;
+
+  __device__ __forceinline__ void init(const Ctx& x, int w_, int l) {
+    w = w_;
+    g = l >> 4;
+    c = l & 15;
+    const int H = x.H, T = x.T, DV = x.DV;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = x.dv0 + 16 * NT * w + 16 * t + c;
+#pragma unroll
+      for (int d = 0; d < NDT; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          S[t][d][j] = x.S0g ? x.S0g[((size_t)x.chain * DK + 16 * d + 4 * g + j) * DV + col] : 0.f;
+    }
+    // Output: lane (g, c) writes token c of each 16-token block, value columns
+    // 16 NT w + 16t + 4g .. + 3 (one 8-byte store).
+    const size_t obase = ((size_t)x.b * T * H + x.h) * DV + x.dv0;
+    ro = make_rsrc(x.outg + obase, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
+    rowO = H * DV * 2;
+    vofO = c * rowO + (16 * NT * w + 4 * g) * 2;
+    offRow = c * LDK + 4 * g;                                       // row c, k sub-block 4g
+    offTrK = (4 * g + (c >> 2)) * LDK + 4 * (c & 3);                // transposed K reads
+    offTrV = (4 * g + (c >> 2)) * LDV + 16 * NT * w + 4 * (c & 3);  // transposed V reads
+    offT16 = c * LD16 + 4 * g;                                      // 16x16 tiles
+  }
+
+  // Chunk n from stage buffer R; G holds gamma (G[0..63]) and lambda
+  // (G[64..127]) per token, gC = gamma_C.
+  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
+    auto tile = [&](int o) { return ld4(R + o + offT16); };
+    // ---- Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S), block rows in order
+    u32x2 kr[4][NKP][2], vv[4][NT], NG[6], TP[4];
+    f32x4 gg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const __bf16* pr = R + Cf::oK + 16 * i * LDK + 32 * p + offRow;
+        kr[i][p][0] = ld4(pr);
+        kr[i][p][1] = ld4(pr + 16);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vv[i][t] = ld4_tr(R + Cf::oV + 16 * i * LDV + 16 * t + offTrV);
+      gg[i] = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
+      TP[i] = tile(Cf::oTP + i * Cf::szTile);
+    }
+#pragma unroll
+    for (int e = 0; e < 6; ++e) NG[e] = tile(Cf::oNG + e * Cf::szTile);
+    issue_fence();
+    u32x2 sfr[NT][NDT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) sfr[t][d] = cvt4(S[t][d]);
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[i][t] = zero4();
+#pragma unroll
+        for (int p = 0; p < NKP; ++p)
+          acc[i][t] = mma2(kr[i][p][0], kr[i][p][1], sfr[t][2 * p], sfr[t][2 * p + 1], acc[i][t]);
+      }
+    // operands of the state update, in flight during the substitution
+    u32x2 kt[NDT][4];
+    f32x4 lm[4];
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kt[d][i] = ld4_tr(R + Cf::oK + 16 * i * LDK + 16 * d + offTrK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lm[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
+    const float gC = G[gCoff];
+    issue_fence();
+    u32x2 Xf[4][NT], XL[4][NT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 y;
+        const u32x2 v = vv[i][t];
+        y[0] = lo_f(v[0]) - gg[i][0] * acc[i][t][0];
+        y[1] = hi_f(v[0]) - gg[i][1] * acc[i][t][1];
+        y[2] = lo_f(v[1]) - gg[i][2] * acc[i][t][2];
+        y[3] = hi_f(v[1]) - gg[i][3] * acc[i][t][3];
+        // y -= sum_{j < i} Gt_ij Ut_j   (the tiles hold -Gt)
+        if (i == 1) y = mma1(NG[stri(1, 0)], Xf[0][t], y);
+        if (i == 2) y = mma2(NG[stri(2, 0)], NG[stri(2, 1)], Xf[0][t], Xf[1][t], y);
+        if (i == 3) {
+          y = mma2(NG[stri(3, 0)], NG[stri(3, 1)], Xf[0][t], Xf[1][t], y);
+          y = mma2(NG[stri(3, 2)], z4(), Xf[2][t], z4(), y);
+        }
+        const f32x4 X = mma1(TP[i], cvt4(y), zero4());
+        Xf[i][t] = cvt4(X);
+        f32x4 xl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xl[j] = X[j] * lm[i][j];
+        XL[i][t] = cvt4(xl);
+      }
+    // operands of the output, in flight during the state update
+    u32x2 qr[4][NKP][2], Pm[10];
+    float gm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
+        qr[i][p][0] = ld4(pr);
+        qr[i][p][1] = ld4(pr + 16);
+      }
+      gm[i] = G[16 * i + c];  // gamma of token 16i + c
+    }
+#pragma unroll
+    for (int e = 0; e < 10; ++e) Pm[e] = tile(Cf::oP + e * Cf::szTile);
+    issue_fence();
+    // S <- gamma_C S + K^T (lambda * Ut)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) {
+        f32x4 sd = S[t][d];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sd[j] *= gC;
+        sd = mma2(kt[d][0], kt[d][1], XL[0][t], XL[1][t], sd);
+        sd = mma2(kt[d][2], kt[d][3], XL[2][t], XL[3][t], sd);
+        S[t][d] = sd;
+      }
+    // ---- output, computed transposed so each lane holds four consecutive
+    // value columns of one token:
+    //   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{j <= i} Ut_j^T P_ij^T.
+    const int c0 = n * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 o = zero4();
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) o = mma2(sfr[t][2 * p], sfr[t][2 * p + 1], qr[i][p][0], qr[i][p][1], o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] *= gm[i];
+        if (i == 0) o = mma1(Xf[0][t], Pm[tri(0, 0)], o);
+        if (i == 1) o = mma2(Xf[0][t], Xf[1][t], Pm[tri(1, 0)], Pm[tri(1, 1)], o);
+        if (i == 2) {
+          o = mma2(Xf[0][t], Xf[1][t], Pm[tri(2, 0)], Pm[tri(2, 1)], o);
+          o = mma2(Xf[2][t], z4(), Pm[tri(2, 2)], z4(), o);
+        }
+        if (i == 3) {
+          o = mma2(Xf[0][t], Xf[1][t], Pm[tri(3, 0)], Pm[tri(3, 1)], o);
+          o = mma2(Xf[2][t], Xf[3][t], Pm[tri(3, 2)], Pm[tri(3, 3)], o);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(cvt4(o), ro, vofO + 32 * t, (c0 + 16 * i) * rowO, 0);
+      }
+  }
+
+  __device__ __forceinline__ void finish(const Ctx& x) {
+    if (!x.Sfg) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = x.dv0 + 16 * NT * w + 16 * t + c;
+#pragma unroll
+      for (int d = 0; d < NDT; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x.Sfg[((size_t)x.chain * DK + 16 * d + 4 * g + j) * x.DV + col] = S[t][d][j];
+    }
+  }
+};
+
+// Waves 0 and 1 of the two-stage kernel.
+template <int DK>
+__device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l) {
+  using Cf = Cfg<DK>;
+  const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
+  const float* const sf = reinterpret_cast<const float*>(smem + Cf::fBase);
+  Consumer<DK> cs;
+  cs.init(x, w, l);
+  stage_barrier();  // prologue: chunk 0 staged
+  auto body = [&](auto bufc, int n) {
+    constexpr int BUF = decltype(bufc)::value;
+    cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
+    stage_barrier();
+  };
+  for (int n = 0; n < x.nchunks; n += 2) {
+    body(ic<0>{}, n);
+    if (n + 1 < x.nchunks) body(ic<1>{}, n + 1);
+  }
+  cs.finish(x);
+}
+
+template <int DK>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                                                             const __bf16* __restrict__ vg,
                                                             const float* __restrict__ alpha,
                                                             const float* __restrict__ beta, const float* S0g,
                                                             __bf16* __restrict__ outg, float* Sfg, int T, int H,
                                                             int DV, int nslices) {
-  using Cf = Cfg<DK>;
-  constexpr int NDT = Cf::NDT, NKP = Cf::NKP, LDK = Cf::LDK, LDV = Cf::LDV, LD16 = Cf::LD16;
-  __shared__ __attribute__((aligned(16))) char smem[Cf::bytes];
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
-
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<DK>::bytes];
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // keep neighbours on one XCD
   const int slice = bid % nslices, chain = bid / nslices;
-  const int b = chain / H, h = chain % H, dv0 = slice * Cf::NV;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int nchunks = (T + 63) >> 6;
+  Ctx x;
+  x.qg = qg;
+  x.kg = kg;
+  x.vg = vg;
+  x.alpha = alpha;
+  x.beta = beta;
+  x.S0g = S0g;
+  x.outg = outg;
+  x.Sfg = Sfg;
+  x.T = T;
+  x.H = H;
+  x.DV = DV;
+  x.b = chain / H;
+  x.h = chain % H;
+  x.chain = chain;
+  x.dv0 = slice * Cfg<DK>::NV;
+  x.nchunks = (T + 63) >> 6;
+  // The wave index is made explicitly uniform: role branches must be scalar
+  // branches, never exec-masked ones, because matrix-core instructions do not
+  // honour the exec mask.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (w < 2)
+    consumer<DK>(x, smem, w, l);
+  else if (w < 4)
+    producer_rows<DK>(x, smem, 2 * (w - 2), l);
+  else if (w < 6)
+    producer_lower<DK>(x, smem, w - 2, l);
+  else
+    producer_v<DK>(x, smem, l);
+}
 
-  if (w >= 4) {
-    // ======================================================== PRODUCERS
-    const int pt = tid - 256, pw = w - 4;
-    const size_t tokbase = (size_t)b * T * H + h;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + tokbase * DK, (uint32_t)((size_t)T * H * DK * 2 - (size_t)h * DK * 2));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + tokbase * DK, (uint32_t)((size_t)T * H * DK * 2 - (size_t)h * DK * 2));
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(vg + tokbase * DV + dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)h * DV + dv0) * 2));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(alpha + tokbase, (uint32_t)(((size_t)T * H - h) * 4));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + tokbase, (uint32_t)(((size_t)T * H - h) * 4));
-    const int rowK = H * DK * 2, rowV = H * DV * 2;  // bytes between consecutive tokens
-    uint4 pk[Cf::NUK], pq[Cf::NUK], pv[Cf::NUV];
-    float pa = 1.f, pb = 0.f;
-    int vofK[Cf::NUK], vofV[Cf::NUV], ldsK[Cf::NUK], ldsV[Cf::NUV];
-#pragma unroll
-    for (int u = 0; u < Cf::NUK; ++u) {
-      const int unit = pt + 256 * u, row = unit / Cf::UPRK, cu = unit % Cf::UPRK;
-      vofK[u] = row * rowK + cu * 16;
-      ldsK[u] = row * LDK + cu * 8;
-    }
-#pragma unroll
-    for (int u = 0; u < Cf::NUV; ++u) {
-      const int unit = pt + 256 * u, row = unit / Cf::UPRV, cu = unit % Cf::UPRV;
-      vofV[u] = row * rowV + cu * 16;
-      ldsV[u] = row * LDV + cu * 8;
-    }
-    auto prefetch = [&](int n) {
-      const int c0 = n * 64;
-#pragma unroll
-      for (int u = 0; u < Cf::NUK; ++u) {
-        pk[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofK[u], c0 * rowK, 0));
-        pq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofK[u], c0 * rowK, 0));
-      }
-#pragma unroll
-      for (int u = 0; u < Cf::NUV; ++u)
-        pv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vofV[u], c0 * rowV, 0));
-      pa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-      pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
-    };
+}  // namespace pipe
 
-    // Stage chunk n (prefetched registers) into raw buffer BUF, run the gate
-    // scan, publish gates for the consumers and decay factors for the Gram.
-    auto stage = [&](auto bufc, int n) {
-      constexpr int BUF = decltype(bufc)::value;
-      __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
-#pragma unroll
-      for (int u = 0; u < Cf::NUK; ++u) {
-        *reinterpret_cast<uint4*>(R + Cf::oRK + ldsK[u]) = pk[u];
-        *reinterpret_cast<uint4*>(R + Cf::oRQ + ldsK[u]) = pq[u];
-      }
-#pragma unroll
-      for (int u = 0; u < Cf::NUV; ++u) *reinterpret_cast<uint4*>(R + Cf::oRV + ldsV[u]) = pv[u];
-      if (pw == 0) {
-        const float a = (n * 64 + l < T) ? pa : 1.f;  // padding token: alpha = 1 (beta reads as 0)
-        const float x = wave_prefix_sum(__builtin_amdgcn_logf(a));
-        const float g63 = __shfl(x, 63, 64);
-        const float gblk = __shfl(x, l & ~15, 64);
-        const float gam = __builtin_amdgcn_exp2f(x);
-        float* G = sf + Cf::fGate + BUF * Cf::szGate;
-        G[l] = pb;
-        G[64 + l] = pb * gam;
-        G[128 + l] = gam;
-        G[192 + l] = __builtin_amdgcn_exp2f(g63 - x);
-        if (l == 63) G[256] = gam;
-        float* PG = sf + Cf::fPG;
-        PG[l] = x;
-        PG[64 + l] = pb;
-        PG[128 + l] = __builtin_amdgcn_exp2f(x - gblk);
-#pragma unroll
-        for (int i = 1; i < 4; ++i) {
-          const float gi = __shfl(x, 16 * i, 64);
-          PG[128 + 64 * i + l] = __builtin_amdgcn_exp2f(l < 16 * i ? gi - x : -INFINITY);
-        }
-      }
-    };
+// ============================================================================
+// Three-stage variant (dk = 64).  Per step k of the loop (one barrier each):
+//   Gram waves 2..5 and the V wave 6 build chunk k + 2 (K/Q/V rows, decayed
+//   Gram tiles, gates, and the fp32 rows of the four diagonal blocks of A);
+//   the inverse wave 7 turns chunk k + 1's diagonal blocks into T_ii diag(beta_i);
+//   the consumer waves 0, 1 run chunk k.
+// Stage buffers rotate over three slots (chunk m uses slot m % 3); the
+// diagonal-block rows over two (m & 1).  Taking the inverses out of the Gram
+// waves removes the longest dependency chain from them, and the inverse wave
+// does all four blocks at once in a row-per-lane layout that skips the zero
+// upper triangle (120 fused DPP FMAs per chunk instead of 240).
+namespace pipe3 {
+using namespace pipe;
 
-    float* const DS = sf + Cf::fDS + pw * Cf::szDS;
-    // Operands of one Gram tile: K rows of the column block (A operand) and the
-    // K and Q rows of the row block (B operands), NKP k-pairs each.
-    struct TileOps {
-      bf16x4 a[NKP][2], k[NKP][2], q[NKP][2];
-    };
-    auto load_tile = [&](const __bf16* R, int ti, int tj, TileOps& o) {
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const __bf16* ra_ = R + Cf::oRK + (16 * tj + c) * LDK + 32 * p + 4 * g;
-        const __bf16* rk_ = R + Cf::oRK + (16 * ti + c) * LDK + 32 * p + 4 * g;
-        const __bf16* rq_ = R + Cf::oRQ + (16 * ti + c) * LDK + 32 * p + 4 * g;
-        o.a[p][0] = ld4(ra_);
-        o.a[p][1] = ld4(ra_ + 16);
-        o.k[p][0] = ld4(rk_);
-        o.k[p][1] = ld4(rk_ + 16);
-        o.q[p][0] = ld4(rq_);
-        o.q[p][1] = ld4(rq_ + 16);
-      }
-    };
-    // accumulators [s][r] = k_s . k_r and k_s . q_r of one tile
-    auto tile_mma = [&](const TileOps& o, f32x4& aG, f32x4& aP) {
-      aG = zero4();
-      aP = zero4();
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        aG = mma2(o.a[p][0], o.a[p][1], o.k[p][0], o.k[p][1], aG);
-        aP = mma2(o.a[p][0], o.a[p][1], o.q[p][0], o.q[p][1], aP);
-      }
-    };
-    auto store_tile = [&](__bf16* Hd, int t, const f32x4& va, const f32x4& vp) {
-      *reinterpret_cast<bf16x4*>(Hd + Cf::oHA + t * Cf::szTile + c * LD16 + 4 * g) = cvt4(va);
-      *reinterpret_cast<bf16x4*>(Hd + Cf::oHP + t * Cf::szTile + c * LD16 + 4 * g) = cvt4(vp);
-    };
+struct Cfg3 {
+  using B = Cfg<64>;
+  static constexpr int NBUF = 3;
+  static constexpr int fBase = ((NBUF * B::szBuf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
+  // fp32 region (floats): per stage slot gamma[64], lambda[64], beta[64],
+  // gamma_C (padded); two slots of diagonal-block rows (4 blocks x 16 rows,
+  // row stride 20); the private gate tables of the four Gram waves; the 16 x 16
+  // identity (row stride 20).
+  static constexpr int szGate = 196, fGate = 0;
+  static constexpr int szDS = 4 * 16 * 20, fDS = NBUF * szGate;
+  static constexpr int fPGT = fDS + 2 * szDS, szPGT = 128;
+  static constexpr int fEye = fPGT + 4 * szPGT;
+  static constexpr int nF = fEye + 16 * 20;
+  static constexpr int bytes = fBase + nF * 4;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fPGT * 4) % 16 == 0 && (fEye * 4) % 16 == 0,
+                "fp32 tables must be 16-byte aligned");
+};
+constexpr int kThreads3 = 8 * 64;
 
-    // (I + A_pw,pw)^{-1} by forward substitution.  Lane (q = l & 3, cc = l >> 2)
-    // owns column cc and rows 4k + q; once row s is final its value is
-    // broadcast inside the quad and subtracted from every later row.
-    auto solve = [&](__bf16* Hd) {
-      __bf16* Td = Hd + Cf::oHT + pw * Cf::szTile;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int q = l & 3, cc = l >> 2;
-      float a[4][16], t[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(DS + (4 * k + q) * 20 + 4 * s4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) a[k][4 * s4 + j] = v[j];
-        }
-        t[k] = (4 * k + q == cc) ? 1.f : 0.f;
-      }
-      auto step = [&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        const float ts = bcast_quad<s & 3>(t[s >> 2]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (4 * k + 3 > s) t[k] -= a[k][s] * ts;  // a[k][s] = 0 unless row 4k+q > s
-      };
-      step(ic<0>{}); step(ic<1>{}); step(ic<2>{}); step(ic<3>{}); step(ic<4>{});
-      step(ic<5>{}); step(ic<6>{}); step(ic<7>{}); step(ic<8>{}); step(ic<9>{});
-      step(ic<10>{}); step(ic<11>{}); step(ic<12>{}); step(ic<13>{}); step(ic<14>{});
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Td[(4 * k + q) * LD16 + cc] = (__bf16)t[k];
-    };
-
-    // Tiles of this wave: its diagonal tile (pw, pw) and two tiles below the
-    // diagonal.  The six sub-diagonal tiles are split two per wave over waves
-    // 0..2; wave 3 recomputes wave 2's pair and does not store it, so every
-    // wave runs the same straight-line code.
-    const int o1i = pw == 0 ? 1 : pw == 1 ? 2 : 3, o1j = pw == 0 ? 0 : pw == 1 ? 1 : 2;
-    const int o2i = pw == 0 ? 2 : 3, o2j = pw == 0 ? 0 : pw == 1 ? 0 : 1;
-    const bool storeOff = pw < 3;
-    auto gram = [&](auto bufc) {
-      constexpr int BUF = decltype(bufc)::value;
-      const __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
-      __bf16* Hd = sb + Cf::oHand0 + BUF * Cf::szHand;
-      const float* PG = sf + Cf::fPG;
-      TileOps od, o1, o2;
-      load_tile(R, pw, pw, od);
-      load_tile(R, o1i, o1j, o1);
-      load_tile(R, o2i, o2j, o2);
-      // decay factors: diagonal tile (g2 and beta of row r, g2 of columns s) and
-      // the row / column factors of the two sub-diagonal tiles
-      const int rd = 16 * pw + c, r1 = 16 * o1i + c, r2 = 16 * o2i + c;
-      const float gr = PG[rd], br = PG[64 + rd];
-      const f32x4 gs = *reinterpret_cast<const f32x4*>(PG + 16 * pw + 4 * g);
-      const float rf1 = PG[128 + r1], nb1 = -PG[64 + r1] * rf1;
-      const float rf2 = PG[128 + r2], nb2 = -PG[64 + r2] * rf2;
-      const f32x4 cf1 = *reinterpret_cast<const f32x4*>(PG + 128 + 64 * o1i + 16 * o1j + 4 * g);
-      const f32x4 cf2 = *reinterpret_cast<const f32x4*>(PG + 128 + 64 * o2i + 16 * o2j + 4 * g);
-      issue_fence();
-      f32x4 gD, pD, g1, p1, g2, p2;
-      tile_mma(od, gD, pD);
-      tile_mma(o1, g1, p1);
-      tile_mma(o2, g2, p2);
-      // diagonal tile: per-element decay, masked before the exponential
-      f32x4 ad, va, vp;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = 16 * pw + 4 * g + j;
-        const float gm = __builtin_amdgcn_exp2f(rd >= s ? gr - gs[j] : -INFINITY);
-        ad[j] = rd > s ? br * gm * gD[j] : 0.f;
-        va[j] = -ad[j];
-        vp[j] = gm * pD[j];
-      }
-      *reinterpret_cast<f32x4*>(DS + c * 20 + 4 * g) = ad;
-      store_tile(Hd, tri(pw, pw), va, vp);
-      // sub-diagonal tiles: decay = row factor x column factor
-      f32x4 va1, vp1, va2, vp2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        va1[j] = g1[j] * (nb1 * cf1[j]);
-        vp1[j] = p1[j] * (rf1 * cf1[j]);
-        va2[j] = g2[j] * (nb2 * cf2[j]);
-        vp2[j] = p2[j] * (rf2 * cf2[j]);
-      }
-      if (storeOff) {
-        store_tile(Hd, tri(o1i, o1j), va1, vp1);
-        store_tile(Hd, tri(o2i, o2j), va2, vp2);
-      }
-      solve(Hd);
-    };
-
-    // prologue: chunk 0 staged and solved before the consumers start
-    if (nchunks > 0) {
-      prefetch(0);
-      stage(ic<0>{}, 0);
-      if (nchunks > 1) prefetch(1);
-    }
-    phase_barrier();
-    if (nchunks > 0) gram(ic<0>{});
-    phase_barrier();
-    // iteration n: stage / solve chunk n+1 into buffer (n+1) & 1
-    // iteration n: stage / solve chunk n+1 into buffer (n+1) & 1
-    auto iter = [&](auto nbufc, int n) {
-      if (n + 1 < nchunks) {
-        stage(nbufc, n + 1);
-        if (n + 2 < nchunks) prefetch(n + 2);
-      }
-      phase_barrier();
-      if (n + 1 < nchunks) gram(nbufc);
-      phase_barrier();
-    };
-    for (int n = 0; n < nchunks; n += 2) {
-      iter(ic<1>{}, n);
-      if (n + 1 < nchunks) iter(ic<0>{}, n + 1);
-    }
-  } else {
-    // ======================================================== CONSUMERS
-    f32x4 S[NDT];
-    const int col = dv0 + 16 * w + c;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        S[d][j] = S0g ? S0g[((size_t)chain * DK + 16 * d + 4 * g + j) * DV + col] : 0.f;
-
-    // Output: lane (g, c) of wave w writes token c of each 16-token block,
-    // value columns 16w + 4g .. 16w + 4g + 3 (one 8-byte store).
-    const size_t obase = ((size_t)b * T * H + h) * DV + dv0;
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(outg + obase, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)h * DV + dv0) * 2));
-    const int rowO = H * DV * 2;
-    const int vofO = c * rowO + (16 * w + 4 * g) * 2;
-    // per-lane LDS element offsets (relative to a raw / hand-off buffer)
-    const int offRow = c * LDK + 4 * g;                                  // row c, k sub-block 4g
-    const int offTrK = (4 * g + (c >> 2)) * LDK + 4 * (c & 3);           // transposed K reads
-    const int offTrV = (4 * g + (c >> 2)) * LDV + 16 * w + 4 * (c & 3);  // transposed V reads
-    const int offT16 = c * LD16 + 4 * g;                                 // 16x16 hand-off tiles
-
-    auto body = [&](auto bufc, int n) {
-      constexpr int BUF = decltype(bufc)::value;
-      const __bf16* R = sb + Cf::oRaw0 + BUF * Cf::szRaw;
-      const __bf16* Hd = sb + Cf::oHand0 + BUF * Cf::szHand;
-      const float* G = sf + Cf::fGate + BUF * Cf::szGate;
-      auto Atile = [&](int i, int j) { return ld4(Hd + Cf::oHA + tri(i, j) * Cf::szTile + offT16); };
-      auto Ptile = [&](int i, int j) { return ld4(Hd + Cf::oHP + tri(i, j) * Cf::szTile + offT16); };
-      // ---- phase 1: Ut = (I + A)^{-1}(diag(beta) V - diag(beta gamma) K S); state update.
-      // Operand loads for the whole phase are issued first.
-      bf16x4 kr[4][NKP][2], vv[4], Am[6], Tm[4];
-      f32x4 bt[4], bg[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-          const __bf16* pr = R + Cf::oRK + 16 * i * LDK + 32 * p + offRow;
-          kr[i][p][0] = ld4(pr);
-          kr[i][p][1] = ld4(pr + 16);
-        }
-        vv[i] = ld4_tr(R + Cf::oRV + 16 * i * LDV + offTrV);
-        bt[i] = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
-        bg[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
-        Tm[i] = ld4(Hd + Cf::oHT + i * Cf::szTile + offT16);
-      }
-      Am[0] = Atile(1, 0); Am[1] = Atile(2, 0); Am[2] = Atile(2, 1);
-      Am[3] = Atile(3, 0); Am[4] = Atile(3, 1); Am[5] = Atile(3, 2);
-      issue_fence();
-      bf16x4 sfr[NDT];
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) sfr[d] = cvt4(S[d]);
-      f32x4 acc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = zero4();
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) acc[i] = mma2(kr[i][p][0], kr[i][p][1], sfr[2 * p], sfr[2 * p + 1], acc[i]);
-      }
-      // operands of the state update, in flight during the substitution
-      bf16x4 kt[NDT][4];
-      f32x4 lm[4];
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) {
-        const __bf16* pk = R + Cf::oRK + 16 * d + offTrK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kt[d][i] = ld4_tr(pk + 16 * i * LDK);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lm[i] = *reinterpret_cast<const f32x4*>(G + 192 + 16 * i + 4 * g);
-      const float gC = G[256];
-      issue_fence();
-      f32x4 X[4];
-      bf16x4 Xf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 y;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = bt[i][j] * (float)vv[i][j] - bg[i][j] * acc[i][j];
-        // y -= sum_{i' < i} A_{i i'} X_{i'}   (the hand-off holds -A)
-        if (i == 1) y = mma1(Am[0], Xf[0], y);
-        if (i == 2) y = mma2(Am[1], Am[2], Xf[0], Xf[1], y);
-        if (i == 3) {
-          y = mma2(Am[3], Am[4], Xf[0], Xf[1], y);
-          y = mma2(Am[5], z4(), Xf[2], z4(), y);
-        }
-        X[i] = mma1(Tm[i], cvt4(y), zero4());
-        Xf[i] = cvt4(X[i]);
-      }
-      // S <- gamma_C S + K^T diag(lambda) Ut
-      bf16x4 XL[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 t;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = X[i][j] * lm[i][j];
-        XL[i] = cvt4(t);
-      }
-      // operands of the output, in flight during the state update
-      bf16x4 qr[4][NKP][2], Pm[10];
-      float gm[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-          const __bf16* pr = R + Cf::oRQ + 16 * i * LDK + 32 * p + offRow;
-          qr[i][p][0] = ld4(pr);
-          qr[i][p][1] = ld4(pr + 16);
-        }
-        gm[i] = G[128 + 16 * i + c];  // gamma of token 16i + c
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j <= i; ++j) Pm[tri(i, j)] = Ptile(i, j);
-      issue_fence();
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) {
-        f32x4 sd = S[d];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sd[j] *= gC;
-        sd = mma2(kt[d][0], kt[d][1], XL[0], XL[1], sd);
-        sd = mma2(kt[d][2], kt[d][3], XL[2], XL[3], sd);
-        S[d] = sd;
-      }
-      reader_barrier();
-      // ---- phase 2: output, computed transposed so each lane holds four
-      // consecutive value columns of one token:
-      //   O_i^T = S^T Q_i^T diag(gamma_i) + sum_{i' <= i} Ut_{i'}^T P_{i i'}^T.
-      // S^T and Ut^T in A-operand layout are exactly the accumulator layouts of
-      // S and Ut; Q_i^T and P^T in B-operand layout are row-major reads.
-      const int c0 = n * 64;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 o = zero4();
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) o = mma2(sfr[2 * p], sfr[2 * p + 1], qr[i][p][0], qr[i][p][1], o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= gm[i];
-        if (i == 0) o = mma1(Xf[0], Pm[tri(0, 0)], o);
-        if (i == 1) o = mma2(Xf[0], Xf[1], Pm[tri(1, 0)], Pm[tri(1, 1)], o);
-        if (i == 2) {
-          o = mma2(Xf[0], Xf[1], Pm[tri(2, 0)], Pm[tri(2, 1)], o);
-          o = mma2(Xf[2], z4(), Pm[tri(2, 2)], z4(), o);
-        }
-        if (i == 3) {
-          o = mma2(Xf[0], Xf[1], Pm[tri(3, 0)], Pm[tri(3, 1)], o);
-          o = mma2(Xf[2], Xf[3], Pm[tri(3, 2)], Pm[tri(3, 3)], o);
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(o)), ro, vofO, (c0 + 16 * i) * rowO, 0);
-      }
-      phase_barrier();
-    };
-
-    phase_barrier();  // prologue: chunk 0 staged
-    phase_barrier();  // prologue: chunk 0 Gram and diagonal inverses ready
-    for (int n = 0; n < nchunks; n += 2) {
-      body(ic<0>{}, n);
-      if (n + 1 < nchunks) body(ic<1>{}, n + 1);
-    }
-    if (Sfg) {
-#pragma unroll
-      for (int d = 0; d < NDT; ++d)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Sfg[((size_t)chain * DK + 16 * d + 4 * g + j) * DV + col] = S[d][j];
+// Runs step(parity, k) for k = -2 .. nch - 1, each followed by the barrier.
+// Every wave executes exactly nch + 2 barriers.
+template <class Step>
+__device__ __forceinline__ void run_steps(int nch, Step&& step) {
+  for (int k = -2; k < nch; k += 2) {
+    step(ic<0>{}, k);
+    stage_barrier();
+    if (k + 1 < nch) {
+      step(ic<1>{}, k + 1);
+      stage_barrier();
     }
   }
 }
 
-}  // namespace pipe
+// Fp32 rows of -A for a diagonal block: lane (g, c) writes -A[c][4g .. 4g + 3].
+__device__ __forceinline__ void diag_rows(const f32x4& G, const f32x4& gm, const float* PGT, int i, int g, int c,
+                                          float* dst) {
+  const float br = PGT[64 + 16 * i + c];
+  f32x4 na;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) na[j] = c > 4 * g + j ? -br * gm[j] * G[j] : 0.f;
+  *reinterpret_cast<f32x4*>(dst + c * 20 + 4 * g) = na;
+}
+
+// Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).
+__device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int l) {
+  using Cf = Cfg<64>;
+  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
+  float* const PGT = sf + Cfg3::fPGT + (b0 >> 1) * Cfg3::szPGT;
+  const int g = l >> 4, c = l & 15, H = x.H, T = x.T, nch = x.nchunks;
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const uint32_t spanK = (uint32_t)((size_t)T * H * 64 * 2 - (size_t)x.h * 64 * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * 64, spanK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * 64, spanK);
+  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
+  const int rowK = H * 64 * 2;
+  int vofs[2][NKP];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) vofs[e][p] = (16 * (b0 + e) + c) * rowK + 64 * p + 16 * g;
+  struct Set {
+    u32x4 k[2][NKP], q[2][NKP];
+    float a, b;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = m * 64;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        st[s].k[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofs[e][p], c0 * rowK, 0));
+        st[s].q[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofs[e][p], c0 * rowK, 0));
+      }
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const Set& S = st[s];
+    __bf16* const R = sb + (m % 3) * Cf::szBuf;
+    float* const D = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
+        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
+      }
+    gate_scan(S.a, S.b, m * 64, T, l, PGT);
+    f32x4 G0 = zero4(), P0 = zero4(), Go = zero4(), Po = zero4(), G1 = zero4(), P1 = zero4();
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      G0 = mma32(S.k[0][p], S.k[0][p], G0);
+      P0 = mma32(S.k[0][p], S.q[0][p], P0);
+      Go = mma32(S.k[0][p], S.k[1][p], Go);
+      Po = mma32(S.k[0][p], S.q[1][p], Po);
+      G1 = mma32(S.k[1][p], S.k[1][p], G1);
+      P1 = mma32(S.k[1][p], S.q[1][p], P1);
+    }
+    offdiag_tiles<64>(Go, Po, PGT, b0 + 1, b0, g, c, R);
+    const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
+    diag_p_tile<64>(P0, gm0, b0, g, c, R);
+    diag_p_tile<64>(P1, gm1, b0 + 1, g, c, R);
+    diag_rows(G0, gm0, PGT, b0, g, c, D + b0 * 320);
+    diag_rows(G1, gm1, PGT, b0 + 1, g, c, D + (b0 + 1) * 320);
+  };
+  if (nch > 0) load(ic<0>{}, 0);
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int par = decltype(pc)::value;  // k & 1 == (k + 2) & 1
+    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
+    issue_fence();
+    if (k + 2 < nch) process(ic<par>{}, k + 2);
+  });
+}
+
+// Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).
+__device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
+  using Cf = Cfg<64>;
+  constexpr int NKP = Cf::NKP;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
+  float* const PGT = sf + Cfg3::fPGT + i * Cfg3::szPGT;  // tables 2 and 3
+  const int g = l >> 4, c = l & 15, H = x.H, T = x.T, nch = x.nchunks;
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const uint32_t spanK = (uint32_t)((size_t)T * H * 64 * 2 - (size_t)x.h * 64 * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * 64, spanK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * 64, spanK);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, (uint32_t)(((size_t)T * H - x.h) * 4));
+  const int rowK = H * 64 * 2;
+  int vof0[NKP], vof1[NKP], vofi[NKP];
+#pragma unroll
+  for (int p = 0; p < NKP; ++p) {
+    vof0[p] = c * rowK + 64 * p + 16 * g;
+    vof1[p] = (16 + c) * rowK + 64 * p + 16 * g;
+    vofi[p] = (16 * i + c) * rowK + 64 * p + 16 * g;
+  }
+  struct Set {
+    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
+    float a;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = m * 64;
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      st[s].k0[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof0[p], c0 * rowK, 0));
+      st[s].k1[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof1[p], c0 * rowK, 0));
+      st[s].ki[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofi[p], c0 * rowK, 0));
+      st[s].qi[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofi[p], c0 * rowK, 0));
+    }
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const Set& S = st[s];
+    __bf16* const R = sb + (m % 3) * Cf::szBuf;
+    gate_scan(S.a, 0.f, m * 64, T, l, PGT);
+    f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4();
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      G0 = mma32(S.k0[p], S.ki[p], G0);
+      P0 = mma32(S.k0[p], S.qi[p], P0);
+      G1 = mma32(S.k1[p], S.ki[p], G1);
+      P1 = mma32(S.k1[p], S.qi[p], P1);
+    }
+    offdiag_tiles<64>(G0, P0, PGT, i, 0, g, c, R);
+    offdiag_tiles<64>(G1, P1, PGT, i, 1, g, c, R);
+  };
+  if (nch > 0) load(ic<0>{}, 0);
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int par = decltype(pc)::value;
+    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
+    issue_fence();
+    if (k + 2 < nch) process(ic<par>{}, k + 2);
+  });
+}
+
+// Wave 6: the 64 x 32 V tile, and gamma, lambda, beta and gamma_C per chunk.
+__device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
+  using Cf = Cfg<64>;
+  constexpr int LDV = Cf::LDV;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
+  const int H = x.H, T = x.T, DV = x.DV, nch = x.nchunks;
+  const size_t tokbase = (size_t)x.b * T * H + x.h;
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(x.vg + tokbase * DV + x.dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
+  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
+  const int rowV = H * DV * 2;
+  int vof[4], lof[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
+    vof[u] = row * rowV + cu * 16;
+    lof[u] = row * LDV + cu * 8;
+  }
+  struct Set {
+    u32x4 v[4];
+    float a, b;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const int c0 = m * 64;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
+    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
+    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
+  };
+  auto process = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const int slot = m % 3;
+    __bf16* const R = sb + slot * Cf::szBuf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
+    const float a = (m * 64 + l < T) ? st[s].a : 1.f;
+    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
+    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
+    float* G = sf + Cfg3::fGate + slot * Cfg3::szGate;
+    G[l] = __builtin_amdgcn_exp2f(xg);
+    G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
+    G[128 + l] = st[s].b;
+    if (l == 63) G[192] = __builtin_amdgcn_exp2f(gC);
+  };
+  if (nch > 0) load(ic<0>{}, 0);
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int par = decltype(pc)::value;
+    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
+    issue_fence();
+    if (k + 2 < nch) process(ic<par>{}, k + 2);
+  });
+}
+
+// One forward-substitution step for the row-per-lane inverse: columns s <= M
+// of every row get t_s += row_bcast<M>(t_s) * (-A[c][M]).
+#define GDN_ST(R, A, M) "v_fmac_f32_dpp %" #R ", %" #R ", %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"
+
+// Wave 7: T_ii diag(beta_i) for all four diagonal blocks of chunk m.  Lane
+// (b, c) owns row c of block b: t starts as row c of the identity and, once
+// row M of the block is final (after step M - 1), it is broadcast along the
+// 16-lane row and added, scaled by -A[c][M], to every row; rows with c <= M
+// have A[c][M] = 0.  Row M has no entries right of the diagonal, so step M only
+// touches columns 0..M.  Wait states: a DPP source must be written two
+// instructions earlier; step M + 1 reads column s M + 1 instructions after step
+// M wrote it, so only steps 1 and 2 need padding.
+__device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
+  using Cf = Cfg<64>;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
+  const int b = l >> 4, c = l & 15, nch = x.nchunks;
+  float* const eye = sf + Cfg3::fEye;
+  if (l < 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(eye + l * 20 + 4 * q) =
+          f32x4{l == 4 * q ? 1.f : 0.f, l == 4 * q + 1 ? 1.f : 0.f, l == 4 * q + 2 ? 1.f : 0.f,
+                l == 4 * q + 3 ? 1.f : 0.f};
+  }
+  run_steps(nch, [&](auto, int k) {
+    const int m = k + 1;
+    if (m < 0 || m >= nch) return;
+    const float* rowA = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS + b * 320 + c * 20;
+    float a[16], t[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(rowA + 4 * q);
+      const f32x4 vt = *reinterpret_cast<const f32x4*>(eye + c * 20 + 4 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[4 * q + j] = va[j];
+        t[4 * q + j] = vt[j];
+      }
+    }
+    asm volatile("s_nop 1\n"
+                 GDN_ST(0, 8, 0) "s_nop 1\n"
+                 GDN_ST(0, 9, 1) GDN_ST(1, 9, 1) "s_nop 0\n"
+                 GDN_ST(0, 10, 2) GDN_ST(1, 10, 2) GDN_ST(2, 10, 2)
+                 GDN_ST(0, 11, 3) GDN_ST(1, 11, 3) GDN_ST(2, 11, 3) GDN_ST(3, 11, 3)
+                 GDN_ST(0, 12, 4) GDN_ST(1, 12, 4) GDN_ST(2, 12, 4) GDN_ST(3, 12, 4) GDN_ST(4, 12, 4)
+                 GDN_ST(0, 13, 5) GDN_ST(1, 13, 5) GDN_ST(2, 13, 5) GDN_ST(3, 13, 5) GDN_ST(4, 13, 5)
+                 GDN_ST(5, 13, 5)
+                 GDN_ST(0, 14, 6) GDN_ST(1, 14, 6) GDN_ST(2, 14, 6) GDN_ST(3, 14, 6) GDN_ST(4, 14, 6)
+                 GDN_ST(5, 14, 6) GDN_ST(6, 14, 6)
+                 GDN_ST(0, 15, 7) GDN_ST(1, 15, 7) GDN_ST(2, 15, 7) GDN_ST(3, 15, 7) GDN_ST(4, 15, 7)
+                 GDN_ST(5, 15, 7) GDN_ST(6, 15, 7) GDN_ST(7, 15, 7)
+                 : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+    asm volatile("s_nop 1\n"
+                 GDN_ST(0, 15, 8) GDN_ST(1, 15, 8) GDN_ST(2, 15, 8) GDN_ST(3, 15, 8) GDN_ST(4, 15, 8)
+                 GDN_ST(5, 15, 8) GDN_ST(6, 15, 8) GDN_ST(7, 15, 8) GDN_ST(8, 15, 8)
+                 GDN_ST(0, 16, 9) GDN_ST(1, 16, 9) GDN_ST(2, 16, 9) GDN_ST(3, 16, 9) GDN_ST(4, 16, 9)
+                 GDN_ST(5, 16, 9) GDN_ST(6, 16, 9) GDN_ST(7, 16, 9) GDN_ST(8, 16, 9) GDN_ST(9, 16, 9)
+                 GDN_ST(0, 17, 10) GDN_ST(1, 17, 10) GDN_ST(2, 17, 10) GDN_ST(3, 17, 10) GDN_ST(4, 17, 10)
+                 GDN_ST(5, 17, 10) GDN_ST(6, 17, 10) GDN_ST(7, 17, 10) GDN_ST(8, 17, 10) GDN_ST(9, 17, 10)
+                 GDN_ST(10, 17, 10)
+                 GDN_ST(0, 18, 11) GDN_ST(1, 18, 11) GDN_ST(2, 18, 11) GDN_ST(3, 18, 11) GDN_ST(4, 18, 11)
+                 GDN_ST(5, 18, 11) GDN_ST(6, 18, 11) GDN_ST(7, 18, 11) GDN_ST(8, 18, 11) GDN_ST(9, 18, 11)
+                 GDN_ST(10, 18, 11) GDN_ST(11, 18, 11)
+                 GDN_ST(0, 19, 12) GDN_ST(1, 19, 12) GDN_ST(2, 19, 12) GDN_ST(3, 19, 12) GDN_ST(4, 19, 12)
+                 GDN_ST(5, 19, 12) GDN_ST(6, 19, 12) GDN_ST(7, 19, 12) GDN_ST(8, 19, 12) GDN_ST(9, 19, 12)
+                 GDN_ST(10, 19, 12) GDN_ST(11, 19, 12) GDN_ST(12, 19, 12)
+                 GDN_ST(0, 20, 13) GDN_ST(1, 20, 13) GDN_ST(2, 20, 13) GDN_ST(3, 20, 13) GDN_ST(4, 20, 13)
+                 GDN_ST(5, 20, 13) GDN_ST(6, 20, 13) GDN_ST(7, 20, 13) GDN_ST(8, 20, 13) GDN_ST(9, 20, 13)
+                 GDN_ST(10, 20, 13) GDN_ST(11, 20, 13) GDN_ST(12, 20, 13) GDN_ST(13, 20, 13)
+                 GDN_ST(0, 21, 14) GDN_ST(1, 21, 14) GDN_ST(2, 21, 14) GDN_ST(3, 21, 14) GDN_ST(4, 21, 14)
+                 GDN_ST(5, 21, 14) GDN_ST(6, 21, 14) GDN_ST(7, 21, 14) GDN_ST(8, 21, 14) GDN_ST(9, 21, 14)
+                 GDN_ST(10, 21, 14) GDN_ST(11, 21, 14) GDN_ST(12, 21, 14) GDN_ST(13, 21, 14) GDN_ST(14, 21, 14)
+                 : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
+                   "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14])
+                 : "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
+    const int slot = m % 3;
+    const float* G = sf + Cfg3::fGate + slot * Cfg3::szGate + 128 + 16 * b;  // beta of block b
+    u32x4 w0, w1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 bq = *reinterpret_cast<const f32x4*>(G + 4 * q);
+      const unsigned lo = cvt2(t[4 * q] * bq[0], t[4 * q + 1] * bq[1]);
+      const unsigned hi = cvt2(t[4 * q + 2] * bq[2], t[4 * q + 3] * bq[3]);
+      if (q < 2) {
+        w0[2 * q] = lo;
+        w0[2 * q + 1] = hi;
+      } else {
+        w1[2 * q - 4] = lo;
+        w1[2 * q - 3] = hi;
+      }
+    }
+    __bf16* dst = sb + slot * Cf::szBuf + Cf::oTP + b * Cf::szTile + c * Cf::LD16;
+    *reinterpret_cast<u32x4*>(dst) = w0;
+    *reinterpret_cast<u32x4*>(dst + 8) = w1;
+  });
+}
+#undef GDN_ST
+
+// Waves 0 and 1: consumers.
+__device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) {
+  using Cf = Cfg<64>;
+  const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
+  const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
+  Consumer<64> cs;
+  cs.init(x, w, l);
+  run_steps(x.nchunks, [&](auto, int k) {
+    if (k < 0) return;
+    const int slot = k % 3;
+    cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
+  });
+  cs.finish(x);
+}
+
+__global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16* __restrict__ qg,
+                                                                  const __bf16* __restrict__ kg,
+                                                                  const __bf16* __restrict__ vg,
+                                                                  const float* __restrict__ alpha,
+                                                                  const float* __restrict__ beta, const float* S0g,
+                                                                  __bf16* __restrict__ outg, float* Sfg, int T, int H,
+                                                                  int DV, int nslices) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg3::bytes];
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // keep neighbours on one XCD
+  const int slice = bid % nslices, chain = bid / nslices;
+  Ctx x;
+  x.qg = qg;
+  x.kg = kg;
+  x.vg = vg;
+  x.alpha = alpha;
+  x.beta = beta;
+  x.S0g = S0g;
+  x.outg = outg;
+  x.Sfg = Sfg;
+  x.T = T;
+  x.H = H;
+  x.DV = DV;
+  x.b = chain / H;
+  x.h = chain % H;
+  x.chain = chain;
+  x.dv0 = slice * Cfg<64>::NV;
+  x.nchunks = (T + 63) >> 6;
+  // The wave index is uniform (scalar branches only: matrix-core instructions
+  // do not honour the exec mask).
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (w < 2)
+    consume(x, smem, w, l);
+  else if (w < 4)
+    gram_rows(x, smem, 2 * (w - 2), l);
+  else if (w < 6)
+    gram_lower(x, smem, w - 2, l);
+  else if (w == 6)
+    stage_v(x, smem, l);
+  else
+    inverter(x, smem, l);
+}
+
+}  // namespace pipe3
 
 template <int DK>
 static hipError_t launch_pipe_dk(const ChunkArgs& a) {
   const int nslices = a.dv / pipe::Cfg<DK>::NV;
   const long nblk = (long)a.B * a.H * nslices;
-  hipLaunchKernelGGL((pipe::chunk_pipe_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, (hipStream_t)a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                     a.alpha, a.beta, static_cast<const float*>(a.S0), static_cast<__bf16*>(a.out),
-                     static_cast<float*>(a.S_final), a.T, a.H, a.dv, nslices);
-  return hipGetLastError();
+  return launch_kernel(pipe::chunk_pipe_kernel<DK>, dim3((unsigned)nblk), dim3(pipe::kPipeThreads), (hipStream_t)a.stream, a.q, a.k,
+                       a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
 }
 
 hipError_t launch_chunk_pipe(const ChunkArgs& a) {
-  if (a.dtype == kDtBF16 && a.dk == 64) return launch_pipe_dk<64>(a);
+  if (a.dtype == kDtBF16 && a.dk == 64) {
+    const int nslices = a.dv / pipe::Cfg<64>::NV;
+    const long nblk = (long)a.B * a.H * nslices;
+    return launch_kernel(pipe3::chunk_pipe3_kernel, dim3((unsigned)nblk), dim3(pipe3::kThreads3), (hipStream_t)a.stream,
+                         a.q, a.k, a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
+  }
   if (a.dtype == kDtBF16 && a.dk == 128) return launch_pipe_dk<128>(a);
   return hipErrorInvalidValue;
 }

@@ -168,9 +168,8 @@ template <int DT, int D, int TPS>
 static hipError_t launch_decode(const StepArgs& a) {
   constexpr int SPB = 256 / TPS;
   const long nblk = ((long)a.N + SPB - 1) / SPB;
-  hipLaunchKernelGGL((decode_kernel<DT, D, TPS>), dim3((unsigned)nblk), dim3(256), 0, (hipStream_t)a.stream, a.q, a.k,
-                     a.v, a.alpha, a.beta, static_cast<float*>(a.S), a.out, a.N);
-  return hipGetLastError();
+  return launch_kernel(decode_kernel<DT, D, TPS>, dim3((unsigned)nblk), dim3(256), (hipStream_t)a.stream, a.q, a.k, a.v,
+                       a.alpha, a.beta, a.S, a.out, a.N);
 }
 
 hipError_t launch_recurrent_step(const StepArgs& a) {

@@ -4,7 +4,25 @@
 
 #include <hip/hip_runtime.h>
 
+#include <tuple>
+
 namespace gdn {
+
+// Launches `kernel` and returns the status of this launch itself.  (The
+// runtime's last-error slot may hold an earlier, unrelated error from the
+// caller's own HIP calls, so it is neither read nor cleared here.)
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                                Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 struct ChunkArgs {
   const void* q;
