@@ -504,6 +504,10 @@ struct Consumer {
   f32x4 S[NT][NDT];
   int g, c, w, rowO, vofO, offRow, offTrK, offTrV, offT16;
   __amdgpu_buffer_rsrc_t ro;
+  // Carried from begin() to chunk(): the state and K S of the chunk's start
+  // state, and the chunk's V and decay operands.
+  u32x2 sfr[NT][NDT], vv[4][NT];
+  f32x4 acc[4][NT], gg[4];
 
   __device__ __forceinline__ void init(const Ctx& x, int w_, int l) {
     w = w_;
@@ -531,13 +535,11 @@ struct Consumer {
     offT16 = c * LD16 + 4 * g;                                      // 16x16 tiles
   }
 
-  // Chunk n from stage buffer R; G holds gamma (G[0..63]) and lambda
-  // (G[64..127]) per token, gC = gamma_C.
-  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
-    auto tile = [&](int o) { return ld4(R + o + offT16); };
-    // ---- Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S), block rows in order
-    u32x2 kr[4][NKP][2], vv[4][NT], NG[6], TP[4];
-    f32x4 gg[4];
+  // First half of a chunk, which needs only operands published a step earlier:
+  // V and gamma from stage buffer R / gate table G, and K S for the current
+  // state.
+  __device__ __forceinline__ void begin(const __bf16* R, const float* G) {
+    u32x2 kr[4][NKP][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -549,17 +551,12 @@ struct Consumer {
 #pragma unroll
       for (int t = 0; t < NT; ++t) vv[i][t] = ld4_tr(R + Cf::oV + 16 * i * LDV + 16 * t + offTrV);
       gg[i] = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
-      TP[i] = tile(Cf::oTP + i * Cf::szTile);
     }
-#pragma unroll
-    for (int e = 0; e < 6; ++e) NG[e] = tile(Cf::oNG + e * Cf::szTile);
     issue_fence();
-    u32x2 sfr[NT][NDT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int d = 0; d < NDT; ++d) sfr[t][d] = cvt4(S[t][d]);
-    f32x4 acc[4][NT];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -569,6 +566,20 @@ struct Consumer {
         for (int p = 0; p < NKP; ++p)
           acc[i][t] = mma2(kr[i][p][0], kr[i][p][1], sfr[t][2 * p], sfr[t][2 * p + 1], acc[i][t]);
       }
+  }
+
+  // Rest of chunk n (after begin() on the same stage buffer): the diagonal
+  // factors T_ii diag(beta_i) and -Gt, the substitution, the state update and
+  // the output.  G holds gamma (G[0..63]) and lambda (G[64..127]) per token and
+  // gamma_C at G[gCoff].
+  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
+    auto tile = [&](int o) { return ld4(R + o + offT16); };
+    // ---- Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S), block rows in order
+    u32x2 TP[4], NG[6];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) TP[i] = tile(Cf::oTP + i * Cf::szTile);
+#pragma unroll
+    for (int e = 0; e < 6; ++e) NG[e] = tile(Cf::oNG + e * Cf::szTile);
     // operands of the state update, in flight during the substitution
     u32x2 kt[NDT][4];
     f32x4 lm[4];
@@ -684,6 +695,7 @@ __device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l)
   stage_barrier();  // prologue: chunk 0 staged
   auto body = [&](auto bufc, int n) {
     constexpr int BUF = decltype(bufc)::value;
+    cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
     cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
     stage_barrier();
   };
@@ -741,8 +753,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf1
 
 // ============================================================================
 // Three-stage variant (dk = 64).  Per step k of the loop (one barrier each):
-//   Gram waves 2..5 and the V wave 6 build chunk k + 2 (K/Q/V rows, decayed
-//   Gram tiles, gates, and the fp32 rows of the four diagonal blocks of A);
+//   Gram waves 2, 3 and the V wave 6 build chunk k + 2 (K/Q/V rows, gates,
+//   decayed Gram tiles of row blocks 0..1 / 2..3 on and next to the diagonal,
+//   and the fp32 rows of the four diagonal blocks of A);
+//   Gram waves 4, 5 add chunk k + 1's remaining tiles from the published rows;
 //   the inverse wave 7 turns chunk k + 1's diagonal blocks into T_ii diag(beta_i);
 //   the consumer waves 0, 1 run chunk k.
 // Stage buffers rotate over three slots (chunk m uses slot m % 3); the
@@ -758,13 +772,13 @@ struct Cfg3 {
   static constexpr int NBUF = 3;
   static constexpr int fBase = ((NBUF * B::szBuf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
   // fp32 region (floats): per stage slot gamma[64], lambda[64], beta[64],
-  // gamma_C (padded); two slots of diagonal-block rows (4 blocks x 16 rows,
-  // row stride 20); the private gate tables of the four Gram waves; the 16 x 16
-  // identity (row stride 20).
-  static constexpr int szGate = 196, fGate = 0;
+  // gamma_C (padded), g[64] (log2 prefix of alpha); two slots of
+  // diagonal-block rows (4 blocks x 16 rows, row stride 20); the private gate
+  // tables of the two row waves; the 16 x 16 identity (row stride 20).
+  static constexpr int szGate = 260, fGate = 0, oG = 196;
   static constexpr int szDS = 4 * 16 * 20, fDS = NBUF * szGate;
   static constexpr int fPGT = fDS + 2 * szDS, szPGT = 128;
-  static constexpr int fEye = fPGT + 4 * szPGT;
+  static constexpr int fEye = fPGT + 2 * szPGT;
   static constexpr int nF = fEye + 16 * 20;
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -773,15 +787,22 @@ struct Cfg3 {
 };
 constexpr int kThreads3 = 8 * 64;
 
-// Runs step(parity, k) for k = -2 .. nch - 1, each followed by the barrier.
-// Every wave executes exactly nch + 2 barriers.
+// Runs step(phase, k) for k = -2 .. nch - 1, each followed by the barrier,
+// with phase = (k + 2) % 3 known at compile time: chunk k + 2 (built in this
+// step) uses stage slot and register set `phase`, chunk k + 1 slot
+// (phase + 2) % 3 and chunk k slot (phase + 1) % 3.  Every wave executes
+// exactly nch + 2 barriers.
 template <class Step>
 __device__ __forceinline__ void run_steps(int nch, Step&& step) {
-  for (int k = -2; k < nch; k += 2) {
+  for (int k = -2; k < nch; k += 3) {
     step(ic<0>{}, k);
     stage_barrier();
     if (k + 1 < nch) {
       step(ic<1>{}, k + 1);
+      stage_barrier();
+    }
+    if (k + 2 < nch) {
+      step(ic<2>{}, k + 2);
       stage_barrier();
     }
   }
@@ -822,7 +843,7 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     u32x4 k[2][NKP], q[2][NKP];
     float a, b;
   };
-  Set st[2];
+  Set st[3];
   auto load = [&](auto sc, int m) {
     constexpr int s = decltype(sc)::value;
     const int c0 = m * 64;
@@ -839,7 +860,7 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   auto process = [&](auto sc, int m) {
     constexpr int s = decltype(sc)::value;
     const Set& S = st[s];
-    __bf16* const R = sb + (m % 3) * Cf::szBuf;
+    __bf16* const R = sb + s * Cf::szBuf;  // slot m % 3 == s
     float* const D = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -868,78 +889,54 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     diag_rows(G1, gm1, PGT, b0 + 1, g, c, D + (b0 + 1) * 320);
   };
   if (nch > 0) load(ic<0>{}, 0);
+  if (nch > 1) load(ic<1>{}, 1);
   run_steps(nch, [&](auto pc, int k) {
-    constexpr int par = decltype(pc)::value;  // k & 1 == (k + 2) & 1
-    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
+    constexpr int ph = decltype(pc)::value;
+    if (k + 2 < nch) process(ic<ph>{}, k + 2);
     issue_fence();
-    if (k + 2 < nch) process(ic<par>{}, k + 2);
+    if (k + 4 < nch) load(ic<(ph + 2) % 3>{}, k + 4);  // set of chunk k + 1, already consumed
   });
 }
 
-// Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).
+// Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
+// step behind the row waves and read K and Q of the chunk from the stage slot
+// the row waves published (in MFMA operand layout), and g from the gate table,
+// so they issue no global loads.
 __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<64>;
-  constexpr int NKP = Cf::NKP;
+  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
   __bf16* const sb = reinterpret_cast<__bf16*>(smem);
   float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
-  float* const PGT = sf + Cfg3::fPGT + i * Cfg3::szPGT;  // tables 2 and 3
-  const int g = l >> 4, c = l & 15, H = x.H, T = x.T, nch = x.nchunks;
-  const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = (uint32_t)((size_t)T * H * 64 * 2 - (size_t)x.h * 64 * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * 64, spanK);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * 64, spanK);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, (uint32_t)(((size_t)T * H - x.h) * 4));
-  const int rowK = H * 64 * 2;
-  int vof0[NKP], vof1[NKP], vofi[NKP];
-#pragma unroll
-  for (int p = 0; p < NKP; ++p) {
-    vof0[p] = c * rowK + 64 * p + 16 * g;
-    vof1[p] = (16 + c) * rowK + 64 * p + 16 * g;
-    vofi[p] = (16 * i + c) * rowK + 64 * p + 16 * g;
-  }
-  struct Set {
+  const int g = l >> 4, c = l & 15, nch = x.nchunks;
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int slot = (decltype(pc)::value + 2) % 3;  // chunk k + 1
+    const int m = k + 1;
+    if (m < 0 || m >= nch) return;
+    __bf16* const R = sb + slot * Cf::szBuf;
+    const float* const gt = sf + Cfg3::fGate + slot * Cfg3::szGate + Cfg3::oG;
     u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
-    float a;
-  };
-  Set st[2];
-  auto load = [&](auto sc, int m) {
-    constexpr int s = decltype(sc)::value;
-    const int c0 = m * 64;
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      st[s].k0[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof0[p], c0 * rowK, 0));
-      st[s].k1[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof1[p], c0 * rowK, 0));
-      st[s].ki[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofi[p], c0 * rowK, 0));
-      st[s].qi[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofi[p], c0 * rowK, 0));
+      const int o = c * LDK + 32 * p + 8 * g;
+      k0[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
+      k1[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * LDK + o);
+      ki[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + o);
+      qi[p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + o);
     }
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-  };
-  auto process = [&](auto sc, int m) {
-    constexpr int s = decltype(sc)::value;
-    const Set& S = st[s];
-    __bf16* const R = sb + (m % 3) * Cf::szBuf;
-    gate_scan(S.a, 0.f, m * 64, T, l, PGT);
     f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4();
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      G0 = mma32(S.k0[p], S.ki[p], G0);
-      P0 = mma32(S.k0[p], S.qi[p], P0);
-      G1 = mma32(S.k1[p], S.ki[p], G1);
-      P1 = mma32(S.k1[p], S.qi[p], P1);
+      G0 = mma32(k0[p], ki[p], G0);
+      P0 = mma32(k0[p], qi[p], P0);
+      G1 = mma32(k1[p], ki[p], G1);
+      P1 = mma32(k1[p], qi[p], P1);
     }
-    offdiag_tiles<64>(G0, P0, PGT, i, 0, g, c, R);
-    offdiag_tiles<64>(G1, P1, PGT, i, 1, g, c, R);
-  };
-  if (nch > 0) load(ic<0>{}, 0);
-  run_steps(nch, [&](auto pc, int k) {
-    constexpr int par = decltype(pc)::value;
-    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
-    issue_fence();
-    if (k + 2 < nch) process(ic<par>{}, k + 2);
+    offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
+    offdiag_tiles<64>(G1, P1, gt, i, 1, g, c, R);
   });
 }
 
-// Wave 6: the 64 x 32 V tile, and gamma, lambda, beta and gamma_C per chunk.
+// Wave 6: the 64 x 32 V tile, and gamma, lambda, beta, gamma_C and g per chunk.
 __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
   using Cf = Cfg<64>;
   constexpr int LDV = Cf::LDV;
@@ -964,7 +961,7 @@ __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
     u32x4 v[4];
     float a, b;
   };
-  Set st[2];
+  Set st[3];
   auto load = [&](auto sc, int m) {
     constexpr int s = decltype(sc)::value;
     const int c0 = m * 64;
@@ -976,7 +973,7 @@ __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
   };
   auto process = [&](auto sc, int m) {
     constexpr int s = decltype(sc)::value;
-    const int slot = m % 3;
+    constexpr int slot = s;  // m % 3
     __bf16* const R = sb + slot * Cf::szBuf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
@@ -987,14 +984,16 @@ __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
     G[l] = __builtin_amdgcn_exp2f(xg);
     G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
     G[128 + l] = st[s].b;
+    G[Cfg3::oG + l] = xg;
     if (l == 63) G[192] = __builtin_amdgcn_exp2f(gC);
   };
   if (nch > 0) load(ic<0>{}, 0);
+  if (nch > 1) load(ic<1>{}, 1);
   run_steps(nch, [&](auto pc, int k) {
-    constexpr int par = decltype(pc)::value;
-    if (k + 3 < nch) load(ic<par ^ 1>{}, k + 3);
+    constexpr int ph = decltype(pc)::value;
+    if (k + 2 < nch) process(ic<ph>{}, k + 2);
     issue_fence();
-    if (k + 2 < nch) process(ic<par>{}, k + 2);
+    if (k + 4 < nch) load(ic<(ph + 2) % 3>{}, k + 4);  // set of chunk k + 1, already consumed
   });
 }
 
@@ -1023,7 +1022,8 @@ __device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
           f32x4{l == 4 * q ? 1.f : 0.f, l == 4 * q + 1 ? 1.f : 0.f, l == 4 * q + 2 ? 1.f : 0.f,
                 l == 4 * q + 3 ? 1.f : 0.f};
   }
-  run_steps(nch, [&](auto, int k) {
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int slot = (decltype(pc)::value + 2) % 3;  // (k + 1) % 3
     const int m = k + 1;
     if (m < 0 || m >= nch) return;
     const float* rowA = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS + b * 320 + c * 20;
@@ -1075,7 +1075,6 @@ __device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
                  : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
                    "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14])
                  : "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
-    const int slot = m % 3;
     const float* G = sf + Cfg3::fGate + slot * Cfg3::szGate + 128 + 16 * b;  // beta of block b
     u32x4 w0, w1;
 #pragma unroll
@@ -1105,10 +1104,13 @@ __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) 
   const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
   Consumer<64> cs;
   cs.init(x, w, l);
-  run_steps(x.nchunks, [&](auto, int k) {
-    if (k < 0) return;
-    const int slot = k % 3;
-    cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
+  // Step k finishes chunk k and, since the rows, V and gates of chunk k + 1
+  // were published a step earlier, starts chunk k + 1 before the barrier.
+  run_steps(x.nchunks, [&](auto pc, int k) {
+    constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
+    constexpr int next = (slot + 1) % 3;
+    if (k >= 0) cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
+    if (k >= -1 && k + 1 < x.nchunks) cs.begin(sb + next * Cf::szBuf, sf + Cfg3::fGate + next * Cfg3::szGate);
   });
   cs.finish(x);
 }
