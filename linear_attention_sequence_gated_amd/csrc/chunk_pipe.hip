@@ -65,6 +65,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
+// Bytes from `begin` to `end` of a chain's data, or 0 when there is none
+// (T = 0): with a zero range every buffer access is dropped by the range
+// check, so loads issued for no chunk never touch memory.
+__device__ __forceinline__ uint32_t span_bytes(size_t end, size_t begin) {
+  return end > begin ? (uint32_t)(end - begin) : 0u;
+}
+
 // Barrier between pipeline stages: waits for this wave's LDS traffic only (so
 // global prefetches stay in flight) and stops the scheduler from moving any
 // instruction across it.
@@ -312,10 +319,10 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
   float* const DS = sf + Cf::fDS + wi * Cf::szDS;
   const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
   const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = (uint32_t)((size_t)T * H * DK * 2 - (size_t)x.h * DK * 2);
+  const uint32_t spanK = span_bytes((size_t)T * H * DK * 2, (size_t)x.h * DK * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
-  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * DK * 2;
@@ -390,10 +397,10 @@ __device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, 
   const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
   const int id = i == 2 ? 1 : 3;  // diagonal block inverted here
   const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = (uint32_t)((size_t)T * H * DK * 2 - (size_t)x.h * DK * 2);
+  const uint32_t spanK = span_bytes((size_t)T * H * DK * 2, (size_t)x.h * DK * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
-  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * DK * 2;
@@ -454,8 +461,8 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
   const int H = x.H, T = x.T, DV = x.DV;
   const size_t tokbase = (size_t)x.b * T * H + x.h;
   const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(x.vg + tokbase * DV + x.dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, (uint32_t)(((size_t)T * H - x.h) * 4));
+      make_rsrc(x.vg + tokbase * DV + x.dv0, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, span_bytes((size_t)T * H * 4, (size_t)x.h * 4));
   const int rowV = H * DV * 2;
   int vof[4], lof[4];
 #pragma unroll
@@ -526,7 +533,7 @@ struct Consumer {
     // Output: lane (g, c) writes token c of each 16-token block, value columns
     // 16 NT w + 16t + 4g .. + 3 (one 8-byte store).
     const size_t obase = ((size_t)x.b * T * H + x.h) * DV + x.dv0;
-    ro = make_rsrc(x.outg + obase, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
+    ro = make_rsrc(x.outg + obase, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
     rowO = H * DV * 2;
     vofO = c * rowO + (16 * NT * w + 4 * g) * 2;
     offRow = c * LDK + 4 * g;                                       // row c, k sub-block 4g
@@ -787,24 +794,22 @@ struct Cfg3 {
 };
 constexpr int kThreads3 = 8 * 64;
 
-// Runs step(phase, k) for k = -2 .. nch - 1, each followed by the barrier,
-// with phase = (k + 2) % 3 known at compile time: chunk k + 2 (built in this
-// step) uses stage slot and register set `phase`, chunk k + 1 slot
-// (phase + 2) % 3 and chunk k slot (phase + 1) % 3.  Every wave executes
-// exactly nch + 2 barriers.
+// Runs step(phase, k) for k = -2, -1, ..., each followed by the barrier, with
+// phase = (k + 2) % 3 known at compile time: chunk k + 2 (built in this step)
+// uses stage slot and register set `phase`, chunk k + 1 slot (phase + 2) % 3
+// and chunk k slot (phase + 1) % 3.  Steps come in whole triples (up to two
+// trailing steps have nothing to do: every role skips chunks outside
+// [0, nch)), so every wave executes the same barriers and the loop body has no
+// conditional paths that would make the compiler's wait counts conservative.
 template <class Step>
 __device__ __forceinline__ void run_steps(int nch, Step&& step) {
   for (int k = -2; k < nch; k += 3) {
     step(ic<0>{}, k);
     stage_barrier();
-    if (k + 1 < nch) {
-      step(ic<1>{}, k + 1);
-      stage_barrier();
-    }
-    if (k + 2 < nch) {
-      step(ic<2>{}, k + 2);
-      stage_barrier();
-    }
+    step(ic<1>{}, k + 1);
+    stage_barrier();
+    step(ic<2>{}, k + 2);
+    stage_barrier();
   }
 }
 
@@ -827,10 +832,10 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   float* const PGT = sf + Cfg3::fPGT + (b0 >> 1) * Cfg3::szPGT;
   const int g = l >> 4, c = l & 15, H = x.H, T = x.T, nch = x.nchunks;
   const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = (uint32_t)((size_t)T * H * 64 * 2 - (size_t)x.h * 64 * 2);
+  const uint32_t spanK = span_bytes((size_t)T * H * 64 * 2, (size_t)x.h * 64 * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * 64, spanK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * 64, spanK);
-  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * 64 * 2;
@@ -888,13 +893,21 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     diag_rows(G0, gm0, PGT, b0, g, c, D + b0 * 320);
     diag_rows(G1, gm1, PGT, b0 + 1, g, c, D + (b0 + 1) * 320);
   };
-  if (nch > 0) load(ic<0>{}, 0);
-  if (nch > 1) load(ic<1>{}, 1);
+  // Loads are issued unconditionally (chunk index clamped; buffer loads are
+  // range-checked) so that every path through the loop has the same number of
+  // loads in flight and the compiler's wait counts stay three steps deep.
+  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
+  load(ic<0>{}, clampc(0));
+  issue_fence();
+  load(ic<1>{}, clampc(1));
+  issue_fence();
+  load(ic<2>{}, clampc(2));
+  issue_fence();
   run_steps(nch, [&](auto pc, int k) {
     constexpr int ph = decltype(pc)::value;
     if (k + 2 < nch) process(ic<ph>{}, k + 2);
     issue_fence();
-    if (k + 4 < nch) load(ic<(ph + 2) % 3>{}, k + 4);  // set of chunk k + 1, already consumed
+    load(ic<ph>{}, clampc(k + 5));  // the set just consumed; needed three steps later
   });
 }
 
@@ -945,8 +958,8 @@ __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
   const int H = x.H, T = x.T, DV = x.DV, nch = x.nchunks;
   const size_t tokbase = (size_t)x.b * T * H + x.h;
   const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(x.vg + tokbase * DV + x.dv0, (uint32_t)((size_t)T * H * DV * 2 - ((size_t)x.h * DV + x.dv0) * 2));
-  const uint32_t spanG = (uint32_t)(((size_t)T * H - x.h) * 4);
+      make_rsrc(x.vg + tokbase * DV + x.dv0, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
+  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowV = H * DV * 2;
@@ -987,13 +1000,21 @@ __device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
     G[Cfg3::oG + l] = xg;
     if (l == 63) G[192] = __builtin_amdgcn_exp2f(gC);
   };
-  if (nch > 0) load(ic<0>{}, 0);
-  if (nch > 1) load(ic<1>{}, 1);
+  // Loads are issued unconditionally (chunk index clamped; buffer loads are
+  // range-checked) so that every path through the loop has the same number of
+  // loads in flight and the compiler's wait counts stay three steps deep.
+  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
+  load(ic<0>{}, clampc(0));
+  issue_fence();
+  load(ic<1>{}, clampc(1));
+  issue_fence();
+  load(ic<2>{}, clampc(2));
+  issue_fence();
   run_steps(nch, [&](auto pc, int k) {
     constexpr int ph = decltype(pc)::value;
     if (k + 2 < nch) process(ic<ph>{}, k + 2);
     issue_fence();
-    if (k + 4 < nch) load(ic<(ph + 2) % 3>{}, k + 4);  // set of chunk k + 1, already consumed
+    load(ic<ph>{}, clampc(k + 5));  // the set just consumed; needed three steps later
   });
 }
 
@@ -1109,7 +1130,7 @@ __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) 
   run_steps(x.nchunks, [&](auto pc, int k) {
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
     constexpr int next = (slot + 1) % 3;
-    if (k >= 0) cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
+    if (k >= 0 && k < x.nchunks) cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
     if (k >= -1 && k + 1 < x.nchunks) cs.begin(sb + next * Cf::szBuf, sf + Cfg3::fGate + next * Cfg3::szGate);
   });
   cs.finish(x);
