@@ -184,13 +184,18 @@ def main():
     # serving loop would, so host-side checks do not open gaps between launches.
     code = {"bf16": gdn.GDN_BF16, "f32": gdn.GDN_F32, "c64": gdn.GDN_C64}[w.dtype]
     lib = gdn.load()
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, code)
+    # One workspace serves every copy: the calls are ordered on one stream.
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_ptr = ws.data_ptr() if ws_bytes else None
     calls = []
     for d in sets:
         gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], out=d["out"], S_final=d["S"],
                       stream=stream.cuda_stream)
         ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         calls.append((ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]), ptr(d["S0"]), w.chunk,
-                      ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code, None, 0, stream.cuda_stream))
+                      ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code, ws_ptr, ws_bytes,
+                      stream.cuda_stream))
 
     def step(i):
         s = lib.gdn_chunk_fwd(*calls[i % ncopies])

@@ -74,6 +74,12 @@ enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_C64 = 2 };
  * Bytes of device workspace gdn_chunk_fwd needs for these sizes; 0 means the
  * call may pass workspace = NULL.  Returns 0 also for unsupported arguments
  * (gdn_chunk_fwd then reports the error).
+ *
+ * GDN_BF16 and GDN_F32 need none.  GDN_C64 needs B * H * ceil(T / 64) * 57600
+ * bytes: per chunk the factors -W and U, (diag(lambda) K)^T, the decay
+ * prefix and the chunk-start state, handed between its three launches.  The
+ * caller owns the workspace; its contents are scratch on entry and exit.  Two
+ * calls may share one workspace only if they are ordered (same stream).
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
 

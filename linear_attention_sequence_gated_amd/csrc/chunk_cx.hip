@@ -1,0 +1,527 @@
+// chunk_cx.hip -- complex64 chunked forward for head size 32, in three launches.
+//
+// The method is the chunkwise WY / unit-triangular form of the gated delta
+// rule with the read side conjugated (DeltaPhase README, section 1 "Fast
+// Triangular Solve" and section 2 on the complex memory; section 5 "Exact
+// Chunkwise-Parallel Scan" for the log-space decay).  Per chunk of C = 64
+// tokens, with S the state at the chunk start, Kr = conj(K), Qr = conj(Q):
+//   A  = strict_lower(diag(beta) Kr K^T * Gamma),   T = (I + A)^{-1},
+//   W  = T diag(beta gamma) Kr,   U = T diag(beta) V,   Ut = U - W S,
+//   O  = diag(gamma) Qr S + lower(Qr K^T * Gamma) Ut,
+//   S <- gamma_C S + (diag(lambda) K)^T Ut,   lambda_t = gamma_C / gamma_t.
+//
+// One workgroup per (batch, head) walking all chunks leaves most of the chip
+// idle at few heads, and every chunk's Gram, inverse and W/U products sit on
+// the sequential path.  Here only the state recurrence is sequential:
+//   1. prep (one workgroup per chunk): gates, Gram tiles, diagonal inverses,
+//      block substitution -> -W, U, (diag(lambda) K)^T into a workspace;
+//   2. scan (one workgroup per (chain, 8 value columns)): Ut = U - W S and the
+//      state update, chunk after chunk; writes Ut in place of U and the
+//      chunk-start state S_n;
+//   3. out (one workgroup per chunk): P = Qr K^T * Gamma and
+//      O = diag(gamma) Qr S_n + P Ut.
+//
+// Complex products in the prep and out kernels use separate real/imaginary
+// planes and four real fp32 MFMA products (cmma).  The scan kernel instead
+// packs 8 complex columns into the 16 MFMA columns as interleaved (re, im)
+// pairs: for X complex with real form Xr = [re, im] pairs, a complex product
+// M X equals the real product [Mre | Mim] [X ; swz(X)], where swz maps each
+// pair (x, y) to (-y, x).  swz is one DPP lane swap plus a sign flip, so the
+// state and Ut stay in accumulator registers and feed the next product
+// directly.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace cx {
+
+constexpr int D = 32;         // key = value head size (complex elements)
+constexpr int LDK = D + 4;    // LDS row stride (floats) of a [64][32] plane
+constexpr int LD16 = 16 + 4;  // LDS row stride of a 16x16 tile
+constexpr int szK = 64 * LDK, szTri = 10 * 16 * LD16, szTd = 4 * 16 * LD16;
+
+// Workspace of one chunk, in floats.
+constexpr int wG = 64;           // log2 cumulative decay within the chunk
+constexpr int wNW = 2 * 64 * D;  // -W, planes [re|im][t][d]
+constexpr int wU = 64 * D * 2;   // U, then Ut: [t][e] interleaved (re, im)
+constexpr int wKL = 2 * D * 64;  // (diag(lambda) K)^T, planes [re|im][d][t]
+constexpr int wS = D * D * 2;    // chunk-start state [d][e] interleaved
+constexpr int oG = 0, oNW = oG + wG, oU = oNW + wNW, oKL = oU + wU, oS = oKL + wKL;
+constexpr int kChunkFloats = oS + wS;
+static_assert(oNW % 4 == 0 && oU % 4 == 0 && oKL % 4 == 0 && oS % 4 == 0 && kChunkFloats % 4 == 0,
+              "16-byte aligned workspace sections");
+
+__host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
+
+using M = LdsMat<true, float>;
+using CS = CSub<true, float>;
+using CA = Acc<true>;
+
+// Row-major token index of (b, t, h) in a [B, T, H, ...] tensor.
+__device__ __forceinline__ size_t tok(int b, int t, int h, int T, int H) { return ((size_t)b * T + t) * H + h; }
+
+// Loads one 64-token tile of a [B, T, H, 32] complex tensor into planar LDS
+// rows (row t, columns d), zero beyond T.  256 threads, 4 float4 each.
+__device__ __forceinline__ void load_tile(const float* __restrict__ src, float* re, float* im, int b, int h, int c0,
+                                          int T, int H, int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = tid + 256 * u, row = unit >> 4, cu = unit & 15, t = c0 + row;
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < T) f = *reinterpret_cast<const float4*>(src + tok(b, t, h, T, H) * (2 * D) + 4 * cu);
+    *reinterpret_cast<float2*>(re + row * LDK + 2 * cu) = make_float2(f.x, f.z);
+    *reinterpret_cast<float2*>(im + row * LDK + 2 * cu) = make_float2(f.y, f.w);
+  }
+}
+
+// ============================================================== 1. prep
+constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 4 * 64;
+
+__global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
+                                                      const float* __restrict__ alpha,
+                                                      const float* __restrict__ beta, float* __restrict__ ws,
+                                                      int T, int H, int nch) {
+  __shared__ __attribute__((aligned(16))) float smem[kPrepFloats];
+  float* const sK = smem;                 // planes re, im
+  float* const sA = sK + 2 * szK;         // -A, packed lower 16x16 tiles, 2 planes
+  float* const sTd = sA + 2 * szTri;      // (I + A_ii)^{-1}, 2 planes
+  float* const s_g2 = sTd + 2 * szTd;     // log2 cumulative decay
+  float* const s_beta = s_g2 + 64;
+  float* const s_gam = s_g2 + 128;
+  float* const s_lam = s_g2 + 192;
+  const M mK{sK, LDK, szK};
+  auto tileA = [&](int i, int j) { return M{sA + tri(i, j) * 16 * LD16, LD16, szTri}; };
+  auto tileT = [&](int i) { return M{sTd + i * 16 * LD16, LD16, szTd}; };
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  const int n = blockIdx.x, chain = n / nch, ck = n % nch, b = chain / H, h = chain % H, c0 = 64 * ck;
+  float* const wsn = ws + (size_t)n * kChunkFloats;
+
+  // Value rows for this wave's U column tile, straight into accumulator layout.
+  float2 vv[4][4];
+  if (w >= 2) {
+    const int col = 16 * (w - 2) + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = c0 + 16 * i + 4 * g + j;
+        vv[i][j] = t < T ? *reinterpret_cast<const float2*>(vg + tok(b, t, h, T, H) * (2 * D) + 2 * col)
+                         : make_float2(0.f, 0.f);
+      }
+  }
+  load_tile(kg, sK, sK + szK, b, h, c0, T, H, tid);
+  if (w == 0) {
+    const int t = c0 + l;
+    float a = 1.f, be = 0.f;  // padding token: alpha = 1, beta = 0 leaves the state unchanged
+    if (t < T) {
+      a = alpha[tok(b, t, h, T, H)];
+      be = beta[tok(b, t, h, T, H)];
+    }
+    float x = log2f(a);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (l >= off) x += y;
+    }
+    const float glast = __shfl(x, 63, 64);
+    s_g2[l] = x;
+    s_beta[l] = be;
+    s_gam[l] = exp2f(x);
+    s_lam[l] = exp2f(glast - x);
+    wsn[oG + l] = x;
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------- Gram tiles -> -A
+  for (int m = 0; m < 3; ++m) {
+    const int tt = w + 4 * m;
+    if (tt >= 10) break;
+    const int ti = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+    const int tj = tt - tri(ti, 0);
+    CS a[2], bk[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      a[d] = csub_rows(mK, 16 * tj + c, 16 * d);
+      bk[d] = csub_rows(mK, 16 * ti + c, 16 * d);
+    }
+    CA acc = acc_zero<true>();
+    cmma<true, float, false, true, 2>(acc, a, bk, 2);  // [s][r] = k_s . conj(k_r)
+    const int r = 16 * ti + c;
+    const float gr = s_g2[r], br = s_beta[r];
+    CA va;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 16 * tj + 4 * g + j;
+      const float fa = r > s ? br * exp2f(gr - s_g2[s]) : 0.f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) va.v[p][j] = -fa * acc.v[p][j];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<f32x4*>(sA + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = va.v[p];
+  }
+  // (diag(lambda) K)^T to the workspace.  Consecutive lanes take consecutive
+  // key columns so the transposing LDS reads are conflict free.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = tid + 256 * u, d = unit & 31, t4 = 4 * ((unit >> 5) & 15), p = unit >> 9;
+    const float* src = sK + p * szK + d;
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = s_lam[t4 + j] * src[(t4 + j) * LDK];
+    *reinterpret_cast<f32x4*>(wsn + oKL + p * (D * 64) + d * 64 + t4) = o;
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------- diagonal inverses
+  // Wave w inverts (I + A_ww): lane c < 16 owns column c of the inverse and
+  // runs forward substitution down the rows.
+  if (l < 16) {
+    const float* At = sA + tri(w, w) * 16 * LD16;
+    float tr[16], tim[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      tr[r] = r == c ? 1.f : 0.f;
+      tim[r] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 15; ++s)
+#pragma unroll
+      for (int r = s + 1; r < 16; ++r) {
+        const float ar = -At[r * LD16 + s], ai = -At[szTri + r * LD16 + s];
+        tr[r] -= ar * tr[s] - ai * tim[s];
+        tim[r] -= ar * tim[s] + ai * tr[s];
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sTd[w * 16 * LD16 + r * LD16 + c] = tr[r];
+      sTd[szTd + w * 16 * LD16 + r * LD16 + c] = tim[r];
+    }
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------- block substitution
+  // X = (I + A)^{-1} R by 16-row blocks: X_i = T_ii (R_i - sum_{i'<i} A_ii' X_i').
+  CA X[4];
+  auto substitute = [&](auto getR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      CA y = getR(i);
+      if (i > 0) {
+        CS a[3], xb[3];
+#pragma unroll
+        for (int ip = 0; ip < 3; ++ip) {
+          if (ip < i) {
+            a[ip] = csub_rows(tileA(i, ip), c, 0);
+            xb[ip] = csub_from_acc<true, float>(X[ip]);
+          } else {
+            a[ip] = csub_zero<true, float>();
+            xb[ip] = csub_zero<true, float>();
+          }
+        }
+        cmma<true, float, false, false, 3>(y, a, xb, i);
+      }
+      CS at[1] = {csub_rows(tileT(i), c, 0)};
+      CS yb[1] = {csub_from_acc<true, float>(y)};
+      X[i] = acc_zero<true>();
+      cmma<true, float, false, false, 1>(X[i], at, yb, 1);
+    }
+  };
+  if (w < 2) {
+    // W column tile w: R = diag(beta gamma) conj(K); the workspace keeps -W.
+    const int col = 16 * w + c;
+    substitute([&](int i) {
+      CA y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * i + 4 * g + j;
+        const float sc = s_beta[t] * s_gam[t];
+        y.v[0][j] = sc * sK[t * LDK + col];
+        y.v[1][j] = -sc * sK[szK + t * LDK + col];
+      }
+      return y;
+    });
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) wsn[oNW + p * (64 * D) + (16 * i + 4 * g + j) * D + col] = -X[i].v[p][j];
+  } else {
+    // U column tile w - 2: R = diag(beta) V.
+    const int col = 16 * (w - 2) + c;
+    substitute([&](int i) {
+      CA y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float be = s_beta[16 * i + 4 * g + j];
+        y.v[0][j] = be * vv[i][j].x;
+        y.v[1][j] = be * vv[i][j].y;
+      }
+      return y;
+    });
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2) =
+            make_float2(X[i].v[0][j], X[i].v[1][j]);
+  }
+}
+
+// ============================================================== 2. scan
+// Real form of 8 complex value columns: lane column c holds part (c & 1) of
+// complex column e0 + c / 2.  swz(x) at column c is -x[c + 1] for even c and
+// x[c - 1] for odd c: the DPP quad permutation [1, 0, 3, 2] swaps lane pairs.
+__device__ __forceinline__ float swz(float x, uint32_t smask) {
+  const int y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true);
+  return __int_as_float(y ^ smask);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Operands of one scan step for one wave (this wave's 16 tokens).
+struct ScanIn {
+  f32x4 nw[2][2];  // [plane][d block]: -W row 16w + c, columns 16 dd + 4g .. + 3
+  f32x4 kl[2][2];  // [plane][d block]: (lambda K)^T row 16 dd + c, tokens 16w + 4g .. + 3
+  float u[4];      // U rows 16w + 4g + j, real column c of the slice
+  float g2last;
+};
+
+__device__ __forceinline__ void scan_load(ScanIn& r, const float* __restrict__ wn, int w, int g, int c, int e0) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      r.nw[p][dd] = *reinterpret_cast<const f32x4*>(wn + oNW + p * (64 * D) + (16 * w + c) * D + 16 * dd + 4 * g);
+      r.kl[p][dd] = *reinterpret_cast<const f32x4*>(wn + oKL + p * (D * 64) + (16 * dd + c) * 64 + 16 * w + 4 * g);
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.u[j] = wn[oU + (16 * w + 4 * g + j) * (2 * D) + 2 * e0 + c];
+  r.g2last = wn[oG + 63];
+}
+
+__global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf, float* __restrict__ ws, int nch) {
+  __shared__ __attribute__((aligned(16))) f32x4 sPart[2][4][2][64];  // [parity][wave][d block][lane]
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  const int chain = blockIdx.x >> 2, e0 = 8 * (blockIdx.x & 3);
+  const uint32_t smask = (c & 1) ? 0u : 0x80000000u;
+  float* const wsc = ws + (size_t)chain * nch * kChunkFloats;
+
+  // State slice, real form: S[dd][j] = S_real[16 dd + 4g + j][c].
+  f32x4 S[2];
+#pragma unroll
+  for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      S[dd][j] = S0 ? S0[(size_t)chain * (2 * D * D) + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] : 0.f;
+
+  auto step = [&](const ScanIn& r, int n) {
+    float* const wn = wsc + (size_t)n * kChunkFloats;
+    if (w == 0) {
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wn[oS + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] = S[dd][j];
+    }
+    // Ut = U + (-W) S for this wave's 16 tokens.
+    f32x4 u{r.u[0], r.u[1], r.u[2], r.u[3]};
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u = mfma4(r.nw[0][dd][j], S[dd][j], u);
+        u = mfma4(r.nw[1][dd][j], swz(S[dd][j], smask), u);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wn[oU + (16 * w + 4 * g + j) * (2 * D) + 2 * e0 + c] = u[j];
+    // This wave's share of (lambda K)^T Ut.
+    f32x4 part[2];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      part[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        part[dd] = mfma4(r.kl[0][dd][j], u[j], part[dd]);
+        part[dd] = mfma4(r.kl[1][dd][j], swz(u[j], smask), part[dd]);
+      }
+    }
+    const int par = n & 1;
+    sPart[par][w][0][l] = part[0];
+    sPart[par][w][1][l] = part[1];
+    lds_barrier();
+    const float gC = exp2f(r.g2last);
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      f32x4 s = S[dd] * gC;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += sPart[par][q][dd][l];
+      S[dd] = s;
+    }
+  };
+
+  if (nch > 0) {
+    ScanIn ra, rb;
+    scan_load(ra, wsc, w, g, c, e0);
+    for (int n = 0; n < nch; n += 2) {
+      scan_load(rb, wsc + (size_t)min(n + 1, nch - 1) * kChunkFloats, w, g, c, e0);
+      step(ra, n);
+      if (n + 1 < nch) {
+        scan_load(ra, wsc + (size_t)min(n + 2, nch - 1) * kChunkFloats, w, g, c, e0);
+        step(rb, n + 1);
+      }
+    }
+  }
+  if (w == 0 && Sf != nullptr) {
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Sf[(size_t)chain * (2 * D * D) + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] = S[dd][j];
+  }
+}
+
+// ============================================================== 3. out
+constexpr int kOutFloats = 4 * szK + 2 * szTri + 2 * 64;
+
+__global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
+                                                     const float* __restrict__ ws, float* __restrict__ og, int T,
+                                                     int H, int nch) {
+  __shared__ __attribute__((aligned(16))) float smem[kOutFloats];
+  float* const sQ = smem;             // planes re, im
+  float* const sK = sQ + 2 * szK;
+  float* const sP = sK + 2 * szK;     // P, packed lower 16x16 tiles, 2 planes
+  float* const s_g2 = sP + 2 * szTri;
+  float* const s_gam = s_g2 + 64;
+  const M mQ{sQ, LDK, szK}, mK{sK, LDK, szK};
+  auto tileP = [&](int i, int j) { return M{sP + tri(i, j) * 16 * LD16, LD16, szTri}; };
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  const int n = blockIdx.x, chain = n / nch, ck = n % nch, b = chain / H, h = chain % H, c0 = 64 * ck;
+  const float* const wsn = ws + (size_t)n * kChunkFloats;
+
+  // This wave's output column tile and its B operands: S_n rows d, Ut rows s.
+  const int u = w & 1, col = 16 * u + c;
+  CS sb[2], ub[4];
+#pragma unroll
+  for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 x = *reinterpret_cast<const float2*>(wsn + oS + ((16 * dd + 4 * g + j) * D + col) * 2);
+      sb[dd].v[0][j] = x.x;
+      sb[dd].v[1][j] = x.y;
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 x = *reinterpret_cast<const float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2);
+      ub[i].v[0][j] = x.x;
+      ub[i].v[1][j] = x.y;
+    }
+  load_tile(qg, sQ, sQ + szK, b, h, c0, T, H, tid);
+  load_tile(kg, sK, sK + szK, b, h, c0, T, H, tid);
+  if (w == 0) {
+    const float x = wsn[oG + l];
+    s_g2[l] = x;
+    s_gam[l] = exp2f(x);
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------- P tiles
+  for (int m = 0; m < 3; ++m) {
+    const int tt = w + 4 * m;
+    if (tt >= 10) break;
+    const int ti = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+    const int tj = tt - tri(ti, 0);
+    CS a[2], bq[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      a[d] = csub_rows(mK, 16 * tj + c, 16 * d);
+      bq[d] = csub_rows(mQ, 16 * ti + c, 16 * d);
+    }
+    CA acc = acc_zero<true>();
+    cmma<true, float, false, true, 2>(acc, a, bq, 2);  // [s][r] = k_s . conj(q_r)
+    const int r = 16 * ti + c;
+    const float gr = s_g2[r];
+    CA vp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 16 * tj + 4 * g + j;
+      const float gam = r >= s ? exp2f(gr - s_g2[s]) : 0.f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) vp.v[p][j] = gam * acc.v[p][j];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<f32x4*>(sP + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = vp.v[p];
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------- output tiles
+  // Waves 0, 1 take row blocks {0, 3}, waves 2, 3 take {1, 2} (equal work).
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = w < 2 ? 3 * k : 1 + k;
+    CA o = acc_zero<true>();
+    CS a[2];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) a[dd] = csub_rows(mQ, 16 * i + c, 16 * dd);
+    cmma<true, float, true, false, 2>(o, a, sb, 2);  // conj(Q) S
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float gm = s_gam[16 * i + 4 * g + j];
+      o.v[0][j] *= gm;
+      o.v[1][j] *= gm;
+    }
+    CS pa[4], ubb[4];
+#pragma unroll
+    for (int ip = 0; ip < 4; ++ip) {
+      if (ip <= i) {
+        pa[ip] = csub_rows(tileP(i, ip), c, 0);
+        ubb[ip] = ub[ip];
+      } else {
+        pa[ip] = csub_zero<true, float>();
+        ubb[ip] = csub_zero<true, float>();
+      }
+    }
+    cmma<true, float, false, false, 4>(o, pa, ubb, i + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = c0 + 16 * i + 4 * g + j;
+      if (t < T)
+        *reinterpret_cast<float2*>(og + (tok(b, t, h, T, H) * D + col) * 2) = make_float2(o.v[0][j], o.v[1][j]);
+    }
+  }
+}
+
+}  // namespace cx
+
+size_t chunk_cx_workspace_bytes(int B, int T, int H) {
+  const size_t nch = ((size_t)T + 63) / 64;
+  return (size_t)B * H * nch * cx::kChunkFloats * sizeof(float);
+}
+
+hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace) {
+  const int nch = (a.T + 63) / 64;
+  const int nchains = a.B * a.H;
+  const hipStream_t st = (hipStream_t)a.stream;
+  float* ws = static_cast<float*>(workspace);
+  const unsigned nblk = (unsigned)((long)nchains * nch);
+  hipError_t e = hipSuccess;
+  if (nblk > 0) {
+    e = launch_kernel(cx::cx_prep_kernel, dim3(nblk), dim3(256), st, static_cast<const float*>(a.k),
+                      static_cast<const float*>(a.v), a.alpha, a.beta, ws, a.T, a.H, nch);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_kernel(cx::cx_scan_kernel, dim3((unsigned)nchains * 4), dim3(256), st,
+                    static_cast<const float*>(a.S0), static_cast<float*>(a.S_final), ws, nch);
+  if (e != hipSuccess || nblk == 0) return e;
+  return launch_kernel(cx::cx_out_kernel, dim3(nblk), dim3(256), st, static_cast<const float*>(a.q),
+                       static_cast<const float*>(a.k), static_cast<const float*>(ws), static_cast<float*>(a.out),
+                       a.T, a.H, nch);
+}
+
+}  // namespace gdn

@@ -511,7 +511,6 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   if (a.dtype == kDtBF16 && a.dk == 64) return launch_fused<kDtBF16, 64, 64>(a);
   if (a.dtype == kDtBF16 && a.dk == 128) return launch_fused<kDtBF16, 128, 64>(a);
   if (a.dtype == kDtF32 && a.dk == 64) return launch_fused<kDtF32, 64, 64>(a);
-  if (a.dtype == kDtC64 && a.dk == 32) return launch_fused<kDtC64, 32, 32>(a);
   return hipErrorInvalidValue;
 }
 

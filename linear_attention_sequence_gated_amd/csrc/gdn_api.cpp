@@ -54,8 +54,11 @@ const char* gdn_status_str(int status) {
 }
 
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
-  (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk; (void)dtype;
-  return 0;  // the fused kernel keeps every intermediate on chip
+  if (B < 0 || T < 0 || H < 0 || chunk != 64 || !chunk_supported(dtype, dk, dv)) return 0;
+  // The real kernels keep every intermediate on chip; the complex path hands
+  // per-chunk factors from one launch to the next.
+  if (dtype == GDN_C64) return gdn::chunk_cx_workspace_bytes(B, T, H);
+  return 0;
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
@@ -79,6 +82,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   // buffer offsets; larger rows use the fused kernel.
   const bool pipe_fits = (long long)T * H * (dk > dv ? dk : dv) * 2 < (1LL << 31);
   if (dtype == GDN_BF16 && pipe_fits) return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (dtype == GDN_C64) return gdn::launch_chunk_cx(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -49,8 +49,12 @@ struct StepArgs {
   void* stream;
 };
 
-hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, every dtype
+hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, real dtypes
 hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only
 hipError_t launch_recurrent_step(const StepArgs& a);
+// Complex64, head size 32: three launches (prep, state scan, output) that
+// exchange per-chunk intermediates through `workspace`.
+size_t chunk_cx_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 
 }  // namespace gdn
