@@ -34,9 +34,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "tokens/sec gated-delta chunk fwd (H=12,d=64,T=2048,C=64); % of roofline"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["linear_attention_sequence_gated_amd/csrc/chunk_fwd.hip",
-                  "linear_attention_sequence_gated_amd/csrc/chunk_pipe.hip",
-                  "linear_attention_sequence_gated_amd/csrc/gdn_device.hpp"]
+_CSRC = "linear_attention_sequence_gated_amd/csrc/"
+# Sources each measured kernel is compiled from; a counter summary is used only
+# while the hash of these files matches the one recorded with it.
+KERNEL_SOURCES = {
+    "chunk_pipe3_kernel": [_CSRC + "chunk_pipe.hip", _CSRC + "gdn_device.hpp"],
+    "chunk_pipe_kernel": [_CSRC + "chunk_pipe.hip", _CSRC + "gdn_device.hpp"],
+    "chunk_fwd_kernel": [_CSRC + "chunk_fwd.hip", _CSRC + "gdn_device.hpp"],
+    "cx_prep_scan_out": [_CSRC + "chunk_cx.hip", _CSRC + "gdn_device.hpp"],
+}
 
 
 def algorithmic_bytes(w, with_s0: bool) -> int:
@@ -50,9 +56,19 @@ def algorithmic_bytes(w, with_s0: bool) -> int:
     return b
 
 
-def kernel_source_hash() -> str:
+FP32_MFMA_PEAK_TFS = 157.3  # MI355X dense fp32 matrix, published
+
+
+def algorithmic_flops(w) -> float:
+    """Triangular-aware flops of one call: 3C dk + 2C dv + 6 dk dv + C^2/3 per token-head, x4 for complex."""
+    C = w.chunk
+    per = 3 * C * w.dk + 2 * C * w.dv + 6 * w.dk * w.dv + C * C / 3
+    return per * (4 if w.dtype == "c64" else 1) * w.B * w.T * w.H
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -67,7 +83,7 @@ def measured_traffic(kernel: str, workload: str):
     text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
+    if not m_b or not m_h or m_h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_b.group(1))
 
@@ -206,18 +222,18 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # One event pair brackets the K back-to-back launches on the launch stream;
+    # their average duration (gaps between launches included) prices the roofline.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(args.warmup + i)
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = float(np.mean(kern_ms))
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
 
     tokens = w.B * w.T
     value = tokens * args.steps / wall
@@ -225,7 +241,9 @@ def main():
     # The library takes the pipelined kernels for bf16 whenever a chain's row offsets fit 32 bits:
     # the three-stage one for d = 64, the two-stage one for d = 128.
     pipe = w.dtype == "bf16" and w.T * w.H * max(w.dk, w.dv) * 2 < 2 ** 31
-    if pipe and w.dk == 64:
+    if w.dtype == "c64":
+        kernel, qual = "cx_prep_scan_out", "gdn::cx::"
+    elif pipe and w.dk == 64:
         kernel, qual = "chunk_pipe3_kernel", "gdn::pipe3::"
     elif pipe:
         kernel, qual = "chunk_pipe_kernel", "gdn::pipe::"
@@ -250,9 +268,18 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": wbytes, "kernel_avg_ms": avg_ms,
-                     "kernel_min_ms": float(np.min(kern_ms)),
                      "kernel": qual + kernel},
     }
+    if w.dtype == "c64":
+        # Complex products run on fp32 matrix cores, which bind before HBM does.  The three
+        # launches of one call (prep, state scan, output) are priced together.
+        flops = algorithmic_flops(w)
+        tfs = flops / (avg_ms * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": tfs, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                              "frac": tfs / FP32_MFMA_PEAK_TFS, "traffic": traffic,
+                              "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": wbytes,
+                              "hbm_achieved_GBs": achieved, "kernel_avg_ms": avg_ms,
+                              "kernel": "gdn::cx::cx_prep_kernel + cx_scan_kernel + cx_out_kernel"}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(inp, w)
     if args.calibrate_copy:
@@ -312,17 +339,15 @@ def bench_decode(args, w, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(args.warmup + i)
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
-    avg_ms = float(np.mean(kern_ms))
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
     achieved = sbytes / (avg_ms * 1e-3) / 1e9
     result = {
         "metric": f"state-steps/sec gated-delta decode step ({w.name})", "value": w.N * args.steps / wall,
@@ -332,7 +357,7 @@ def bench_decode(args, w, dev):
         "config": {"workload": w.name, "N": w.N, "dk": w.dk, "dv": w.dv, "state_copies_cycled": ncopies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": sbytes,
-                     "kernel_avg_ms": avg_ms, "kernel_min_ms": float(np.min(kern_ms)), "kernel": "gdn::decode_kernel"},
+                     "kernel_avg_ms": avg_ms, "kernel": "gdn::decode_kernel"},
     }
     print(json.dumps(result), flush=True)
 

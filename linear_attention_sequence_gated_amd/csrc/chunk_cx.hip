@@ -363,17 +363,32 @@ __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf
     }
   };
 
+  // Loads run three chunks ahead of the state (four register sets).  The main
+  // loop body is unconditional, with loads clamped to the last chunk, so the
+  // compiler keeps the later loads in flight at every wait; the last 0..3
+  // chunks run from the sets already loaded.
   if (nch > 0) {
-    ScanIn ra, rb;
-    scan_load(ra, wsc, w, g, c, e0);
-    for (int n = 0; n < nch; n += 2) {
-      scan_load(rb, wsc + (size_t)min(n + 1, nch - 1) * kChunkFloats, w, g, c, e0);
-      step(ra, n);
-      if (n + 1 < nch) {
-        scan_load(ra, wsc + (size_t)min(n + 2, nch - 1) * kChunkFloats, w, g, c, e0);
-        step(rb, n + 1);
-      }
+    auto ld = [&](ScanIn& r, int m) {
+      scan_load(r, wsc + (size_t)min(m, nch - 1) * kChunkFloats, w, g, c, e0);
+    };
+    ScanIn r0, r1, r2, r3;
+    ld(r0, 0);
+    ld(r1, 1);
+    ld(r2, 2);
+    int n = 0;
+    for (; n + 4 <= nch; n += 4) {
+      ld(r3, n + 3);
+      step(r0, n);
+      ld(r0, n + 4);
+      step(r1, n + 1);
+      ld(r1, n + 5);
+      step(r2, n + 2);
+      ld(r2, n + 6);
+      step(r3, n + 3);
     }
+    if (n < nch) step(r0, n);
+    if (n + 1 < nch) step(r1, n + 1);
+    if (n + 2 < nch) step(r2, n + 2);
   }
   if (w == 0 && Sf != nullptr) {
 #pragma unroll
