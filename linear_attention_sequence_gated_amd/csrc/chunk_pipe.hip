@@ -288,22 +288,30 @@ __device__ __forceinline__ void diag_p_tile(const f32x4& P, const f32x4& gm, int
 
 // One pipelined producer role: loads for chunk n + 2 are issued before chunk
 // n + 1 is processed; register set and stage buffer are chosen by parity.
+// Loads are unconditional (clamped to the last chunk; with no chunk at all the
+// zero buffer range drops them) and steps come in whole pairs, so the loop has
+// no conditional load path and the compiler keeps the next chunk's loads in
+// flight while this one is processed.  The consumers run the same number of
+// barriers.
 template <class Load, class Process>
 __device__ __forceinline__ void producer_loop(int nch, Load&& load, Process&& process) {
-  if (nch > 0) load(ic<0>{}, 0);
-  if (nch > 1) load(ic<1>{}, 1);
+  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
+  load(ic<0>{}, clampc(0));
+  issue_fence();
+  load(ic<1>{}, clampc(1));
+  issue_fence();
   if (nch > 0) process(ic<0>{}, 0);
   stage_barrier();
   auto iter = [&](auto pc, int n) {
     constexpr int par = decltype(pc)::value;
-    if (n + 2 < nch) load(ic<par>{}, n + 2);
+    load(ic<par>{}, clampc(n + 2));
     issue_fence();
     if (n + 1 < nch) process(ic<par ^ 1>{}, n + 1);
     stage_barrier();
   };
   for (int n = 0; n < nch; n += 2) {
     iter(ic<0>{}, n);
-    if (n + 1 < nch) iter(ic<1>{}, n + 1);
+    iter(ic<1>{}, n + 1);
   }
 }
 
@@ -702,13 +710,16 @@ __device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l)
   stage_barrier();  // prologue: chunk 0 staged
   auto body = [&](auto bufc, int n) {
     constexpr int BUF = decltype(bufc)::value;
-    cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
-    cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
+    if (n < x.nchunks) {
+      cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
+      cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
+    }
     stage_barrier();
   };
+  // whole pairs of steps, matching the producers' barrier count
   for (int n = 0; n < x.nchunks; n += 2) {
     body(ic<0>{}, n);
-    if (n + 1 < x.nchunks) body(ic<1>{}, n + 1);
+    body(ic<1>{}, n + 1);
   }
   cs.finish(x);
 }
