@@ -12,13 +12,16 @@
 //
 // One workgroup per (batch, head) walking all chunks leaves most of the chip
 // idle at few heads, and every chunk's Gram, inverse and W/U products sit on
-// the sequential path.  Here only the state recurrence is sequential:
+// the sequential path.  Here only the state recurrence is sequential, in the
+// form of an affine map per chunk (substitute Ut into the state update):
+//   S <- M_n S + B_n,   M_n = gamma_C I - (diag(lambda) K)^T W,
+//                       B_n = (diag(lambda) K)^T U.
 //   1. prep (one workgroup per chunk): gates, Gram tiles, diagonal inverses,
-//      block substitution -> -W, U, (diag(lambda) K)^T into a workspace;
-//   2. scan (one workgroup per (chain, 8 value columns)): Ut = U - W S and the
-//      state update, chunk after chunk; writes Ut in place of U and the
-//      chunk-start state S_n;
-//   3. out (one workgroup per chunk): P = Qr K^T * Gamma and
+//      block substitution for W and U, then M_n and B_n; writes -W, U, M_n,
+//      B_n and the decay prefix to a workspace;
+//   2. scan (one workgroup per (chain, 8 value columns)): S <- M_n S + B_n
+//      chunk after chunk, writing each chunk-start state S_n;
+//   3. out (one workgroup per chunk): Ut = U - W S_n, P = Qr K^T * Gamma and
 //      O = diag(gamma) Qr S_n + P Ut.
 //
 // Complex products in the prep and out kernels use separate real/imaginary
@@ -27,8 +30,7 @@
 // pairs: for X complex with real form Xr = [re, im] pairs, a complex product
 // M X equals the real product [Mre | Mim] [X ; swz(X)], where swz maps each
 // pair (x, y) to (-y, x).  swz is one DPP lane swap plus a sign flip, so the
-// state and Ut stay in accumulator registers and feed the next product
-// directly.
+// state stays in accumulator registers and feeds the next product directly.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -43,12 +45,14 @@ constexpr int szK = 64 * LDK, szTri = 10 * 16 * LD16, szTd = 4 * 16 * LD16;
 // Workspace of one chunk, in floats.
 constexpr int wG = 64;           // log2 cumulative decay within the chunk
 constexpr int wNW = 2 * 64 * D;  // -W, planes [re|im][t][d]
-constexpr int wU = 64 * D * 2;   // U, then Ut: [t][e] interleaved (re, im)
-constexpr int wKL = 2 * D * 64;  // (diag(lambda) K)^T, planes [re|im][d][t]
+constexpr int wU = 64 * D * 2;   // U: [t][e] interleaved (re, im)
+constexpr int wM = 2 * D * D;    // M_n, planes [re|im][d][d']
+constexpr int wB = D * D * 2;    // B_n: [d][e] interleaved
 constexpr int wS = D * D * 2;    // chunk-start state [d][e] interleaved
-constexpr int oG = 0, oNW = oG + wG, oU = oNW + wNW, oKL = oU + wU, oS = oKL + wKL;
+constexpr int oG = 0, oNW = oG + wG, oU = oNW + wNW, oM = oU + wU, oB = oM + wM, oS = oB + wB;
 constexpr int kChunkFloats = oS + wS;
-static_assert(oNW % 4 == 0 && oU % 4 == 0 && oKL % 4 == 0 && oS % 4 == 0 && kChunkFloats % 4 == 0,
+static_assert(8 * 2 * 256 <= 2 * szK, "Ut tiles fit in the K planes of the output kernel");
+static_assert(oNW % 4 == 0 && oU % 4 == 0 && oM % 4 == 0 && oB % 4 == 0 && oS % 4 == 0 && kChunkFloats % 4 == 0,
               "16-byte aligned workspace sections");
 
 __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -56,6 +60,34 @@ __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j
 using M = LdsMat<true, float>;
 using CS = CSub<true, float>;
 using CA = Acc<true>;
+
+// c += sum_{s < n} op(a[s]) op(b[s]) for complex planar sub-blocks, op
+// conjugating when CA / CB is set, with three real matrix products per
+// sub-block instead of four (Gauss): with sa, sb = -1 for a conjugated
+// operand, P1 = ar br, P2 = ai bi, P3 = (ar + sa ai)(br + sb bi) give
+// re = P1 - sa sb P2 and im = P3 - P1 - sa sb P2.  The three products are
+// accumulated over all sub-blocks before they are combined.
+template <bool CA, bool CB, int NMAX>
+__device__ __forceinline__ void cmma3(Acc<true>& c, const CSub<true, float> (&a)[NMAX],
+                                      const CSub<true, float> (&b)[NMAX], int n) {
+  f32x4 p1{0.f, 0.f, 0.f, 0.f}, p2 = p1, p3 = p1;
+#pragma unroll
+  for (int s = 0; s < NMAX; ++s) {
+    if (s < n) {
+      const f32x4 as = CA ? a[s].v[0] - a[s].v[1] : a[s].v[0] + a[s].v[1];
+      const f32x4 bs = CB ? b[s].v[0] - b[s].v[1] : b[s].v[0] + b[s].v[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s].v[0][j], b[s].v[0][j], p1, 0, 0, 0);
+        p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s].v[1][j], b[s].v[1][j], p2, 0, 0, 0);
+        p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(as[j], bs[j], p3, 0, 0, 0);
+      }
+    }
+  }
+  constexpr float sg = (CA != CB) ? -1.f : 1.f;  // sa * sb
+  c.v[0] += p1 - sg * p2;
+  c.v[1] += p3 - p1 - sg * p2;
+}
 
 // Row-major token index of (b, t, h) in a [B, T, H, ...] tensor.
 __device__ __forceinline__ size_t tok(int b, int t, int h, int T, int H) { return ((size_t)b * T + t) * H + h; }
@@ -75,9 +107,11 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, float* 
 }
 
 // ============================================================== 1. prep
-constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 4 * 64;
+constexpr int LDT = 64 + 4;  // LDS row stride of a [32][64] plane
+constexpr int szKT = D * LDT;
+constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 2 * szKT + 4 * 64;
 
-__global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
+__global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ ws,
                                                       int T, int H, int nch) {
@@ -85,7 +119,8 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
   float* const sK = smem;                 // planes re, im
   float* const sA = sK + 2 * szK;         // -A, packed lower 16x16 tiles, 2 planes
   float* const sTd = sA + 2 * szTri;      // (I + A_ii)^{-1}, 2 planes
-  float* const s_g2 = sTd + 2 * szTd;     // log2 cumulative decay
+  float* const sKT = sTd + 2 * szTd;      // (diag(lambda) K)^T, 2 planes
+  float* const s_g2 = sKT + 2 * szKT;     // log2 cumulative decay
   float* const s_beta = s_g2 + 64;
   float* const s_gam = s_g2 + 128;
   float* const s_lam = s_g2 + 192;
@@ -146,7 +181,7 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
       bk[d] = csub_rows(mK, 16 * ti + c, 16 * d);
     }
     CA acc = acc_zero<true>();
-    cmma<true, float, false, true, 2>(acc, a, bk, 2);  // [s][r] = k_s . conj(k_r)
+    cmma3<false, true, 2>(acc, a, bk, 2);  // [s][r] = k_s . conj(k_r)
     const int r = 16 * ti + c;
     const float gr = s_g2[r], br = s_beta[r];
     CA va;
@@ -161,8 +196,8 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
     for (int p = 0; p < 2; ++p)
       *reinterpret_cast<f32x4*>(sA + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = va.v[p];
   }
-  // (diag(lambda) K)^T to the workspace.  Consecutive lanes take consecutive
-  // key columns so the transposing LDS reads are conflict free.
+  // (diag(lambda) K)^T into LDS, for M_n and B_n.  Consecutive lanes take
+  // consecutive key columns so the transposing reads are conflict free.
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int unit = tid + 256 * u, d = unit & 31, t4 = 4 * ((unit >> 5) & 15), p = unit >> 9;
@@ -170,7 +205,7 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
     f32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = s_lam[t4 + j] * src[(t4 + j) * LDK];
-    *reinterpret_cast<f32x4*>(wsn + oKL + p * (D * 64) + d * 64 + t4) = o;
+    *reinterpret_cast<f32x4*>(sKT + p * szKT + d * LDT + t4) = o;
   }
   lds_barrier();
 
@@ -220,13 +255,26 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
             xb[ip] = csub_zero<true, float>();
           }
         }
-        cmma<true, float, false, false, 3>(y, a, xb, i);
+        cmma3<false, false, 3>(y, a, xb, i);
       }
       CS at[1] = {csub_rows(tileT(i), c, 0)};
       CS yb[1] = {csub_from_acc<true, float>(y)};
       X[i] = acc_zero<true>();
-      cmma<true, float, false, false, 1>(X[i], at, yb, 1);
+      cmma3<false, false, 1>(X[i], at, yb, 1);
     }
+  };
+  // Rows 16 dd .. 16 dd + 15 of (diag(lambda) K)^T X for this wave's column tile.
+  const M mKT{sKT, LDT, szKT};
+  auto kl_times_x = [&](int dd) {
+    CS a[4], xb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = csub_rows(mKT, 16 * dd + c, 16 * i);
+      xb[i] = csub_from_acc<true, float>(X[i]);
+    }
+    CA acc = acc_zero<true>();
+    cmma3<false, false, 4>(acc, a, xb, 4);
+    return acc;
   };
   if (w < 2) {
     // W column tile w: R = diag(beta gamma) conj(K); the workspace keeps -W.
@@ -248,6 +296,18 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int p = 0; p < 2; ++p) wsn[oNW + p * (64 * D) + (16 * i + 4 * g + j) * D + col] = -X[i].v[p][j];
+    // M_n column tile w: gamma_C I - (diag(lambda) K)^T W.
+    const float gC = s_gam[63];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      const CA m = kl_times_x(dd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 16 * dd + 4 * g + j;
+        wsn[oM + d * D + col] = (d == col ? gC : 0.f) - m.v[0][j];
+        wsn[oM + D * D + d * D + col] = -m.v[1][j];
+      }
+    }
   } else {
     // U column tile w - 2: R = diag(beta) V.
     const int col = 16 * (w - 2) + c;
@@ -267,6 +327,15 @@ __global__ __launch_bounds__(256) void cx_prep_kernel(const float* __restrict__ 
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2) =
             make_float2(X[i].v[0][j], X[i].v[1][j]);
+    // B_n column tile w - 2: (diag(lambda) K)^T U.
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      const CA bn = kl_times_x(dd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float2*>(wsn + oB + ((16 * dd + 4 * g + j) * D + col) * 2) =
+            make_float2(bn.v[0][j], bn.v[1][j]);
+    }
   }
 }
 
@@ -283,84 +352,54 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Operands of one scan step for one wave (this wave's 16 tokens).
+// Operands of one scan step for one wave: wave w = dd + 2 kh forms rows
+// 16 dd .. 16 dd + 15 of M_n S from the key rows 16 kh .. 16 kh + 15 of S.
 struct ScanIn {
-  f32x4 nw[2][2];  // [plane][d block]: -W row 16w + c, columns 16 dd + 4g .. + 3
-  f32x4 kl[2][2];  // [plane][d block]: (lambda K)^T row 16 dd + c, tokens 16w + 4g .. + 3
-  float u[4];      // U rows 16w + 4g + j, real column c of the slice
-  float g2last;
+  f32x4 m[2];  // [plane]: M_n row 16 dd + c, columns 16 kh + 4g .. + 3
+  float b[4];  // B_n rows 16 dd + 4g + j, real column c of the slice
 };
 
-__device__ __forceinline__ void scan_load(ScanIn& r, const float* __restrict__ wn, int w, int g, int c, int e0) {
+__device__ __forceinline__ void scan_load(ScanIn& r, const float* __restrict__ wn, int dd, int kh, int g, int c,
+                                          int e0) {
 #pragma unroll
   for (int p = 0; p < 2; ++p)
+    r.m[p] = *reinterpret_cast<const f32x4*>(wn + oM + p * (D * D) + (16 * dd + c) * D + 16 * kh + 4 * g);
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      r.nw[p][dd] = *reinterpret_cast<const f32x4*>(wn + oNW + p * (64 * D) + (16 * w + c) * D + 16 * dd + 4 * g);
-      r.kl[p][dd] = *reinterpret_cast<const f32x4*>(wn + oKL + p * (D * 64) + (16 * dd + c) * 64 + 16 * w + 4 * g);
-    }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r.u[j] = wn[oU + (16 * w + 4 * g + j) * (2 * D) + 2 * e0 + c];
-  r.g2last = wn[oG + 63];
+  for (int j = 0; j < 4; ++j) r.b[j] = wn[oB + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c];
 }
 
 __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf, float* __restrict__ ws, int nch) {
-  __shared__ __attribute__((aligned(16))) f32x4 sPart[2][4][2][64];  // [parity][wave][d block][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 sPart[2][4][64];  // [parity][wave][lane]
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
+  const int dd = w & 1, kh = w >> 1;
   const int chain = blockIdx.x >> 2, e0 = 8 * (blockIdx.x & 3);
   const uint32_t smask = (c & 1) ? 0u : 0x80000000u;
   float* const wsc = ws + (size_t)chain * nch * kChunkFloats;
+  const size_t sbase = (size_t)chain * (2 * D * D) + 2 * e0 + c;
 
-  // State slice, real form: S[dd][j] = S_real[16 dd + 4g + j][c].
-  f32x4 S[2];
+  // Key rows 16 kh .. 16 kh + 15 of the state slice, real form:
+  // Sk[j] = S_real[16 kh + 4g + j][c].
+  f32x4 Sk;
 #pragma unroll
-  for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S[dd][j] = S0 ? S0[(size_t)chain * (2 * D * D) + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] : 0.f;
+  for (int j = 0; j < 4; ++j) Sk[j] = S0 ? S0[sbase + (16 * kh + 4 * g + j) * (2 * D)] : 0.f;
 
   auto step = [&](const ScanIn& r, int n) {
     float* const wn = wsc + (size_t)n * kChunkFloats;
-    if (w == 0) {
+    if (dd == 0) {
 #pragma unroll
-      for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wn[oS + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] = S[dd][j];
+      for (int j = 0; j < 4; ++j) wn[oS + (16 * kh + 4 * g + j) * (2 * D) + 2 * e0 + c] = Sk[j];
     }
-    // Ut = U + (-W) S for this wave's 16 tokens.
-    f32x4 u{r.u[0], r.u[1], r.u[2], r.u[3]};
+    f32x4 part = kh == 0 ? f32x4{r.b[0], r.b[1], r.b[2], r.b[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u = mfma4(r.nw[0][dd][j], S[dd][j], u);
-        u = mfma4(r.nw[1][dd][j], swz(S[dd][j], smask), u);
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wn[oU + (16 * w + 4 * g + j) * (2 * D) + 2 * e0 + c] = u[j];
-    // This wave's share of (lambda K)^T Ut.
-    f32x4 part[2];
-#pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      part[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        part[dd] = mfma4(r.kl[0][dd][j], u[j], part[dd]);
-        part[dd] = mfma4(r.kl[1][dd][j], swz(u[j], smask), part[dd]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      part = mfma4(r.m[0][j], Sk[j], part);
+      part = mfma4(r.m[1][j], swz(Sk[j], smask), part);
     }
     const int par = n & 1;
-    sPart[par][w][0][l] = part[0];
-    sPart[par][w][1][l] = part[1];
+    sPart[par][w][l] = part;
     lds_barrier();
-    const float gC = exp2f(r.g2last);
-#pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      f32x4 s = S[dd] * gC;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s += sPart[par][q][dd][l];
-      S[dd] = s;
-    }
+    // rows 16 kh .. of the new state: the two waves with dd == kh
+    Sk = sPart[par][kh][l] + sPart[par][kh + 2][l];
   };
 
   // Loads run three chunks ahead of the state (four register sets).  The main
@@ -368,9 +407,7 @@ __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf
   // compiler keeps the later loads in flight at every wait; the last 0..3
   // chunks run from the sets already loaded.
   if (nch > 0) {
-    auto ld = [&](ScanIn& r, int m) {
-      scan_load(r, wsc + (size_t)min(m, nch - 1) * kChunkFloats, w, g, c, e0);
-    };
+    auto ld = [&](ScanIn& r, int m) { scan_load(r, wsc + (size_t)min(m, nch - 1) * kChunkFloats, dd, kh, g, c, e0); };
     ScanIn r0, r1, r2, r3;
     ld(r0, 0);
     ld(r1, 1);
@@ -390,11 +427,9 @@ __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf
     if (n + 1 < nch) step(r1, n + 1);
     if (n + 2 < nch) step(r2, n + 2);
   }
-  if (w == 0 && Sf != nullptr) {
+  if (dd == 0 && Sf != nullptr) {
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Sf[(size_t)chain * (2 * D * D) + (16 * dd + 4 * g + j) * (2 * D) + 2 * e0 + c] = S[dd][j];
+    for (int j = 0; j < 4; ++j) Sf[sbase + (16 * kh + 4 * g + j) * (2 * D)] = Sk[j];
   }
 }
 
@@ -417,9 +452,12 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
   const int n = blockIdx.x, chain = n / nch, ck = n % nch, b = chain / H, h = chain % H, c0 = 64 * ck;
   const float* const wsn = ws + (size_t)n * kChunkFloats;
 
-  // This wave's output column tile and its B operands: S_n rows d, Ut rows s.
+  // This wave's output column tile u and row blocks {0, 3} (waves 0, 1) or
+  // {1, 2} (waves 2, 3): equal work.  B operand S_n (rows d, columns of tile
+  // u); for its two row blocks, U and the A operands of -W.
   const int u = w & 1, col = 16 * u + c;
-  CS sb[2], ub[4];
+  auto rowblk = [&](int k) { return w < 2 ? 3 * k : 1 + k; };
+  CS sb[2];
 #pragma unroll
   for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
@@ -428,14 +466,23 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
       sb[dd].v[0][j] = x.x;
       sb[dd].v[1][j] = x.y;
     }
+  CA ut[2];
+  CS nw[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int k = 0; k < 2; ++k) {
+    const int i = rowblk(k);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float2 x = *reinterpret_cast<const float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2);
-      ub[i].v[0][j] = x.x;
-      ub[i].v[1][j] = x.y;
+      ut[k].v[0][j] = x.x;
+      ut[k].v[1][j] = x.y;
     }
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        nw[k][dd].v[p] = *reinterpret_cast<const f32x4*>(wsn + oNW + p * (64 * D) + (16 * i + c) * D + 16 * dd + 4 * g);
+  }
   load_tile(qg, sQ, sQ + szK, b, h, c0, T, H, tid);
   load_tile(kg, sK, sK + szK, b, h, c0, T, H, tid);
   if (w == 0) {
@@ -444,6 +491,10 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
     s_gam[l] = exp2f(x);
   }
   lds_barrier();
+
+  // ---------------------------------------------------- Ut = U + (-W) S_n, this wave's two tiles
+#pragma unroll
+  for (int k = 0; k < 2; ++k) cmma3<false, false, 2>(ut[k], nw[k], sb, 2);
 
   // ---------------------------------------------------- P tiles
   for (int m = 0; m < 3; ++m) {
@@ -458,7 +509,7 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
       bq[d] = csub_rows(mQ, 16 * ti + c, 16 * d);
     }
     CA acc = acc_zero<true>();
-    cmma<true, float, false, true, 2>(acc, a, bq, 2);  // [s][r] = k_s . conj(q_r)
+    cmma3<false, true, 2>(acc, a, bq, 2);  // [s][r] = k_s . conj(q_r)
     const int r = 16 * ti + c;
     const float gr = s_g2[r];
     CA vp;
@@ -474,17 +525,30 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
       *reinterpret_cast<f32x4*>(sP + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = vp.v[p];
   }
   lds_barrier();
+  // Ut tiles (row block i, column tile u) go to the K planes, which P no longer
+  // needs, stored transposed so that a B operand is one 16-byte read per plane.
+  float* const sU = sK;
+  auto tileU = [&](int i, int uu, int p) { return sU + ((i * 2 + uu) * 2 + p) * 256; };
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) *reinterpret_cast<f32x4*>(tileU(rowblk(k), u, p) + c * 16 + 4 * g) = ut[k].v[p];
+  lds_barrier();
+  CS ub[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) ub[i].v[p] = *reinterpret_cast<const f32x4*>(tileU(i, u, p) + c * 16 + 4 * g);
 
   // ---------------------------------------------------- output tiles
-  // Waves 0, 1 take row blocks {0, 3}, waves 2, 3 take {1, 2} (equal work).
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int i = w < 2 ? 3 * k : 1 + k;
+    const int i = rowblk(k);
     CA o = acc_zero<true>();
     CS a[2];
 #pragma unroll
     for (int dd = 0; dd < 2; ++dd) a[dd] = csub_rows(mQ, 16 * i + c, 16 * dd);
-    cmma<true, float, true, false, 2>(o, a, sb, 2);  // conj(Q) S
+    cmma3<true, false, 2>(o, a, sb, 2);  // conj(Q) S
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float gm = s_gam[16 * i + 4 * g + j];
@@ -502,7 +566,7 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
         ubb[ip] = csub_zero<true, float>();
       }
     }
-    cmma<true, float, false, false, 4>(o, pa, ubb, i + 1);
+    cmma3<false, false, 4>(o, pa, ubb, i + 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = c0 + 16 * i + 4 * g + j;
