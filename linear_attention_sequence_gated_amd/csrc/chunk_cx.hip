@@ -107,6 +107,28 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, float* 
 }
 
 // ============================================================== 1. prep
+// Value of lane M of each 16-lane row, in every lane of that row.
+template <int M> __device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + M, 0xF, 0xF, true));
+}
+
+// Forward-substitution steps M .. 14 for a complex 16 x 16 unit lower-triangular
+// inverse held by rows: t_c += (-A[c][M]) t_M for every row c.
+template <int M>
+__device__ __forceinline__ void inv_rows(f32x4& tr, f32x4& ti, const float (&nar)[16], const float (&nai)[16]) {
+  if constexpr (M < 15) {
+    f32x4 br, bi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      br[j] = row_bcast<M>(tr[j]);
+      bi[j] = row_bcast<M>(ti[j]);
+    }
+    const float ar = nar[M], ai = nai[M];
+    tr += ar * br - ai * bi;
+    ti += ar * bi + ai * br;
+    inv_rows<M + 1>(tr, ti, nar, nai);
+  }
+}
 constexpr int LDT = 64 + 4;  // LDS row stride of a [32][64] plane
 constexpr int szKT = D * LDT;
 constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 2 * szKT + 4 * 64;
@@ -210,29 +232,29 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
   lds_barrier();
 
   // ---------------------------------------------------- diagonal inverses
-  // Wave w inverts (I + A_ww): lane c < 16 owns column c of the inverse and
-  // runs forward substitution down the rows.
-  if (l < 16) {
-    const float* At = sA + tri(w, w) * 16 * LD16;
-    float tr[16], tim[16];
+  // Wave w inverts (I + A_ww) by forward substitution over rows: lane (g, c)
+  // owns row c, complex columns 4g .. 4g + 3.  Once row m is final it is
+  // broadcast along each 16-lane row (DPP row_newbcast) and added, scaled by
+  // -A[c][m], to every row (rows c <= m have A[c][m] = 0).
+  {
+    const float* At = sA + tri(w, w) * 16 * LD16 + c * LD16;
+    float nar[16], nai[16];  // -A[c][m], row c of the tile
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      tr[r] = r == c ? 1.f : 0.f;
-      tim[r] = 0.f;
-    }
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 vr = *reinterpret_cast<const f32x4*>(At + 4 * q);
+      const f32x4 vi = *reinterpret_cast<const f32x4*>(At + szTri + 4 * q);
 #pragma unroll
-    for (int s = 0; s < 15; ++s)
-#pragma unroll
-      for (int r = s + 1; r < 16; ++r) {
-        const float ar = -At[r * LD16 + s], ai = -At[szTri + r * LD16 + s];
-        tr[r] -= ar * tr[s] - ai * tim[s];
-        tim[r] -= ar * tim[s] + ai * tr[s];
+      for (int j = 0; j < 4; ++j) {
+        nar[4 * q + j] = vr[j];
+        nai[4 * q + j] = vi[j];
       }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sTd[w * 16 * LD16 + r * LD16 + c] = tr[r];
-      sTd[szTd + w * 16 * LD16 + r * LD16 + c] = tim[r];
     }
+    f32x4 tr, ti{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tr[j] = c == 4 * g + j ? 1.f : 0.f;
+    inv_rows<0>(tr, ti, nar, nai);
+    *reinterpret_cast<f32x4*>(sTd + w * 16 * LD16 + c * LD16 + 4 * g) = tr;
+    *reinterpret_cast<f32x4*>(sTd + szTd + w * 16 * LD16 + c * LD16 + 4 * g) = ti;
   }
   lds_barrier();
 
@@ -385,10 +407,10 @@ __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf
 
   auto step = [&](const ScanIn& r, int n) {
     float* const wn = wsc + (size_t)n * kChunkFloats;
-    if (dd == 0) {
+    // Chunk-start state: both waves holding key rows 16 kh .. store them (the
+    // same values), so the loop has no conditional memory path.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wn[oS + (16 * kh + 4 * g + j) * (2 * D) + 2 * e0 + c] = Sk[j];
-    }
+    for (int j = 0; j < 4; ++j) wn[oS + (16 * kh + 4 * g + j) * (2 * D) + 2 * e0 + c] = Sk[j];
     f32x4 part = kh == 0 ? f32x4{r.b[0], r.b[1], r.b[2], r.b[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
