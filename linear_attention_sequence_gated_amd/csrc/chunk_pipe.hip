@@ -878,14 +878,6 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;  // slot m % 3 == s
     float* const D = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
-        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
-        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
-      }
     gate_scan(S.a, S.b, m * 64, T, l, PGT);
     f32x4 G0 = zero4(), P0 = zero4(), Go = zero4(), Po = zero4(), G1 = zero4(), P1 = zero4();
 #pragma unroll
@@ -903,6 +895,18 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     diag_p_tile<64>(P1, gm1, b0 + 1, g, c, R);
     diag_rows(G0, gm0, PGT, b0, g, c, D + b0 * 320);
     diag_rows(G1, gm1, PGT, b0 + 1, g, c, D + (b0 + 1) * 320);
+    // K and Q rows for the lower Gram waves and the consumers, published last:
+    // nobody reads them before the next barrier, and right after a barrier the
+    // consumers' own LDS reads are on the critical path.
+    issue_fence();
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
+        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
+      }
   };
   // Loads are issued unconditionally (chunk index clamped; buffer loads are
   // range-checked) so that every path through the loop has the same number of
