@@ -133,10 +133,20 @@ constexpr int LDT = 64 + 4;  // LDS row stride of a [32][64] plane
 constexpr int szKT = D * LDT;
 constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 2 * szKT + 4 * 64;
 
+// Prefetched operands of one prep chunk for one thread.
+struct PrepIn {
+  float4 k[4];  // this thread's four 16-byte units of the K tile
+  float a, b;   // alpha, beta of token l
+};
+
+// Persistent, like the output kernel: chunks blockIdx.x, + gridDim.x, ...,
+// with the next chunk's K and gates loaded during the current one.  V is
+// loaded at the start of its chunk and first used after the Gram tiles and
+// the inverses.
 __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ ws,
-                                                      int T, int H, int nch) {
+                                                      int T, int H, int nch, int total) {
   __shared__ __attribute__((aligned(16))) float smem[kPrepFloats];
   float* const sK = smem;                 // planes re, im
   float* const sA = sK + 2 * szK;         // -A, packed lower 16x16 tiles, 2 planes
@@ -151,31 +161,61 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
   auto tileT = [&](int i) { return M{sTd + i * 16 * LD16, LD16, szTd}; };
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
-  const int n = blockIdx.x, chain = n / nch, ck = n % nch, b = chain / H, h = chain % H, c0 = 64 * ck;
-  float* const wsn = ws + (size_t)n * kChunkFloats;
+  // Loads are unconditional: rows past T are clamped and their values replaced
+  // when used (padding token: k = v = 0, alpha = 1, beta = 0, which leaves the
+  // state unchanged).
+  auto load_in = [&](PrepIn& r, int n) {
+    const int chain = n / nch, c0 = 64 * (n % nch), b = chain / H, h = chain % H;
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int unit = tid + 256 * uu, t = min(c0 + (unit >> 4), T - 1), cu = unit & 15;
+      r.k[uu] = *reinterpret_cast<const float4*>(kg + tok(b, t, h, T, H) * (2 * D) + 4 * cu);
+    }
+    const int t = min(c0 + l, T - 1);
+    r.a = alpha[tok(b, t, h, T, H)];
+    r.b = beta[tok(b, t, h, T, H)];
+  };
 
-  // Value rows for this wave's U column tile, straight into accumulator layout.
+  PrepIn r;
+  load_in(r, blockIdx.x);
+  for (int n = blockIdx.x; n < total; n += gridDim.x) {
+  // Lane indices re-derived from an opaque copy of the thread index, so that
+  // the many per-lane LDS addresses below are formed per chunk instead of being
+  // held in registers across the loop.
+  int tid_it = tid;
+  asm volatile("" : "+v"(tid_it));
+  const int l = tid_it & 63, g = l >> 4, c = l & 15;
+  const int chain = n / nch, c0 = 64 * (n % nch), b = chain / H, h = chain % H;
+  float* const wsn = ws + (size_t)n * kChunkFloats;
+  // Value rows for the U column tile 16 (w & 1) + c (waves 2, 3 use them), in
+  // accumulator layout.
   float2 vv[4][4];
-  if (w >= 2) {
-    const int col = 16 * (w - 2) + c;
+  {
+    const int vcol = 16 * (w & 1) + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = c0 + 16 * i + 4 * g + j;
-        vv[i][j] = t < T ? *reinterpret_cast<const float2*>(vg + tok(b, t, h, T, H) * (2 * D) + 2 * col)
-                         : make_float2(0.f, 0.f);
+        const int t = min(c0 + 16 * i + 4 * g + j, T - 1);
+        vv[i][j] = *reinterpret_cast<const float2*>(vg + tok(b, t, h, T, H) * (2 * D) + 2 * vcol);
       }
   }
-  load_tile(kg, sK, sK + szK, b, h, c0, T, H, tid);
+
+  // ---------------------------------------------------- this chunk's operands
+  // K tile to LDS; value rows for this wave's U column tile, in accumulator layout.
+#pragma unroll
+  for (int uu = 0; uu < 4; ++uu) {
+    const int unit = tid + 256 * uu, row = unit >> 4, cu = unit & 15;
+    const float4 f = c0 + row < T ? r.k[uu] : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float2*>(sK + row * LDK + 2 * cu) = make_float2(f.x, f.z);
+    *reinterpret_cast<float2*>(sK + szK + row * LDK + 2 * cu) = make_float2(f.y, f.w);
+  }
+  const bool tin = c0 + l < T;
+  const float pa = tin ? r.a : 1.f, pb = tin ? r.b : 0.f;
+  // ---------------------------------------------------- next chunk's operands, in flight from here on
+  load_in(r, min(n + (int)gridDim.x, total - 1));
   if (w == 0) {
-    const int t = c0 + l;
-    float a = 1.f, be = 0.f;  // padding token: alpha = 1, beta = 0 leaves the state unchanged
-    if (t < T) {
-      a = alpha[tok(b, t, h, T, H)];
-      be = beta[tok(b, t, h, T, H)];
-    }
-    float x = log2f(a);
+    float x = log2f(pa);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
@@ -183,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
     }
     const float glast = __shfl(x, 63, 64);
     s_g2[l] = x;
-    s_beta[l] = be;
+    s_beta[l] = pb;
     s_gam[l] = exp2f(x);
     s_lam[l] = exp2f(glast - x);
     wsn[oG + l] = x;
@@ -338,6 +378,7 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float be = s_beta[16 * i + 4 * g + j];
+        // padding rows have beta = 0, which also clears their (clamped) values
         y.v[0][j] = be * vv[i][j].x;
         y.v[1][j] = be * vv[i][j].y;
       }
@@ -358,6 +399,8 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
         *reinterpret_cast<float2*>(wsn + oB + ((16 * dd + 4 * g + j) * D + col) * 2) =
             make_float2(bn.v[0][j], bn.v[1][j]);
     }
+  }
+  lds_barrier();  // every wave is done with this chunk's LDS tables
   }
 }
 
@@ -458,9 +501,21 @@ __global__ __launch_bounds__(256) void cx_scan_kernel(const float* S0, float* Sf
 // ============================================================== 3. out
 constexpr int kOutFloats = 4 * szK + 2 * szTri + 2 * 64;
 
-__global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
-                                                     const float* __restrict__ ws, float* __restrict__ og, int T,
-                                                     int H, int nch) {
+// Prefetched operands of one output chunk for one thread.
+struct OutIn {
+  float4 q[4], k[4];   // this thread's four 16-byte units of the Q and K tiles
+  float g;             // log2 decay prefix of token l (wave 0)
+};
+
+// Persistent: each workgroup takes chunks blockIdx.x, + gridDim.x, ...  The
+// next chunk's Q and K tiles are loaded while the current one is computed,
+// into the registers the current one has just been moved out of; the
+// workspace operands are loaded at the start of a chunk and first used after
+// the P tiles.  Loads are unconditional (rows past T are clamped, then
+// zeroed), so the loop has no conditional load path.
+__global__ __launch_bounds__(256, 2) void cx_out_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
+                                                        const float* __restrict__ ws, float* __restrict__ og, int T,
+                                                        int H, int nch, int total) {
   __shared__ __attribute__((aligned(16))) float smem[kOutFloats];
   float* const sQ = smem;             // planes re, im
   float* const sK = sQ + 2 * szK;
@@ -469,132 +524,161 @@ __global__ __launch_bounds__(256) void cx_out_kernel(const float* __restrict__ q
   float* const s_gam = s_g2 + 64;
   const M mQ{sQ, LDK, szK}, mK{sK, LDK, szK};
   auto tileP = [&](int i, int j) { return M{sP + tri(i, j) * 16 * LD16, LD16, szTri}; };
+  // Ut tiles (row block i, column tile u) go to the K planes once P no longer
+  // needs them, stored transposed so that a B operand is one 16-byte read per plane.
+  float* const sU = sK;
+  auto tileU = [&](int i, int uu, int p) { return sU + ((i * 2 + uu) * 2 + p) * 256; };
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
-  const int n = blockIdx.x, chain = n / nch, ck = n % nch, b = chain / H, h = chain % H, c0 = 64 * ck;
-  const float* const wsn = ws + (size_t)n * kChunkFloats;
-
   // This wave's output column tile u and row blocks {0, 3} (waves 0, 1) or
-  // {1, 2} (waves 2, 3): equal work.  B operand S_n (rows d, columns of tile
-  // u); for its two row blocks, U and the A operands of -W.
+  // {1, 2} (waves 2, 3): equal work.
   const int u = w & 1, col = 16 * u + c;
   auto rowblk = [&](int k) { return w < 2 ? 3 * k : 1 + k; };
-  CS sb[2];
+
+  auto load_in = [&](OutIn& r, int n) {
+    const int chain = n / nch, c0 = 64 * (n % nch), b = chain / H, h = chain % H;
+    const float* const wsn = ws + (size_t)n * kChunkFloats;
 #pragma unroll
-  for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float2 x = *reinterpret_cast<const float2*>(wsn + oS + ((16 * dd + 4 * g + j) * D + col) * 2);
-      sb[dd].v[0][j] = x.x;
-      sb[dd].v[1][j] = x.y;
+    for (int uu = 0; uu < 4; ++uu) {
+      const int unit = tid + 256 * uu, t = min(c0 + (unit >> 4), T - 1), cu = unit & 15;
+      r.q[uu] = *reinterpret_cast<const float4*>(qg + tok(b, t, h, T, H) * (2 * D) + 4 * cu);
+      r.k[uu] = *reinterpret_cast<const float4*>(kg + tok(b, t, h, T, H) * (2 * D) + 4 * cu);
     }
-  CA ut[2];
-  CS nw[2][2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = rowblk(k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float2 x = *reinterpret_cast<const float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2);
-      ut[k].v[0][j] = x.x;
-      ut[k].v[1][j] = x.y;
-    }
+    r.g = wsn[oG + l];
+  };
+
+  OutIn r;
+  load_in(r, blockIdx.x);
+  for (int n = blockIdx.x; n < total; n += gridDim.x) {
+    const int chain = n / nch, c0 = 64 * (n % nch), b = chain / H, h = chain % H;
+    const float* const wsn = ws + (size_t)n * kChunkFloats;
+    // ---------------------------------------------------- workspace operands (used after the P tiles):
+    // B operand S_n (rows d, columns of tile u); for this wave's two row
+    // blocks, U and the A operands of -W.
+    CS sb[2], nw[2][2];
+    CA ut[2];
 #pragma unroll
     for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 x = *reinterpret_cast<const float2*>(wsn + oS + ((16 * dd + 4 * g + j) * D + col) * 2);
+        sb[dd].v[0][j] = x.x;
+        sb[dd].v[1][j] = x.y;
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = rowblk(k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 x = *reinterpret_cast<const float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2);
+        ut[k].v[0][j] = x.x;
+        ut[k].v[1][j] = x.y;
+      }
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          nw[k][dd].v[p] =
+              *reinterpret_cast<const f32x4*>(wsn + oNW + p * (64 * D) + (16 * i + c) * D + 16 * dd + 4 * g);
+    }
+    // ---------------------------------------------------- this chunk's Q, K tiles and decay
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int unit = tid + 256 * uu, row = unit >> 4, cu = unit & 15;
+      const bool in = c0 + row < T;
+      const float4 fq = in ? r.q[uu] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 fk = in ? r.k[uu] : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float2*>(sQ + row * LDK + 2 * cu) = make_float2(fq.x, fq.z);
+      *reinterpret_cast<float2*>(sQ + szK + row * LDK + 2 * cu) = make_float2(fq.y, fq.w);
+      *reinterpret_cast<float2*>(sK + row * LDK + 2 * cu) = make_float2(fk.x, fk.z);
+      *reinterpret_cast<float2*>(sK + szK + row * LDK + 2 * cu) = make_float2(fk.y, fk.w);
+    }
+    if (w == 0) {
+      s_g2[l] = r.g;
+      s_gam[l] = exp2f(r.g);
+    }
+    // ---------------------------------------------------- next chunk's Q, K tiles, in flight from here on
+    load_in(r, min(n + (int)gridDim.x, total - 1));
+    lds_barrier();
+
+    // ---------------------------------------------------- P tiles
+    for (int m = 0; m < 3; ++m) {
+      const int tt = w + 4 * m;
+      if (tt >= 10) break;
+      const int ti = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+      const int tj = tt - tri(ti, 0);
+      CS a[2], bq[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        a[d] = csub_rows(mK, 16 * tj + c, 16 * d);
+        bq[d] = csub_rows(mQ, 16 * ti + c, 16 * d);
+      }
+      CA acc = acc_zero<true>();
+      cmma3<false, true, 2>(acc, a, bq, 2);  // [s][r] = k_s . conj(q_r)
+      const int rr = 16 * ti + c;
+      const float gr = s_g2[rr];
+      CA vp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ss = 16 * tj + 4 * g + j;
+        const float gam = rr >= ss ? exp2f(gr - s_g2[ss]) : 0.f;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) vp.v[p][j] = gam * acc.v[p][j];
+      }
+#pragma unroll
       for (int p = 0; p < 2; ++p)
-        nw[k][dd].v[p] = *reinterpret_cast<const f32x4*>(wsn + oNW + p * (64 * D) + (16 * i + c) * D + 16 * dd + 4 * g);
-  }
-  load_tile(qg, sQ, sQ + szK, b, h, c0, T, H, tid);
-  load_tile(kg, sK, sK + szK, b, h, c0, T, H, tid);
-  if (w == 0) {
-    const float x = wsn[oG + l];
-    s_g2[l] = x;
-    s_gam[l] = exp2f(x);
-  }
-  lds_barrier();
-
-  // ---------------------------------------------------- Ut = U + (-W) S_n, this wave's two tiles
-#pragma unroll
-  for (int k = 0; k < 2; ++k) cmma3<false, false, 2>(ut[k], nw[k], sb, 2);
-
-  // ---------------------------------------------------- P tiles
-  for (int m = 0; m < 3; ++m) {
-    const int tt = w + 4 * m;
-    if (tt >= 10) break;
-    const int ti = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
-    const int tj = tt - tri(ti, 0);
-    CS a[2], bq[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      a[d] = csub_rows(mK, 16 * tj + c, 16 * d);
-      bq[d] = csub_rows(mQ, 16 * ti + c, 16 * d);
+        *reinterpret_cast<f32x4*>(sP + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = vp.v[p];
     }
-    CA acc = acc_zero<true>();
-    cmma3<false, true, 2>(acc, a, bq, 2);  // [s][r] = k_s . conj(q_r)
-    const int r = 16 * ti + c;
-    const float gr = s_g2[r];
-    CA vp;
+    // ---------------------------------------------------- Ut = U + (-W) S_n, this wave's two tiles
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 16 * tj + 4 * g + j;
-      const float gam = r >= s ? exp2f(gr - s_g2[s]) : 0.f;
+    for (int k = 0; k < 2; ++k) cmma3<false, false, 2>(ut[k], nw[k], sb, 2);
+    lds_barrier();
 #pragma unroll
-      for (int p = 0; p < 2; ++p) vp.v[p][j] = gam * acc.v[p][j];
-    }
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *reinterpret_cast<f32x4*>(sP + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = vp.v[p];
-  }
-  lds_barrier();
-  // Ut tiles (row block i, column tile u) go to the K planes, which P no longer
-  // needs, stored transposed so that a B operand is one 16-byte read per plane.
-  float* const sU = sK;
-  auto tileU = [&](int i, int uu, int p) { return sU + ((i * 2 + uu) * 2 + p) * 256; };
+      for (int p = 0; p < 2; ++p) *reinterpret_cast<f32x4*>(tileU(rowblk(k), u, p) + c * 16 + 4 * g) = ut[k].v[p];
+    lds_barrier();
+    CS ub[4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) *reinterpret_cast<f32x4*>(tileU(rowblk(k), u, p) + c * 16 + 4 * g) = ut[k].v[p];
-  lds_barrier();
-  CS ub[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) ub[i].v[p] = *reinterpret_cast<const f32x4*>(tileU(i, u, p) + c * 16 + 4 * g);
+      for (int p = 0; p < 2; ++p) ub[i].v[p] = *reinterpret_cast<const f32x4*>(tileU(i, u, p) + c * 16 + 4 * g);
 
-  // ---------------------------------------------------- output tiles
+    // ---------------------------------------------------- output tiles
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = rowblk(k);
-    CA o = acc_zero<true>();
-    CS a[2];
+    for (int k = 0; k < 2; ++k) {
+      const int i = rowblk(k);
+      CA o = acc_zero<true>();
+      CS a[2];
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd) a[dd] = csub_rows(mQ, 16 * i + c, 16 * dd);
-    cmma3<true, false, 2>(o, a, sb, 2);  // conj(Q) S
+      for (int dd = 0; dd < 2; ++dd) a[dd] = csub_rows(mQ, 16 * i + c, 16 * dd);
+      cmma3<true, false, 2>(o, a, sb, 2);  // conj(Q) S
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float gm = s_gam[16 * i + 4 * g + j];
-      o.v[0][j] *= gm;
-      o.v[1][j] *= gm;
-    }
-    CS pa[4], ubb[4];
+      for (int j = 0; j < 4; ++j) {
+        const float gm = s_gam[16 * i + 4 * g + j];
+        o.v[0][j] *= gm;
+        o.v[1][j] *= gm;
+      }
+      CS pa[4], ubb[4];
 #pragma unroll
-    for (int ip = 0; ip < 4; ++ip) {
-      if (ip <= i) {
-        pa[ip] = csub_rows(tileP(i, ip), c, 0);
-        ubb[ip] = ub[ip];
-      } else {
-        pa[ip] = csub_zero<true, float>();
-        ubb[ip] = csub_zero<true, float>();
+      for (int ip = 0; ip < 4; ++ip) {
+        if (ip <= i) {
+          pa[ip] = csub_rows(tileP(i, ip), c, 0);
+          ubb[ip] = ub[ip];
+        } else {
+          pa[ip] = csub_zero<true, float>();
+          ubb[ip] = csub_zero<true, float>();
+        }
+      }
+      cmma3<false, false, 4>(o, pa, ubb, i + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = c0 + 16 * i + 4 * g + j;
+        if (t < T)
+          *reinterpret_cast<float2*>(og + (tok(b, t, h, T, H) * D + col) * 2) = make_float2(o.v[0][j], o.v[1][j]);
       }
     }
-    cmma3<false, false, 4>(o, pa, ubb, i + 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = c0 + 16 * i + 4 * g + j;
-      if (t < T)
-        *reinterpret_cast<float2*>(og + (tok(b, t, h, T, H) * D + col) * 2) = make_float2(o.v[0][j], o.v[1][j]);
-    }
+    lds_barrier();  // every wave is done with this chunk's Q, K, P and Ut tiles
   }
 }
 
@@ -605,6 +689,16 @@ size_t chunk_cx_workspace_bytes(int B, int T, int H) {
   return (size_t)B * H * nch * cx::kChunkFloats * sizeof(float);
 }
 
+// Two resident workgroups per CU for the persistent chunk kernels.
+static unsigned persistent_grid(unsigned nblk) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 256;
+  const unsigned want = 2u * (unsigned)ncu;
+  return nblk < want ? nblk : want;
+}
+
 hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace) {
   const int nch = (a.T + 63) / 64;
   const int nchains = a.B * a.H;
@@ -613,16 +707,16 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace) {
   const unsigned nblk = (unsigned)((long)nchains * nch);
   hipError_t e = hipSuccess;
   if (nblk > 0) {
-    e = launch_kernel(cx::cx_prep_kernel, dim3(nblk), dim3(256), st, static_cast<const float*>(a.k),
-                      static_cast<const float*>(a.v), a.alpha, a.beta, ws, a.T, a.H, nch);
+    e = launch_kernel(cx::cx_prep_kernel, dim3(persistent_grid(nblk)), dim3(256), st, static_cast<const float*>(a.k),
+                      static_cast<const float*>(a.v), a.alpha, a.beta, ws, a.T, a.H, nch, (int)nblk);
     if (e != hipSuccess) return e;
   }
   e = launch_kernel(cx::cx_scan_kernel, dim3((unsigned)nchains * 4), dim3(256), st,
                     static_cast<const float*>(a.S0), static_cast<float*>(a.S_final), ws, nch);
   if (e != hipSuccess || nblk == 0) return e;
-  return launch_kernel(cx::cx_out_kernel, dim3(nblk), dim3(256), st, static_cast<const float*>(a.q),
+  return launch_kernel(cx::cx_out_kernel, dim3(persistent_grid(nblk)), dim3(256), st, static_cast<const float*>(a.q),
                        static_cast<const float*>(a.k), static_cast<const float*>(ws), static_cast<float*>(a.out),
-                       a.T, a.H, nch);
+                       a.T, a.H, nch, (int)nblk);
 }
 
 }  // namespace gdn
