@@ -291,22 +291,28 @@ __device__ __forceinline__ void diag_p_tile(const f32x4& P, const f32x4& gm, int
 // Loads are unconditional (clamped to the last chunk; with no chunk at all the
 // zero buffer range drops them) and steps come in whole pairs, so the loop has
 // no conditional load path and the compiler keeps the next chunk's loads in
-// flight while this one is processed.  The consumers run the same number of
-// barriers.
-template <class Load, class Process>
-__device__ __forceinline__ void producer_loop(int nch, Load&& load, Process&& process) {
+// flight while this one is processed.  Each step has two barriers: the row
+// waves publish the chunk's K and Q rows in phase A, and the lower Gram waves
+// read them after the mid-step barrier, in phase B, instead of fetching them
+// from HBM again.  The consumers run the same barriers.
+template <class Load, class ProcA, class ProcB>
+__device__ __forceinline__ void producer_loop(int nch, Load&& load, ProcA&& procA, ProcB&& procB) {
   auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
   load(ic<0>{}, clampc(0));
   issue_fence();
   load(ic<1>{}, clampc(1));
   issue_fence();
-  if (nch > 0) process(ic<0>{}, 0);
+  if (nch > 0) procA(ic<0>{}, 0);
+  stage_barrier();
+  if (nch > 0) procB(ic<0>{}, 0);
   stage_barrier();
   auto iter = [&](auto pc, int n) {
     constexpr int par = decltype(pc)::value;
     load(ic<par>{}, clampc(n + 2));
     issue_fence();
-    if (n + 1 < nch) process(ic<par ^ 1>{}, n + 1);
+    if (n + 1 < nch) procA(ic<par ^ 1>{}, n + 1);
+    stage_barrier();
+    if (n + 1 < nch) procB(ic<par ^ 1>{}, n + 1);
     stage_barrier();
   };
   for (int n = 0; n < nch; n += 2) {
@@ -358,11 +364,11 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
     st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
     st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
   };
-  auto process = [&](auto sc, int n) {
+  auto procA = [&](auto sc, int n) {
     constexpr int s = decltype(sc)::value;  // register set == stage buffer == n & 1
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;
-    // K and Q rows of both blocks, for the consumers
+    // K and Q rows of both blocks, for the lower Gram waves and the consumers
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -371,6 +377,11 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
         *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
         *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
       }
+  };
+  auto process = [&](auto sc, int n) {
+    constexpr int s = decltype(sc)::value;
+    const Set& S = st[s];
+    __bf16* const R = sb + s * Cf::szBuf;
     gate_scan(S.a, S.b, n * 64, T, l, PGT);
     // accumulator [s][r]: s from the A operand (column block), r from the B
     // operand (row block)
@@ -389,15 +400,16 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
     diag_p_tile<DK>(P1, gm1, b0 + 1, g, c, R);
     diag_inverse<DK>(Gd, gm0, PGT, DS, b0, g, c, R + Cf::oTP + b0 * Cf::szTile);
   };
-  producer_loop(x.nchunks, load, process);
+  producer_loop(x.nchunks, load, procA, process);
 }
 
 // Waves 4 and 5: row block i = 2 / 3 below the first two column blocks, tiles
-// (i, 0) and (i, 1), and the inverse of diagonal block 1 / 3.
+// (i, 0) and (i, 1), and the inverse of diagonal block 1 / 3, from the K and Q
+// rows the row waves publish in phase A of the same step.
 template <int DK>
 __device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<DK>;
-  constexpr int NKP = Cf::NKP;
+  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
   __bf16* const sb = reinterpret_cast<__bf16*>(smem);
   float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
   float* const PGT = sf + Cf::fPGT + i * Cf::szPGT;  // tables 2 and 3
@@ -405,58 +417,49 @@ __device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, 
   const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
   const int id = i == 2 ? 1 : 3;  // diagonal block inverted here
   const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = span_bytes((size_t)T * H * DK * 2, (size_t)x.h * DK * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
   const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
-  const int rowK = H * DK * 2;
-  int vof0[NKP], vof1[NKP], vofi[NKP];
-#pragma unroll
-  for (int p = 0; p < NKP; ++p) {
-    vof0[p] = c * rowK + 64 * p + 16 * g;
-    vof1[p] = (16 + c) * rowK + 64 * p + 16 * g;
-    vofi[p] = (16 * i + c) * rowK + 64 * p + 16 * g;
-  }
   struct Set {
-    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
     float a, b;
   };
   Set st[2];
   auto load = [&](auto sc, int n) {
     constexpr int s = decltype(sc)::value;
     const int c0 = n * 64;
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      st[s].k0[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof0[p], c0 * rowK, 0));
-      st[s].k1[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vof1[p], c0 * rowK, 0));
-      st[s].ki[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofi[p], c0 * rowK, 0));
-      st[s].qi[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofi[p], c0 * rowK, 0));
-    }
     st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
     st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
   };
+  // Phase B: the chunk's K and Q rows, published by the row waves in phase A.
   auto process = [&](auto sc, int n) {
     constexpr int s = decltype(sc)::value;
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;
+    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      const int o = c * LDK + 32 * p + 8 * g;
+      k0[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
+      k1[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * LDK + o);
+      ki[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + o);
+      qi[p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + o);
+    }
     gate_scan(S.a, S.b, n * 64, T, l, PGT);
     f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4(), Gd = zero4();
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      G0 = mma32(S.k0[p], S.ki[p], G0);
-      P0 = mma32(S.k0[p], S.qi[p], P0);
-      G1 = mma32(S.k1[p], S.ki[p], G1);
-      P1 = mma32(S.k1[p], S.qi[p], P1);
-      const u32x4 kd = id == 1 ? S.k1[p] : S.ki[p];  // uniform choice
+      G0 = mma32(k0[p], ki[p], G0);
+      P0 = mma32(k0[p], qi[p], P0);
+      G1 = mma32(k1[p], ki[p], G1);
+      P1 = mma32(k1[p], qi[p], P1);
+      const u32x4 kd = id == 1 ? k1[p] : ki[p];  // uniform choice
       Gd = mma32(kd, kd, Gd);
     }
     offdiag_tiles<DK>(G0, P0, PGT, i, 0, g, c, R);
     offdiag_tiles<DK>(G1, P1, PGT, i, 1, g, c, R);
     diag_inverse<DK>(Gd, diag_gamma(PGT, id, g, c), PGT, DS, id, g, c, R + Cf::oTP + id * Cf::szTile);
   };
-  producer_loop(x.nchunks, load, process);
+  producer_loop(x.nchunks, load, [](auto, int) {}, process);
 }
 
 // Wave 6: the 64 x 32 V tile of the chunk, and gamma, lambda and gamma_C.
@@ -505,7 +508,7 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
     G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
     if (l == 63) G[128] = __builtin_amdgcn_exp2f(gC);
   };
-  producer_loop(x.nchunks, load, process);
+  producer_loop(x.nchunks, load, process, [](auto, int) {});
 }
 
 // ---------------------------------------------------------------- consumers
@@ -707,13 +710,13 @@ __device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l)
   const float* const sf = reinterpret_cast<const float*>(smem + Cf::fBase);
   Consumer<DK> cs;
   cs.init(x, w, l);
-  stage_barrier();  // prologue: chunk 0 staged
+  stage_barrier();  // prologue: chunk 0 staged (two barriers, as in every step)
+  stage_barrier();
   auto body = [&](auto bufc, int n) {
     constexpr int BUF = decltype(bufc)::value;
-    if (n < x.nchunks) {
-      cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
-      cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
-    }
+    if (n < x.nchunks) cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
+    stage_barrier();  // mid-step: the producers' phase A is done
+    if (n < x.nchunks) cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
     stage_barrier();
   };
   // whole pairs of steps, matching the producers' barrier count
