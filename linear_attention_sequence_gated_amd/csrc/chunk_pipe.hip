@@ -308,9 +308,12 @@ __device__ __forceinline__ void producer_loop(int nch, Load&& load, ProcA&& proc
   stage_barrier();
   auto iter = [&](auto pc, int n) {
     constexpr int par = decltype(pc)::value;
+    // Phase A first (it only moves registers of chunk n + 1 to LDS), so the
+    // mid-step barrier is not held up by issuing chunk n + 2's loads.
+    if (n + 1 < nch) procA(ic<par ^ 1>{}, n + 1);
+    issue_fence();
     load(ic<par>{}, clampc(n + 2));
     issue_fence();
-    if (n + 1 < nch) procA(ic<par ^ 1>{}, n + 1);
     stage_barrier();
     if (n + 1 < nch) procB(ic<par ^ 1>{}, n + 1);
     stage_barrier();
