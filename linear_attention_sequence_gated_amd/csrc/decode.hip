@@ -23,7 +23,19 @@ template <> struct StepIn<kDtF32> { typedef float el; };
 template <> struct StepIn<kDtBF16> { typedef __bf16 el; };
 template <> struct StepIn<kDtC64> { typedef float el; };
 
-// TPS threads per state.  Each thread holds NP rows x one 16-byte column group.
+// Element e of a run of El values held as 32-bit words, as fp32 (bf16 halves
+// are taken with shifts, never by extracting a 16-bit vector element).
+template <class El> __device__ __forceinline__ float elem(const uint32_t* w, int e) {
+  if constexpr (std::is_same_v<El, __bf16>) {
+    const uint32_t u = w[e >> 1];
+    return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+  } else {
+    return __uint_as_float(w[e]);
+  }
+}
+
+// TPS threads per state.  Each thread holds NP consecutive rows x one 16-byte
+// column group, so its slices of k and q are contiguous 16-byte-aligned runs.
 template <int DT, int D, int TPS>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg, const void* __restrict__ kg,
                                                      const void* __restrict__ vg, const float* __restrict__ alpha,
@@ -54,15 +66,33 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
   const El* v = static_cast<const El*>(vg) + (size_t)sts * D * NC;
   float4* Sv = reinterpret_cast<float4*>(S + (size_t)sts * D * D * NC);
   const float a = alpha[sts], bt = beta[sts];
+  const int row0 = NP * rg;  // this thread's rows row0 .. row0 + NP - 1
+
+  // k and q over this thread's rows, and v over its columns, as 16-byte loads.
+  constexpr int KW = NP * NC * (int)sizeof(El) / 4;  // 32-bit words
+  static_assert(KW % 4 == 0, "row runs of k and q are whole 16-byte units");
+  uint32_t kw[KW], qw[KW];
+#pragma unroll
+  for (int i = 0; i < KW / 4; ++i) {
+    reinterpret_cast<uint4*>(kw)[i] = reinterpret_cast<const uint4*>(k + row0 * NC)[i];
+    reinterpret_cast<uint4*>(qw)[i] = reinterpret_cast<const uint4*>(q + row0 * NC)[i];
+  }
+  constexpr int VW = VC * NC * (int)sizeof(El) / 4;
+  uint32_t vw[VW];
+  if constexpr (VW == 4) {
+    *reinterpret_cast<uint4*>(vw) = *reinterpret_cast<const uint4*>(v + cg * VC * NC);
+  } else {
+    static_assert(VW == 2, "column group of v is 8 or 16 bytes");
+    *reinterpret_cast<uint2*>(vw) = *reinterpret_cast<const uint2*>(v + cg * VC * NC);
+  }
 
   float4 s[NP];
   float kr[NP][NC];
 #pragma unroll
   for (int m = 0; m < NP; ++m) {
-    const int row = rg + RPP * m;
-    s[m] = Sv[(row * D * NC) / 4 + cg];
+    s[m] = Sv[((row0 + m) * D * NC) / 4 + cg];
 #pragma unroll
-    for (int p = 0; p < NC; ++p) kr[m][p] = static_cast<float>(k[row * NC + p]);
+    for (int p = 0; p < NC; ++p) kr[m][p] = elem<El>(kw, m * NC + p);
   }
 
   // partial reductions over this thread's rows
@@ -71,10 +101,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
   for (int i = 0; i < NRED; ++i) red_v[i] = 0.f;
 #pragma unroll
   for (int m = 0; m < NP; ++m) {
-    const int row = rg + RPP * m;
     const float* sv = reinterpret_cast<const float*>(&s[m]);
     if constexpr (!CX) {
-      const float qv = static_cast<float>(q[row]);
+      const float qv = elem<El>(qw, m);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         red_v[e] += sv[e] * kr[m][0];
@@ -82,7 +111,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
       }
       red_v[8] += kr[m][0] * qv;
     } else {
-      const float qre = q[2 * row], qim = q[2 * row + 1];
+      const float qre = elem<El>(qw, 2 * m), qim = elem<El>(qw, 2 * m + 1);
       const float kre = kr[m][0], kim = kr[m][1];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -123,10 +152,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
   float ut[VC][NC], o[VC][NC];
 #pragma unroll
   for (int e = 0; e < VC; ++e) {
-    const int col = cg * VC + e;
 #pragma unroll
     for (int p = 0; p < NC; ++p) {
-      const float vv = static_cast<float>(v[col * NC + p]);
+      const float vv = elem<El>(vw, e * NC + p);
       ut[e][p] = bt * (vv - a * red_v[e * NC + p]);
     }
     if constexpr (!CX) {
@@ -141,7 +169,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
   // S <- alpha S + k ut^T
 #pragma unroll
   for (int m = 0; m < NP; ++m) {
-    const int row = rg + RPP * m;
     float* sv = reinterpret_cast<float*>(&s[m]);
 #pragma unroll
     for (int e = 0; e < VC; ++e) {
@@ -153,7 +180,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qg
         sv[2 * e + 1] = a * sim + (kr[m][0] * ut[e][1] + kr[m][1] * ut[e][0]);
       }
     }
-    Sv[(row * D * NC) / 4 + cg] = s[m];
+    Sv[((row0 + m) * D * NC) / 4 + cg] = s[m];
   }
   if (rg == 0) {
     El* out = static_cast<El*>(outg) + (size_t)st * D * NC;
