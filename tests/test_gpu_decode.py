@@ -49,6 +49,20 @@ def test_decode_small(dtype, d, N):
     check_steps(f"decode_{dtype}_{d}", inp, dtype, outs, states)
 
 
+# Two rounds per workgroup start at 1024 groups of 256 / TPS states (4 states per group for d = 64 and
+# complex d = 32, one for d = 128); each N leaves the last workgroup's second round partly or wholly past N.
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 64, 4099), ("f32", 64, 4101), ("f32", 128, 1027),
+                                       ("c64", 32, 4097)])
+def test_decode_two_rounds_ragged(dtype, d, N):
+    """Grids large enough for two states per wave, with a last workgroup whose second round is past N
+    (it loads state N - 1 and must store nothing): every state compared, including the last one."""
+    torch_dev()
+    inp = gen_decode(N, d, d, 3, dtype=dtype, seed=31 + N, beta_scale=2.0 if dtype == "c64" else 1.0)
+    note(f"decode two rounds dtype={dtype} d={d} N={N}")
+    outs, states = run_steps(inp, dtype)
+    check_steps(f"decode_rounds_{dtype}_{d}_{N}", inp, dtype, outs, states)
+
+
 def test_decode_full_workload():
     """4096 states x 64 steps, every state and step compared."""
     torch_dev()
