@@ -73,7 +73,7 @@ class Workload:
         return self.B * self.T
 
 
-# The five workloads the pages' models suggest (see the design doc for the mapping).
+# The five workloads, shaped like the models the pages describe.
 WORKLOADS = {
     "single_head_f32": Workload(
         "single_head_f32", "chunk", "f32", B=1, T=256, H=1, dk=64, dv=64, seed=0,

@@ -20,7 +20,7 @@ def torch_dev():
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
     import linear_attention_sequence_gated_amd as gdn
-    gdn.load()  # on a GPU machine the library must load; a missing build is an error, not a skip
+    gdn.load()  # where a GPU is present the library must load; a missing build is an error, not a skip
     return torch
 
 
