@@ -40,7 +40,7 @@ namespace cx {
 constexpr int D = 32;         // key = value head size (complex elements)
 constexpr int LDK = D + 4;    // LDS row stride (floats) of a [64][32] plane
 constexpr int LD16 = 16 + 4;  // LDS row stride of a 16x16 tile
-constexpr int szK = 64 * LDK, szTri = 10 * 16 * LD16, szTd = 4 * 16 * LD16;
+constexpr int szK = 64 * LDK, szTri = 10 * 16 * LD16;
 
 // Workspace of one chunk, in floats.
 constexpr int wG = 64;           // log2 cumulative decay within the chunk
@@ -131,7 +131,12 @@ __device__ __forceinline__ void inv_rows(f32x4& tr, f32x4& ti, const float (&nar
 }
 constexpr int LDT = 64 + 4;  // LDS row stride of a [32][64] plane
 constexpr int szKT = D * LDT;
-constexpr int kPrepFloats = 2 * szK + 2 * szTri + 2 * szTd + 2 * szKT + 4 * 64;
+// LDS of the prep kernel: the K planes, the -A tiles and the gates.  Each
+// diagonal inverse overwrites its own diagonal tile of -A, and (diag(lambda)
+// K)^T is formed over the -A tiles once every wave has finished its
+// substitution, so three workgroups fit in a CU.
+constexpr int kPrepFloats = 2 * szK + 2 * szTri + 4 * 64;
+static_assert(2 * szKT <= 2 * szTri, "(diag(lambda) K)^T fits over the -A tiles");
 
 // Prefetched operands of one prep chunk for one thread.
 struct PrepIn {
@@ -142,23 +147,23 @@ struct PrepIn {
 // Persistent, like the output kernel: chunks blockIdx.x, + gridDim.x, ...,
 // with the next chunk's K and gates loaded during the current one.  V is
 // loaded at the start of its chunk and first used after the Gram tiles and
-// the inverses.
-__global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
+// the inverses.  Three workgroups per CU.
+__global__ __launch_bounds__(256, 3) void cx_prep_kernel(const float* __restrict__ kg, const float* __restrict__ vg,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta, float* __restrict__ ws,
                                                       int T, int H, int nch, int total) {
   __shared__ __attribute__((aligned(16))) float smem[kPrepFloats];
   float* const sK = smem;                 // planes re, im
-  float* const sA = sK + 2 * szK;         // -A, packed lower 16x16 tiles, 2 planes
-  float* const sTd = sA + 2 * szTri;      // (I + A_ii)^{-1}, 2 planes
-  float* const sKT = sTd + 2 * szTd;      // (diag(lambda) K)^T, 2 planes
-  float* const s_g2 = sKT + 2 * szKT;     // log2 cumulative decay
+  float* const sA = sK + 2 * szK;         // -A, packed lower 16x16 tiles, 2 planes;
+                                          // diagonal tiles become (I + A_ii)^{-1}
+  float* const sKT = sA;                  // (diag(lambda) K)^T, 2 planes, after the substitution
+  float* const s_g2 = sA + 2 * szTri;     // log2 cumulative decay
   float* const s_beta = s_g2 + 64;
   float* const s_gam = s_g2 + 128;
   float* const s_lam = s_g2 + 192;
   const M mK{sK, LDK, szK};
   auto tileA = [&](int i, int j) { return M{sA + tri(i, j) * 16 * LD16, LD16, szTri}; };
-  auto tileT = [&](int i) { return M{sTd + i * 16 * LD16, LD16, szTd}; };
+  auto tileT = [&](int i) { return tileA(i, i); };  // (I + A_ii)^{-1} once inverted
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, c = l & 15;
   // Loads are unconditional: rows past T are clamped and their values replaced
@@ -258,24 +263,14 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
     for (int p = 0; p < 2; ++p)
       *reinterpret_cast<f32x4*>(sA + p * szTri + tt * 16 * LD16 + c * LD16 + 4 * g) = va.v[p];
   }
-  // (diag(lambda) K)^T into LDS, for M_n and B_n.  Consecutive lanes take
-  // consecutive key columns so the transposing reads are conflict free.
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int unit = tid + 256 * u, d = unit & 31, t4 = 4 * ((unit >> 5) & 15), p = unit >> 9;
-    const float* src = sK + p * szK + d;
-    f32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = s_lam[t4 + j] * src[(t4 + j) * LDK];
-    *reinterpret_cast<f32x4*>(sKT + p * szKT + d * LDT + t4) = o;
-  }
   lds_barrier();
 
   // ---------------------------------------------------- diagonal inverses
   // Wave w inverts (I + A_ww) by forward substitution over rows: lane (g, c)
   // owns row c, complex columns 4g .. 4g + 3.  Once row m is final it is
   // broadcast along each 16-lane row (DPP row_newbcast) and added, scaled by
-  // -A[c][m], to every row (rows c <= m have A[c][m] = 0).
+  // -A[c][m], to every row (rows c <= m have A[c][m] = 0).  The inverse
+  // replaces the tile: only this wave reads it, and all its reads come first.
   {
     const float* At = sA + tri(w, w) * 16 * LD16 + c * LD16;
     float nar[16], nai[16];  // -A[c][m], row c of the tile
@@ -293,8 +288,8 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) tr[j] = c == 4 * g + j ? 1.f : 0.f;
     inv_rows<0>(tr, ti, nar, nai);
-    *reinterpret_cast<f32x4*>(sTd + w * 16 * LD16 + c * LD16 + 4 * g) = tr;
-    *reinterpret_cast<f32x4*>(sTd + szTd + w * 16 * LD16 + c * LD16 + 4 * g) = ti;
+    *reinterpret_cast<f32x4*>(sA + tri(w, w) * 16 * LD16 + c * LD16 + 4 * g) = tr;
+    *reinterpret_cast<f32x4*>(sA + szTri + tri(w, w) * 16 * LD16 + c * LD16 + 4 * g) = ti;
   }
   lds_barrier();
 
@@ -358,18 +353,6 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int p = 0; p < 2; ++p) wsn[oNW + p * (64 * D) + (16 * i + 4 * g + j) * D + col] = -X[i].v[p][j];
-    // M_n column tile w: gamma_C I - (diag(lambda) K)^T W.
-    const float gC = s_gam[63];
-#pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      const CA m = kl_times_x(dd);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 16 * dd + 4 * g + j;
-        wsn[oM + d * D + col] = (d == col ? gC : 0.f) - m.v[0][j];
-        wsn[oM + D * D + d * D + col] = -m.v[1][j];
-      }
-    }
   } else {
     // U column tile w - 2: R = diag(beta) V.
     const int col = 16 * (w - 2) + c;
@@ -390,7 +373,39 @@ __global__ __launch_bounds__(256, 2) void cx_prep_kernel(const float* __restrict
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float2*>(wsn + oU + ((16 * i + 4 * g + j) * D + col) * 2) =
             make_float2(X[i].v[0][j], X[i].v[1][j]);
+  }
+  lds_barrier();  // every wave is done with the -A tiles and the inverses
+
+  // (diag(lambda) K)^T over the -A tiles, for M_n and B_n.  Consecutive lanes
+  // take consecutive key columns so the transposing reads are conflict free.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit = tid + 256 * u, d = unit & 31, t4 = 4 * ((unit >> 5) & 15), p = unit >> 9;
+    const float* src = sK + p * szK + d;
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = s_lam[t4 + j] * src[(t4 + j) * LDK];
+    *reinterpret_cast<f32x4*>(sKT + p * szKT + d * LDT + t4) = o;
+  }
+  lds_barrier();
+
+  if (w < 2) {
+    // M_n column tile w: gamma_C I - (diag(lambda) K)^T W.
+    const int col = 16 * w + c;
+    const float gC = s_gam[63];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      const CA m = kl_times_x(dd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 16 * dd + 4 * g + j;
+        wsn[oM + d * D + col] = (d == col ? gC : 0.f) - m.v[0][j];
+        wsn[oM + D * D + d * D + col] = -m.v[1][j];
+      }
+    }
+  } else {
     // B_n column tile w - 2: (diag(lambda) K)^T U.
+    const int col = 16 * (w - 2) + c;
 #pragma unroll
     for (int dd = 0; dd < 2; ++dd) {
       const CA bn = kl_times_x(dd);
@@ -689,13 +704,13 @@ size_t chunk_cx_workspace_bytes(int B, int T, int H) {
   return (size_t)B * H * nch * cx::kChunkFloats * sizeof(float);
 }
 
-// Two resident workgroups per CU for the persistent chunk kernels.
-static unsigned persistent_grid(unsigned nblk) {
+// `per_cu` resident workgroups per CU for the persistent chunk kernels.
+static unsigned persistent_grid(unsigned nblk, unsigned per_cu) {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
     ncu = 256;
-  const unsigned want = 2u * (unsigned)ncu;
+  const unsigned want = per_cu * (unsigned)ncu;
   return nblk < want ? nblk : want;
 }
 
@@ -707,14 +722,14 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace) {
   const unsigned nblk = (unsigned)((long)nchains * nch);
   hipError_t e = hipSuccess;
   if (nblk > 0) {
-    e = launch_kernel(cx::cx_prep_kernel, dim3(persistent_grid(nblk)), dim3(256), st, static_cast<const float*>(a.k),
+    e = launch_kernel(cx::cx_prep_kernel, dim3(persistent_grid(nblk, 3)), dim3(256), st, static_cast<const float*>(a.k),
                       static_cast<const float*>(a.v), a.alpha, a.beta, ws, a.T, a.H, nch, (int)nblk);
     if (e != hipSuccess) return e;
   }
   e = launch_kernel(cx::cx_scan_kernel, dim3((unsigned)nchains * 4), dim3(256), st,
                     static_cast<const float*>(a.S0), static_cast<float*>(a.S_final), ws, nch);
   if (e != hipSuccess || nblk == 0) return e;
-  return launch_kernel(cx::cx_out_kernel, dim3(persistent_grid(nblk)), dim3(256), st, static_cast<const float*>(a.q),
+  return launch_kernel(cx::cx_out_kernel, dim3(persistent_grid(nblk, 2)), dim3(256), st, static_cast<const float*>(a.q),
                        static_cast<const float*>(a.k), static_cast<const float*>(ws), static_cast<float*>(a.out),
                        a.T, a.H, nch, (int)nblk);
 }
