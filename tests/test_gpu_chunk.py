@@ -153,3 +153,35 @@ def test_chunk_full_size_sampled_chains(wname, chains):
     S_s = np.stack([S[b, h] for b, h in chains])[None]
     assert_close(f"full_{wname}", w.dtype, o_s, S_s, o_ref, S_ref)
     assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+def test_chunk_bf16_rows_beyond_32bit_offsets():
+    """bf16, d = 64, with T * H * 64 * 2 >= 2^31 bytes in one batch row, so offsets into q, k, v and o
+    no longer fit 32 bits and the library runs the fused kernel with 64-bit addressing.  Inputs are drawn
+    on the device from a seeded generator, with the distributions of the bf16 layer workload.  The first
+    and the last head (whose late rows lie past the 2 GiB offset) are checked against the oracle."""
+    import oracle
+    torch = torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    B, T, H, d = 1, 65536, 256, 64
+    assert T * H * d * 2 >= 2 ** 31
+    note(f"chunk bf16 rows beyond 32-bit offsets: B{B} T{T} H{H} d{d}")
+    gen = torch.Generator(device="cuda").manual_seed(2031)
+
+    def unit_rows():
+        x = torch.randn((B, T, H, d), generator=gen, device="cuda")
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q, k = unit_rows(), unit_rows()
+    v = torch.randn((B, T, H, d), generator=gen, device="cuda").to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn((B, T, H), generator=gen, device="cuda"))
+    alpha = torch.exp(-torch.nn.functional.softplus(torch.randn((B, T, H), generator=gen, device="cuda") - 4.0))
+    o, S = gdn.chunk_fwd(q, k, v, alpha, beta, None)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        chain = lambda t: t[:, :, h:h + 1].float().cpu().numpy()
+        o_ref, S_ref, _ = oracle.recurrent_fwd(chain(q), chain(k), chain(v), chain(alpha), chain(beta), None)
+        eo, es = chain_rel_errors(chain(o), S[:, h:h + 1].cpu().numpy(), o_ref, S_ref)
+        print(f"[parity] bf16 rows beyond 32-bit offsets, head {h}: o={eo:.3e} S={es:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (h, eo, es)
