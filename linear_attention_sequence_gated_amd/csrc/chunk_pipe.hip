@@ -514,6 +514,39 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
   producer_loop(x.nchunks, load, process, [](auto, int) {});
 }
 
+// ---------------------------------------------------------------- output
+// The output is computed transposed, so that each lane holds four consecutive
+// value columns of one token:
+//   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{j <= i} Ut_j^T P_ij^T.
+// For one 16-column tile, lane (g, c) gets token 16 i + c, columns 4g .. 4g + 3.
+// First term: s = the state's bf16 operands for the tile (2 NKP sub-blocks),
+// qr = Q rows of block i, gm = gamma of the lane's token.
+template <int NKP>
+__device__ __forceinline__ f32x4 out_qs(const u32x2* s, const u32x2 (&qr)[NKP][2], float gm) {
+  f32x4 o = zero4();
+#pragma unroll
+  for (int p = 0; p < NKP; ++p) o = mma2(s[2 * p], s[2 * p + 1], qr[p][0], qr[p][1], o);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] *= gm;
+  return o;
+}
+
+// Second term, added to o: X[j][t] = Ut_j for the tile, Pm the ten lower P tiles.
+template <int NTT>
+__device__ __forceinline__ f32x4 out_pu(f32x4 o, int i, int t, const u32x2 (&X)[4][NTT], const u32x2 (&Pm)[10]) {
+  if (i == 0) o = mma1(X[0][t], Pm[tri(0, 0)], o);
+  if (i == 1) o = mma2(X[0][t], X[1][t], Pm[tri(1, 0)], Pm[tri(1, 1)], o);
+  if (i == 2) {
+    o = mma2(X[0][t], X[1][t], Pm[tri(2, 0)], Pm[tri(2, 1)], o);
+    o = mma2(X[2][t], z4(), Pm[tri(2, 2)], z4(), o);
+  }
+  if (i == 3) {
+    o = mma2(X[0][t], X[1][t], Pm[tri(3, 0)], Pm[tri(3, 1)], o);
+    o = mma2(X[2][t], X[3][t], Pm[tri(3, 2)], Pm[tri(3, 3)], o);
+  }
+  return o;
+}
+
 // ---------------------------------------------------------------- consumers
 // A consumer wave owns value columns 16 NT w .. 16 NT (w + 1) - 1 of the
 // workgroup's slice, as NT 16-column tiles t.  The state lives in MFMA
@@ -558,8 +591,9 @@ struct Consumer {
 
   // First half of a chunk, which needs only operands published a step earlier:
   // V and gamma from stage buffer R / gate table G, and K S for the current
-  // state.
-  __device__ __forceinline__ void begin(const __bf16* R, const float* G) {
+  // state.  With `pub` set, lane l also writes the state's bf16 operands
+  // sfr[t][d] to pub[2 ((t NDT + d) 64 + l)] for a wave that forms the output.
+  __device__ __forceinline__ void begin(const __bf16* R, const float* G, unsigned* pub = nullptr) {
     u32x2 kr[4][NKP][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -577,7 +611,10 @@ struct Consumer {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int d = 0; d < NDT; ++d) sfr[t][d] = cvt4(S[t][d]);
+      for (int d = 0; d < NDT; ++d) {
+        sfr[t][d] = cvt4(S[t][d]);
+        if (pub) *reinterpret_cast<u32x2*>(pub + 2 * ((t * NDT + d) * 64 + 16 * g + c)) = sfr[t][d];
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -589,30 +626,41 @@ struct Consumer {
       }
   }
 
-  // Rest of chunk n (after begin() on the same stage buffer): the diagonal
-  // factors T_ii diag(beta_i) and -Gt, the substitution, the state update and
-  // the output.  G holds gamma (G[0..63]) and lambda (G[64..127]) per token and
-  // gamma_C at G[gCoff].
-  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
+  // Operands of the state update, loaded with the diagonal factors so that
+  // they are in flight during the substitution.
+  struct Upd {
+    u32x2 kt[NDT][4];
+    f32x4 lm[4];
+    float gC;
+  };
+  // Operands of the output: Q rows, gamma per token, the ten P tiles.
+  struct OutOps {
+    u32x2 qr[4][NKP][2], Pm[10];
+    float gm[4];
+  };
+
+  // Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S) of the chunk in
+  // stage buffer R, block rows in order (after begin() on the same buffer):
+  // Xf = Ut and XL = lambda * Ut as bf16 operands.  G holds gamma (G[0..63])
+  // and lambda (G[64..127]) per token and gamma_C at G[gCoff].  With `pub`
+  // set, lane l also writes Xf[i][t] to pub[2 ((i NT + t) 64 + l)] for a wave
+  // that forms the output.
+  __device__ __forceinline__ void solve(const __bf16* R, const float* G, int gCoff, Upd& u, u32x2 (&Xf)[4][NT],
+                                        u32x2 (&XL)[4][NT], unsigned* pub) {
     auto tile = [&](int o) { return ld4(R + o + offT16); };
-    // ---- Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S), block rows in order
     u32x2 TP[4], NG[6];
 #pragma unroll
     for (int i = 0; i < 4; ++i) TP[i] = tile(Cf::oTP + i * Cf::szTile);
 #pragma unroll
     for (int e = 0; e < 6; ++e) NG[e] = tile(Cf::oNG + e * Cf::szTile);
-    // operands of the state update, in flight during the substitution
-    u32x2 kt[NDT][4];
-    f32x4 lm[4];
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kt[d][i] = ld4_tr(R + Cf::oK + 16 * i * LDK + 16 * d + offTrK);
+      for (int i = 0; i < 4; ++i) u.kt[d][i] = ld4_tr(R + Cf::oK + 16 * i * LDK + 16 * d + offTrK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lm[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
-    const float gC = G[gCoff];
+    for (int i = 0; i < 4; ++i) u.lm[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
+    u.gC = G[gCoff];
     issue_fence();
-    u32x2 Xf[4][NT], XL[4][NT];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -632,64 +680,67 @@ struct Consumer {
         }
         const f32x4 X = mma1(TP[i], cvt4(y), zero4());
         Xf[i][t] = cvt4(X);
+        if (pub) *reinterpret_cast<u32x2*>(pub + 2 * ((i * NT + t) * 64 + 16 * g + c)) = Xf[i][t];
         f32x4 xl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xl[j] = X[j] * lm[i][j];
+        for (int j = 0; j < 4; ++j) xl[j] = X[j] * u.lm[i][j];
         XL[i][t] = cvt4(xl);
       }
-    // operands of the output, in flight during the state update
-    u32x2 qr[4][NKP][2], Pm[10];
-    float gm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
-        qr[i][p][0] = ld4(pr);
-        qr[i][p][1] = ld4(pr + 16);
-      }
-      gm[i] = G[16 * i + c];  // gamma of token 16i + c
-    }
-#pragma unroll
-    for (int e = 0; e < 10; ++e) Pm[e] = tile(Cf::oP + e * Cf::szTile);
-    issue_fence();
-    // S <- gamma_C S + K^T (lambda * Ut)
+  }
+
+  // S <- gamma_C S + K^T (lambda * Ut)
+  __device__ __forceinline__ void update(const Upd& u, const u32x2 (&XL)[4][NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int d = 0; d < NDT; ++d) {
         f32x4 sd = S[t][d];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sd[j] *= gC;
-        sd = mma2(kt[d][0], kt[d][1], XL[0][t], XL[1][t], sd);
-        sd = mma2(kt[d][2], kt[d][3], XL[2][t], XL[3][t], sd);
+        for (int j = 0; j < 4; ++j) sd[j] *= u.gC;
+        sd = mma2(u.kt[d][0], u.kt[d][1], XL[0][t], XL[1][t], sd);
+        sd = mma2(u.kt[d][2], u.kt[d][3], XL[2][t], XL[3][t], sd);
         S[t][d] = sd;
       }
-    // ---- output, computed transposed so each lane holds four consecutive
-    // value columns of one token:
-    //   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{j <= i} Ut_j^T P_ij^T.
+  }
+
+  __device__ __forceinline__ void load_out(const __bf16* R, const float* G, OutOps& op) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
+        op.qr[i][p][0] = ld4(pr);
+        op.qr[i][p][1] = ld4(pr + 16);
+      }
+      op.gm[i] = G[16 * i + c];  // gamma of token 16i + c
+    }
+#pragma unroll
+    for (int e = 0; e < 10; ++e) op.Pm[e] = ld4(R + Cf::oP + e * Cf::szTile + offT16);
+  }
+
+  // Output of chunk n from the state at its start (sfr) and Ut.
+  __device__ __forceinline__ void output(const OutOps& op, const u32x2 (&Xf)[4][NT], int n) {
     const int c0 = n * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        f32x4 o = zero4();
-#pragma unroll
-        for (int p = 0; p < NKP; ++p) o = mma2(sfr[t][2 * p], sfr[t][2 * p + 1], qr[i][p][0], qr[i][p][1], o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= gm[i];
-        if (i == 0) o = mma1(Xf[0][t], Pm[tri(0, 0)], o);
-        if (i == 1) o = mma2(Xf[0][t], Xf[1][t], Pm[tri(1, 0)], Pm[tri(1, 1)], o);
-        if (i == 2) {
-          o = mma2(Xf[0][t], Xf[1][t], Pm[tri(2, 0)], Pm[tri(2, 1)], o);
-          o = mma2(Xf[2][t], z4(), Pm[tri(2, 2)], z4(), o);
-        }
-        if (i == 3) {
-          o = mma2(Xf[0][t], Xf[1][t], Pm[tri(3, 0)], Pm[tri(3, 1)], o);
-          o = mma2(Xf[2][t], Xf[3][t], Pm[tri(3, 2)], Pm[tri(3, 3)], o);
-        }
+        const f32x4 o = out_pu(out_qs<NKP>(sfr[t], op.qr[i], op.gm[i]), i, t, Xf, op.Pm);
         __builtin_amdgcn_raw_buffer_store_b64(cvt4(o), ro, vofO + 32 * t, (c0 + 16 * i) * rowO, 0);
       }
+  }
+
+  // Rest of chunk n (after begin() on the same stage buffer): the
+  // substitution, the state update and the output.
+  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
+    Upd u;
+    u32x2 Xf[4][NT], XL[4][NT];
+    solve(R, G, gCoff, u, Xf, XL, nullptr);
+    OutOps op;  // in flight during the state update
+    load_out(R, G, op);
+    issue_fence();
+    update(u, XL);
+    output(op, Xf, n);
   }
 
   __device__ __forceinline__ void finish(const Ctx& x) {
@@ -777,17 +828,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf1
 
 // ============================================================================
 // Three-stage variant (dk = 64).  Per step k of the loop (one barrier each):
-//   Gram waves 2, 3 and the V wave 6 build chunk k + 2 (K/Q/V rows, gates,
+//   Gram waves 2, 3 and wave 5 build chunk k + 2 (K/Q rows, V tile, gates,
 //   decayed Gram tiles of row blocks 0..1 / 2..3 on and next to the diagonal,
 //   and the fp32 rows of the four diagonal blocks of A);
 //   Gram waves 4, 5 add chunk k + 1's remaining tiles from the published rows;
 //   the inverse wave 7 turns chunk k + 1's diagonal blocks into T_ii diag(beta_i);
-//   the consumer waves 0, 1 run chunk k.
+//   the consumer waves 0, 1 run chunk k (the substitution and the state
+//   update) and hand Ut and their start-of-chunk state to the output wave 6,
+//   which forms chunk k's Q S term and chunk k - 1's P Ut term and output.
 // Stage buffers rotate over three slots (chunk m uses slot m % 3); the
-// diagonal-block rows over two (m & 1).  Taking the inverses out of the Gram
-// waves removes the longest dependency chain from them, and the inverse wave
-// does all four blocks at once in a row-per-lane layout that skips the zero
-// upper triangle (120 fused DPP FMAs per chunk instead of 240).
+// diagonal-block rows and the hand-off buffers over two (m & 1).  Taking the
+// inverses and the output off the chain waves shortens their steps, and the
+// inverse wave does all four blocks at once in a row-per-lane layout that
+// skips the zero upper triangle (120 fused DPP FMAs per chunk instead of 240).
 namespace pipe3 {
 using namespace pipe;
 
@@ -799,15 +852,23 @@ struct Cfg3 {
   // gamma_C (padded), g[64] (log2 prefix of alpha); two slots of
   // diagonal-block rows (4 blocks x 16 rows, row stride 20); the private gate
   // tables of the two row waves; the 16 x 16 identity (row stride 20).
+  // Then, as 32-bit words, two slots (by chunk parity) of the consumers' Ut
+  // and two of their start-of-chunk states, both as bf16 MFMA operands in
+  // lane order (4 operands of 64 lanes x 2 words per consumer wave), for the
+  // wave that forms the output.
   static constexpr int szGate = 260, fGate = 0, oG = 196;
   static constexpr int szDS = 4 * 16 * 20, fDS = NBUF * szGate;
   static constexpr int fPGT = fDS + 2 * szDS, szPGT = 128;
   static constexpr int fEye = fPGT + 2 * szPGT;
-  static constexpr int nF = fEye + 16 * 20;
+  static constexpr int szHand = 4 * 64 * 2, szHand2 = 2 * szHand;  // one consumer / both consumers
+  static constexpr int fXU = fEye + 16 * 20, fXS = fXU + 2 * szHand2;
+  static constexpr int nF = fXS + 2 * szHand2;
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fPGT * 4) % 16 == 0 && (fEye * 4) % 16 == 0,
+  static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fPGT * 4) % 16 == 0 && (fEye * 4) % 16 == 0 &&
+                    (fXU * 4) % 16 == 0,
                 "fp32 tables must be 16-byte aligned");
+  static_assert(B::NT == 1 && B::NDT == 4, "one 16-column tile and four 16-row blocks per consumer wave");
 };
 constexpr int kThreads3 = 8 * 64;
 
@@ -829,6 +890,12 @@ __device__ __forceinline__ void run_steps(int nch, Step&& step) {
     stage_barrier();
   }
 }
+
+// The output of chunk n is finished in step n + 1.  run_steps ends with step
+// 3 ceil((nch + 2) / 3) - 3, which is nch - 1 when nch = 1 (mod 3); then
+// every wave runs one more barrier and the output wave finishes the last
+// chunk after it.
+__device__ __forceinline__ bool needs_tail_step(int nch) { return 3 * ((nch + 4) / 3) - 3 < nch; }
 
 // Fp32 rows of -A for a diagonal block: lane (g, c) writes -A[c][4g .. 4g + 3].
 __device__ __forceinline__ void diag_rows(const f32x4& G, const f32x4& gm, const float* PGT, int i, int g, int c,
@@ -932,111 +999,194 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   });
 }
 
-// Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
-// step behind the row waves and read K and Q of the chunk from the stage slot
-// the row waves published (in MFMA operand layout), and g from the gate table,
-// so they issue no global loads.
-__device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
+// The 64 x 32 V tile, and gamma, lambda, beta, gamma_C and g per chunk, for
+// chunk k + 2 in step k, from registers loaded three steps ahead.
+struct VStage {
   using Cf = Cfg<64>;
-  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
-  const int g = l >> 4, c = l & 15, nch = x.nchunks;
-  run_steps(nch, [&](auto pc, int k) {
-    constexpr int slot = (decltype(pc)::value + 2) % 3;  // chunk k + 1
-    const int m = k + 1;
-    if (m < 0 || m >= nch) return;
-    __bf16* const R = sb + slot * Cf::szBuf;
-    const float* const gt = sf + Cfg3::fGate + slot * Cfg3::szGate + Cfg3::oG;
-    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      const int o = c * LDK + 32 * p + 8 * g;
-      k0[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
-      k1[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * LDK + o);
-      ki[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + o);
-      qi[p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + o);
-    }
-    f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4();
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      G0 = mma32(k0[p], ki[p], G0);
-      P0 = mma32(k0[p], qi[p], P0);
-      G1 = mma32(k1[p], ki[p], G1);
-      P1 = mma32(k1[p], qi[p], P1);
-    }
-    offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
-    offdiag_tiles<64>(G1, P1, gt, i, 1, g, c, R);
-  });
-}
-
-// Wave 6: the 64 x 32 V tile, and gamma, lambda, beta, gamma_C and g per chunk.
-__device__ __forceinline__ void stage_v(const Ctx& x, char* smem, int l) {
-  using Cf = Cfg<64>;
-  constexpr int LDV = Cf::LDV;
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
-  const int H = x.H, T = x.T, DV = x.DV, nch = x.nchunks;
-  const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(x.vg + tokbase * DV + x.dv0, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
-  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
-  const int rowV = H * DV * 2;
-  int vof[4], lof[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
-    vof[u] = row * rowV + cu * 16;
-    lof[u] = row * LDV + cu * 8;
-  }
   struct Set {
     u32x4 v[4];
     float a, b;
   };
+  __amdgpu_buffer_rsrc_t rv, ra, rb;
+  int rowV, H, T, nch, l, vof[4], lof[4];
   Set st[3];
-  auto load = [&](auto sc, int m) {
-    constexpr int s = decltype(sc)::value;
+
+  __device__ __forceinline__ void init(const Ctx& x, int l_) {
+    l = l_;
+    H = x.H;
+    T = x.T;
+    nch = x.nchunks;
+    const size_t tokbase = (size_t)x.b * T * H + x.h;
+    rv = make_rsrc(x.vg + tokbase * x.DV + x.dv0,
+                   span_bytes((size_t)T * H * x.DV * 2, ((size_t)x.h * x.DV + x.dv0) * 2));
+    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
+    ra = make_rsrc(x.alpha + tokbase, spanG);
+    rb = make_rsrc(x.beta + tokbase, spanG);
+    rowV = H * x.DV * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
+      vof[u] = row * rowV + cu * 16;
+      lof[u] = row * Cf::LDV + cu * 8;
+    }
+  }
+  // Loads are issued unconditionally (chunk index clamped; buffer loads are
+  // range-checked) so that every path through the loop has the same number of
+  // loads in flight and the compiler's wait counts stay three steps deep.
+  __device__ __forceinline__ int clampc(int m) const { return max(0, min(m, nch - 1)); }
+  template <int s> __device__ __forceinline__ void load(int m) {
     const int c0 = m * 64;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
     st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
     st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
-  };
-  auto process = [&](auto sc, int m) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int slot = s;  // m % 3
-    __bf16* const R = sb + slot * Cf::szBuf;
+  }
+  __device__ __forceinline__ void prologue() {
+    load<0>(clampc(0));
+    issue_fence();
+    load<1>(clampc(1));
+    issue_fence();
+    load<2>(clampc(2));
+    issue_fence();
+  }
+  // Chunk m from register set / stage slot s (= m % 3).
+  template <int s> __device__ __forceinline__ void process(char* smem, int m) {
+    __bf16* const R = reinterpret_cast<__bf16*>(smem) + s * Cf::szBuf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
     const float a = (m * 64 + l < T) ? st[s].a : 1.f;
     const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
     const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
-    float* G = sf + Cfg3::fGate + slot * Cfg3::szGate;
+    float* G = reinterpret_cast<float*>(smem + Cfg3::fBase) + Cfg3::fGate + s * Cfg3::szGate;
     G[l] = __builtin_amdgcn_exp2f(xg);
     G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
     G[128 + l] = st[s].b;
     G[Cfg3::oG + l] = xg;
     if (l == 63) G[192] = __builtin_amdgcn_exp2f(gC);
-  };
-  // Loads are issued unconditionally (chunk index clamped; buffer loads are
-  // range-checked) so that every path through the loop has the same number of
-  // loads in flight and the compiler's wait counts stay three steps deep.
-  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
-  load(ic<0>{}, clampc(0));
-  issue_fence();
-  load(ic<1>{}, clampc(1));
-  issue_fence();
-  load(ic<2>{}, clampc(2));
-  issue_fence();
+  }
+  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
+    if (k + 2 < nch) process<ph>(smem, k + 2);
+    issue_fence();
+    load<ph>(clampc(k + 5));  // the set just consumed; needed three steps later
+  }
+};
+
+// Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
+// step behind the row waves and read K and Q of the chunk from the stage slot
+// the row waves published (in MFMA operand layout), and g from the gate table,
+// so they issue no global loads.  Wave 5 also stages V and the gates.
+template <bool kWithV>
+__device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
+  using Cf = Cfg<64>;
+  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
+  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
+  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
+  const int g = l >> 4, c = l & 15, nch = x.nchunks;
+  VStage vs;
+  if constexpr (kWithV) {
+    vs.init(x, l);
+    vs.prologue();
+  }
   run_steps(nch, [&](auto pc, int k) {
     constexpr int ph = decltype(pc)::value;
-    if (k + 2 < nch) process(ic<ph>{}, k + 2);
-    issue_fence();
-    load(ic<ph>{}, clampc(k + 5));  // the set just consumed; needed three steps later
+    constexpr int slot = (ph + 2) % 3;  // chunk k + 1
+    const int m = k + 1;
+    if (m >= 0 && m < nch) {
+      __bf16* const R = sb + slot * Cf::szBuf;
+      const float* const gt = sf + Cfg3::fGate + slot * Cfg3::szGate + Cfg3::oG;
+      u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = c * LDK + 32 * p + 8 * g;
+        k0[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
+        k1[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * LDK + o);
+        ki[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + o);
+        qi[p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + o);
+      }
+      f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4();
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        G0 = mma32(k0[p], ki[p], G0);
+        P0 = mma32(k0[p], qi[p], P0);
+        G1 = mma32(k1[p], ki[p], G1);
+        P1 = mma32(k1[p], qi[p], P1);
+      }
+      offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
+      offdiag_tiles<64>(G1, P1, gt, i, 1, g, c, R);
+    }
+    if constexpr (kWithV) vs.step<ph>(smem, k);
   });
+}
+
+// Wave 6: the output of both consumers' columns, one step behind them:
+// chunk n's Q S term in step n from their start-of-chunk state, its P Ut term
+// in step n + 1 from their Ut.
+__device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
+  using Cf = Cfg<64>;
+  constexpr int LDK = Cf::LDK;
+  const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
+  const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
+  const unsigned* const hand = reinterpret_cast<const unsigned*>(smem + Cfg3::fBase);
+  const int H = x.H, T = x.T, DV = x.DV, nch = x.nchunks;
+  const int g = l >> 4, c = l & 15;
+  // Lane (g, c) writes token c of each 16-token block, value columns
+  // 16t + 4g .. + 3 of the slice (one 8-byte store per tile t).
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(x.outg + ((size_t)x.b * T * H + x.h) * DV + x.dv0,
+                                              span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
+  const int rowO = H * DV * 2, vofO = c * rowO + 8 * g;
+  const int offRow = c * LDK + 4 * g, offT16 = c * Cf::LD16 + 4 * g;
+  f32x4 o[4][2];  // Q S term of the chunk in progress, per block row and tile
+  u32x2 Pm[10];   // its P tiles
+  auto out_start = [&](int n, const __bf16* R, const float* G) {
+    const unsigned* const hs = hand + Cfg3::fXS + (n & 1) * Cfg3::szHand2;
+    u32x2 st[2][4], qr[4][2][2];
+    float gm[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) st[t][d] = *reinterpret_cast<const u32x2*>(hs + t * Cfg3::szHand + 2 * (d * 64 + l));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
+        qr[i][p][0] = ld4(pr);
+        qr[i][p][1] = ld4(pr + 16);
+      }
+      gm[i] = G[16 * i + c];  // gamma of token 16i + c
+    }
+    issue_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) o[i][t] = out_qs<2>(st[t], qr[i], gm[i]);
+#pragma unroll
+    for (int e = 0; e < 10; ++e) Pm[e] = ld4(R + Cf::oP + e * Cf::szTile + offT16);
+  };
+  auto out_finish = [&](int n) {
+    const unsigned* const hu = hand + Cfg3::fXU + (n & 1) * Cfg3::szHand2;
+    u32x2 X[4][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[i][t] = *reinterpret_cast<const u32x2*>(hu + t * Cfg3::szHand + 2 * (i * 64 + l));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        __builtin_amdgcn_raw_buffer_store_b64(cvt4(out_pu(o[i][t], i, t, X, Pm)), ro, vofO + 32 * t,
+                                              (n * 64 + 16 * i) * rowO, 0);
+  };
+  run_steps(nch, [&](auto pc, int k) {
+    constexpr int cur = (decltype(pc)::value + 1) % 3;  // stage slot of chunk k
+    if (k >= 1 && k <= nch) out_finish(k - 1);
+    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, sf + Cfg3::fGate + cur * Cfg3::szGate);
+  });
+  if (needs_tail_step(nch)) {
+    stage_barrier();
+    out_finish(nch - 1);
+  }
 }
 
 // One forward-substitution step for the row-per-lane inverse: columns s <= M
@@ -1139,20 +1289,31 @@ __device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
 }
 #undef GDN_ST
 
-// Waves 0 and 1: consumers.
+// Waves 0 and 1: consumers.  They hand Ut and the start-of-chunk state to the
+// V wave, which forms the output.
 __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) {
   using Cf = Cfg<64>;
+  using Cs = Consumer<64>;
   const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
   const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
-  Consumer<64> cs;
+  unsigned* const hand = reinterpret_cast<unsigned*>(smem + Cfg3::fBase) + w * Cfg3::szHand;
+  Cs cs;
   cs.init(x, w, l);
   // Step k finishes chunk k and, since the rows, V and gates of chunk k + 1
   // were published a step earlier, starts chunk k + 1 before the barrier.
   run_steps(x.nchunks, [&](auto pc, int k) {
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
     constexpr int next = (slot + 1) % 3;
-    if (k >= 0 && k < x.nchunks) cs.chunk(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, k);
-    if (k >= -1 && k + 1 < x.nchunks) cs.begin(sb + next * Cf::szBuf, sf + Cfg3::fGate + next * Cfg3::szGate);
+    if (k >= 0 && k < x.nchunks) {
+      Cs::Upd u;
+      u32x2 Xf[4][1], XL[4][1];
+      cs.solve(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, u, Xf, XL,
+               hand + Cfg3::fXU + (k & 1) * Cfg3::szHand2);
+      cs.update(u, XL);
+    }
+    if (k >= -1 && k + 1 < x.nchunks)
+      cs.begin(sb + next * Cf::szBuf, sf + Cfg3::fGate + next * Cfg3::szGate,
+               hand + Cfg3::fXS + ((k + 1) & 1) * Cfg3::szHand2);
   });
   cs.finish(x);
 }
@@ -1189,16 +1350,21 @@ __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16*
   // The wave index is uniform (scalar branches only: matrix-core instructions
   // do not honour the exec mask).
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (w == 6) {
+    out_wave(x, smem, l);  // runs the tail step itself
+    return;
+  }
   if (w < 2)
     consume(x, smem, w, l);
   else if (w < 4)
     gram_rows(x, smem, 2 * (w - 2), l);
-  else if (w < 6)
-    gram_lower(x, smem, w - 2, l);
-  else if (w == 6)
-    stage_v(x, smem, l);
+  else if (w == 4)
+    gram_lower<false>(x, smem, 2, l);
+  else if (w == 5)
+    gram_lower<true>(x, smem, 3, l);
   else
     inverter(x, smem, l);
+  if (needs_tail_step(x.nchunks)) stage_barrier();
 }
 
 }  // namespace pipe3
