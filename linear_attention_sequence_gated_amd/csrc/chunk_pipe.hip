@@ -297,7 +297,9 @@ __device__ __forceinline__ void diag_p_tile(const f32x4& P, const f32x4& gm, int
 // from HBM again.  The consumers run the same barriers.
 template <class Load, class ProcA, class ProcB>
 __device__ __forceinline__ void producer_loop(int nch, Load&& load, ProcA&& procA, ProcB&& procB) {
-  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
+  // Clamped chunk index, kept in a scalar register: buffer-load offsets the
+  // compiler cannot prove uniform become per-lane loops.
+  auto clampc = [&](int m) { return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1))); };
   load(ic<0>{}, clampc(0));
   issue_fence();
   load(ic<1>{}, clampc(1));
@@ -881,6 +883,12 @@ constexpr int kThreads3 = 8 * 64;
 // conditional paths that would make the compiler's wait counts conservative.
 template <class Step>
 __device__ __forceinline__ void run_steps(int nch, Step&& step) {
+  // T >= 0 (checked on the host), so the first triple always runs.  Without
+  // this the loop gets an entry test, and the prologue's loads are sunk past it
+  // and regrouped by address; the loop's static wait counts must also hold on
+  // entry from the prologue, so every later iteration would then wait for
+  // loads issued one step earlier instead of three.
+  __builtin_assume(nch >= 0);
   for (int k = -2; k < nch; k += 3) {
     step(ic<0>{}, k);
     stage_barrier();
@@ -923,11 +931,21 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * 64 * 2;
-  int vofs[2][NKP];
+  // Loads read whole 128-byte rows: load (e, p) gives lane l 16 bytes of row
+  // 16 (b0 + e) + 8 p + l / 8.  Per-CU load throughput scales with the number
+  // of cache lines an instruction touches, and MFMA operand order (16 rows of
+  // 64 bytes per instruction) would touch twice as many.  The rows go to LDS
+  // row-major, and the operands are read back from there.
+  int vofs[2][NKP], lofs[2][NKP];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int p = 0; p < NKP; ++p) vofs[e][p] = (16 * (b0 + e) + c) * rowK + 64 * p + 16 * g;
+    for (int p = 0; p < NKP; ++p) {
+      const int row = 16 * (b0 + e) + 8 * p + (l >> 3);
+      vofs[e][p] = row * rowK + 16 * (l & 7);
+      lofs[e][p] = row * LDK + 8 * (l & 7);
+    }
+  static_assert(NKP == 2, "two 8-row loads per 16-row block");
   struct Set {
     u32x4 k[2][NKP], q[2][NKP];
     float a, b;
@@ -951,16 +969,33 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;  // slot m % 3 == s
     float* const D = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS;
+    // K and Q rows for this wave, the lower Gram waves and the consumers
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        *reinterpret_cast<u32x4*>(R + Cf::oK + lofs[e][p]) = S.k[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oQ + lofs[e][p]) = S.q[e][p];
+      }
     gate_scan(S.a, S.b, m * 64, T, l, PGT);
+    u32x4 kk[2][NKP], qq[2][NKP];  // MFMA operands: lane (g, c) holds row c, k = 32 p + 8 g .. + 7
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
+        kk[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
+        qq[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + o);
+      }
     f32x4 G0 = zero4(), P0 = zero4(), Go = zero4(), Po = zero4(), G1 = zero4(), P1 = zero4();
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      G0 = mma32(S.k[0][p], S.k[0][p], G0);
-      P0 = mma32(S.k[0][p], S.q[0][p], P0);
-      Go = mma32(S.k[0][p], S.k[1][p], Go);
-      Po = mma32(S.k[0][p], S.q[1][p], Po);
-      G1 = mma32(S.k[1][p], S.k[1][p], G1);
-      P1 = mma32(S.k[1][p], S.q[1][p], P1);
+      G0 = mma32(kk[0][p], kk[0][p], G0);
+      P0 = mma32(kk[0][p], qq[0][p], P0);
+      Go = mma32(kk[0][p], kk[1][p], Go);
+      Po = mma32(kk[0][p], qq[1][p], Po);
+      G1 = mma32(kk[1][p], kk[1][p], G1);
+      P1 = mma32(kk[1][p], qq[1][p], P1);
     }
     offdiag_tiles<64>(Go, Po, PGT, b0 + 1, b0, g, c, R);
     const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
@@ -968,23 +1003,13 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     diag_p_tile<64>(P1, gm1, b0 + 1, g, c, R);
     diag_rows(G0, gm0, PGT, b0, g, c, D + b0 * 320);
     diag_rows(G1, gm1, PGT, b0 + 1, g, c, D + (b0 + 1) * 320);
-    // K and Q rows for the lower Gram waves and the consumers, published last:
-    // nobody reads them before the next barrier, and right after a barrier the
-    // consumers' own LDS reads are on the critical path.
-    issue_fence();
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
-        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
-        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
-      }
   };
   // Loads are issued unconditionally (chunk index clamped; buffer loads are
   // range-checked) so that every path through the loop has the same number of
   // loads in flight and the compiler's wait counts stay three steps deep.
-  auto clampc = [&](int m) { return max(0, min(m, nch - 1)); };
+  // Clamped chunk index, kept in a scalar register: buffer-load offsets the
+  // compiler cannot prove uniform become per-lane loops.
+  auto clampc = [&](int m) { return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1))); };
   load(ic<0>{}, clampc(0));
   issue_fence();
   load(ic<1>{}, clampc(1));
@@ -1033,7 +1058,9 @@ struct VStage {
   // Loads are issued unconditionally (chunk index clamped; buffer loads are
   // range-checked) so that every path through the loop has the same number of
   // loads in flight and the compiler's wait counts stay three steps deep.
-  __device__ __forceinline__ int clampc(int m) const { return max(0, min(m, nch - 1)); }
+  __device__ __forceinline__ int clampc(int m) const {
+    return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1)));  // scalar: see gram_rows
+  }
   template <int s> __device__ __forceinline__ void load(int m) {
     const int c0 = m * 64;
 #pragma unroll
