@@ -830,9 +830,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf1
 
 // ============================================================================
 // Three-stage variant (dk = 64).  Per step k of the loop (one barrier each):
-//   Gram waves 2, 3 and wave 5 build chunk k + 2 (K/Q rows, V tile, gates,
-//   decayed Gram tiles of row blocks 0..1 / 2..3 on and next to the diagonal,
-//   and the fp32 rows of the four diagonal blocks of A);
+//   Gram waves 2, 3 and wave 5 build chunk k + 2 (K/Q rows, V tile, decayed
+//   Gram tiles of row blocks 0..1 / 2..3 on and next to the diagonal, and the
+//   fp32 rows of the four diagonal blocks of A); wave 4 also writes chunk
+//   k + 3's gate table, so only it loads alpha and beta;
 //   Gram waves 4, 5 add chunk k + 1's remaining tiles from the published rows;
 //   the inverse wave 7 turns chunk k + 1's diagonal blocks into T_ii diag(beta_i);
 //   the consumer waves 0, 1 run chunk k (the substitution and the state
@@ -850,31 +851,43 @@ struct Cfg3 {
   using B = Cfg<64>;
   static constexpr int NBUF = 3;
   static constexpr int fBase = ((NBUF * B::szBuf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
-  // fp32 region (floats): per stage slot gamma[64], lambda[64], beta[64],
-  // gamma_C (padded), g[64] (log2 prefix of alpha); two slots of
-  // diagonal-block rows (4 blocks x 16 rows, row stride 20); the private gate
-  // tables of the two row waves; the 16 x 16 identity (row stride 20).
+  // fp32 region (floats): a ring of NGATE gate tables (chunk m uses table
+  // m % NGATE), each gamma[64], lambda[64], g[64] (log2 prefix of alpha),
+  // beta[64], gamma_C (padded); two slots of diagonal-block rows (4 blocks x
+  // 16 rows, row stride 20); the 16 x 16 identity (row stride 20).
   // Then, as 32-bit words, two slots (by chunk parity) of the consumers' Ut
   // and two of their start-of-chunk states, both as bf16 MFMA operands in
   // lane order (4 operands of 64 lanes x 2 words per consumer wave), for the
   // wave that forms the output.
-  static constexpr int szGate = 260, fGate = 0, oG = 196;
-  static constexpr int szDS = 4 * 16 * 20, fDS = NBUF * szGate;
-  static constexpr int fPGT = fDS + 2 * szDS, szPGT = 128;
-  static constexpr int fEye = fPGT + 2 * szPGT;
+  // Gate tables are written one step before the K/Q rows of their chunk, so
+  // the ring is one deeper than the stage slots.
+  static constexpr int NGATE = 4;
+  static constexpr int szGate = 260, fGate = 0, oLam = 64, oG = 128, oBeta = 192, oGC = 256;
+  static constexpr int szDS = 4 * 16 * 20, fDS = NGATE * szGate;
+  static constexpr int fEye = fDS + 2 * szDS;
   static constexpr int szHand = 4 * 64 * 2, szHand2 = 2 * szHand;  // one consumer / both consumers
   static constexpr int fXU = fEye + 16 * 20, fXS = fXU + 2 * szHand2;
   static constexpr int nF = fXS + 2 * szHand2;
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fPGT * 4) % 16 == 0 && (fEye * 4) % 16 == 0 &&
+  static_assert(oBeta == oG + 64, "g and beta adjacent: the Gram code reads them as one table");
+  static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fEye * 4) % 16 == 0 &&
                     (fXU * 4) % 16 == 0,
                 "fp32 tables must be 16-byte aligned");
   static_assert(B::NT == 1 && B::NDT == 4, "one 16-column tile and four 16-row blocks per consumer wave");
 };
 constexpr int kThreads3 = 8 * 64;
 
-// Runs step(phase, k) for k = -2, -1, ..., each followed by the barrier, with
+// Gate table of chunk m.
+__device__ __forceinline__ float* gate_table(char* smem, int m) {
+  return reinterpret_cast<float*>(smem + Cfg3::fBase) + Cfg3::fGate + (m & (Cfg3::NGATE - 1)) * Cfg3::szGate;
+}
+__device__ __forceinline__ const float* gate_table(const char* smem, int m) {
+  return reinterpret_cast<const float*>(smem + Cfg3::fBase) + Cfg3::fGate + (m & (Cfg3::NGATE - 1)) * Cfg3::szGate;
+}
+
+// Runs one barrier (after the gate table of chunk 0 is written), then
+// step(phase, k) for k = -2, -1, ..., each followed by the barrier, with
 // phase = (k + 2) % 3 known at compile time: chunk k + 2 (built in this step)
 // uses stage slot and register set `phase`, chunk k + 1 slot (phase + 2) % 3
 // and chunk k slot (phase + 1) % 3.  Steps come in whole triples (up to two
@@ -889,6 +902,7 @@ __device__ __forceinline__ void run_steps(int nch, Step&& step) {
   // entry from the prologue, so every later iteration would then wait for
   // loads issued one step earlier instead of three.
   __builtin_assume(nch >= 0);
+  stage_barrier();  // the gate table of chunk 0 is written before the loop
   for (int k = -2; k < nch; k += 3) {
     step(ic<0>{}, k);
     stage_barrier();
@@ -921,15 +935,11 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
   __bf16* const sb = reinterpret_cast<__bf16*>(smem);
   float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
-  float* const PGT = sf + Cfg3::fPGT + (b0 >> 1) * Cfg3::szPGT;
   const int g = l >> 4, c = l & 15, H = x.H, T = x.T, nch = x.nchunks;
   const size_t tokbase = (size_t)x.b * T * H + x.h;
   const uint32_t spanK = span_bytes((size_t)T * H * 64 * 2, (size_t)x.h * 64 * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * 64, spanK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * 64, spanK);
-  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * 64 * 2;
   // Loads read whole 128-byte rows: load (e, p) gives lane l 16 bytes of row
   // 16 (b0 + e) + 8 p + l / 8.  Per-CU load throughput scales with the number
@@ -948,7 +958,6 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   static_assert(NKP == 2, "two 8-row loads per 16-row block");
   struct Set {
     u32x4 k[2][NKP], q[2][NKP];
-    float a, b;
   };
   Set st[3];
   auto load = [&](auto sc, int m) {
@@ -961,14 +970,13 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
         st[s].k[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofs[e][p], c0 * rowK, 0));
         st[s].q[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofs[e][p], c0 * rowK, 0));
       }
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
   };
   auto process = [&](auto sc, int m) {
     constexpr int s = decltype(sc)::value;
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;  // slot m % 3 == s
     float* const D = sf + Cfg3::fDS + (m & 1) * Cfg3::szDS;
+    const float* const PGT = gate_table(smem, m) + Cfg3::oG;  // g[64], then beta[64]
     // K and Q rows for this wave, the lower Gram waves and the consumers
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -977,7 +985,6 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
         *reinterpret_cast<u32x4*>(R + Cf::oK + lofs[e][p]) = S.k[e][p];
         *reinterpret_cast<u32x4*>(R + Cf::oQ + lofs[e][p]) = S.q[e][p];
       }
-    gate_scan(S.a, S.b, m * 64, T, l, PGT);
     u32x4 kk[2][NKP], qq[2][NKP];  // MFMA operands: lane (g, c) holds row c, k = 32 p + 8 g .. + 7
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -1024,30 +1031,28 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   });
 }
 
-// The 64 x 32 V tile, and gamma, lambda, beta, gamma_C and g per chunk, for
-// chunk k + 2 in step k, from registers loaded three steps ahead.
+// Loads are issued unconditionally (chunk index clamped; buffer loads are
+// range-checked) so that every path through the loop has the same number of
+// loads in flight and the compiler's wait counts stay three steps deep.  The
+// clamped index is kept scalar (see gram_rows).
+__device__ __forceinline__ int clamp_chunk(int m, int nch) {
+  return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1)));
+}
+
+// The 64 x 32 V tile of chunk k + 2 in step k, from registers loaded three
+// steps ahead.
 struct VStage {
   using Cf = Cfg<64>;
-  struct Set {
-    u32x4 v[4];
-    float a, b;
-  };
-  __amdgpu_buffer_rsrc_t rv, ra, rb;
-  int rowV, H, T, nch, l, vof[4], lof[4];
-  Set st[3];
+  __amdgpu_buffer_rsrc_t rv;
+  int rowV, nch, vof[4], lof[4];
+  u32x4 st[3][4];
 
-  __device__ __forceinline__ void init(const Ctx& x, int l_) {
-    l = l_;
-    H = x.H;
-    T = x.T;
+  __device__ __forceinline__ void init(const Ctx& x, int l) {
     nch = x.nchunks;
-    const size_t tokbase = (size_t)x.b * T * H + x.h;
+    const size_t tokbase = (size_t)x.b * x.T * x.H + x.h;
     rv = make_rsrc(x.vg + tokbase * x.DV + x.dv0,
-                   span_bytes((size_t)T * H * x.DV * 2, ((size_t)x.h * x.DV + x.dv0) * 2));
-    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-    ra = make_rsrc(x.alpha + tokbase, spanG);
-    rb = make_rsrc(x.beta + tokbase, spanG);
-    rowV = H * x.DV * 2;
+                   span_bytes((size_t)x.T * x.H * x.DV * 2, ((size_t)x.h * x.DV + x.dv0) * 2));
+    rowV = x.H * x.DV * 2;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
@@ -1055,73 +1060,107 @@ struct VStage {
       lof[u] = row * Cf::LDV + cu * 8;
     }
   }
-  // Loads are issued unconditionally (chunk index clamped; buffer loads are
-  // range-checked) so that every path through the loop has the same number of
-  // loads in flight and the compiler's wait counts stay three steps deep.
-  __device__ __forceinline__ int clampc(int m) const {
-    return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1)));  // scalar: see gram_rows
-  }
   template <int s> __device__ __forceinline__ void load(int m) {
-    const int c0 = m * 64;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
+      st[s][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], m * 64 * rowV, 0));
   }
-  __device__ __forceinline__ void prologue() {
-    load<0>(clampc(0));
+  __device__ __forceinline__ void prologue(char*) {
+    load<0>(clamp_chunk(0, nch));
     issue_fence();
-    load<1>(clampc(1));
+    load<1>(clamp_chunk(1, nch));
     issue_fence();
-    load<2>(clampc(2));
+    load<2>(clamp_chunk(2, nch));
     issue_fence();
-  }
-  // Chunk m from register set / stage slot s (= m % 3).
-  template <int s> __device__ __forceinline__ void process(char* smem, int m) {
-    __bf16* const R = reinterpret_cast<__bf16*>(smem) + s * Cf::szBuf;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
-    const float a = (m * 64 + l < T) ? st[s].a : 1.f;
-    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
-    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
-    float* G = reinterpret_cast<float*>(smem + Cfg3::fBase) + Cfg3::fGate + s * Cfg3::szGate;
-    G[l] = __builtin_amdgcn_exp2f(xg);
-    G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
-    G[128 + l] = st[s].b;
-    G[Cfg3::oG + l] = xg;
-    if (l == 63) G[192] = __builtin_amdgcn_exp2f(gC);
   }
   template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
-    if (k + 2 < nch) process<ph>(smem, k + 2);
+    if (k + 2 < nch) {
+      __bf16* const R = reinterpret_cast<__bf16*>(smem) + ph * Cf::szBuf;  // slot (k + 2) % 3
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[ph][u];
+    }
     issue_fence();
-    load<ph>(clampc(k + 5));  // the set just consumed; needed three steps later
+    load<ph>(clamp_chunk(k + 5, nch));  // the set just consumed; needed three steps later
+  }
+};
+
+// The gate table (gamma, lambda, g, beta, gamma_C) of chunk k + 3 in step k,
+// from alpha and beta loaded three steps ahead; chunk 0's before the loop.
+struct GateStage {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int H, T, nch, l;
+  float sa[3], sb[3];
+
+  __device__ __forceinline__ void init(const Ctx& x, int l_) {
+    l = l_;
+    H = x.H;
+    T = x.T;
+    nch = x.nchunks;
+    const size_t tokbase = (size_t)x.b * T * H + x.h;
+    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
+    ra = make_rsrc(x.alpha + tokbase, spanG);
+    rb = make_rsrc(x.beta + tokbase, spanG);
+  }
+  template <int s> __device__ __forceinline__ void load(int m) {
+    sa[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, m * 64 * H * 4, 0));
+    sb[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, m * 64 * H * 4, 0));
+  }
+  // Gate table of chunk m from register set s (= m % 3).  g is the inclusive
+  // prefix of log2 alpha (alpha = 1 on padding tokens; beta reads as 0 there).
+  template <int s> __device__ __forceinline__ void gates(char* smem, int m) {
+    const float a = (m * 64 + l < T) ? sa[s] : 1.f;
+    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
+    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
+    float* const G = gate_table(smem, m);
+    G[l] = __builtin_amdgcn_exp2f(xg);
+    G[Cfg3::oLam + l] = __builtin_amdgcn_exp2f(gC - xg);
+    G[Cfg3::oG + l] = xg;
+    G[Cfg3::oBeta + l] = sb[s];
+    if (l == 63) G[Cfg3::oGC] = __builtin_amdgcn_exp2f(gC);
+  }
+  // Sets hold chunks 0, 1, 2; chunk 0's table is written and set 0 refilled
+  // with chunk 3, so step k finds chunk k + 3 in set (k + 3) % 3.
+  __device__ __forceinline__ void prologue(char* smem) {
+    load<0>(clamp_chunk(0, nch));
+    issue_fence();
+    load<1>(clamp_chunk(1, nch));
+    issue_fence();
+    load<2>(clamp_chunk(2, nch));
+    issue_fence();
+    if (nch > 0) gates<0>(smem, 0);
+    issue_fence();
+    load<0>(clamp_chunk(3, nch));
+    issue_fence();
+  }
+  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
+    constexpr int s = (ph + 1) % 3;  // (k + 3) % 3
+    if (k + 3 < nch) gates<s>(smem, k + 3);
+    issue_fence();
+    load<s>(clamp_chunk(k + 6, nch));  // the set just consumed; needed three steps later
   }
 };
 
 // Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
 // step behind the row waves and read K and Q of the chunk from the stage slot
-// the row waves published (in MFMA operand layout), and g from the gate table,
-// so they issue no global loads.  Wave 5 also stages V and the gates.
-template <bool kWithV>
+// the row waves published (in MFMA operand layout), and g from the gate table.
+// Wave 4 also writes the gate tables (Extra = GateStage), wave 5 the V tiles
+// (Extra = VStage).
+template <class Extra>
 __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<64>;
   constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
   __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cfg3::fBase);
   const int g = l >> 4, c = l & 15, nch = x.nchunks;
-  VStage vs;
-  if constexpr (kWithV) {
-    vs.init(x, l);
-    vs.prologue();
-  }
+  Extra ex;
+  ex.init(x, l);
+  ex.prologue(smem);
   run_steps(nch, [&](auto pc, int k) {
     constexpr int ph = decltype(pc)::value;
     constexpr int slot = (ph + 2) % 3;  // chunk k + 1
     const int m = k + 1;
     if (m >= 0 && m < nch) {
       __bf16* const R = sb + slot * Cf::szBuf;
-      const float* const gt = sf + Cfg3::fGate + slot * Cfg3::szGate + Cfg3::oG;
+      const float* const gt = gate_table(smem, m) + Cfg3::oG;
       u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
 #pragma unroll
       for (int p = 0; p < NKP; ++p) {
@@ -1142,7 +1181,7 @@ __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int 
       offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
       offdiag_tiles<64>(G1, P1, gt, i, 1, g, c, R);
     }
-    if constexpr (kWithV) vs.step<ph>(smem, k);
+    ex.template step<ph>(smem, k);
   });
 }
 
@@ -1153,7 +1192,6 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   using Cf = Cfg<64>;
   constexpr int LDK = Cf::LDK;
   const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
-  const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
   const unsigned* const hand = reinterpret_cast<const unsigned*>(smem + Cfg3::fBase);
   const int H = x.H, T = x.T, DV = x.DV, nch = x.nchunks;
   const int g = l >> 4, c = l & 15;
@@ -1208,7 +1246,7 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   run_steps(nch, [&](auto pc, int k) {
     constexpr int cur = (decltype(pc)::value + 1) % 3;  // stage slot of chunk k
     if (k >= 1 && k <= nch) out_finish(k - 1);
-    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, sf + Cfg3::fGate + cur * Cfg3::szGate);
+    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, gate_table(smem, k));
   });
   if (needs_tail_step(nch)) {
     stage_barrier();
@@ -1294,7 +1332,7 @@ __device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
                  : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
                    "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14])
                  : "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
-    const float* G = sf + Cfg3::fGate + slot * Cfg3::szGate + 128 + 16 * b;  // beta of block b
+    const float* G = gate_table(smem, m) + Cfg3::oBeta + 16 * b;  // beta of block b
     u32x4 w0, w1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1322,7 +1360,6 @@ __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) 
   using Cf = Cfg<64>;
   using Cs = Consumer<64>;
   const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
-  const float* const sf = reinterpret_cast<const float*>(smem + Cfg3::fBase);
   unsigned* const hand = reinterpret_cast<unsigned*>(smem + Cfg3::fBase) + w * Cfg3::szHand;
   Cs cs;
   cs.init(x, w, l);
@@ -1334,12 +1371,12 @@ __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) 
     if (k >= 0 && k < x.nchunks) {
       Cs::Upd u;
       u32x2 Xf[4][1], XL[4][1];
-      cs.solve(sb + slot * Cf::szBuf, sf + Cfg3::fGate + slot * Cfg3::szGate, 192, u, Xf, XL,
+      cs.solve(sb + slot * Cf::szBuf, gate_table(smem, k), Cfg3::oGC, u, Xf, XL,
                hand + Cfg3::fXU + (k & 1) * Cfg3::szHand2);
       cs.update(u, XL);
     }
     if (k >= -1 && k + 1 < x.nchunks)
-      cs.begin(sb + next * Cf::szBuf, sf + Cfg3::fGate + next * Cfg3::szGate,
+      cs.begin(sb + next * Cf::szBuf, gate_table(smem, k + 1),
                hand + Cfg3::fXS + ((k + 1) & 1) * Cfg3::szHand2);
   });
   cs.finish(x);
@@ -1386,9 +1423,9 @@ __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16*
   else if (w < 4)
     gram_rows(x, smem, 2 * (w - 2), l);
   else if (w == 4)
-    gram_lower<false>(x, smem, 2, l);
+    gram_lower<GateStage>(x, smem, 2, l);
   else if (w == 5)
-    gram_lower<true>(x, smem, 3, l);
+    gram_lower<VStage>(x, smem, 3, l);
   else
     inverter(x, smem, l);
   if (needs_tail_step(x.nchunks)) stage_barrier();
