@@ -59,7 +59,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // eight bf16
 template <int V> using ic = std::integral_constant<int, V>;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
-constexpr int kPipeThreads = 7 * 64;     // waves: 2 consumers, 4 Gram, 1 V
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
@@ -154,8 +153,14 @@ __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j
 __host__ __device__ constexpr int stri(int i, int j) { return i * (i - 1) / 2 + j; }  // i > j
 
 template <int DK> struct Cfg {
-  static constexpr int NV = 32;  // value columns per workgroup
-  static constexpr int NT = NV / 32;  // 16-column tiles per consumer wave (two consumer waves)
+  // Value columns per workgroup: 32 at d = 64 (two consumer waves), 16 at
+  // d = 128 (one), so that a d = 128 layer has twice the workgroups to fill
+  // the CUs; the per-step work of a consumer and of the producers is the same.
+  static constexpr int NV = DK == 64 ? 32 : 16;
+  static constexpr int NT = 1;               // 16-column tiles per consumer wave
+  static constexpr int NCONS = NV / 16;      // consumer waves
+  static constexpr int NVU = NV / 8;         // 16-byte units per V row
+  static constexpr int kThreads = (NCONS + 5) * 64;  // consumers, 4 Gram waves, the V wave
   static constexpr int NDT = DK / 16, NKP = DK / 32;
   static constexpr int LDK = DK + 8, LDV = NV + 8, LD16 = 16 + 8;
   // bf16 element offsets inside one of the two stage buffers
@@ -345,11 +350,23 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
   const int rowK = H * DK * 2;
-  int vofs[2][NKP];
+  // Loads read whole rows (DK / 8 lanes of 16 bytes per row): load (e, p) gives
+  // lane l 16 bytes of row 16 b0 + RPI (e NKP + p) + l / NL.  Per-CU load
+  // throughput scales with the cache lines an instruction touches, and MFMA
+  // operand order (16 rows of 64 bytes per instruction) touches more.  The
+  // rows go to LDS row-major in phase A and the operands are read back from
+  // there in phase B.
+  constexpr int NL = DK / 8, RPI = 64 / NL;
+  static_assert(2 * NKP * RPI == 32, "the loads cover the wave's 32 rows");
+  int vofs[2][NKP], lofs[2][NKP];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int p = 0; p < NKP; ++p) vofs[e][p] = (16 * (b0 + e) + c) * rowK + 64 * p + 16 * g;
+    for (int p = 0; p < NKP; ++p) {
+      const int row = 16 * b0 + RPI * (e * NKP + p) + l / NL;
+      vofs[e][p] = row * rowK + 16 * (l % NL);
+      lofs[e][p] = row * LDK + 8 * (l % NL);
+    }
 
   struct Set {
     u32x4 k[2][NKP], q[2][NKP];
@@ -373,31 +390,40 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
     constexpr int s = decltype(sc)::value;  // register set == stage buffer == n & 1
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;
-    // K and Q rows of both blocks, for the lower Gram waves and the consumers
+    // K and Q rows of both blocks, for this wave, the lower Gram waves and
+    // the consumers
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int p = 0; p < NKP; ++p) {
-        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
-        *reinterpret_cast<u32x4*>(R + Cf::oK + o) = S.k[e][p];
-        *reinterpret_cast<u32x4*>(R + Cf::oQ + o) = S.q[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oK + lofs[e][p]) = S.k[e][p];
+        *reinterpret_cast<u32x4*>(R + Cf::oQ + lofs[e][p]) = S.q[e][p];
       }
   };
   auto process = [&](auto sc, int n) {
     constexpr int s = decltype(sc)::value;
     const Set& S = st[s];
     __bf16* const R = sb + s * Cf::szBuf;
+    u32x4 kk[2][NKP], qq[2][NKP];  // MFMA operands: lane (g, c) holds row c, k = 32 p + 8 g .. + 7
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
+        kk[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
+        qq[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + o);
+      }
     gate_scan(S.a, S.b, n * 64, T, l, PGT);
     // accumulator [s][r]: s from the A operand (column block), r from the B
     // operand (row block)
     f32x4 Gd = zero4(), Go = zero4(), P0 = zero4(), P1 = zero4(), Po = zero4();
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      Gd = mma32(S.k[0][p], S.k[0][p], Gd);
-      P0 = mma32(S.k[0][p], S.q[0][p], P0);
-      Go = mma32(S.k[0][p], S.k[1][p], Go);
-      Po = mma32(S.k[0][p], S.q[1][p], Po);
-      P1 = mma32(S.k[1][p], S.q[1][p], P1);
+      Gd = mma32(kk[0][p], kk[0][p], Gd);
+      P0 = mma32(kk[0][p], qq[0][p], P0);
+      Go = mma32(kk[0][p], kk[1][p], Go);
+      Po = mma32(kk[0][p], qq[1][p], Po);
+      P1 = mma32(kk[1][p], qq[1][p], P1);
     }
     offdiag_tiles<DK>(Go, Po, PGT, b0 + 1, b0, g, c, R);
     const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
@@ -467,11 +493,12 @@ __device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, 
   producer_loop(x.nchunks, load, [](auto, int) {}, process);
 }
 
-// Wave 6: the 64 x 32 V tile of the chunk, and gamma, lambda and gamma_C.
+// The 64 x NV V tile of the chunk (NVU 16-byte units per row, one per lane and
+// load), and gamma, lambda and gamma_C.
 template <int DK>
 __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
   using Cf = Cfg<DK>;
-  constexpr int LDV = Cf::LDV;
+  constexpr int LDV = Cf::LDV, NVU = Cf::NVU;
   __bf16* const sb = reinterpret_cast<__bf16*>(smem);
   float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
   const int H = x.H, T = x.T, DV = x.DV;
@@ -480,15 +507,15 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
       make_rsrc(x.vg + tokbase * DV + x.dv0, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, span_bytes((size_t)T * H * 4, (size_t)x.h * 4));
   const int rowV = H * DV * 2;
-  int vof[4], lof[4];
+  int vof[NVU], lof[NVU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
+  for (int u = 0; u < NVU; ++u) {
+    const int unit = l + 64 * u, row = unit / NVU, cu = unit % NVU;
     vof[u] = row * rowV + cu * 16;
     lof[u] = row * LDV + cu * 8;
   }
   struct Set {
-    u32x4 v[4];
+    u32x4 v[NVU];
     float a;
   };
   Set st[2];
@@ -496,7 +523,7 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
     constexpr int s = decltype(sc)::value;
     const int c0 = n * 64;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NVU; ++u)
       st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
     st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
   };
@@ -504,7 +531,7 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
     constexpr int s = decltype(sc)::value;
     __bf16* const R = sb + s * Cf::szBuf;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
+    for (int u = 0; u < NVU; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
     const float a = (n * 64 + l < T) ? st[s].a : 1.f;
     const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
     const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
@@ -784,7 +811,7 @@ __device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l)
 }
 
 template <int DK>
-__global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
+__global__ __launch_bounds__(Cfg<DK>::kThreads, 1) void chunk_pipe_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                                                             const __bf16* __restrict__ vg,
                                                             const float* __restrict__ alpha,
                                                             const float* __restrict__ beta, const float* S0g,
@@ -816,14 +843,29 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_pipe_kernel(const __bf1
   // branches, never exec-masked ones, because matrix-core instructions do not
   // honour the exec mask.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  if (w < 2)
-    consumer<DK>(x, smem, w, l);
-  else if (w < 4)
-    producer_rows<DK>(x, smem, 2 * (w - 2), l);
-  else if (w < 6)
-    producer_lower<DK>(x, smem, w - 2, l);
-  else
-    producer_v<DK>(x, smem, l);
+  // Waves are dealt to the four SIMDs in turn (wave w on SIMD w % 4).  With
+  // one consumer, the V wave (idle after phase A) shares its SIMD, and the
+  // four Gram waves, busy in phase B, get one each.
+  constexpr int NC = Cfg<DK>::NCONS;
+  if constexpr (NC == 1) {
+    if (w == 0)
+      consumer<DK>(x, smem, 0, l);
+    else if (w < 3)
+      producer_rows<DK>(x, smem, 2 * (w - 1), l);
+    else if (w == 4)
+      producer_v<DK>(x, smem, l);
+    else
+      producer_lower<DK>(x, smem, w == 3 ? 2 : 3, l);
+  } else {
+    if (w < NC)
+      consumer<DK>(x, smem, w, l);
+    else if (w < NC + 2)
+      producer_rows<DK>(x, smem, 2 * (w - NC), l);
+    else if (w < NC + 4)
+      producer_lower<DK>(x, smem, w - NC, l);
+    else
+      producer_v<DK>(x, smem, l);
+  }
 }
 
 }  // namespace pipe
@@ -1437,7 +1479,7 @@ template <int DK>
 static hipError_t launch_pipe_dk(const ChunkArgs& a) {
   const int nslices = a.dv / pipe::Cfg<DK>::NV;
   const long nblk = (long)a.B * a.H * nslices;
-  return launch_kernel(pipe::chunk_pipe_kernel<DK>, dim3((unsigned)nblk), dim3(pipe::kPipeThreads), (hipStream_t)a.stream, a.q, a.k,
+  return launch_kernel(pipe::chunk_pipe_kernel<DK>, dim3((unsigned)nblk), dim3(pipe::Cfg<DK>::kThreads), (hipStream_t)a.stream, a.q, a.k,
                        a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
 }
 
