@@ -8,20 +8,22 @@
 // bandwidth, vector-ALU issue (a wave64 instruction occupies its SIMD for four
 // cycles) and matrix-core issue -- are spread over the four SIMDs.
 //
-// One workgroup of 7 waves per (batch, head, 32 value columns), so a head's
-// columns are spread over two CUs; one barrier per chunk.  While the two
-// CONSUMER waves run chunk n out of LDS buffer n & 1, the five PRODUCER waves
-// fill buffer (n + 1) & 1 for chunk n + 1 from registers loaded from HBM two
-// chunks ahead:
+// Two kernels.  The three-stage kernel (namespace pipe3, d = 64, below) is
+// the one used at d = 64.  The two-stage kernel here runs d = 128: one
+// workgroup of 6 waves per (batch, head, 16 value columns), so a head's
+// columns are spread over eight CUs, with two barriers per chunk.  While the
+// CONSUMER wave runs chunk n out of LDS buffer n & 1, the five PRODUCER waves
+// fill buffer (n + 1) & 1 for chunk n + 1 from registers loaded from HBM a
+// chunk ahead:
 //
-//   wave 0, 1   consumers: 16 value columns each (one MFMA tile).
-//   wave 2, 3   Gram waves for row blocks {0,1} / {2,3}: K and Q straight from
-//               HBM in MFMA operand layout (published to LDS for the consumers),
+//   consumer    16 value columns (one MFMA tile).
+//   row Gram    row blocks {0,1} / {2,3}: K and Q as whole rows from HBM,
+//               published to LDS in phase A (operands read back from there),
 //               tiles (i,i), (i+1,i), (i+1,i+1) of Q K^T and the sub-diagonal
 //               tile of K K^T, and the inverse of diagonal block i.
-//   wave 4, 5   Gram waves for row block i = 2 / 3: tiles (i,0), (i,1) of
-//               K K^T and Q K^T, and the inverse of diagonal block 1 / 3.
-//   wave 6      the V tile, gamma and lambda.
+//   lower Gram  row block i = 2 / 3: tiles (i,0), (i,1) of K K^T and Q K^T,
+//               and the inverse of diagonal block 1 / 3, in phase B.
+//   V wave      the V tile, gamma and lambda, in phase A.
 //
 // With S the state at the chunk start, g the within-chunk prefix sum of
 // log alpha, gamma_r = exp(g_r), lambda_r = exp(g_C - g_r), Gamma_rs =
@@ -331,7 +333,7 @@ __device__ __forceinline__ void producer_loop(int nch, Load&& load, ProcA&& proc
   }
 }
 
-// Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).
+// Row Gram waves of the two-stage kernel: row blocks b0 and b0 + 1 (b0 = 0 or 2).
 template <int DK>
 __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, int l) {
   using Cf = Cfg<DK>;
@@ -434,9 +436,10 @@ __device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, 
   producer_loop(x.nchunks, load, procA, process);
 }
 
-// Waves 4 and 5: row block i = 2 / 3 below the first two column blocks, tiles
-// (i, 0) and (i, 1), and the inverse of diagonal block 1 / 3, from the K and Q
-// rows the row waves publish in phase A of the same step.
+// Lower Gram waves of the two-stage kernel: row block i = 2 / 3 below the
+// first two column blocks, tiles (i, 0) and (i, 1), and the inverse of
+// diagonal block 1 / 3, from the K and Q rows the row waves publish in phase A
+// of the same step.
 template <int DK>
 __device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<DK>;
@@ -785,7 +788,7 @@ struct Consumer {
   }
 };
 
-// Waves 0 and 1 of the two-stage kernel.
+// Consumer wave(s) of the two-stage kernel.
 template <int DK>
 __device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l) {
   using Cf = Cfg<DK>;
@@ -1184,7 +1187,7 @@ struct GateStage {
 
 // Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
 // step behind the row waves and read K and Q of the chunk from the stage slot
-// the row waves published (in MFMA operand layout), and g from the gate table.
+// the row waves published (row-major), and g from the gate table.
 // Wave 4 also writes the gate tables (Extra = GateStage), wave 5 the V tiles
 // (Extra = VStage).
 template <class Extra>

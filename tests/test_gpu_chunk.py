@@ -33,7 +33,7 @@ def test_chunk_small(name, dtype, B, T, H, d, extra):
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("c64", 32)])
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 191, 250])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 191, 250, 385])
 def test_chunk_lengths(dtype, d, T):
     torch_dev()
     inp = gen_chunk(2, T, 2, d, d, dtype=dtype, seed=7 + T, s0_var=0.1,
@@ -62,7 +62,7 @@ def test_chunk_empty_sequence_copies_state(dtype, d):
     assert not down(S).any()
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("c64", 32)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("c64", 32)])
 def test_chunk_state_in_place(dtype, d):
     """S_final may alias S0."""
     torch_dev()
