@@ -142,6 +142,9 @@ __device__ __forceinline__ f32x4 mma2(const u32x2& a0, const u32x2& a1, const u3
   return mma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, u32x4{b0[0], b0[1], b1[0], b1[1]}, c);
 }
 
+// Two 4-element operand pieces as one 8-element 16x16x32 operand.
+__device__ __forceinline__ u32x4 pair(const u32x2& a, const u32x2& b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
 // c += a b  (one 16-wide k sub-block).  Only used where c comes from VALU code
 // or is zero: a 16x16x16 issue that reads as its accumulator the result of a
 // 16x16x32 issue was observed to be scheduled without the wait states that
@@ -551,13 +554,14 @@ __device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
 // value columns of one token:
 //   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{j <= i} Ut_j^T P_ij^T.
 // For one 16-column tile, lane (g, c) gets token 16 i + c, columns 4g .. 4g + 3.
-// First term: s = the state's bf16 operands for the tile (2 NKP sub-blocks),
-// qr = Q rows of block i, gm = gamma of the lane's token.
+// First term: s = the state's bf16 operands for the tile (2 NKP sub-blocks, in
+// key_row order), qr = keys 32p + 8g .. + 7 of Q row 16i + c, gm = gamma of
+// the lane's token.
 template <int NKP>
-__device__ __forceinline__ f32x4 out_qs(const u32x2* s, const u32x2 (&qr)[NKP][2], float gm) {
+__device__ __forceinline__ f32x4 out_qs(const u32x2* s, const u32x4 (&qr)[NKP], float gm) {
   f32x4 o = zero4();
 #pragma unroll
-  for (int p = 0; p < NKP; ++p) o = mma2(s[2 * p], s[2 * p + 1], qr[p][0], qr[p][1], o);
+  for (int p = 0; p < NKP; ++p) o = mma32(pair(s[2 * p], s[2 * p + 1]), qr[p], o);
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] *= gm;
   return o;
@@ -580,9 +584,16 @@ __device__ __forceinline__ f32x4 out_pu(f32x4 o, int i, int t, const u32x2 (&X)[
 }
 
 // ---------------------------------------------------------------- consumers
+// Key row of the state held by accumulator block d, lane group g, element j.
+// The state update reads K^T with a per-lane address (the transposed LDS read
+// takes one per lane), so its output rows can be any 4-row groups: blocks 2p
+// and 2p + 1 give lane group g the 8 consecutive keys 32p + 8g .. 32p + 8g + 7.
+// K S and Q S then read their K and Q operands as one 16-byte row piece.
+__host__ __device__ constexpr int key_row(int d, int g, int j) { return 32 * (d / 2) + 8 * g + 4 * (d % 2) + j; }
+
 // A consumer wave owns value columns 16 NT w .. 16 NT (w + 1) - 1 of the
 // workgroup's slice, as NT 16-column tiles t.  The state lives in MFMA
-// accumulators: S[t][d] holds rows 16d + 4g + j of column 16t + c.
+// accumulators: S[t][d] holds rows key_row(d, g, j) of column 16t + c.
 template <int DK>
 struct Consumer {
   using Cf = Cfg<DK>;
@@ -607,7 +618,7 @@ struct Consumer {
       for (int d = 0; d < NDT; ++d)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          S[t][d][j] = x.S0g ? x.S0g[((size_t)x.chain * DK + 16 * d + 4 * g + j) * DV + col] : 0.f;
+          S[t][d][j] = x.S0g ? x.S0g[((size_t)x.chain * DK + key_row(d, g, j)) * DV + col] : 0.f;
     }
     // Output: lane (g, c) writes token c of each 16-token block, value columns
     // 16 NT w + 16t + 4g .. + 3 (one 8-byte store).
@@ -615,8 +626,8 @@ struct Consumer {
     ro = make_rsrc(x.outg + obase, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
     rowO = H * DV * 2;
     vofO = c * rowO + (16 * NT * w + 4 * g) * 2;
-    offRow = c * LDK + 4 * g;                                       // row c, k sub-block 4g
-    offTrK = (4 * g + (c >> 2)) * LDK + 4 * (c & 3);                // transposed K reads
+    offRow = c * LDK + 8 * g;                                       // row c, keys 8g .. 8g + 7
+    offTrK = (4 * g + (c >> 2)) * LDK + 8 * (c & 3);                // transposed K reads (key_row order)
     offTrV = (4 * g + (c >> 2)) * LDV + 16 * NT * w + 4 * (c & 3);  // transposed V reads
     offT16 = c * LD16 + 4 * g;                                      // 16x16 tiles
   }
@@ -626,15 +637,11 @@ struct Consumer {
   // state.  With `pub` set, lane l also writes the state's bf16 operands
   // sfr[t][d] to pub[2 ((t NDT + d) 64 + l)] for a wave that forms the output.
   __device__ __forceinline__ void begin(const __bf16* R, const float* G, unsigned* pub = nullptr) {
-    u32x2 kr[4][NKP][2];
+    u32x4 kr[4][NKP];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const __bf16* pr = R + Cf::oK + 16 * i * LDK + 32 * p + offRow;
-        kr[i][p][0] = ld4(pr);
-        kr[i][p][1] = ld4(pr + 16);
-      }
+      for (int p = 0; p < NKP; ++p) kr[i][p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + 32 * p + offRow);
 #pragma unroll
       for (int t = 0; t < NT; ++t) vv[i][t] = ld4_tr(R + Cf::oV + 16 * i * LDV + 16 * t + offTrV);
       gg[i] = *reinterpret_cast<const f32x4*>(G + 16 * i + 4 * g);
@@ -654,7 +661,7 @@ struct Consumer {
         acc[i][t] = zero4();
 #pragma unroll
         for (int p = 0; p < NKP; ++p)
-          acc[i][t] = mma2(kr[i][p][0], kr[i][p][1], sfr[t][2 * p], sfr[t][2 * p + 1], acc[i][t]);
+          acc[i][t] = mma32(kr[i][p], pair(sfr[t][2 * p], sfr[t][2 * p + 1]), acc[i][t]);
       }
   }
 
@@ -667,7 +674,8 @@ struct Consumer {
   };
   // Operands of the output: Q rows, gamma per token, the ten P tiles.
   struct OutOps {
-    u32x2 qr[4][NKP][2], Pm[10];
+    u32x4 qr[4][NKP];
+    u32x2 Pm[10];
     float gm[4];
   };
 
@@ -688,7 +696,7 @@ struct Consumer {
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u.kt[d][i] = ld4_tr(R + Cf::oK + 16 * i * LDK + 16 * d + offTrK);
+      for (int i = 0; i < 4; ++i) u.kt[d][i] = ld4_tr(R + Cf::oK + 16 * i * LDK + 32 * (d / 2) + 4 * (d % 2) + offTrK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) u.lm[i] = *reinterpret_cast<const f32x4*>(G + 64 + 16 * i + 4 * g);
     u.gC = G[gCoff];
@@ -739,11 +747,7 @@ struct Consumer {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
-        op.qr[i][p][0] = ld4(pr);
-        op.qr[i][p][1] = ld4(pr + 16);
-      }
+      for (int p = 0; p < NKP; ++p) op.qr[i][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + 32 * p + offRow);
       op.gm[i] = G[16 * i + c];  // gamma of token 16i + c
     }
 #pragma unroll
@@ -783,7 +787,7 @@ struct Consumer {
 #pragma unroll
       for (int d = 0; d < NDT; ++d)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x.Sfg[((size_t)x.chain * DK + 16 * d + 4 * g + j) * x.DV + col] = S[t][d][j];
+        for (int j = 0; j < 4; ++j) x.Sfg[((size_t)x.chain * DK + key_row(d, g, j)) * x.DV + col] = S[t][d][j];
     }
   }
 };
@@ -877,8 +881,8 @@ __global__ __launch_bounds__(Cfg<DK>::kThreads, 1) void chunk_pipe_kernel(const 
 // Three-stage variant (dk = 64).  Per step k of the loop (one barrier each):
 //   Gram waves 2, 3 and wave 5 build chunk k + 2 (K/Q rows, V tile, decayed
 //   Gram tiles of row blocks 0..1 / 2..3 on and next to the diagonal, and the
-//   fp32 rows of the four diagonal blocks of A); wave 4 also writes chunk
-//   k + 3's gate table, so only it loads alpha and beta;
+//   fp32 rows of the four diagonal blocks of A); waves 3 and 2 also write
+//   chunk k + 3's gate table from alpha and beta (one each);
 //   Gram waves 4, 5 add chunk k + 1's remaining tiles from the published rows;
 //   the inverse wave 7 turns chunk k + 1's diagonal blocks into T_ii diag(beta_i);
 //   the consumer waves 0, 1 run chunk k (the substitution and the state
@@ -974,7 +978,129 @@ __device__ __forceinline__ void diag_rows(const f32x4& G, const f32x4& gm, const
   *reinterpret_cast<f32x4*>(dst + c * 20 + 4 * g) = na;
 }
 
-// Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).
+// Loads are issued unconditionally (chunk index clamped; buffer loads are
+// range-checked) so that every path through the loop has the same number of
+// loads in flight and the compiler's wait counts stay three steps deep.  The
+// clamped index is kept scalar.
+__device__ __forceinline__ int clamp_chunk(int m, int nch) {
+  return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1)));
+}
+
+// The 64 x 32 V tile of chunk k + 2 in step k, from registers loaded three
+// steps ahead.
+struct VStage {
+  using Cf = Cfg<64>;
+  __amdgpu_buffer_rsrc_t rv;
+  int rowV, nch, vof[4], lof[4];
+  u32x4 st[3][4];
+
+  __device__ __forceinline__ void init(const Ctx& x, int l) {
+    nch = x.nchunks;
+    const size_t tokbase = (size_t)x.b * x.T * x.H + x.h;
+    rv = make_rsrc(x.vg + tokbase * x.DV + x.dv0,
+                   span_bytes((size_t)x.T * x.H * x.DV * 2, ((size_t)x.h * x.DV + x.dv0) * 2));
+    rowV = x.H * x.DV * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
+      vof[u] = row * rowV + cu * 16;
+      lof[u] = row * Cf::LDV + cu * 8;
+    }
+  }
+  template <int s> __device__ __forceinline__ void load(int m) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st[s][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], m * 64 * rowV, 0));
+  }
+  __device__ __forceinline__ void prologue(char*) {
+    load<0>(clamp_chunk(0, nch));
+    issue_fence();
+    load<1>(clamp_chunk(1, nch));
+    issue_fence();
+    load<2>(clamp_chunk(2, nch));
+    issue_fence();
+  }
+  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
+    if (k + 2 < nch) {
+      __bf16* const R = reinterpret_cast<__bf16*>(smem) + ph * Cf::szBuf;  // slot (k + 2) % 3
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[ph][u];
+    }
+    issue_fence();
+    load<ph>(clamp_chunk(k + 5, nch));  // the set just consumed; needed three steps later
+  }
+};
+
+// The gate table of chunk k + 3 in step k, from alpha or beta loaded three
+// steps ahead; chunk 0's before the loop.  With kAlpha the wave writes gamma,
+// lambda, g and gamma_C; with kBeta it writes beta.  The two halves run on
+// different waves: each strided 4-byte load touches 24 cache lines for 256
+// bytes, which costs a loading wave several hundred cycles per step when the
+// inputs come from HBM.
+template <bool kAlpha, bool kBeta>
+struct GateStage {
+  __amdgpu_buffer_rsrc_t rs;
+  int H, T, nch, l;
+  float sv[3];
+
+  __device__ __forceinline__ void init(const Ctx& x, int l_) {
+    l = l_;
+    H = x.H;
+    T = x.T;
+    nch = x.nchunks;
+    const size_t tokbase = (size_t)x.b * T * H + x.h;
+    rs = make_rsrc((kAlpha ? x.alpha : x.beta) + tokbase, span_bytes((size_t)T * H * 4, (size_t)x.h * 4));
+  }
+  template <int s> __device__ __forceinline__ void load(int m) {
+    sv[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, l * H * 4, m * 64 * H * 4, 0));
+  }
+  // Gate table of chunk m from register set s (= m % 3).  g is the inclusive
+  // prefix of log2 alpha (alpha = 1 on padding tokens; beta reads as 0 there).
+  template <int s> __device__ __forceinline__ void gates(char* smem, int m) {
+    float* const G = gate_table(smem, m);
+    if constexpr (kAlpha) {
+      const float a = (m * 64 + l < T) ? sv[s] : 1.f;
+      const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
+      const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
+      G[l] = __builtin_amdgcn_exp2f(xg);
+      G[Cfg3::oLam + l] = __builtin_amdgcn_exp2f(gC - xg);
+      G[Cfg3::oG + l] = xg;
+      if (l == 63) G[Cfg3::oGC] = __builtin_amdgcn_exp2f(gC);
+    }
+    if constexpr (kBeta) G[Cfg3::oBeta + l] = sv[s];
+  }
+  // Sets hold chunks 0, 1, 2; chunk 0's table is written and set 0 refilled
+  // with chunk 3, so step k finds chunk k + 3 in set (k + 3) % 3.
+  __device__ __forceinline__ void prologue(char* smem) {
+    load<0>(clamp_chunk(0, nch));
+    issue_fence();
+    load<1>(clamp_chunk(1, nch));
+    issue_fence();
+    load<2>(clamp_chunk(2, nch));
+    issue_fence();
+    if (nch > 0) gates<0>(smem, 0);
+    issue_fence();
+    load<0>(clamp_chunk(3, nch));
+    issue_fence();
+  }
+  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
+    constexpr int s = (ph + 1) % 3;  // (k + 3) % 3
+    if (k + 3 < nch) gates<s>(smem, k + 3);
+    issue_fence();
+    load<s>(clamp_chunk(k + 6, nch));  // the set just consumed; needed three steps later
+  }
+};
+
+// No extra work.
+struct NoStage {
+  __device__ __forceinline__ void init(const Ctx&, int) {}
+  __device__ __forceinline__ void prologue(char*) {}
+  template <int ph> __device__ __forceinline__ void step(char*, int) {}
+};
+
+// Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).  They also write the
+// gate tables (Extra = GateStage): wave 2 beta, wave 3 the rest.
+template <class Extra>
 __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int l) {
   using Cf = Cfg<64>;
   constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
@@ -1062,6 +1188,9 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
   // Clamped chunk index, kept in a scalar register: buffer-load offsets the
   // compiler cannot prove uniform become per-lane loops.
   auto clampc = [&](int m) { return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1))); };
+  Extra ex;  // first, so that its prologue waits only for its own first loads
+  ex.init(x, l);
+  ex.prologue(smem);
   load(ic<0>{}, clampc(0));
   issue_fence();
   load(ic<1>{}, clampc(1));
@@ -1073,123 +1202,15 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
     if (k + 2 < nch) process(ic<ph>{}, k + 2);
     issue_fence();
     load(ic<ph>{}, clampc(k + 5));  // the set just consumed; needed three steps later
+    issue_fence();
+    ex.template step<ph>(smem, k);
   });
 }
-
-// Loads are issued unconditionally (chunk index clamped; buffer loads are
-// range-checked) so that every path through the loop has the same number of
-// loads in flight and the compiler's wait counts stay three steps deep.  The
-// clamped index is kept scalar (see gram_rows).
-__device__ __forceinline__ int clamp_chunk(int m, int nch) {
-  return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1)));
-}
-
-// The 64 x 32 V tile of chunk k + 2 in step k, from registers loaded three
-// steps ahead.
-struct VStage {
-  using Cf = Cfg<64>;
-  __amdgpu_buffer_rsrc_t rv;
-  int rowV, nch, vof[4], lof[4];
-  u32x4 st[3][4];
-
-  __device__ __forceinline__ void init(const Ctx& x, int l) {
-    nch = x.nchunks;
-    const size_t tokbase = (size_t)x.b * x.T * x.H + x.h;
-    rv = make_rsrc(x.vg + tokbase * x.DV + x.dv0,
-                   span_bytes((size_t)x.T * x.H * x.DV * 2, ((size_t)x.h * x.DV + x.dv0) * 2));
-    rowV = x.H * x.DV * 2;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int unit = l + 64 * u, row = unit / 4, cu = unit % 4;
-      vof[u] = row * rowV + cu * 16;
-      lof[u] = row * Cf::LDV + cu * 8;
-    }
-  }
-  template <int s> __device__ __forceinline__ void load(int m) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st[s][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], m * 64 * rowV, 0));
-  }
-  __device__ __forceinline__ void prologue(char*) {
-    load<0>(clamp_chunk(0, nch));
-    issue_fence();
-    load<1>(clamp_chunk(1, nch));
-    issue_fence();
-    load<2>(clamp_chunk(2, nch));
-    issue_fence();
-  }
-  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
-    if (k + 2 < nch) {
-      __bf16* const R = reinterpret_cast<__bf16*>(smem) + ph * Cf::szBuf;  // slot (k + 2) % 3
-#pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[ph][u];
-    }
-    issue_fence();
-    load<ph>(clamp_chunk(k + 5, nch));  // the set just consumed; needed three steps later
-  }
-};
-
-// The gate table (gamma, lambda, g, beta, gamma_C) of chunk k + 3 in step k,
-// from alpha and beta loaded three steps ahead; chunk 0's before the loop.
-struct GateStage {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  int H, T, nch, l;
-  float sa[3], sb[3];
-
-  __device__ __forceinline__ void init(const Ctx& x, int l_) {
-    l = l_;
-    H = x.H;
-    T = x.T;
-    nch = x.nchunks;
-    const size_t tokbase = (size_t)x.b * T * H + x.h;
-    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-    ra = make_rsrc(x.alpha + tokbase, spanG);
-    rb = make_rsrc(x.beta + tokbase, spanG);
-  }
-  template <int s> __device__ __forceinline__ void load(int m) {
-    sa[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, m * 64 * H * 4, 0));
-    sb[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, m * 64 * H * 4, 0));
-  }
-  // Gate table of chunk m from register set s (= m % 3).  g is the inclusive
-  // prefix of log2 alpha (alpha = 1 on padding tokens; beta reads as 0 there).
-  template <int s> __device__ __forceinline__ void gates(char* smem, int m) {
-    const float a = (m * 64 + l < T) ? sa[s] : 1.f;
-    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
-    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
-    float* const G = gate_table(smem, m);
-    G[l] = __builtin_amdgcn_exp2f(xg);
-    G[Cfg3::oLam + l] = __builtin_amdgcn_exp2f(gC - xg);
-    G[Cfg3::oG + l] = xg;
-    G[Cfg3::oBeta + l] = sb[s];
-    if (l == 63) G[Cfg3::oGC] = __builtin_amdgcn_exp2f(gC);
-  }
-  // Sets hold chunks 0, 1, 2; chunk 0's table is written and set 0 refilled
-  // with chunk 3, so step k finds chunk k + 3 in set (k + 3) % 3.
-  __device__ __forceinline__ void prologue(char* smem) {
-    load<0>(clamp_chunk(0, nch));
-    issue_fence();
-    load<1>(clamp_chunk(1, nch));
-    issue_fence();
-    load<2>(clamp_chunk(2, nch));
-    issue_fence();
-    if (nch > 0) gates<0>(smem, 0);
-    issue_fence();
-    load<0>(clamp_chunk(3, nch));
-    issue_fence();
-  }
-  template <int ph> __device__ __forceinline__ void step(char* smem, int k) {
-    constexpr int s = (ph + 1) % 3;  // (k + 3) % 3
-    if (k + 3 < nch) gates<s>(smem, k + 3);
-    issue_fence();
-    load<s>(clamp_chunk(k + 6, nch));  // the set just consumed; needed three steps later
-  }
-};
 
 // Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
 // step behind the row waves and read K and Q of the chunk from the stage slot
 // the row waves published (row-major), and g from the gate table.
-// Wave 4 also writes the gate tables (Extra = GateStage), wave 5 the V tiles
-// (Extra = VStage).
+// Wave 5 also writes the V tiles (Extra = VStage).
 template <class Extra>
 __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<64>;
@@ -1245,12 +1266,13 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(x.outg + ((size_t)x.b * T * H + x.h) * DV + x.dv0,
                                               span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
   const int rowO = H * DV * 2, vofO = c * rowO + 8 * g;
-  const int offRow = c * LDK + 4 * g, offT16 = c * Cf::LD16 + 4 * g;
+  const int offRow = c * LDK + 8 * g, offT16 = c * Cf::LD16 + 4 * g;  // Q row c, keys 8g .. + 7
   f32x4 o[4][2];  // Q S term of the chunk in progress, per block row and tile
   u32x2 Pm[10];   // its P tiles
   auto out_start = [&](int n, const __bf16* R, const float* G) {
     const unsigned* const hs = hand + Cfg3::fXS + (n & 1) * Cfg3::szHand2;
-    u32x2 st[2][4], qr[4][2][2];
+    u32x2 st[2][4];
+    u32x4 qr[4][2];
     float gm[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -1259,11 +1281,7 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const __bf16* pr = R + Cf::oQ + 16 * i * LDK + 32 * p + offRow;
-        qr[i][p][0] = ld4(pr);
-        qr[i][p][1] = ld4(pr + 16);
-      }
+      for (int p = 0; p < 2; ++p) qr[i][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + 32 * p + offRow);
       gm[i] = G[16 * i + c];  // gamma of token 16i + c
     }
     issue_fence();
@@ -1465,10 +1483,12 @@ __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16*
   }
   if (w < 2)
     consume(x, smem, w, l);
-  else if (w < 4)
-    gram_rows(x, smem, 2 * (w - 2), l);
+  else if (w == 2)
+    gram_rows<GateStage<false, true>>(x, smem, 0, l);
+  else if (w == 3)
+    gram_rows<GateStage<true, false>>(x, smem, 2, l);
   else if (w == 4)
-    gram_lower<GateStage>(x, smem, 2, l);
+    gram_lower<NoStage>(x, smem, 2, l);
   else if (w == 5)
     gram_lower<VStage>(x, smem, 3, l);
   else
