@@ -19,6 +19,12 @@ complex workloads
 decode
     S ~ N(0, s_var) [N, dk, dv] fp32, then for each step (step index outermost) the
     token draws q, k, v, beta-logit, alpha-logit as in the real recipe with B*T*H -> N.
+raw layer inputs (for the fused-prologue entry point)
+    q, k ~ N(0, 1) [B, T, H, dk], each token's vector scaled by its own U(0.25, 4)
+         factor (not normalised)
+    v    ~ N(0, 1) [B, T, H, dv]
+    b    ~ N(0, 1), a ~ N(alpha_mu, 1)  [B, T, H]   (the logits, stored as drawn)
+    S0   as above when s0_var is given
 
 Storage: q, k, v are cast fp64 -> fp32 -> bf16 (round to nearest even) for bf16
 workloads, fp32 / complex64 otherwise; alpha, beta and states are fp32
@@ -130,6 +136,21 @@ def gen_chunk(B, T, H, dk, dv, dtype="f32", seed=0, alpha_mu=-4.0, beta_scale=1.
             S0 = rng.normal(0.0, sd, (B, H, dk, dv)).astype(np.float32)
     return dict(q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype),
                 alpha=alpha.astype(np.float32), beta=beta.astype(np.float32), S0=S0)
+
+
+def gen_raw_layer(B, T, H, d, seed=0, alpha_mu=-4.0, s0_var=None):
+    """Raw bf16 q, k, v and fp32 logits for the fused-prologue entry point.
+
+    Returns dict q, k, v (bf16 values in float32 arrays), a_logit, b_logit, S0 (None if absent)."""
+    rng = np.random.default_rng(seed)
+    q = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+    k = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+    v = rng.normal(0.0, 1.0, (B, T, H, d))
+    b = rng.normal(0.0, 1.0, (B, T, H))
+    a = rng.normal(alpha_mu, 1.0, (B, T, H))
+    S0 = rng.normal(0.0, np.sqrt(s0_var), (B, H, d, d)).astype(np.float32) if s0_var is not None else None
+    return dict(q=_store(q, "bf16"), k=_store(k, "bf16"), v=_store(v, "bf16"), a_logit=a.astype(np.float32),
+                b_logit=b.astype(np.float32), S0=S0)
 
 
 def gen_workload(w: Workload, **overrides):

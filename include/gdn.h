@@ -113,6 +113,37 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *alph
                   int dv, int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_chunk_fwd for a layer's raw projections, with its input transforms
+ * computed inside the kernel:
+ *
+ *   q_t <- q_t / max(|q_t|, 1e-12),  k_t <- k_t / max(|k_t|, 1e-12)
+ *          (L2 over the key dimension, per token and head; the unit-norm keys
+ *          and queries the chunkwise form is usually run on)
+ *   beta_t  = beta_scale * sigmoid(b_t)
+ *          (DeltaPhase README, section 1 "Extended Householder Beta Range":
+ *          beta_scale = 2 gives beta in (0, 2); 1 gives (0, 1))
+ *   alpha_t = exp(-softplus(a_t)) = 1 / (1 + e^{a_t})
+ *          (the data-dependent forget gate of the Sykra README, "Architectural
+ *          Highlights", as a logistic map of a logit into (0, 1))
+ *
+ *   q, k      [B, T, H, dk]  bfloat16   raw queries and keys
+ *   v         [B, T, H, dv]  bfloat16   values
+ *   a_logit   [B, T, H]      float32    forget-gate logits
+ *   b_logit   [B, T, H]      float32    write-strength logits
+ *   beta_scale                          finite, 0 <= beta_scale <= 2
+ *   S0, chunk, out, S_final, B, T, H, dk, dv, stream: as for gdn_chunk_fwd.
+ *
+ * Supported: dtype == GDN_BF16, dk == dv == 64, chunk == 64, and each batch
+ * row of q, k, v, out under 2^31 bytes; otherwise GDN_ERR_UNSUPPORTED.  No
+ * workspace.  The normalisation is folded into the arithmetic (1/|k| and 1/|q|
+ * scale the Gram tiles and the per-token gates), so q and k are read once, as
+ * stored.
+ */
+int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const float *a_logit,
+                           const float *b_logit, float beta_scale, const void *S0, int chunk, void *out,
+                           void *S_final, int B, int T, int H, int dk, int dv, int dtype, void *stream);
+
+/*
  * One single-token decode step on N independent states, in place.
  *
  *   q, k   [N, dk] dtype;  v [N, dv] dtype;  alpha, beta [N] float32

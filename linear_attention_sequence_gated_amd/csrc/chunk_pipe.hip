@@ -197,6 +197,7 @@ struct Ctx {
   __bf16* outg;
   float* Sfg;
   int T, H, DV, b, h, chain, dv0, nchunks;
+  float beta_scale;  // fused-prologue kernel only: beta = beta_scale * sigmoid(b)
 };
 
 // ---------------------------------------------------------------- producers
@@ -902,8 +903,10 @@ struct Cfg3 {
   static constexpr int fBase = ((NBUF * B::szBuf * 2 + 15) / 16) * 16;  // byte offset of the fp32 region
   // fp32 region (floats): a ring of NGATE gate tables (chunk m uses table
   // m % NGATE), each gamma[64], lambda[64], g[64] (log2 prefix of alpha),
-  // beta[64], gamma_C (padded); two slots of diagonal-block rows (4 blocks x
-  // 16 rows, row stride 20); the 16 x 16 identity (row stride 20).
+  // beta[64], gamma_C (padded), and for the fused prologue gamma / |k|,
+  // lambda / |k|, gamma / |q|, 1 / |k| and 1 / |q| per token [64 each]; two
+  // slots of diagonal-block rows (4 blocks x 16 rows, row stride 20); the
+  // 16 x 16 identity (row stride 20).
   // Then, as 32-bit words, two slots (by chunk parity) of the consumers' Ut
   // and two of their start-of-chunk states, both as bf16 MFMA operands in
   // lane order (4 operands of 64 lanes x 2 words per consumer wave), for the
@@ -911,7 +914,8 @@ struct Cfg3 {
   // Gate tables are written one step before the K/Q rows of their chunk, so
   // the ring is one deeper than the stage slots.
   static constexpr int NGATE = 4;
-  static constexpr int szGate = 260, fGate = 0, oLam = 64, oG = 128, oBeta = 192, oGC = 256;
+  static constexpr int fGate = 0, oLam = 64, oG = 128, oBeta = 192, oGC = 256;
+  static constexpr int oGk = 260, oLk = 324, oGq = 388, oIk = 452, oIq = 516, szGate = 580;
   static constexpr int szDS = 4 * 16 * 20, fDS = NGATE * szGate;
   static constexpr int fEye = fDS + 2 * szDS;
   static constexpr int szHand = 4 * 64 * 2, szHand2 = 2 * szHand;  // one consumer / both consumers
@@ -920,6 +924,9 @@ struct Cfg3 {
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(oBeta == oG + 64, "g and beta adjacent: the Gram code reads them as one table");
+  static_assert((oGk * 4) % 16 == 0 && (oLk * 4) % 16 == 0 && (oGq * 4) % 16 == 0 && (oIk * 4) % 16 == 0 &&
+                    (oIq * 4) % 16 == 0,
+                "per-token tables are read as 16-byte vectors");
   static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fEye * 4) % 16 == 0 &&
                     (fXU * 4) % 16 == 0,
                 "fp32 tables must be 16-byte aligned");
@@ -1037,17 +1044,18 @@ struct VStage {
 // different waves: each strided 4-byte load touches 24 cache lines for 256
 // bytes, which costs a loading wave several hundred cycles per step when the
 // inputs come from HBM.
-template <bool kAlpha, bool kBeta>
+template <bool kAlpha, bool kBeta, bool kPro>
 struct GateStage {
   __amdgpu_buffer_rsrc_t rs;
   int H, T, nch, l;
-  float sv[3];
+  float sv[3], bscale;
 
   __device__ __forceinline__ void init(const Ctx& x, int l_) {
     l = l_;
     H = x.H;
     T = x.T;
     nch = x.nchunks;
+    bscale = x.beta_scale;
     const size_t tokbase = (size_t)x.b * T * H + x.h;
     rs = make_rsrc((kAlpha ? x.alpha : x.beta) + tokbase, span_bytes((size_t)T * H * 4, (size_t)x.h * 4));
   }
@@ -1056,18 +1064,33 @@ struct GateStage {
   }
   // Gate table of chunk m from register set s (= m % 3).  g is the inclusive
   // prefix of log2 alpha (alpha = 1 on padding tokens; beta reads as 0 there).
+  // With kPro the loads are logits: log2 alpha = -softplus(a) / ln 2 and
+  // beta = bscale * sigmoid(b), both on padding tokens replaced as above.
   template <int s> __device__ __forceinline__ void gates(char* smem, int m) {
     float* const G = gate_table(smem, m);
+    const bool live = m * 64 + l < T;
     if constexpr (kAlpha) {
-      const float a = (m * 64 + l < T) ? sv[s] : 1.f;
-      const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
+      float la;
+      if constexpr (kPro) {
+        // softplus(a) / ln 2 = max(a, 0) log2(e) + log2(1 + 2^(-|a| log2(e)))
+        const float u = sv[s] * 1.4426950408889634f;
+        la = live ? -(fmaxf(u, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(u)))) : 0.f;
+      } else {
+        la = __builtin_amdgcn_logf(live ? sv[s] : 1.f);
+      }
+      const float xg = wave_prefix_sum(la);
       const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
       G[l] = __builtin_amdgcn_exp2f(xg);
       G[Cfg3::oLam + l] = __builtin_amdgcn_exp2f(gC - xg);
       G[Cfg3::oG + l] = xg;
       if (l == 63) G[Cfg3::oGC] = __builtin_amdgcn_exp2f(gC);
     }
-    if constexpr (kBeta) G[Cfg3::oBeta + l] = sv[s];
+    if constexpr (kBeta) {
+      if constexpr (kPro)
+        G[Cfg3::oBeta + l] = live ? bscale * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-sv[s] * 1.4426950408889634f)) : 0.f;
+      else
+        G[Cfg3::oBeta + l] = sv[s];
+    }
   }
   // Sets hold chunks 0, 1, 2; chunk 0's table is written and set 0 refilled
   // with chunk 3, so step k finds chunk k + 3 in set (k + 3) % 3.
@@ -1098,9 +1121,32 @@ struct NoStage {
   template <int ph> __device__ __forceinline__ void step(char*, int) {}
 };
 
+// 1 / max(|x|, 1e-12) from |x|^2, as the layer's L2 normalisation divides.
+__device__ __forceinline__ float inv_norm(float sq) { return __builtin_amdgcn_rsqf(fmaxf(sq, 1e-24f)); }
+
+// Element c & 3 of v (lane (g, c) with g = c / 4 holds diagonal entry c of a
+// 16 x 16 accumulator tile there).
+__device__ __forceinline__ float diag_pick(const f32x4& v, int c) {
+  const int j = c & 3;
+  return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
+}
+
+// x of lane `src` (0..63).  A cross-lane read, not an LDS round trip: lanes of
+// one wave that exchange values through LDS with no synchronisation may have
+// the reads ordered before the writes by the compiler.
+__device__ __forceinline__ float lane_read(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, x)));
+}
+
 // Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).  They also write the
-// gate tables (Extra = GateStage): wave 2 beta, wave 3 the rest.
-template <class Extra>
+// gate tables (Extra = GateStage): wave 2 beta, wave 3 the rest.  With kPro
+// (fused prologue: raw q and k) they also find 1/|k_r| and 1/|q_r| of their 32
+// rows -- |k_r|^2 is the diagonal of the K K^T tiles they form anyway, |q_r|^2
+// that of four extra Q Q^T products -- scale their tiles by them, and write
+// them and gamma / |k|, lambda / |k|, gamma / |q| to the chunk's gate table.
+// Normalising the rows themselves would cost every row wave about a thousand
+// cycles of vector work per step.
+template <class Extra, bool kPro>
 __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int l) {
   using Cf = Cfg<64>;
   constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
@@ -1175,6 +1221,48 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
       G1 = mma32(kk[1][p], kk[1][p], G1);
       P1 = mma32(kk[1][p], qq[1][p], P1);
     }
+    if constexpr (kPro) {
+      // lane (g, c) holds [s = 16b + 4g + j][r = 16b' + c] of each tile
+      f32x4 Q0 = zero4(), Q1 = zero4();
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        Q0 = mma32(qq[0][p], qq[0][p], Q0);
+        Q1 = mma32(qq[1][p], qq[1][p], Q1);
+      }
+      // Every lane takes the inverse norm of the entry it would hold on the
+      // diagonal (finite where it is not there); row c's comes from lane
+      // (c / 4, c), row 4g + j's from lane (g, 4g + j) = 20g + j.
+      const float dk0 = inv_norm(diag_pick(G0, c)), dk1 = inv_norm(diag_pick(G1, c));
+      const float dq0 = inv_norm(diag_pick(Q0, c)), dq1 = inv_norm(diag_pick(Q1, c));
+      const int own = 16 * (c >> 2) + c;
+      const float ik0 = lane_read(dk0, own), ik1 = lane_read(dk1, own);
+      const float iq0 = lane_read(dq0, own), iq1 = lane_read(dq1, own);
+      f32x4 is0, is1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        is0[j] = lane_read(dk0, 20 * g + j);
+        is1[j] = lane_read(dk1, 20 * g + j);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        G0[j] *= ik0 * is0[j];
+        P0[j] *= iq0 * is0[j];
+        Go[j] *= ik1 * is0[j];
+        Po[j] *= iq1 * is0[j];
+        G1[j] *= ik1 * is1[j];
+        P1[j] *= iq1 * is1[j];
+      }
+      if (l < 32) {  // row 16 b0 + l: lane (g, c) with g = 0 / 1 holds block b0 / b0 + 1's row c
+        float* const Gt = gate_table(smem, m);
+        const int r = 16 * b0 + l;
+        const float ik = l < 16 ? ik0 : ik1, iq = l < 16 ? iq0 : iq1, ga = Gt[r];
+        Gt[Cfg3::oIk + r] = ik;
+        Gt[Cfg3::oIq + r] = iq;
+        Gt[Cfg3::oGk + r] = ga * ik;
+        Gt[Cfg3::oGq + r] = ga * iq;
+        Gt[Cfg3::oLk + r] = Gt[Cfg3::oLam + r] * ik;
+      }
+    }
     offdiag_tiles<64>(Go, Po, PGT, b0 + 1, b0, g, c, R);
     const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
     diag_p_tile<64>(P0, gm0, b0, g, c, R);
@@ -1210,8 +1298,9 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
 // Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
 // step behind the row waves and read K and Q of the chunk from the stage slot
 // the row waves published (row-major), and g from the gate table.
-// Wave 5 also writes the V tiles (Extra = VStage).
-template <class Extra>
+// Wave 5 also writes the V tiles (Extra = VStage).  With kPro the tiles are
+// scaled by the inverse row norms the row waves wrote a step earlier.
+template <class Extra, bool kPro>
 __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<64>;
   constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
@@ -1244,6 +1333,19 @@ __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int 
         G1 = mma32(k1[p], ki[p], G1);
         P1 = mma32(k1[p], qi[p], P1);
       }
+      if constexpr (kPro) {  // lane (g, c): [s = 16 jb + 4g + j][r = 16i + c]
+        const float* const Gt = gate_table(smem, m);
+        const float ikr = Gt[Cfg3::oIk + 16 * i + c], iqr = Gt[Cfg3::oIq + 16 * i + c];
+        const f32x4 is0 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 4 * g);
+        const f32x4 is1 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 16 + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          G0[j] *= ikr * is0[j];
+          P0[j] *= iqr * is0[j];
+          G1[j] *= ikr * is1[j];
+          P1[j] *= iqr * is1[j];
+        }
+      }
       offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
       offdiag_tiles<64>(G1, P1, gt, i, 1, g, c, R);
     }
@@ -1251,9 +1353,11 @@ __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int 
   });
 }
 
-// Wave 6: the output of both consumers' columns, one step behind them:
+// Wave 6 (with kPro reading gamma / |q| in place of gamma, for raw queries):
+// the output of both consumers' columns, one step behind them:
 // chunk n's Q S term in step n from their start-of-chunk state, its P Ut term
 // in step n + 1 from their Ut.
+template <bool kPro>
 __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   using Cf = Cfg<64>;
   constexpr int LDK = Cf::LDK;
@@ -1309,7 +1413,7 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   run_steps(nch, [&](auto pc, int k) {
     constexpr int cur = (decltype(pc)::value + 1) % 3;  // stage slot of chunk k
     if (k >= 1 && k <= nch) out_finish(k - 1);
-    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, gate_table(smem, k));
+    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, gate_table(smem, k) + (kPro ? Cfg3::oGq : 0));
   });
   if (needs_tail_step(nch)) {
     stage_barrier();
@@ -1418,7 +1522,11 @@ __device__ __forceinline__ void inverter(const Ctx& x, char* smem, int l) {
 #undef GDN_ST
 
 // Waves 0 and 1: consumers.  They hand Ut and the start-of-chunk state to the
-// V wave, which forms the output.
+// output wave.  With kPro the keys are raw, so K S and the update take
+// gamma / |k| and lambda / |k| from the gate table in place of gamma and
+// lambda: (K / |k|) S = diag(1 / |k|) (K S) and (K / |k|)^T (lambda Ut) =
+// K^T (lambda / |k| * Ut).
+template <bool kPro>
 __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) {
   using Cf = Cfg<64>;
   using Cs = Consumer<64>;
@@ -1434,24 +1542,31 @@ __device__ __forceinline__ void consume(const Ctx& x, char* smem, int w, int l) 
     if (k >= 0 && k < x.nchunks) {
       Cs::Upd u;
       u32x2 Xf[4][1], XL[4][1];
-      cs.solve(sb + slot * Cf::szBuf, gate_table(smem, k), Cfg3::oGC, u, Xf, XL,
+      // solve() reads lambda at G + 64 and gamma_C at G[gCoff]
+      constexpr int shift = kPro ? Cfg3::oLk - Cfg3::oLam : 0;
+      cs.solve(sb + slot * Cf::szBuf, gate_table(smem, k) + shift, Cfg3::oGC - shift, u, Xf, XL,
                hand + Cfg3::fXU + (k & 1) * Cfg3::szHand2);
       cs.update(u, XL);
     }
     if (k >= -1 && k + 1 < x.nchunks)
-      cs.begin(sb + next * Cf::szBuf, gate_table(smem, k + 1),
+      cs.begin(sb + next * Cf::szBuf, gate_table(smem, k + 1) + (kPro ? Cfg3::oGk : 0),
                hand + Cfg3::fXS + ((k + 1) & 1) * Cfg3::szHand2);
   });
   cs.finish(x);
 }
 
+// kPro = false: q, k are used as given and alpha, beta are the gates.
+// kPro = true (fused prologue): q, k are raw and normalised per row inside the
+// arithmetic; alpha and beta point to the logits a, b, with alpha =
+// exp(-softplus(a)) and beta = beta_scale * sigmoid(b).
+template <bool kPro>
 __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16* __restrict__ qg,
                                                                   const __bf16* __restrict__ kg,
                                                                   const __bf16* __restrict__ vg,
                                                                   const float* __restrict__ alpha,
                                                                   const float* __restrict__ beta, const float* S0g,
                                                                   __bf16* __restrict__ outg, float* Sfg, int T, int H,
-                                                                  int DV, int nslices) {
+                                                                  int DV, int nslices, float beta_scale) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg3::bytes];
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
@@ -1474,23 +1589,24 @@ __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16*
   x.chain = chain;
   x.dv0 = slice * Cfg<64>::NV;
   x.nchunks = (T + 63) >> 6;
+  x.beta_scale = beta_scale;
   // The wave index is uniform (scalar branches only: matrix-core instructions
   // do not honour the exec mask).
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   if (w == 6) {
-    out_wave(x, smem, l);  // runs the tail step itself
+    out_wave<kPro>(x, smem, l);  // runs the tail step itself
     return;
   }
   if (w < 2)
-    consume(x, smem, w, l);
+    consume<kPro>(x, smem, w, l);
   else if (w == 2)
-    gram_rows<GateStage<false, true>>(x, smem, 0, l);
+    gram_rows<GateStage<false, true, kPro>, kPro>(x, smem, 0, l);
   else if (w == 3)
-    gram_rows<GateStage<true, false>>(x, smem, 2, l);
+    gram_rows<GateStage<true, false, kPro>, kPro>(x, smem, 2, l);
   else if (w == 4)
-    gram_lower<NoStage>(x, smem, 2, l);
+    gram_lower<NoStage, kPro>(x, smem, 2, l);
   else if (w == 5)
-    gram_lower<VStage>(x, smem, 3, l);
+    gram_lower<VStage, kPro>(x, smem, 3, l);
   else
     inverter(x, smem, l);
   if (needs_tail_step(x.nchunks)) stage_barrier();
@@ -1510,9 +1626,11 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a) {
   if (a.dtype == kDtBF16 && a.dk == 64) {
     const int nslices = a.dv / pipe::Cfg<64>::NV;
     const long nblk = (long)a.B * a.H * nslices;
-    return launch_kernel(pipe3::chunk_pipe3_kernel, dim3((unsigned)nblk), dim3(pipe3::kThreads3), (hipStream_t)a.stream,
-                         a.q, a.k, a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
+    auto kern = a.prologue ? pipe3::chunk_pipe3_kernel<true> : pipe3::chunk_pipe3_kernel<false>;
+    return launch_kernel(kern, dim3((unsigned)nblk), dim3(pipe3::kThreads3), (hipStream_t)a.stream, a.q, a.k, a.v,
+                         a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices, a.beta_scale);
   }
+  if (a.prologue) return hipErrorInvalidValue;
   if (a.dtype == kDtBF16 && a.dk == 128) return launch_pipe_dk<128>(a);
   return hipErrorInvalidValue;
 }

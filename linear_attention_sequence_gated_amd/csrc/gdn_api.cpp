@@ -86,6 +86,28 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const float* a_logit,
+                           const float* b_logit, float beta_scale, const void* S0, int chunk, void* out,
+                           void* S_final, int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
+  if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems)
+    return GDN_ERR_SHAPE;
+  if (chunk != 64 || dtype != GDN_BF16 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  if (!(beta_scale >= 0.f && beta_scale <= 2.f)) return GDN_ERR_SHAPE;
+  if ((long long)T * H * dk * 2 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
+  const bool tokens = (long long)B * T * H > 0;
+  if (tokens && (!q || !k || !v || !a_logit || !b_logit || !out)) return GDN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, a_logit, b_logit, S0, out, S_final};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+  if ((long long)B * H == 0) return GDN_OK;
+  gdn::ChunkArgs a{q, k, v, a_logit, b_logit, S0, out, S_final, B, T, H, dk, dv, dtype, stream};
+  a.prologue = 1;
+  a.beta_scale = beta_scale;
+  return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                        void* S, void* out, int N, int dk, int dv, int dtype, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;

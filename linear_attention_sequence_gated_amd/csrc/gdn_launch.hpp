@@ -35,6 +35,10 @@ struct ChunkArgs {
   void* S_final;
   int B, T, H, dk, dv, dtype;
   void* stream;
+  // Fused prologue (d64 bf16 pipelined kernel only): q and k raw, alpha and
+  // beta hold the logits a and b; beta = beta_scale * sigmoid(b).
+  int prologue = 0;
+  float beta_scale = 1.f;
 };
 
 struct StepArgs {

@@ -1,8 +1,9 @@
 """ctypes binding of libgdn (include/gdn.h).
 
 The raw entry points keep the C names and take integer device addresses:
-``gdn_chunk_fwd``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
-``gdn_status_str``.  ``chunk_fwd`` and ``recurrent_step`` are conveniences for
+``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_recurrent_step``,
+``gdn_chunk_fwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
+``chunk_fwd_prologue`` and ``recurrent_step`` are conveniences for
 torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
 ``data_ptr()`` and the current HIP stream, and raise on a non-OK status.  Every
 step of the computation runs in the HIP kernels; there is no fallback path.
@@ -19,7 +20,8 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3
 GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
 GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
 
-EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_str")
+EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_recurrent_step",
+           "gdn_status_str")
 
 _lib = None
 
@@ -44,6 +46,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = ci
+    lib.gdn_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, ci, vp, vp, ci, ci, ci, ci, ci,
+                                           ci, vp]
+    lib.gdn_chunk_fwd_prologue.restype = ci
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
     lib.gdn_recurrent_step.restype = ci
     lib.gdn_status_str.argtypes = [ci]
@@ -66,6 +71,12 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv
                   workspace, workspace_bytes, stream) -> int:
     return int(load().gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype,
                                     workspace, workspace_bytes, stream))
+
+
+def gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale, S0, chunk, out, S_final, B, T, H, dk, dv,
+                           dtype, stream) -> int:
+    return int(load().gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, float(beta_scale), S0, chunk, out, S_final,
+                                             B, T, H, dk, dv, dtype, stream))
 
 
 def gdn_recurrent_step(q, k, v, alpha, beta, S, out, N, dk, dv, dtype, stream) -> int:
@@ -135,6 +146,41 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, chunk: int = 64, out=None, S_final=
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     s = gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), chunk, _ptr(out),
                       _ptr(S_final), B, T, H, dk, dv, code, _ptr(ws), ws_bytes, st)
+    if s != GDN_OK:
+        raise GdnError(s)
+    return out, S_final
+
+
+def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=None, chunk: int = 64, out=None,
+                       S_final=None, stream=None):
+    """Chunked forward from raw projections: q and k are L2-normalised per row, alpha = exp(-softplus(a_logit))
+    and beta = beta_scale * sigmoid(b_logit), all inside the kernel.  q, k, v [B,T,H,64] bfloat16; a_logit,
+    b_logit [B,T,H] float32.  Returns (out [B,T,H,64], S_final [B,H,64,64] float32).
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_prologue: tensors must live on a HIP device")
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(a_logit, "a_logit", (B, T, H), torch.float32, dev)
+    _check(b_logit, "b_logit", (B, T, H), torch.float32, dev)
+    sdt = _state_dtype(code)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), sdt, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, T, H, dv), q.dtype, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=sdt, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), sdt, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    s = gdn_chunk_fwd_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(a_logit), _ptr(b_logit), beta_scale, _ptr(S0), chunk,
+                               _ptr(out), _ptr(S_final), B, T, H, dk, dv, code, st)
     if s != GDN_OK:
         raise GdnError(s)
     return out, S_final

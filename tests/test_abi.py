@@ -75,6 +75,37 @@ def test_chunk_empty_is_noop():
     assert chunk(H=0) == raw.GDN_OK
 
 
+def prologue(**kw):
+    args = dict(q=A, k=A, v=A, a_logit=A, b_logit=A, beta_scale=2.0, S0=None, chunk=64, out=A, S_final=A, B=2,
+                T=128, H=3, dk=64, dv=64, dtype=gdn.GDN_BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_chunk_fwd_prologue(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), raw.GDN_ERR_DTYPE),
+    (dict(T=-1), raw.GDN_ERR_SHAPE),
+    (dict(beta_scale=-0.5), raw.GDN_ERR_SHAPE),
+    (dict(beta_scale=2.5), raw.GDN_ERR_SHAPE),
+    (dict(beta_scale=float("nan")), raw.GDN_ERR_SHAPE),
+    (dict(chunk=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_F32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(B=1, T=1 << 22, H=64), raw.GDN_ERR_UNSUPPORTED),
+    (dict(a_logit=None), raw.GDN_ERR_NULL),
+    (dict(b_logit=None), raw.GDN_ERR_NULL),
+    (dict(q=A + 8), raw.GDN_ERR_ALIGN),
+    (dict(b_logit=A + 4), raw.GDN_ERR_ALIGN),
+])
+def test_prologue_argument_errors(kw, status):
+    assert prologue(**kw) == status
+
+
+def test_prologue_empty_is_noop():
+    assert prologue(B=0, q=None, k=None, v=None, a_logit=None, b_logit=None, out=None, S_final=None) == raw.GDN_OK
+
+
 def test_workspace_query():
     assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
 

@@ -1,0 +1,104 @@
+"""Fused-prologue entry point on the GPU (through the C ABI) against the fp64 oracle.
+
+The kernel takes raw bf16 q, k (normalised per row inside its arithmetic) and the
+gate logits; the oracle applies the same transforms in fp64 to the same stored
+values (oracle/prologue.py) and runs the token loop.
+"""
+import numpy as np
+import pytest
+
+from gdn_inputs import WORKLOADS, gen_raw_layer
+from gpu_util import TOL, assert_close, chain_rel_errors, down, note, torch_dev, up
+from oracle.prologue import prologue_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prologue(inp, beta_scale, S0=True, S_final_alias=False):
+    import torch
+    import linear_attention_sequence_gated_amd as gdn
+    q, k, v = up(inp["q"], "bf16"), up(inp["k"], "bf16"), up(inp["v"], "bf16")
+    a, b = up(inp["a_logit"], "f32"), up(inp["b_logit"], "f32")
+    s0 = up(inp["S0"], "f32") if (S0 and inp.get("S0") is not None) else None
+    if S_final_alias and s0 is not None:
+        o, S = gdn.chunk_fwd_prologue(q, k, v, a, b, beta_scale, s0, S_final=s0)
+    else:
+        o, S = gdn.chunk_fwd_prologue(q, k, v, a, b, beta_scale, s0)
+    torch.cuda.synchronize()
+    return down(o), down(S)
+
+
+def oracle_prologue(inp, beta_scale):
+    return prologue_fwd(inp["q"], inp["k"], inp["v"], inp["a_logit"], inp["b_logit"], beta_scale, inp.get("S0"))
+
+
+@pytest.mark.parametrize("beta_scale", [1.0, 2.0])
+@pytest.mark.parametrize("B,T,H,s0", [(2, 300, 3, None), (1, 129, 2, 0.01), (2, 250, 1, 0.1)])
+def test_prologue_small(B, T, H, s0, beta_scale):
+    torch_dev()
+    inp = gen_raw_layer(B, T, H, 64, seed=17 + T + H, s0_var=s0)
+    note(f"prologue B{B} T{T} H{H} s0={s0} beta_scale={beta_scale}")
+    o, S = run_prologue(inp, beta_scale)
+    o_ref, S_ref = oracle_prologue(inp, beta_scale)
+    assert_close(f"prologue_{B}_{T}_{H}_{beta_scale}", "bf16", o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 191, 385])
+def test_prologue_lengths(T):
+    torch_dev()
+    inp = gen_raw_layer(2, T, 2, 64, seed=5 + T, s0_var=0.1)
+    note(f"prologue lengths T={T}")
+    o, S = run_prologue(inp, 2.0)
+    if T == 0:  # nothing to process: S_final is S0
+        assert np.array_equal(S, inp["S0"])
+        return
+    o_ref, S_ref = oracle_prologue(inp, 2.0)
+    assert_close(f"prologue_len{T}", "bf16", o, S, o_ref, S_ref)
+
+
+def test_prologue_zero_rows_and_in_place_state():
+    """Rows of q or k that are exactly zero stay zero (no division by zero); S_final may alias S0."""
+    torch_dev()
+    inp = gen_raw_layer(1, 200, 3, 64, seed=23, s0_var=0.1)
+    inp["k"][0, 5, 1] = 0.0
+    inp["q"][0, 77, 2] = 0.0
+    inp["k"][0, 130:140, 0] = 0.0
+    note("prologue zero rows, aliased state")
+    o, S = run_prologue(inp, 1.0, S_final_alias=True)
+    o_ref, S_ref = oracle_prologue(inp, 1.0)
+    assert_close("prologue_zero_rows", "bf16", o, S, o_ref, S_ref)
+
+
+def test_prologue_row_rescaling():
+    """Scaling raw q and k rows by powers of two (exact in bf16 and in every fp32 step of the
+    normalisation) leaves the outputs unchanged to fp32 rounding."""
+    torch_dev()
+    inp = gen_raw_layer(2, 190, 2, 64, seed=29, s0_var=0.1)
+    rng = np.random.default_rng(1)
+    sc = dict(inp)
+    for key in ("q", "k"):
+        f = (2.0 ** rng.integers(-3, 4, size=inp[key].shape[:3] + (1,))).astype(np.float32)
+        sc[key] = inp[key] * f
+    note("prologue row rescaling")
+    o1, S1 = run_prologue(inp, 2.0)
+    o2, S2 = run_prologue(sc, 2.0)
+    eo, es = chain_rel_errors(o2, S2, o1, S1)
+    print(f"[parity] prologue rescaling: o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= 1e-5 and es <= 1e-5
+
+
+def test_prologue_full_size_sampled_chains():
+    """The 8 x 2048 x 12 d64 layer from raw inputs, as the benchmark runs it; sampled chains vs the oracle."""
+    torch_dev()
+    w = WORKLOADS["sykra_layer_bf16"]
+    inp = gen_raw_layer(w.B, w.T, w.H, w.dk, seed=w.seed)
+    note("prologue full size sykra_layer_bf16")
+    o, S = run_prologue(inp, 1.0)
+    chains = [(0, 0), (3, 7), (7, 11)]
+    sub = {key: np.stack([inp[key][b, :, h] for b, h in chains], axis=1)[None] for key in ("q", "k", "v", "a_logit", "b_logit")}
+    sub["S0"] = None
+    o_ref, S_ref = oracle_prologue(sub, 1.0)
+    o_s = np.stack([o[b, :, h] for b, h in chains], axis=1)[None]
+    S_s = np.stack([S[b, h] for b, h in chains])[None]
+    assert_close("prologue_full", "bf16", o_s, S_s, o_ref, S_ref)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
