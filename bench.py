@@ -5,7 +5,10 @@
 One step = one gdn_chunk_fwd call over the whole workload (gate scan, Gram tiles,
 triangular solve, WY factors, state pass and output for every chunk of every
 chain), on inputs already resident in HBM.  The default workload is the
-Sykra-shaped layer (B=8, T=2048, H=12, d=64, chunk 64, bf16 q/k/v).  To keep
+Sykra-shaped layer (B=8, T=2048, H=12, d=64, chunk 64, bf16 q/k/v);
+``--workload sykra_layer_bf16_prologue`` runs the same layer from raw inputs
+through gdn_chunk_fwd_prologue (q, k normalised and the gates formed from their
+logits inside the kernel).  To keep
 the 256 MB Infinity Cache from serving a step's inputs, the timed loop cycles
 through enough independent copies of the inputs (>= 1 GiB in total) that each
 step reads data not touched for several steps.
@@ -96,24 +99,30 @@ def decode_bytes(w) -> int:
 
 
 def cpu_baseline(inp, w, budget_s: float = 12.0):
-    """Time the fp64 oracle (as it stands) on the host over the full workload."""
+    """Time the fp64 oracle (as it stands) on the host over the full workload.  For raw
+    layer inputs that is the oracle's input transforms followed by its token loop."""
     import oracle
+    from oracle import prologue as oracle_prologue
     q, k, v = (np.asarray(inp[x], dtype=np.float64) for x in ("q", "k", "v"))
-    a, b = np.asarray(inp["alpha"], np.float64), np.asarray(inp["beta"], np.float64)
     s0 = None if inp.get("S0") is None else np.asarray(inp["S0"], np.float64)
     threads = os.cpu_count() or 1
     reps, t0 = 0, time.perf_counter()
     used = threads
     while True:
-        _, _, used = oracle.recurrent_fwd(q, k, v, a, b, s0, threads=threads)
+        if w.kind == "prologue":
+            qh, kh, a, b = oracle_prologue.prologue(q, k, inp["a_logit"], inp["b_logit"], w.beta_scale)
+        else:
+            qh, kh, a, b = q, k, np.asarray(inp["alpha"], np.float64), np.asarray(inp["beta"], np.float64)
+        _, _, used = oracle.recurrent_fwd(qh, kh, v, a, b, s0, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 400:
             break
     tokens = w.B * w.T * reps
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"whole workload ({w.B}x{w.T} tokens x {w.H} heads, fp64 C token loop, OpenMP over "
-                      f"{w.B * w.H} chains) repeated {reps}x in {el:.1f} s"}
+            "sample": f"whole workload ({w.B}x{w.T} tokens x {w.H} heads, "
+                      f"{'fp64 NumPy input transforms, ' if w.kind == 'prologue' else ''}fp64 C token loop, "
+                      f"OpenMP over {w.B * w.H} chains) repeated {reps}x in {el:.1f} s"}
 
 
 def summarize(path: str) -> None:
@@ -183,8 +192,11 @@ def main():
     wbytes = algorithmic_bytes(w, inp["S0"] is not None)
     ncopies = args.copies or max(2, int(np.ceil((1 << 30) / wbytes)))
 
+    pro = w.kind == "prologue"  # raw q, k and gate logits through gdn_chunk_fwd_prologue
+    gates = ("a_logit", "b_logit") if pro else ("alpha", "beta")
+
     def upload():
-        d = {x: torch.from_numpy(inp[x]).to(dev) for x in ("q", "k", "v", "alpha", "beta")}
+        d = {x: torch.from_numpy(inp[x]).to(dev) for x in ("q", "k", "v") + gates}
         for x in ("q", "k", "v"):
             d[x] = d[x].to(tdt)
         d["S0"] = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
@@ -205,16 +217,24 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_ptr = ws.data_ptr() if ws_bytes else None
     calls = []
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     for d in sets:
-        gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], out=d["out"], S_final=d["S"],
-                      stream=stream.cuda_stream)
-        ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-        calls.append((ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]), ptr(d["S0"]), w.chunk,
-                      ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code, ws_ptr, ws_bytes,
-                      stream.cuda_stream))
+        if pro:
+            gdn.chunk_fwd_prologue(d["q"], d["k"], d["v"], d["a_logit"], d["b_logit"], w.beta_scale, d["S0"],
+                                   out=d["out"], S_final=d["S"], stream=stream.cuda_stream)
+            calls.append((ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["a_logit"]), ptr(d["b_logit"]), w.beta_scale,
+                          ptr(d["S0"]), w.chunk, ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code,
+                          stream.cuda_stream))
+        else:
+            gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], out=d["out"], S_final=d["S"],
+                          stream=stream.cuda_stream)
+            calls.append((ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]), ptr(d["S0"]),
+                          w.chunk, ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code, ws_ptr, ws_bytes,
+                          stream.cuda_stream))
+    entry = lib.gdn_chunk_fwd_prologue if pro else lib.gdn_chunk_fwd
 
     def step(i):
-        s = lib.gdn_chunk_fwd(*calls[i % ncopies])
+        s = entry(*calls[i % ncopies])
         if s != 0:  # GDN_OK
             raise gdn.GdnError(s)
 
@@ -262,7 +282,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded; unit-norm q/k, N(0,1) v, sigmoid beta, exp(-softplus) alpha)",
+        "data": ("synthetic (seeded; raw q/k rows N(0,1) x U(0.25,4), N(0,1) v, logits b ~ N(0,1), a ~ N(-4,1); "
+                 "normalisation and gates inside the kernel)" if pro else
+                 "synthetic (seeded; unit-norm q/k, N(0,1) v, sigmoid beta, exp(-softplus) alpha)"),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
                    "S0": inp["S0"] is not None, "input_copies_cycled": ncopies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -56,7 +56,7 @@ def _softplus(x):
 
 @dataclass(frozen=True)
 class Workload:
-    """One synthetic workload shape.  ``kind`` is 'chunk' or 'decode'."""
+    """One synthetic workload shape.  ``kind`` is 'chunk', 'prologue' (raw layer inputs) or 'decode'."""
     name: str
     kind: str
     dtype: str  # 'f32', 'bf16' or 'c64'
@@ -93,6 +93,9 @@ WORKLOADS = {
     "deltaphase_c64": Workload(
         "deltaphase_c64", "chunk", "c64", B=4, T=4096, H=8, dk=32, dv=32, seed=3,
         beta_scale=2.0, note="complex phasor keys/queries, beta in (0, 2)"),
+    "sykra_layer_bf16_prologue": Workload(
+        "sykra_layer_bf16_prologue", "prologue", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
+        note="the Sykra-shaped layer from raw inputs: q, k not normalised, gate logits a, b"),
     "decode_4096x64": Workload(
         "decode_4096x64", "decode", "bf16", N=4096, dk=64, dv=64, steps=64, seed=4,
         s0_var=0.1, note="4096 independent 64x64 states, 64 single-token steps"),
@@ -158,6 +161,9 @@ def gen_workload(w: Workload, **overrides):
     p = dict(B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dv, dtype=w.dtype, seed=w.seed,
              alpha_mu=w.alpha_mu, beta_scale=w.beta_scale, s0_var=w.s0_var)
     p.update(overrides)
+    if w.kind == "prologue":
+        return gen_raw_layer(p["B"], p["T"], p["H"], p["dk"], seed=p["seed"], alpha_mu=p["alpha_mu"],
+                             s0_var=p["s0_var"])
     return gen_chunk(**p)
 
 

@@ -7,7 +7,7 @@ values (oracle/prologue.py) and runs the token loop.
 import numpy as np
 import pytest
 
-from gdn_inputs import WORKLOADS, gen_raw_layer
+from gdn_inputs import WORKLOADS, gen_raw_layer, gen_workload
 from gpu_util import TOL, assert_close, chain_rel_errors, down, note, torch_dev, up
 from oracle.prologue import prologue_fwd
 
@@ -90,9 +90,9 @@ def test_prologue_row_rescaling():
 def test_prologue_full_size_sampled_chains():
     """The 8 x 2048 x 12 d64 layer from raw inputs, as the benchmark runs it; sampled chains vs the oracle."""
     torch_dev()
-    w = WORKLOADS["sykra_layer_bf16"]
-    inp = gen_raw_layer(w.B, w.T, w.H, w.dk, seed=w.seed)
-    note("prologue full size sykra_layer_bf16")
+    w = WORKLOADS["sykra_layer_bf16_prologue"]
+    inp = gen_workload(w)
+    note("prologue full size sykra_layer_bf16_prologue")
     o, S = run_prologue(inp, 1.0)
     chains = [(0, 0), (3, 7), (7, 11)]
     sub = {key: np.stack([inp[key][b, :, h] for b, h in chains], axis=1)[None] for key in ("q", "k", "v", "a_logit", "b_logit")}
