@@ -904,7 +904,7 @@ struct Cfg3 {
   // fp32 region (floats): a ring of NGATE gate tables (chunk m uses table
   // m % NGATE), each gamma[64], lambda[64], g[64] (log2 prefix of alpha),
   // beta[64], gamma_C (padded), and for the fused prologue gamma / |k|,
-  // lambda / |k|, gamma / |q|, 1 / |k| and 1 / |q| per token [64 each]; two
+  // lambda / |k| and 1 / |k| per token [64 each]; two
   // slots of diagonal-block rows (4 blocks x 16 rows, row stride 20); the
   // 16 x 16 identity (row stride 20).
   // Then, as 32-bit words, two slots (by chunk parity) of the consumers' Ut
@@ -915,7 +915,7 @@ struct Cfg3 {
   // the ring is one deeper than the stage slots.
   static constexpr int NGATE = 4;
   static constexpr int fGate = 0, oLam = 64, oG = 128, oBeta = 192, oGC = 256;
-  static constexpr int oGk = 260, oLk = 324, oGq = 388, oIk = 452, oIq = 516, szGate = 580;
+  static constexpr int oGk = 260, oLk = 324, oIk = 388, szGate = 452;
   static constexpr int szDS = 4 * 16 * 20, fDS = NGATE * szGate;
   static constexpr int fEye = fDS + 2 * szDS;
   static constexpr int szHand = 4 * 64 * 2, szHand2 = 2 * szHand;  // one consumer / both consumers
@@ -924,8 +924,7 @@ struct Cfg3 {
   static constexpr int bytes = fBase + nF * 4;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(oBeta == oG + 64, "g and beta adjacent: the Gram code reads them as one table");
-  static_assert((oGk * 4) % 16 == 0 && (oLk * 4) % 16 == 0 && (oGq * 4) % 16 == 0 && (oIk * 4) % 16 == 0 &&
-                    (oIq * 4) % 16 == 0,
+  static_assert((oGk * 4) % 16 == 0 && (oLk * 4) % 16 == 0 && (oIk * 4) % 16 == 0,
                 "per-token tables are read as 16-byte vectors");
   static_assert((szGate * 4) % 16 == 0 && (fDS * 4) % 16 == 0 && (fEye * 4) % 16 == 0 &&
                     (fXU * 4) % 16 == 0,
@@ -1131,21 +1130,30 @@ __device__ __forceinline__ float diag_pick(const f32x4& v, int c) {
   return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
 }
 
-// x of lane `src` (0..63).  A cross-lane read, not an LDS round trip: lanes of
-// one wave that exchange values through LDS with no synchronisation may have
-// the reads ordered before the writes by the compiler.
+// x of lane `src` (0..63), through the cross-lane permute.
 __device__ __forceinline__ float lane_read(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, x)));
 }
 
+// Orders this wave's LDS writes before its later LDS reads in every lane.
+// Without it, lanes of one wave that exchange values through LDS may have a
+// read placed before another lane's write: the compiler sees each lane as a
+// thread of its own, and with a divergent write it splits the code into an
+// if / else whose else side (the reads) can run first.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Waves 2 and 3: row blocks b0 and b0 + 1 (b0 = 0 or 2).  They also write the
 // gate tables (Extra = GateStage): wave 2 beta, wave 3 the rest.  With kPro
-// (fused prologue: raw q and k) they also find 1/|k_r| and 1/|q_r| of their 32
-// rows -- |k_r|^2 is the diagonal of the K K^T tiles they form anyway, |q_r|^2
-// that of four extra Q Q^T products -- scale their tiles by them, and write
-// them and gamma / |k|, lambda / |k|, gamma / |q| to the chunk's gate table.
-// Normalising the rows themselves would cost every row wave about a thousand
-// cycles of vector work per step.
+// (fused prologue: raw q and k) they also find 1/|k_r| of their 32 rows from
+// the diagonal of the K K^T tiles they form anyway, scale their K K^T tiles
+// by it on both sides and their P tiles on the key side, and write it and
+// gamma / |k|, lambda / |k| to the chunk's gate table.  (The output wave
+// applies 1/|q|.)  Normalising the rows themselves would cost every row wave
+// about a thousand cycles of vector work per step.
 template <class Extra, bool kPro>
 __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int l) {
   using Cf = Cfg<64>;
@@ -1222,44 +1230,31 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
       P1 = mma32(kk[1][p], qq[1][p], P1);
     }
     if constexpr (kPro) {
-      // lane (g, c) holds [s = 16b + 4g + j][r = 16b' + c] of each tile
-      f32x4 Q0 = zero4(), Q1 = zero4();
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        Q0 = mma32(qq[0][p], qq[0][p], Q0);
-        Q1 = mma32(qq[1][p], qq[1][p], Q1);
+      // Lane (g, c) holds [s = 16b + 4g + j][r = 16b' + c] of each tile, and
+      // lane (c / 4, c) the diagonal entry of row c.  The diagonal lanes write
+      // 1/|k| to the table; every lane then reads row c's and rows 4g .. 4g + 3's.
+      float* const Gt = gate_table(smem, m);
+      if (g == (c >> 2)) {
+        Gt[Cfg3::oIk + 16 * b0 + c] = inv_norm(diag_pick(G0, c));
+        Gt[Cfg3::oIk + 16 * (b0 + 1) + c] = inv_norm(diag_pick(G1, c));
       }
-      // Every lane takes the inverse norm of the entry it would hold on the
-      // diagonal (finite where it is not there); row c's comes from lane
-      // (c / 4, c), row 4g + j's from lane (g, 4g + j) = 20g + j.
-      const float dk0 = inv_norm(diag_pick(G0, c)), dk1 = inv_norm(diag_pick(G1, c));
-      const float dq0 = inv_norm(diag_pick(Q0, c)), dq1 = inv_norm(diag_pick(Q1, c));
-      const int own = 16 * (c >> 2) + c;
-      const float ik0 = lane_read(dk0, own), ik1 = lane_read(dk1, own);
-      const float iq0 = lane_read(dq0, own), iq1 = lane_read(dq1, own);
-      f32x4 is0, is1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        is0[j] = lane_read(dk0, 20 * g + j);
-        is1[j] = lane_read(dk1, 20 * g + j);
-      }
+      wave_sync();
+      const float ik0 = Gt[Cfg3::oIk + 16 * b0 + c], ik1 = Gt[Cfg3::oIk + 16 * (b0 + 1) + c];
+      const f32x4 is0 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 16 * b0 + 4 * g);
+      const f32x4 is1 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 16 * (b0 + 1) + 4 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         G0[j] *= ik0 * is0[j];
-        P0[j] *= iq0 * is0[j];
+        P0[j] *= is0[j];
         Go[j] *= ik1 * is0[j];
-        Po[j] *= iq1 * is0[j];
+        Po[j] *= is0[j];
         G1[j] *= ik1 * is1[j];
-        P1[j] *= iq1 * is1[j];
+        P1[j] *= is1[j];
       }
       if (l < 32) {  // row 16 b0 + l: lane (g, c) with g = 0 / 1 holds block b0 / b0 + 1's row c
-        float* const Gt = gate_table(smem, m);
         const int r = 16 * b0 + l;
-        const float ik = l < 16 ? ik0 : ik1, iq = l < 16 ? iq0 : iq1, ga = Gt[r];
-        Gt[Cfg3::oIk + r] = ik;
-        Gt[Cfg3::oIq + r] = iq;
-        Gt[Cfg3::oGk + r] = ga * ik;
-        Gt[Cfg3::oGq + r] = ga * iq;
+        const float ik = l < 16 ? ik0 : ik1;
+        Gt[Cfg3::oGk + r] = Gt[r] * ik;
         Gt[Cfg3::oLk + r] = Gt[Cfg3::oLam + r] * ik;
       }
     }
@@ -1298,8 +1293,9 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
 // Waves 4 and 5: row block i = 2 / 3, tiles (i, 0) and (i, 1).  They run one
 // step behind the row waves and read K and Q of the chunk from the stage slot
 // the row waves published (row-major), and g from the gate table.
-// Wave 5 also writes the V tiles (Extra = VStage).  With kPro the tiles are
-// scaled by the inverse row norms the row waves wrote a step earlier.
+// Wave 5 also writes the V tiles (Extra = VStage).  With kPro the K K^T tiles
+// are scaled on both sides, the P tiles on the key side, by the 1/|k| the
+// row waves wrote a step earlier.
 template <class Extra, bool kPro>
 __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int l) {
   using Cf = Cfg<64>;
@@ -1335,15 +1331,15 @@ __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int 
       }
       if constexpr (kPro) {  // lane (g, c): [s = 16 jb + 4g + j][r = 16i + c]
         const float* const Gt = gate_table(smem, m);
-        const float ikr = Gt[Cfg3::oIk + 16 * i + c], iqr = Gt[Cfg3::oIq + 16 * i + c];
+        const float ikr = Gt[Cfg3::oIk + 16 * i + c];
         const f32x4 is0 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 4 * g);
         const f32x4 is1 = *reinterpret_cast<const f32x4*>(Gt + Cfg3::oIk + 16 + 4 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           G0[j] *= ikr * is0[j];
-          P0[j] *= iqr * is0[j];
+          P0[j] *= is0[j];
           G1[j] *= ikr * is1[j];
-          P1[j] *= iqr * is1[j];
+          P1[j] *= is1[j];
         }
       }
       offdiag_tiles<64>(G0, P0, gt, i, 0, g, c, R);
@@ -1353,10 +1349,12 @@ __device__ __forceinline__ void gram_lower(const Ctx& x, char* smem, int i, int 
   });
 }
 
-// Wave 6 (with kPro reading gamma / |q| in place of gamma, for raw queries):
-// the output of both consumers' columns, one step behind them:
+// Wave 6: the output of both consumers' columns, one step behind them:
 // chunk n's Q S term in step n from their start-of-chunk state, its P Ut term
-// in step n + 1 from their Ut.
+// in step n + 1 from their Ut.  With kPro (raw queries; P tiles scaled on the
+// key side only) it also finds 1/|q| of each token from the diagonal of
+// Q Q^T, two products per 16-token block on the Q operands it holds, and
+// scales the token's output row by it: o = (gamma Q S + P Ut) / |q|.
 template <bool kPro>
 __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   using Cf = Cfg<64>;
@@ -1373,6 +1371,7 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
   const int offRow = c * LDK + 8 * g, offT16 = c * Cf::LD16 + 4 * g;  // Q row c, keys 8g .. + 7
   f32x4 o[4][2];  // Q S term of the chunk in progress, per block row and tile
   u32x2 Pm[10];   // its P tiles
+  [[maybe_unused]] float iq[4];  // with kPro: 1/|q| of token 16i + c
   auto out_start = [&](int n, const __bf16* R, const float* G) {
     const unsigned* const hs = hand + Cfg3::fXS + (n & 1) * Cfg3::szHand2;
     u32x2 st[2][4];
@@ -1393,6 +1392,13 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < 2; ++t) o[i][t] = out_qs<2>(st[t], qr[i], gm[i]);
+    if constexpr (kPro) {  // |q|^2 of row c: lane (c / 4, c) of Q_i Q_i^T
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 d = mma32(qr[i][1], qr[i][1], mma32(qr[i][0], qr[i][0], zero4()));
+        iq[i] = lane_read(inv_norm(diag_pick(d, c)), 16 * (c >> 2) + c);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 10; ++e) Pm[e] = ld4(R + Cf::oP + e * Cf::szTile + offT16);
   };
@@ -1406,14 +1412,19 @@ __device__ __forceinline__ void out_wave(const Ctx& x, char* smem, int l) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        __builtin_amdgcn_raw_buffer_store_b64(cvt4(out_pu(o[i][t], i, t, X, Pm)), ro, vofO + 32 * t,
-                                              (n * 64 + 16 * i) * rowO, 0);
+      for (int t = 0; t < 2; ++t) {
+        f32x4 r = out_pu(o[i][t], i, t, X, Pm);
+        if constexpr (kPro) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r[j] *= iq[i];
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(cvt4(r), ro, vofO + 32 * t, (n * 64 + 16 * i) * rowO, 0);
+      }
   };
   run_steps(nch, [&](auto pc, int k) {
     constexpr int cur = (decltype(pc)::value + 1) % 3;  // stage slot of chunk k
     if (k >= 1 && k <= nch) out_finish(k - 1);
-    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, gate_table(smem, k) + (kPro ? Cfg3::oGq : 0));
+    if (k >= 0 && k < nch) out_start(k, sb + cur * Cf::szBuf, gate_table(smem, k));
   });
   if (needs_tail_step(nch)) {
     stage_barrier();
