@@ -1,0 +1,78 @@
+"""Reverse-mode gradients of the gated delta rule's token loop, in plain NumPy fp64.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE (see the package docstring): only tests,
+the smoke check and the benchmark's CPU baseline use it, and it shares nothing
+with the HIP path.
+
+For real data the forward is, per (batch, head) chain and token t,
+
+    u_t = S_{t-1}^T k_t,
+    S_t = alpha_t (S_{t-1} - beta_t k_t u_t^T) + beta_t k_t v_t^T,
+    o_t = S_t^T q_t,
+
+the recurrence of DeltaPhase section 2 with the data-dependent forget gate of
+the Sykra README ("Architectural Highlights"), gate applied to the whole
+Householder-updated state.  Given upstream gradients dO (of o) and dS_T (of
+the final state), the chain rule taken token by token in reverse gives, with
+G the gradient reaching S_t from later tokens (G = dS_T at t = T):
+
+    D     = G + q_t dO_t^T                      (o_t reads S_t)
+    dq_t  = S_t dO_t
+    w     = D^T k_t
+    dv_t  = beta_t w
+    dbeta_t  = w . (v_t - alpha_t u_t)
+    dalpha_t = <D, S_{t-1} - beta_t k_t u_t^T>
+    dk_t  = D (beta_t v_t - alpha_t beta_t u_t) - alpha_t beta_t S_{t-1} w
+    G     <- alpha_t (D - beta_t k_t w^T)       (the gradient reaching S_{t-1})
+
+and dS0 is the final G.  The pins in tests/test_oracle_backward.py check these
+against central finite differences of the C oracle's forward, not against
+this derivation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def recurrent_bwd(q, k, v, alpha, beta, S0, dO, dS_final):
+    """Gradients of  sum(o * dO) + sum(S_T * dS_final)  for the real token loop.
+
+    q, k [B, T, H, dk]; v, dO [B, T, H, dv]; alpha, beta [B, T, H]; S0 and
+    dS_final [B, H, dk, dv] or None (zero).  Returns (dq, dk, dv, dalpha,
+    dbeta, dS0) in fp64 with the shapes of the inputs.
+    """
+    q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
+    alpha, beta = np.asarray(alpha, np.float64), np.asarray(beta, np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+
+    # Forward, keeping every state: states[t] = S_t (states[0] = S0).
+    states = np.empty((T + 1, B, H, dk, dv))
+    states[0] = S
+    for t in range(T):
+        kt, vt = k[:, t], v[:, t]
+        a, b = alpha[:, t, :, None, None], beta[:, t, :, None, None]
+        u = np.einsum("bhij,bhi->bhj", S, kt)
+        S = a * (S - b * kt[..., :, None] * u[..., None, :]) + b * kt[..., :, None] * vt[..., None, :]
+        states[t + 1] = S
+
+    G = np.zeros((B, H, dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dalpha, dbeta = np.zeros_like(alpha), np.zeros_like(beta)
+    for t in range(T - 1, -1, -1):
+        Sp, St = states[t], states[t + 1]
+        qt, kt, vt, dot = q[:, t], k[:, t], v[:, t], dO[:, t]
+        a, b = alpha[:, t], beta[:, t]
+        D = G + qt[..., :, None] * dot[..., None, :]
+        dq[:, t] = np.einsum("bhij,bhj->bhi", St, dot)
+        u = np.einsum("bhij,bhi->bhj", Sp, kt)
+        w = np.einsum("bhij,bhi->bhj", D, kt)
+        dv_[:, t] = b[..., None] * w
+        dbeta[:, t] = np.sum(w * (vt - a[..., None] * u), axis=-1)
+        dalpha[:, t] = np.sum(D * (Sp - b[..., None, None] * kt[..., :, None] * u[..., None, :]), axis=(-2, -1))
+        y = b[..., None] * vt - (a * b)[..., None] * u
+        dk_[:, t] = (np.einsum("bhij,bhj->bhi", D, y)
+                     - (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, w))
+        G = a[..., None, None] * (D - b[..., None, None] * kt[..., :, None] * w[..., None, :])
+    return dq, dk_, dv_, dalpha, dbeta, G
