@@ -156,6 +156,15 @@ def gen_raw_layer(B, T, H, d, seed=0, alpha_mu=-4.0, s0_var=None):
                 b_logit=b.astype(np.float32), S0=S0)
 
 
+def gen_upstream_grads(B, T, H, dk, dv, seed=0, with_dS=True):
+    """Upstream gradients for the backward: dO ~ N(0, 1) [B, T, H, dv] stored in fp32 (cast to the
+    forward's dtype by the caller) and, if asked, dS_T ~ N(0, 1) [B, H, dk, dv] fp32."""
+    rng = np.random.default_rng(seed + 1000)
+    dO = rng.normal(0.0, 1.0, (B, T, H, dv)).astype(np.float32)
+    dS = rng.normal(0.0, 1.0, (B, H, dk, dv)).astype(np.float32) if with_dS else None
+    return dO, dS
+
+
 def gen_workload(w: Workload, **overrides):
     """Inputs for a named chunk workload (fields may be overridden, e.g. T=...)."""
     p = dict(B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dv, dtype=w.dtype, seed=w.seed,

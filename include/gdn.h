@@ -144,6 +144,49 @@ int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const fl
                            void *S_final, int B, int T, int H, int dk, int dv, int dtype, void *stream);
 
 /*
+ * Bytes of workspace gdn_chunk_bwd needs: B * H * ceil(T / 8) * 64 * 64 * 4
+ * (the forward state every 8 tokens).  0 for an unsupported combination or
+ * T == 0.
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
+ * Reverse-mode gradients of gdn_chunk_fwd for real data: given the gradients
+ * grad_out of out and grad_S_final of S_final, the gradients of
+ * sum(out * grad_out) + sum(S_final * grad_S_final) with respect to q, k, v,
+ * alpha, beta and S0.  The forward is the recurrence of DeltaPhase README
+ * section 2 with the data-dependent forget gate of the Sykra README
+ * ("Architectural Highlights"), applied to the whole Householder-updated
+ * state, as for gdn_chunk_fwd; the gradients follow it token by token in
+ * reverse.  The pages train through this layer; they print no gradient
+ * formula.
+ *
+ *   q, k, v, alpha, beta, S0   the forward's inputs, as for gdn_chunk_fwd
+ *                              (S0 may be NULL: zero)
+ *   grad_out      [B, T, H, dv]  dtype     gradient of out
+ *   grad_S_final  [B, H, dk, dv] float32   gradient of S_final (NULL: zero)
+ *   grad_q, grad_k [B, T, H, dk], grad_v [B, T, H, dv]   float32, written
+ *   grad_alpha, grad_beta [B, T, H]                      float32, written
+ *   grad_S0       [B, H, dk, dv] float32, written (NULL: not computed)
+ *   workspace     device memory of at least gdn_chunk_bwd_workspace_bytes(...)
+ *                 bytes, owned by the caller, overwritten (may be NULL when
+ *                 that is 0)
+ *
+ * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0;
+ * otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).  Arithmetic is fp32
+ * throughout; bf16 inputs are read exactly.  The forward is recomputed inside
+ * the call (checkpoints every 8 tokens in the workspace), so nothing from a
+ * forward call is needed.  Gradient outputs must not alias any input.
+ * B * H == 0 is a no-op; T == 0 copies grad_S_final (or zeros) to grad_S0.
+ * Errors as for gdn_chunk_fwd.
+ */
+int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                  const float *S0, const void *grad_out, const float *grad_S_final, float *grad_q,
+                  float *grad_k, float *grad_v, float *grad_alpha, float *grad_beta, float *grad_S0,
+                  int B, int T, int H, int dk, int dv, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * One single-token decode step on N independent states, in place.
  *
  *   q, k   [N, dk] dtype;  v [N, dv] dtype;  alpha, beta [N] float32

@@ -108,6 +108,37 @@ int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const fl
   return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
+  if (B < 0 || T < 0 || H < 0 || (dtype != GDN_F32 && dtype != GDN_BF16) || dk != 64 || dv != 64) return 0;
+  return gdn::chunk_bwd_workspace_bytes(B, T, H);
+}
+
+int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                  const float* S0, const void* grad_out, const float* grad_S_final, float* grad_q, float* grad_k,
+                  float* grad_v, float* grad_alpha, float* grad_beta, float* grad_S0, int B, int T, int H, int dk,
+                  int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
+  if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
+      (long long)B * H >= (1LL << 31))
+    return GDN_ERR_SHAPE;
+  if (dtype == GDN_C64 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  const bool tokens = (long long)B * T * H > 0;
+  if (tokens && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v || !grad_alpha ||
+                 !grad_beta))
+    return GDN_ERR_NULL;
+  const void* ptrs[] = {q,      k,      v,      alpha,      beta,      S0,      grad_out, grad_S_final,
+                        grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_S0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+  const size_t need = gdn::chunk_bwd_workspace_bytes(B, T, H);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+  if ((long long)B * H == 0) return GDN_OK;
+  gdn::BwdArgs a{q,      k,      v,      alpha,      beta,      S0,      grad_out, grad_S_final, grad_q, grad_k,
+                 grad_v, grad_alpha, grad_beta, grad_S0, workspace, B, T, H, dtype, stream};
+  return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                        void* S, void* out, int N, int dk, int dv, int dtype, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;

@@ -53,6 +53,28 @@ struct StepArgs {
   void* stream;
 };
 
+// Reverse-mode gradients of the chunk forward (real dtypes, d = 64); all
+// gradient outputs are fp32.  dS_final, S0 and dS0 may be NULL.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;
+  const void* dout;
+  const float* dS_final;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dalpha;
+  float* dbeta;
+  float* dS0;
+  void* workspace;
+  int B, T, H, dtype;
+  void* stream;
+};
+
 hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, real dtypes
 hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only
 hipError_t launch_recurrent_step(const StepArgs& a);
@@ -60,5 +82,8 @@ hipError_t launch_recurrent_step(const StepArgs& a);
 // exchange per-chunk intermediates through `workspace`.
 size_t chunk_cx_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
+// Backward: forward checkpoints every 8 tokens in `workspace`.
+size_t chunk_bwd_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
 
 }  // namespace gdn

@@ -1,9 +1,10 @@
 """ctypes binding of libgdn (include/gdn.h).
 
 The raw entry points keep the C names and take integer device addresses:
-``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_recurrent_step``,
-``gdn_chunk_fwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
-``chunk_fwd_prologue`` and ``recurrent_step`` are conveniences for
+``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_chunk_bwd``,
+``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
+``gdn_chunk_bwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
+``chunk_fwd_prologue``, ``chunk_bwd`` and ``recurrent_step`` are conveniences for
 torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
 ``data_ptr()`` and the current HIP stream, and raise on a non-OK status.  Every
 step of the computation runs in the HIP kernels; there is no fallback path.
@@ -20,8 +21,8 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3
 GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
 GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
 
-EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_recurrent_step",
-           "gdn_status_str")
+EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_bwd_workspace_bytes",
+           "gdn_chunk_bwd", "gdn_recurrent_step", "gdn_status_str")
 
 _lib = None
 
@@ -49,6 +50,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, ci, vp, vp, ci, ci, ci, ci, ci,
                                            ci, vp]
     lib.gdn_chunk_fwd_prologue.restype = ci
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [ci] * 6
+    lib.gdn_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn_chunk_bwd.argtypes = [vp] * 14 + [ci] * 6 + [vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = ci
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
     lib.gdn_recurrent_step.restype = ci
     lib.gdn_status_str.argtypes = [ci]
@@ -77,6 +82,17 @@ def gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale, S0, chunk, out
                            dtype, stream) -> int:
     return int(load().gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, float(beta_scale), S0, chunk, out, S_final,
                                              B, T, H, dk, dv, dtype, stream))
+
+
+def gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dtype) -> int:
+    return int(load().gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dtype))
+
+
+def gdn_chunk_bwd(q, k, v, alpha, beta, S0, grad_out, grad_S_final, grad_q, grad_k, grad_v, grad_alpha, grad_beta,
+                  grad_S0, B, T, H, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(load().gdn_chunk_bwd(q, k, v, alpha, beta, S0, grad_out, grad_S_final, grad_q, grad_k, grad_v,
+                                    grad_alpha, grad_beta, grad_S0, B, T, H, dk, dv, dtype, workspace,
+                                    workspace_bytes, stream))
 
 
 def gdn_recurrent_step(q, k, v, alpha, beta, S, out, N, dk, dv, dtype, stream) -> int:
@@ -184,6 +200,44 @@ def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=No
     if s != GDN_OK:
         raise GdnError(s)
     return out, S_final
+
+
+def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream=None):
+    """Gradients of sum(out * grad_out) + sum(S_final * grad_S_final) for chunk_fwd's forward (real data, d = 64).
+
+    q, k, v, grad_out [B,T,H,64] float32 or bfloat16 (one dtype); alpha, beta [B,T,H] float32; S0 and
+    grad_S_final [B,H,64,64] float32 or None.  Returns fp32 (grad_q, grad_k, grad_v, grad_alpha, grad_beta,
+    grad_S0).  The workspace is allocated here with torch.
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd: tensors must live on a HIP device")
+    for t, name, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)),
+                         (grad_out, "grad_out", (B, T, H, dv))):
+        _check(t, name, shp, q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if grad_S_final is not None:
+        _check(grad_S_final, "grad_S_final", (B, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gq, gk, gv = torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dv), **f32)
+    ga, gb = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
+    gS0 = torch.empty((B, H, dk, dv), **f32)
+    ws_bytes = gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, code)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    s = gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(grad_out),
+                      _ptr(grad_S_final), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(ga), _ptr(gb), _ptr(gS0), B, T, H, dk, dv,
+                      code, ws.data_ptr() if ws_bytes else None, ws_bytes, st)
+    if s != GDN_OK:
+        raise GdnError(s)
+    return gq, gk, gv, ga, gb, gS0
 
 
 def recurrent_step(q, k, v, alpha, beta, S, out=None, stream=None):

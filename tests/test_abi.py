@@ -106,6 +106,41 @@ def test_prologue_empty_is_noop():
     assert prologue(B=0, q=None, k=None, v=None, a_logit=None, b_logit=None, out=None, S_final=None) == raw.GDN_OK
 
 
+def backward(**kw):
+    args = dict(q=A, k=A, v=A, alpha=A, beta=A, S0=None, grad_out=A, grad_S_final=None, grad_q=A, grad_k=A, grad_v=A,
+                grad_alpha=A, grad_beta=A, grad_S0=A, B=2, T=128, H=3, dk=64, dv=64, dtype=gdn.GDN_F32, workspace=A,
+                workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return gdn.gdn_chunk_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), raw.GDN_ERR_DTYPE),
+    (dict(H=-1), raw.GDN_ERR_SHAPE),
+    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(grad_out=None), raw.GDN_ERR_NULL),
+    (dict(grad_beta=None), raw.GDN_ERR_NULL),
+    (dict(alpha=None), raw.GDN_ERR_NULL),
+    (dict(grad_k=A + 4), raw.GDN_ERR_ALIGN),
+    (dict(workspace=None), raw.GDN_ERR_WORKSPACE),
+    (dict(workspace_bytes=2 * 3 * 16 * 64 * 64 * 4 - 1), raw.GDN_ERR_WORKSPACE),
+])
+def test_backward_argument_errors(kw, status):
+    assert backward(**kw) == status
+
+
+def test_backward_empty_and_workspace_query():
+    assert backward(B=0, q=None, k=None, v=None, alpha=None, beta=None, grad_out=None, grad_q=None, grad_k=None,
+                    grad_v=None, grad_alpha=None, grad_beta=None, grad_S0=None, workspace=None,
+                    workspace_bytes=0) == raw.GDN_OK
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_BF16) == 2 * 3 * 16 * 64 * 64 * 4
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == 2 * 3 * 17 * 64 * 64 * 4
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
+
+
 def test_workspace_query():
     assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
 
