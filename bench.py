@@ -187,6 +187,8 @@ def main():
     dev = torch.device("cuda:0")
     if w.kind == "decode":
         return bench_decode(args, w, dev)
+    if w.kind == "backward":
+        return bench_backward(args, w, dev)
     inp = gen_workload(w)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
     wbytes = algorithmic_bytes(w, inp["S0"] is not None)
@@ -382,6 +384,109 @@ def bench_decode(args, w, dev):
                      "kernel_avg_ms": avg_ms, "kernel": "gdn::decode_kernel"},
     }
     print(json.dumps(result), flush=True)
+
+
+FP32_VALU_PEAK_TFS = 157.3  # MI355X fp32 vector, published (256 CUs at 2.4 GHz)
+
+
+def backward_flops(w) -> float:
+    """Vector flops of the backward per call: one forward recompute (u = S^T k and the rank-one update,
+    5 d^2 per token-head) and the reverse step (D, u, w, <D, S>, the two row sums and the carried
+    gradient, 17 d^2), i.e. 22 d^2 per token-head.  The checkpoint pass's second forward is not counted."""
+    return 22.0 * w.dk * w.dv * w.B * w.T * w.H
+
+
+def bench_backward(args, w, dev):
+    """One step = one gdn_chunk_bwd over the whole layer (all chains): forward checkpoints, recompute and the
+    reverse pass.  Two input sets are cycled."""
+    import torch
+
+    import linear_attention_sequence_gated_amd as gdn
+    from gdn_inputs import bf16_round, gen_upstream_grads, gen_workload
+    inp = gen_workload(w)
+    dO, dS = gen_upstream_grads(w.B, w.T, w.H, w.dk, w.dv, seed=w.seed, with_dS=True)
+    dO = bf16_round(dO)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
+    ncopies = args.copies or 2
+    f32 = dict(dtype=torch.float32, device=dev)
+    sets = []
+    for _ in range(ncopies):
+        d = {x: torch.from_numpy(inp[x]).to(dev).to(tdt) for x in ("q", "k", "v")}
+        d.update({x: torch.from_numpy(inp[x]).to(dev) for x in ("alpha", "beta")})
+        d["dO"], d["dS"] = torch.from_numpy(dO).to(dev).to(tdt), torch.from_numpy(dS).to(dev)
+        sets.append(d)
+    outs = [torch.empty((w.B, w.T, w.H, w.dk), **f32), torch.empty((w.B, w.T, w.H, w.dk), **f32),
+            torch.empty((w.B, w.T, w.H, w.dv), **f32), torch.empty((w.B, w.T, w.H), **f32),
+            torch.empty((w.B, w.T, w.H), **f32), torch.empty((w.B, w.H, w.dk, w.dv), **f32)]
+    ws_bytes = gdn.gdn_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, code)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    d0 = sets[0]
+    gdn.chunk_bwd(d0["q"], d0["k"], d0["v"], d0["alpha"], d0["beta"], d0["dO"], None, d0["dS"],
+                  stream=stream.cuda_stream)  # validates once through the torch helper
+    lib = gdn.load()
+    calls = [tuple(d[x].data_ptr() for x in ("q", "k", "v", "alpha", "beta")) + (None, d["dO"].data_ptr(),
+             d["dS"].data_ptr()) + tuple(o.data_ptr() for o in outs)
+             + (w.B, w.T, w.H, w.dk, w.dv, code, ws.data_ptr(), ws_bytes, stream.cuda_stream) for d in sets]
+
+    def step(i):
+        s = lib.gdn_chunk_bwd(*calls[i % ncopies])
+        if s != 0:  # GDN_OK
+            raise gdn.GdnError(s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = backward_flops(w)
+    tfs = flops / (avg_ms * 1e-3) / 1e12
+    tok = w.B * w.T * w.H
+    hbm_bytes = tok * (3 * w.dk * 2 + w.dv * 2 + 8) + tok * (2 * w.dk + w.dv) * 4 + tok * 8 + 2 * w.B * w.H * w.dk * w.dv * 4
+    result = {
+        "metric": f"tokens/sec gated-delta chunk bwd ({w.name})", "value": w.B * w.T * args.steps / wall,
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; inputs as sykra_layer_bf16, upstream gradients N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "input_copies_cycled": ncopies, "workspace_bytes": ws_bytes},
+        "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": hbm_bytes,
+                     "hbm_achieved_GBs": hbm_bytes / (avg_ms * 1e-3) / 1e9, "kernel_avg_ms": avg_ms,
+                     "kernel": "gdn::bwd::bwd_kernel"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_backward(inp, dO, dS, w)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_backward(inp, dO, dS, w, budget_s: float = 12.0):
+    """The oracle's reverse-mode gradients (NumPy fp64, as they stand) on a sample of chains."""
+    from oracle.backward import recurrent_bwd
+    chains = [(0, 0), (3, 7)]
+    sub = {x: np.stack([inp[x][b, :, h] for b, h in chains], axis=1)[None] for x in ("q", "k", "v", "alpha", "beta")}
+    dO_s = np.stack([dO[b, :, h] for b, h in chains], axis=1)[None]
+    dS_s = np.stack([dS[b, h] for b, h in chains])[None]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        recurrent_bwd(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], None, dO_s, dS_s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    tokens = reps * w.T * len(chains) / w.H  # a token is all H heads of one position
+    return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(chains)} of {w.B * w.H} chains x {w.T} tokens, NumPy fp64 token loop (one thread), "
+                      f"repeated {reps}x in {el:.1f} s; tokens counted as chains x T / H"}
 
 
 if __name__ == "__main__":

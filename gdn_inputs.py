@@ -56,7 +56,7 @@ def _softplus(x):
 
 @dataclass(frozen=True)
 class Workload:
-    """One synthetic workload shape.  ``kind`` is 'chunk', 'prologue' (raw layer inputs) or 'decode'."""
+    """One synthetic workload shape.  ``kind`` is 'chunk', 'prologue' (raw layer inputs), 'backward' or 'decode'."""
     name: str
     kind: str
     dtype: str  # 'f32', 'bf16' or 'c64'
@@ -96,6 +96,9 @@ WORKLOADS = {
     "sykra_layer_bf16_prologue": Workload(
         "sykra_layer_bf16_prologue", "prologue", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="the Sykra-shaped layer from raw inputs: q, k not normalised, gate logits a, b"),
+    "sykra_layer_bf16_bwd": Workload(
+        "sykra_layer_bf16_bwd", "backward", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
+        note="gradients of the Sykra-shaped layer (inputs as sykra_layer_bf16, upstream dO, dS_T ~ N(0,1))"),
     "decode_4096x64": Workload(
         "decode_4096x64", "decode", "bf16", N=4096, dk=64, dv=64, steps=64, seed=4,
         s0_var=0.1, note="4096 independent 64x64 states, 64 single-token steps"),

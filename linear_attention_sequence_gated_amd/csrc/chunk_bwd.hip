@@ -15,10 +15,16 @@
 //
 // One wave per chain; lane j owns column j of S and of G (64 registers
 // each).  Column sums (u, w) are in-lane; the two row sums per token (for dq
-// and dk) go through a padded LDS buffer.  S_{t-1} is needed in reverse
+// and dk) go through a padded LDS buffer, each lane writing its column as a
+// row of it.  The workgroup is one wave, so LDS exchanges between its lanes
+// are ordered with wavefront-scope fences: a workgroup barrier's fence would
+// also wait for every global load and store in flight.  S_{t-1} is needed in reverse
 // order, so a first pass runs the forward and checkpoints S every 8 tokens to
 // the workspace; the reverse pass recomputes each 8-token block from its
-// checkpoint into LDS (128 KB) and walks it backwards.
+// checkpoint into LDS (136 KB) and walks it backwards.  Each chain is one
+// wave alone on its CU, so nothing hides a load's latency: every token's
+// inputs are loaded while the token before it (in the direction of the walk)
+// is computed.
 #include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
@@ -30,10 +36,18 @@ namespace bwd {
 
 constexpr int D = 64;      // head dimension (d_k = d_v)
 constexpr int SUB = 8;     // tokens per checkpoint block
-constexpr int LDR = D + 1; // row stride of the row-sum buffer (conflict-free both ways)
+constexpr int LDC = D + 4; // row stride of the LDS column buffers (16-byte rows, conflict-free)
 
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const __hip_bfloat16* p) { return __bfloat162float(*p); }
+
+// Orders this wave's earlier LDS writes before its later LDS reads in every
+// lane (wavefront-scope release / acquire around a wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -49,8 +63,8 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
                                                  float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
                                                  float* __restrict__ dalpha, float* __restrict__ dbeta,
                                                  float* __restrict__ dS0, float* __restrict__ ckpt, int T, int H) {
-  __shared__ float st[SUB][D][D];  // S_{t-1} of each token of the block, [i][j]
-  __shared__ float red[D * LDR];   // row sums: lane j writes column j, lane i reads row i
+  __shared__ __attribute__((aligned(16))) float st[SUB][D][LDC];  // S_{t-1} of each token of the block, [j][i]
+  __shared__ __attribute__((aligned(16))) float red[D * LDC];      // row sums: lane j writes [j][*], lane i reads [*][i]
   __shared__ float kv[D], qv[D];   // k_t and q_t, read by every lane
   const int j = threadIdx.x, chain = blockIdx.x, b = chain / H, h = chain % H;
   const int nsub = (T + SUB - 1) / SUB;
@@ -61,27 +75,49 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
 #pragma unroll
   for (int i = 0; i < D; ++i) s[i] = S0 ? S0[((size_t)chain * D + i) * D + j] : 0.f;
 
-  // One forward token on s (column j of the state); k_t is left in kv.
-  auto forward = [&](int t) {
-    const size_t r = tok(t);
-    __syncthreads();  // earlier readers of kv are done
-    kv[j] = ld(k + r * D + j);
-    __syncthreads();
-    const float a = alpha[r], be = beta[r], vj = ld(v + r * D + j);
+  // Lane j's inputs of one token (t clamped into [0, T), so always a valid
+  // address when T > 0; never called when T = 0).
+  struct Tok {
+    float k, q, v, dO, a, be;
+  };
+  auto load = [&](int t, bool back) {
+    Tok x;
+    const size_t r = tok(max(0, min(t, T - 1)));
+    x.k = ld(k + r * D + j);
+    x.v = ld(v + r * D + j);
+    x.a = alpha[r];
+    x.be = beta[r];
+    x.q = back ? ld(q + r * D + j) : 0.f;
+    x.dO = back ? ld(dO + r * D + j) : 0.f;
+    return x;
+  };
+
+  // One forward token on s (column j of the state).
+  auto forward = [&](const Tok& x) {
+    wave_sync();  // earlier readers of kv are done
+    kv[j] = x.k;
+    wave_sync();
     float u = 0.f;
 #pragma unroll
     for (int i = 0; i < D; ++i) u += s[i] * kv[i];
-    const float y = be * vj - a * be * u;
+    const float y = x.be * x.v - x.a * x.be * u;
 #pragma unroll
-    for (int i = 0; i < D; ++i) s[i] = a * s[i] + kv[i] * y;
+    for (int i = 0; i < D; ++i) s[i] = x.a * s[i] + kv[i] * y;
   };
 
   // Pass 1: checkpoints S at the start of every block.
-  for (int c = 0; c < nsub; ++c) {
+  {
+    Tok cur{};
+    if (T > 0) cur = load(0, false);  // T = 0: the input buffers may be empty
+    for (int t = 0; t < T; ++t) {
+      if (t % SUB == 0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) ck[((size_t)c * D + i) * D + j] = s[i];
-    const int mend = min(SUB, T - c * SUB);
-    for (int m = 0; m < mend; ++m) forward(c * SUB + m);
+        for (int i = 0; i < D; ++i) ck[((size_t)(t / SUB) * D + i) * D + j] = s[i];
+      }
+      const Tok nxt = load(t + 1, false);
+      forward(cur);
+      cur = nxt;
+    }
   }
 
   // Pass 2: blocks in reverse; g is column j of G.
@@ -92,25 +128,32 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
     const int mend = min(SUB, T - c * SUB);
 #pragma unroll
     for (int i = 0; i < D; ++i) s[i] = ck[((size_t)c * D + i) * D + j];
+    Tok cur = load(c * SUB, false);
     for (int m = 0; m < mend; ++m) {
 #pragma unroll
-      for (int i = 0; i < D; ++i) st[m][i][j] = s[i];
-      if (m + 1 < mend) forward(c * SUB + m);  // the block's last state is not needed
+      for (int i = 0; i < D; ++i) st[m][j][i] = s[i];
+      if (m + 1 < mend) {  // the block's last state is not needed
+        const Tok nxt = load(c * SUB + m + 1, false);
+        forward(cur);
+        cur = nxt;
+      }
     }
+    cur = load(c * SUB + mend - 1, true);
     for (int m = mend - 1; m >= 0; --m) {
       const size_t r = tok(c * SUB + m);
-      __syncthreads();  // st written, earlier readers of kv / qv / red done
-      kv[j] = ld(k + r * D + j);
-      qv[j] = ld(q + r * D + j);
-      __syncthreads();
-      const float a = alpha[r], be = beta[r], vj = ld(v + r * D + j), doj = ld(dO + r * D + j);
+      const Tok nxt = load(c * SUB + m - 1, true);
+      wave_sync();  // st written, earlier readers of kv / qv / red done
+      kv[j] = cur.k;
+      qv[j] = cur.q;
+      wave_sync();
+      const float a = cur.a, be = cur.be, vj = cur.v, doj = cur.dO;
       float u = 0.f, w = 0.f, dsp = 0.f;
 #pragma unroll
       for (int i = 0; i < D; ++i) {
         g[i] += qv[i] * doj;  // D = G + q dO^T
-        u += st[m][i][j] * kv[i];
+        u += st[m][j][i] * kv[i];
         w += g[i] * kv[i];
-        dsp += g[i] * st[m][i][j];
+        dsp += g[i] * st[m][j][i];
       }
       const float y = be * vj - a * be * u;
       dv[r * D + j] = be * w;
@@ -124,23 +167,24 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
       // Row sums over the columns: sum_j S_{t-1}[i][j] dO_j, then
       // sum_j (D[i][j] y_j - alpha beta S_{t-1}[i][j] w_j).
 #pragma unroll
-      for (int i = 0; i < D; ++i) red[i * LDR + j] = st[m][i][j] * doj;
-      __syncthreads();
+      for (int i = 0; i < D; ++i) red[j * LDC + i] = st[m][j][i] * doj;
+      wave_sync();
       float r1 = 0.f;
 #pragma unroll
-      for (int x = 0; x < D; ++x) r1 += red[j * LDR + x];
-      __syncthreads();
+      for (int x = 0; x < D; ++x) r1 += red[x * LDC + j];
+      wave_sync();
       const float ab = a * be;
 #pragma unroll
-      for (int i = 0; i < D; ++i) red[i * LDR + j] = g[i] * y - ab * st[m][i][j] * w;
-      __syncthreads();
+      for (int i = 0; i < D; ++i) red[j * LDC + i] = g[i] * y - ab * st[m][j][i] * w;
+      wave_sync();
       float r2 = 0.f;
 #pragma unroll
-      for (int x = 0; x < D; ++x) r2 += red[j * LDR + x];
+      for (int x = 0; x < D; ++x) r2 += red[x * LDC + j];
       dq[r * D + j] = a * r1 + kv[j] * ydo;  // lane j now stands for row j
       dk[r * D + j] = r2;
 #pragma unroll
       for (int i = 0; i < D; ++i) g[i] = a * (g[i] - be * kv[i] * w);
+      cur = nxt;
     }
   }
   if (dS0) {
