@@ -13,18 +13,20 @@
 //   dalpha_t = <D, S_{t-1}> - beta_t (w . u_t),
 //   G <- alpha_t (D - beta_t k_t w^T);  dS0 is the last G.
 //
-// One wave per chain; lane j owns column j of S and of G (64 registers
-// each).  Column sums (u, w) are in-lane; the two row sums per token (for dq
-// and dk) go through a padded LDS buffer, each lane writing its column as a
-// row of it.  The workgroup is one wave, so LDS exchanges between its lanes
-// are ordered with wavefront-scope fences: a workgroup barrier's fence would
-// also wait for every global load and store in flight.  S_{t-1} is needed in reverse
-// order, so a first pass runs the forward and checkpoints S every 8 tokens to
-// the workspace; the reverse pass recomputes each 8-token block from its
-// checkpoint into LDS (136 KB) and walks it backwards.  Each chain is one
-// wave alone on its CU, so nothing hides a load's latency: every token's
-// inputs are loaded while the token before it (in the direction of the walk)
-// is computed.
+// Four waves per chain (256 threads).  Thread (w, l) owns column
+// c = 16 w + l / 4 and rows 16 (l % 4) .. + 15 of the state S and of the
+// carried gradient G, 16 registers each.  Column sums (u, w) are a 16-term
+// in-lane sum and two DPP adds within the lane quad that holds the column;
+// wave sums are DPP adds within rows of 16 lanes and four lane reads.  The two row sums per token (for dq
+// and dk) go through LDS: every thread writes its 16 products of each, then
+// thread (w, l) sums row l over the 16 columns of wave w, and wave 0 adds the
+// four partial sums.  S_{t-1} is needed in reverse order: a first pass runs
+// the forward and checkpoints S every 8 tokens to the workspace (column-major
+// per chain); the reverse pass recomputes each 8-token block from its
+// checkpoint into registers (8 x 16 per thread) and walks it backwards.
+// Barriers wait for LDS only (a workgroup barrier's fence would also wait for
+// every global load and store in flight), and each token's inputs are loaded
+// while the token before it in the walk is computed.
 #include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
@@ -34,75 +36,109 @@
 namespace gdn {
 namespace bwd {
 
-constexpr int D = 64;      // head dimension (d_k = d_v)
-constexpr int SUB = 8;     // tokens per checkpoint block
-constexpr int LDC = D + 4; // row stride of the LDS column buffers (16-byte rows, conflict-free)
+constexpr int D = 64;       // head dimension (d_k = d_v)
+constexpr int SUB = 8;      // tokens per checkpoint block
+constexpr int NWV = 4;      // waves per chain
+constexpr int R = 16;       // rows per thread
+constexpr int LDC = D + 4;  // row stride of the product buffers (16-byte rows)
 
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const __hip_bfloat16* p) { return __bfloat162float(*p); }
+__device__ __forceinline__ float f32(float x) { return x; }
+__device__ __forceinline__ float f32(__hip_bfloat16 x) { return __bfloat162float(x); }
 
-// Orders this wave's earlier LDS writes before its later LDS reads in every
-// lane (wavefront-scope release / acquire around a wave barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// All waves of the workgroup meet; LDS writes before it are visible after it.
+// Global loads and stores in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
+// x + (x of the lane selected by DPP control `ctrl`).
+template <int ctrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;  // quad_perm [1,0,3,2] and [2,3,0,1]
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;  // row_ror:4 and row_ror:8
+
+// Sum over the lane quad (the four row quarters of a column), in every lane of it.
+__device__ __forceinline__ float quad_sum(float x) { return dpp_add<kQuadXor2>(dpp_add<kQuadXor1>(x)); }
+
+// Sum over the wave (uniform result).
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x = dpp_add<kRowRor8>(dpp_add<kRowRor4>(quad_sum(x)));  // every lane: the sum of its row of 16
+  const int xi = __builtin_bit_cast(int, x);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48)));
 }
 
 template <class IT>
-__global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
-                                                 const IT* __restrict__ v, const float* __restrict__ alpha,
-                                                 const float* __restrict__ beta, const float* __restrict__ S0,
-                                                 const IT* __restrict__ dO, const float* __restrict__ dSf,
-                                                 float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-                                                 float* __restrict__ dalpha, float* __restrict__ dbeta,
-                                                 float* __restrict__ dS0, float* __restrict__ ckpt, int T, int H) {
-  __shared__ __attribute__((aligned(16))) float st[SUB][D][LDC];  // S_{t-1} of each token of the block, [j][i]
-  __shared__ __attribute__((aligned(16))) float red[D * LDC];      // row sums: lane j writes [j][*], lane i reads [*][i]
-  __shared__ float kv[D], qv[D];   // k_t and q_t, read by every lane
-  const int j = threadIdx.x, chain = blockIdx.x, b = chain / H, h = chain % H;
+__global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
+                                                  const IT* __restrict__ v, const float* __restrict__ alpha,
+                                                  const float* __restrict__ beta, const float* __restrict__ S0,
+                                                  const IT* __restrict__ dO, const float* __restrict__ dSf,
+                                                  float* __restrict__ dq, float* __restrict__ dk,
+                                                  float* __restrict__ dv, float* __restrict__ dalpha,
+                                                  float* __restrict__ dbeta, float* __restrict__ dS0,
+                                                  float* __restrict__ ckpt, int T, int H) {
+  __shared__ __attribute__((aligned(16))) float kv[2][D], qv[2][D];  // k_t, q_t (double-buffered by token)
+  __shared__ __attribute__((aligned(16))) float red[2][D * LDC];     // [column][row] products for the row sums
+  __shared__ float rowp[2][NWV][D];                                  // per-wave partial row sums
+  __shared__ float scal[3][NWV];                                     // per-wave partial dbeta, dalpha, y . dO
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = 16 * w + (l >> 2), rq = l & 3, i0 = R * rq;
+  const int chain = blockIdx.x, b = chain / H, h = chain % H;
   const int nsub = (T + SUB - 1) / SUB;
   float* const ck = ckpt + (size_t)chain * nsub * D * D;
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
 
-  float s[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) s[i] = S0 ? S0[((size_t)chain * D + i) * D + j] : 0.f;
-
-  // Lane j's inputs of one token (t clamped into [0, T), so always a valid
-  // address when T > 0; never called when T = 0).
+  // This thread's inputs of one token: k and q element l (wave 0 puts them
+  // in LDS for every thread), v and dO of column c, the gates.  t is clamped
+  // into [0, T), so the address is valid whenever T > 0.  Values are kept as
+  // stored and converted where used, and every wave issues the same loads:
+  // the compiler's in-order load counts are then static, and no wave waits
+  // for the next token's loads where it only needs this token's.
   struct Tok {
-    float k, q, v, dO, a, be;
+    IT k, q, v, dO;
+    float a, be;
   };
   auto load = [&](int t, bool back) {
-    Tok x;
+    Tok x{};
     const size_t r = tok(max(0, min(t, T - 1)));
-    x.k = ld(k + r * D + j);
-    x.v = ld(v + r * D + j);
+    x.k = k[r * D + l];
+    if (back) x.q = q[r * D + l];
+    x.v = v[r * D + c];
+    if (back) x.dO = dO[r * D + c];
     x.a = alpha[r];
     x.be = beta[r];
-    x.q = back ? ld(q + r * D + j) : 0.f;
-    x.dO = back ? ld(dO + r * D + j) : 0.f;
     return x;
   };
 
-  // One forward token on s (column j of the state).
+  float s[R];
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii) s[ii] = S0 ? S0[((size_t)chain * D + i0 + ii) * D + c] : 0.f;
+
+  int par = 0;  // LDS buffer parity, flipped per token
+  // One forward token on s.
   auto forward = [&](const Tok& x) {
-    wave_sync();  // earlier readers of kv are done
-    kv[j] = x.k;
-    wave_sync();
+    if (w == 0) kv[par][l] = f32(x.k);
+    lds_barrier();
+    float kk[R];
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) kk[ii] = kv[par][i0 + ii];
     float u = 0.f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) u += s[i] * kv[i];
-    const float y = x.be * x.v - x.a * x.be * u;
+    for (int ii = 0; ii < R; ++ii) u += s[ii] * kk[ii];
+    u = quad_sum(u);
+    const float y = x.be * f32(x.v) - x.a * x.be * u;
 #pragma unroll
-    for (int i = 0; i < D; ++i) s[i] = x.a * s[i] + kv[i] * y;
+    for (int ii = 0; ii < R; ++ii) s[ii] = x.a * s[ii] + kk[ii] * y;
+    par ^= 1;
   };
 
   // Pass 1: checkpoints S at the start of every block.
@@ -112,7 +148,7 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
     for (int t = 0; t < T; ++t) {
       if (t % SUB == 0) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) ck[((size_t)(t / SUB) * D + i) * D + j] = s[i];
+        for (int ii = 0; ii < R; ++ii) ck[((size_t)(t / SUB) * D + c) * D + i0 + ii] = s[ii];
       }
       const Tok nxt = load(t + 1, false);
       forward(cur);
@@ -120,76 +156,114 @@ __global__ __launch_bounds__(64) void bwd_kernel(const IT* __restrict__ q, const
     }
   }
 
-  // Pass 2: blocks in reverse; g is column j of G.
-  float g[D];
+  // Pass 2: blocks in reverse.
+  float g[R];
 #pragma unroll
-  for (int i = 0; i < D; ++i) g[i] = dSf ? dSf[((size_t)chain * D + i) * D + j] : 0.f;
-  for (int c = nsub - 1; c >= 0; --c) {
-    const int mend = min(SUB, T - c * SUB);
+  for (int ii = 0; ii < R; ++ii) g[ii] = dSf ? dSf[((size_t)chain * D + i0 + ii) * D + c] : 0.f;
+  float nck[R];  // the next block's checkpoint, loaded during this block's walk
+  if (nsub > 0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) s[i] = ck[((size_t)c * D + i) * D + j];
-    Tok cur = load(c * SUB, false);
-    for (int m = 0; m < mend; ++m) {
+    for (int ii = 0; ii < R; ++ii) nck[ii] = ck[((size_t)(nsub - 1) * D + c) * D + i0 + ii];
+  }
+  for (int cb = nsub - 1; cb >= 0; --cb) {
+    const int t0 = cb * SUB, mend = min(SUB, T - t0);
 #pragma unroll
-      for (int i = 0; i < D; ++i) st[m][j][i] = s[i];
-      if (m + 1 < mend) {  // the block's last state is not needed
-        const Tok nxt = load(c * SUB + m + 1, false);
-        forward(cur);
-        cur = nxt;
+    for (int ii = 0; ii < R; ++ii) s[ii] = nck[ii];
+    float sp[SUB][R];  // S_{t-1} of each token of the block
+    const Tok wfirst = load(t0 + mend - 1, true);  // the walk's first token, in flight during the recompute
+    Tok cur = load(t0, false);
+#pragma unroll
+    for (int m = 0; m < SUB; ++m) {
+      if (m < mend) {
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) sp[m][ii] = s[ii];
+        if (m + 1 < mend) {  // the block's last state is not needed
+          const Tok nxt = load(t0 + m + 1, false);
+          forward(cur);
+          cur = nxt;
+        }
       }
     }
-    cur = load(c * SUB + mend - 1, true);
-    for (int m = mend - 1; m >= 0; --m) {
-      const size_t r = tok(c * SUB + m);
-      const Tok nxt = load(c * SUB + m - 1, true);
-      wave_sync();  // st written, earlier readers of kv / qv / red done
-      kv[j] = cur.k;
-      qv[j] = cur.q;
-      wave_sync();
-      const float a = cur.a, be = cur.be, vj = cur.v, doj = cur.dO;
-      float u = 0.f, w = 0.f, dsp = 0.f;
+    cur = wfirst;
+    const int cbn = max(cb - 1, 0);
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
-        g[i] += qv[i] * doj;  // D = G + q dO^T
-        u += st[m][j][i] * kv[i];
-        w += g[i] * kv[i];
-        dsp += g[i] * st[m][j][i];
+    for (int ii = 0; ii < R; ++ii) nck[ii] = ck[((size_t)cbn * D + c) * D + i0 + ii];
+    if (w == 0) {  // the walk's first token; later ones are staged before the step's last barrier
+      kv[par][l] = f32(cur.k);
+      qv[par][l] = f32(cur.q);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int m = SUB - 1; m >= 0; --m) {
+      if (m < mend) {
+        const size_t r = tok(t0 + m);
+        const Tok nxt = load(t0 + m - 1, true);
+        const float a = cur.a, be = cur.be, vc = f32(cur.v), doc = f32(cur.dO), ab = a * be;
+        float kk[R];
+        float u = 0.f, wc = 0.f, dsp = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          kk[ii] = kv[par][i0 + ii];
+          g[ii] += qv[par][i0 + ii] * doc;  // D = G + q dO^T
+          u += sp[m][ii] * kk[ii];
+          wc += g[ii] * kk[ii];
+          dsp += g[ii] * sp[m][ii];
+        }
+        u = quad_sum(u);
+        wc = quad_sum(wc);
+        const float y = be * vc - ab * u;
+        if (rq == 0) dv[r * D + c] = be * wc;
+        const float lead = rq == 0 ? 1.f : 0.f;  // one copy of each per-column term
+        const float db = wave_sum(lead * wc * (vc - a * u));
+        const float da = wave_sum(dsp - lead * be * wc * u);
+        const float yd = wave_sum(lead * y * doc);
+        if (l == 0) {
+          scal[0][w] = db;
+          scal[1][w] = da;
+          scal[2][w] = yd;
+        }
+        // Row sums over the columns: sum_c S_{t-1}[i][c] dO_c and
+        // sum_c (D[i][c] y_c - alpha beta S_{t-1}[i][c] w_c).
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          red[0][c * LDC + i0 + ii] = sp[m][ii] * doc;
+          red[1][c * LDC + i0 + ii] = g[ii] * y - ab * sp[m][ii] * wc;
+        }
+        lds_barrier();
+        float p1 = 0.f, p2 = 0.f;  // row l over the columns of wave w
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          p1 += red[0][(16 * w + x) * LDC + l];
+          p2 += red[1][(16 * w + x) * LDC + l];
+        }
+        rowp[0][w][l] = p1;
+        rowp[1][w][l] = p2;
+        if (w == 0 && m > 0) {  // the next token's k and q (that buffer's readers are two steps back)
+          kv[par ^ 1][l] = f32(nxt.k);
+          qv[par ^ 1][l] = f32(nxt.q);
+        }
+        lds_barrier();
+        if (w == 0) {
+          const float r1 = rowp[0][0][l] + rowp[0][1][l] + rowp[0][2][l] + rowp[0][3][l];
+          const float r2 = rowp[1][0][l] + rowp[1][1][l] + rowp[1][2][l] + rowp[1][3][l];
+          const float ydo = scal[2][0] + scal[2][1] + scal[2][2] + scal[2][3];
+          dq[r * D + l] = a * r1 + f32(cur.k) * ydo;  // cur.k is k_l here
+          dk[r * D + l] = r2;
+          if (l == 0) {
+            dbeta[r] = scal[0][0] + scal[0][1] + scal[0][2] + scal[0][3];
+            dalpha[r] = scal[1][0] + scal[1][1] + scal[1][2] + scal[1][3];
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) g[ii] = a * (g[ii] - be * kk[ii] * wc);
+        par ^= 1;
+        cur = nxt;
       }
-      const float y = be * vj - a * be * u;
-      dv[r * D + j] = be * w;
-      const float db = wave_sum(w * (vj - a * u));
-      const float da = wave_sum(dsp - be * w * u);
-      const float ydo = wave_sum(y * doj);
-      if (j == 0) {
-        dbeta[r] = db;
-        dalpha[r] = da;
-      }
-      // Row sums over the columns: sum_j S_{t-1}[i][j] dO_j, then
-      // sum_j (D[i][j] y_j - alpha beta S_{t-1}[i][j] w_j).
-#pragma unroll
-      for (int i = 0; i < D; ++i) red[j * LDC + i] = st[m][j][i] * doj;
-      wave_sync();
-      float r1 = 0.f;
-#pragma unroll
-      for (int x = 0; x < D; ++x) r1 += red[x * LDC + j];
-      wave_sync();
-      const float ab = a * be;
-#pragma unroll
-      for (int i = 0; i < D; ++i) red[j * LDC + i] = g[i] * y - ab * st[m][j][i] * w;
-      wave_sync();
-      float r2 = 0.f;
-#pragma unroll
-      for (int x = 0; x < D; ++x) r2 += red[x * LDC + j];
-      dq[r * D + j] = a * r1 + kv[j] * ydo;  // lane j now stands for row j
-      dk[r * D + j] = r2;
-#pragma unroll
-      for (int i = 0; i < D; ++i) g[i] = a * (g[i] - be * kv[i] * w);
-      cur = nxt;
     }
   }
   if (dS0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) dS0[((size_t)chain * D + i) * D + j] = g[i];
+    for (int ii = 0; ii < R; ++ii) dS0[((size_t)chain * D + i0 + ii) * D + c] = g[ii];
   }
 }
 
@@ -200,7 +274,7 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H) {
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
-  const dim3 grid((unsigned)((long)a.B * a.H)), block(64);
+  const dim3 grid((unsigned)((long)a.B * a.H)), block(bwd::NWV * 64);
   if (a.dtype == kDtBF16)
     return launch_kernel(bwd::bwd_kernel<__hip_bfloat16>, grid, block, (hipStream_t)a.stream,
                          (const __hip_bfloat16*)a.q, (const __hip_bfloat16*)a.k, (const __hip_bfloat16*)a.v, a.alpha,
