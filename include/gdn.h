@@ -172,8 +172,8 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dt
  *                 bytes, owned by the caller, overwritten (may be NULL when
  *                 that is 0)
  *
- * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0;
- * otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).  Arithmetic is fp32
+ * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0 with
+ * T * H * 4 < 2^31; otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).  Arithmetic is fp32
  * throughout; bf16 inputs are read exactly.  The forward is recomputed inside
  * the call (checkpoints every 8 tokens in the workspace), so nothing from a
  * forward call is needed.  Gradient outputs must not alias any input.

@@ -45,6 +45,15 @@ constexpr int LDC = D + 4;  // row stride of the product buffers (16-byte rows)
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const __hip_bfloat16* p) { return __bfloat162float(*p); }
 __device__ __forceinline__ float f32(float x) { return x; }
+
+// Raw buffer resource over `bytes` bytes from `base`.  The gates are read
+// through it so that their (uniform) loads are vector-memory loads: a scalar
+// load would be counted with LDS traffic, and every barrier's LDS wait would
+// then also wait for the next token's gates.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const float* base, size_t end, size_t begin) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, end > begin ? (int)(end - begin) : 0,
+                                           0x00020000);
+}
 __device__ __forceinline__ float f32(__hip_bfloat16 x) { return __bfloat162float(x); }
 
 // All waves of the workgroup meet; LDS writes before it are visible after it.
@@ -96,6 +105,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, cons
   const int nsub = (T + SUB - 1) / SUB;
   float* const ck = ckpt + (size_t)chain * nsub * D * D;
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
+  const size_t gbase = (size_t)b * T * H + h;
+  const __amdgpu_buffer_rsrc_t ra = gate_rsrc(alpha + gbase, (size_t)T * H * 4, (size_t)h * 4);
+  const __amdgpu_buffer_rsrc_t rb = gate_rsrc(beta + gbase, (size_t)T * H * 4, (size_t)h * 4);
 
   // This thread's inputs of one token: k and q element l (wave 0 puts them
   // in LDS for every thread), v and dO of column c, the gates.  t is clamped
@@ -109,13 +121,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, cons
   };
   auto load = [&](int t, bool back) {
     Tok x{};
-    const size_t r = tok(max(0, min(t, T - 1)));
+    const int tc = max(0, min(t, T - 1));
+    const size_t r = tok(tc);
     x.k = k[r * D + l];
     if (back) x.q = q[r * D + l];
     x.v = v[r * D + c];
     if (back) x.dO = dO[r * D + c];
-    x.a = alpha[r];
-    x.be = beta[r];
+    x.a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, tc * H * 4, 0, 0));
+    x.be = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, tc * H * 4, 0, 0));
     return x;
   };
 

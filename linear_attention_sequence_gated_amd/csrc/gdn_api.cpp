@@ -122,7 +122,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
       (long long)B * H >= (1LL << 31))
     return GDN_ERR_SHAPE;
-  if (dtype == GDN_C64 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  if (dtype == GDN_C64 || dk != 64 || dv != 64 || (long long)T * H * 4 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v || !grad_alpha ||
                  !grad_beta))

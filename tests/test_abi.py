@@ -120,6 +120,7 @@ def backward(**kw):
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(B=1, T=1 << 22, H=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(grad_out=None), raw.GDN_ERR_NULL),
     (dict(grad_beta=None), raw.GDN_ERR_NULL),
     (dict(alpha=None), raw.GDN_ERR_NULL),
