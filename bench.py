@@ -189,6 +189,8 @@ def main():
         return bench_decode(args, w, dev)
     if w.kind == "backward":
         return bench_backward(args, w, dev)
+    if w.kind == "channel":
+        return bench_channel(args, w, dev)
     inp = gen_workload(w)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
     wbytes = algorithmic_bytes(w, inp["S0"] is not None)
@@ -487,6 +489,82 @@ def cpu_baseline_backward(inp, dO, dS, w, budget_s: float = 12.0):
     return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(chains)} of {w.B * w.H} chains x {w.T} tokens, NumPy fp64 token loop (one thread), "
                       f"repeated {reps}x in {el:.1f} s; tokens counted as chains x T / H"}
+
+
+def bench_channel(args, w, dev):
+    """One step = one gdn_fwd_channel_decay over the whole layer.  Input copies are cycled over >= 1 GiB."""
+    import torch
+
+    import linear_attention_sequence_gated_amd as gdn
+    from gdn_inputs import gen_workload
+    inp = gen_workload(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
+    eb = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.T * w.H
+    wbytes = tok * ((2 * w.dk + 2 * w.dv) * eb + w.dv * 4 + 4) + w.B * w.H * w.dk * w.dv * 4
+    ncopies = args.copies or max(2, int(np.ceil((1 << 30) / wbytes)))
+    sets = []
+    for _ in range(ncopies):
+        d = {x: torch.from_numpy(inp[x]).to(dev).to(tdt) for x in ("q", "k", "v")}
+        d.update({x: torch.from_numpy(inp[x]).to(dev) for x in ("r", "beta")})
+        d["out"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=dev)
+        d["S"] = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+        sets.append(d)
+    stream = torch.cuda.current_stream(dev)
+    d0 = sets[0]
+    gdn.fwd_channel_decay(d0["q"], d0["k"], d0["v"], d0["r"], d0["beta"], None, out=d0["out"], S_final=d0["S"],
+                          stream=stream.cuda_stream)  # validates once through the torch helper
+    lib = gdn.load()
+    calls = [tuple(d[x].data_ptr() for x in ("q", "k", "v", "r", "beta")) + (None, d["out"].data_ptr(),
+             d["S"].data_ptr(), w.B, w.T, w.H, w.dk, w.dv, code, stream.cuda_stream) for d in sets]
+
+    def step(i):
+        s = lib.gdn_fwd_channel_decay(*calls[i % ncopies])
+        if s != 0:  # GDN_OK
+            raise gdn.GdnError(s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
+    achieved = wbytes / (avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"tokens/sec gated-delta forward, per-channel decay ({w.name})",
+        "value": w.B * w.T * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; unit-norm q/k, N(0,1) v, sigmoid beta, r = exp(-softplus) per token and channel)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "input_copies_cycled": ncopies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": wbytes,
+                     "kernel_avg_ms": avg_ms, "kernel": "gdn::chd::channel_decay_kernel"},
+    }
+    if not args.no_cpu:
+        from oracle.channel_decay import channel_decay_fwd
+        chains = [(0, 0), (3, 7)]
+        sub = {x: np.stack([inp[x][b, :, h] for b, h in chains], axis=1)[None] for x in ("q", "k", "v", "r", "beta")}
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            channel_decay_fwd(sub["q"], sub["k"], sub["v"], sub["r"], sub["beta"], None)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 12.0 or reps >= 100:
+                break
+        result["cpu_baseline"] = {
+            "value": reps * w.T * len(chains) / w.H / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(chains)} of {w.B * w.H} chains x {w.T} tokens, NumPy fp64 token loop (one thread), "
+                      f"repeated {reps}x in {el:.1f} s; tokens counted as chains x T / H"}
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

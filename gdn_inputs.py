@@ -56,7 +56,7 @@ def _softplus(x):
 
 @dataclass(frozen=True)
 class Workload:
-    """One synthetic workload shape.  ``kind`` is 'chunk', 'prologue' (raw layer inputs), 'backward' or 'decode'."""
+    """One synthetic workload shape.  ``kind`` is 'chunk', 'prologue' (raw layer inputs), 'backward', 'channel' or 'decode'."""
     name: str
     kind: str
     dtype: str  # 'f32', 'bf16' or 'c64'
@@ -99,6 +99,9 @@ WORKLOADS = {
     "sykra_layer_bf16_bwd": Workload(
         "sykra_layer_bf16_bwd", "backward", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="gradients of the Sykra-shaped layer (inputs as sykra_layer_bf16, upstream dO, dS_T ~ N(0,1))"),
+    "sykra_layer_bf16_channel_decay": Workload(
+        "sykra_layer_bf16_channel_decay", "channel", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
+        note="the Sykra-shaped layer with a decay per token and value channel (DeltaPhase section 5)"),
     "decode_4096x64": Workload(
         "decode_4096x64", "decode", "bf16", N=4096, dk=64, dv=64, steps=64, seed=4,
         s0_var=0.1, note="4096 independent 64x64 states, 64 single-token steps"),
@@ -168,11 +171,25 @@ def gen_upstream_grads(B, T, H, dk, dv, seed=0, with_dS=True):
     return dO, dS
 
 
+def gen_channel_decay(B, T, H, d, dtype="bf16", seed=0, alpha_mu=-4.0, s0_var=None):
+    """Inputs for the per-output-channel decay: q, k unit-norm rows and v ~ N(0, 1) as in gen_chunk,
+    beta = sigmoid(N(0, 1)) [B, T, H], and r = exp(-softplus(N(alpha_mu, 1))) drawn per token and value
+    channel [B, T, H, d] (fp32).  Returns dict q, k, v, r, beta, S0."""
+    base = gen_chunk(B, T, H, d, d, dtype=dtype, seed=seed, alpha_mu=alpha_mu, s0_var=s0_var)
+    rng = np.random.default_rng(seed + 2000)
+    logit = rng.normal(alpha_mu, 1.0, (B, T, H, d))
+    r = np.exp(-(np.maximum(logit, 0.0) + np.log1p(np.exp(-np.abs(logit)))))
+    return dict(q=base["q"], k=base["k"], v=base["v"], r=r.astype(np.float32), beta=base["beta"], S0=base["S0"])
+
+
 def gen_workload(w: Workload, **overrides):
     """Inputs for a named chunk workload (fields may be overridden, e.g. T=...)."""
     p = dict(B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dv, dtype=w.dtype, seed=w.seed,
              alpha_mu=w.alpha_mu, beta_scale=w.beta_scale, s0_var=w.s0_var)
     p.update(overrides)
+    if w.kind == "channel":
+        return gen_channel_decay(p["B"], p["T"], p["H"], p["dk"], dtype=p["dtype"], seed=p["seed"],
+                                 alpha_mu=p["alpha_mu"], s0_var=p["s0_var"])
     if w.kind == "prologue":
         return gen_raw_layer(p["B"], p["T"], p["H"], p["dk"], seed=p["seed"], alpha_mu=p["alpha_mu"],
                              s0_var=p["s0_var"])

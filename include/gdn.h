@@ -187,6 +187,34 @@ int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *alph
                   size_t workspace_bytes, void *stream);
 
 /*
+ * The forward with a per-output-channel decay in place of the scalar gate:
+ *
+ *   S_t = (I - beta_t k_t k_t^T) S_{t-1} diag(r_t) + beta_t k_t v_t^T,
+ *   o_t = S_t^T q_t,
+ *
+ * where r_t holds one decay factor per value channel (DeltaPhase README,
+ * section 5, LaplacePhaseCore: the decay diag(r_t) acts on the value channels
+ * of the memory), applied to the Householder-updated state as the scalar gate
+ * is in gdn_chunk_fwd.  With every r_t[j] = alpha_t it equals gdn_chunk_fwd.
+ *
+ *   q, k     [B, T, H, dk]  dtype    keys unit-norm for a stable update
+ *   v        [B, T, H, dv]  dtype
+ *   r        [B, T, H, dv]  float32  decay per token and value channel, in (0, 1]
+ *   beta     [B, T, H]      float32
+ *   S0       [B, H, dk, dv] float32  may be NULL (zero)
+ *   out      [B, T, H, dv]  dtype, written
+ *   S_final  [B, H, dk, dv] float32, written; may be NULL, may equal S0
+ *
+ * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0;
+ * otherwise GDN_ERR_UNSUPPORTED.  fp32 arithmetic.  No workspace.  B * H == 0
+ * is a no-op; T == 0 copies S0 (or zeros) to S_final.  Errors as for
+ * gdn_chunk_fwd.
+ */
+int gdn_fwd_channel_decay(const void *q, const void *k, const void *v, const float *r, const float *beta,
+                          const float *S0, void *out, float *S_final, int B, int T, int H, int dk, int dv,
+                          int dtype, void *stream);
+
+/*
  * One single-token decode step on N independent states, in place.
  *
  *   q, k   [N, dk] dtype;  v [N, dv] dtype;  alpha, beta [N] float32

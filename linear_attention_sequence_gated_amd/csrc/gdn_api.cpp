@@ -139,6 +139,25 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const float* r, const float* beta,
+                          const float* S0, void* out, float* S_final, int B, int T, int H, int dk, int dv, int dtype,
+                          void* stream) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
+  if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
+      (long long)B * H * 4 >= (1LL << 31))
+    return GDN_ERR_SHAPE;
+  if (dtype == GDN_C64 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  const bool tokens = (long long)B * T * H > 0;
+  if (tokens && (!q || !k || !v || !r || !beta || !out)) return GDN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, r, beta, S0, out, S_final};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+  if ((long long)B * H == 0) return GDN_OK;
+  gdn::ChannelArgs a{q, k, v, r, beta, S0, out, S_final, B, T, H, dtype, stream};
+  return gdn::launch_channel_decay(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                        void* S, void* out, int N, int dk, int dv, int dtype, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;

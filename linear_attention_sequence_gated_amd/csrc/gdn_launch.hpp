@@ -75,6 +75,20 @@ struct BwdArgs {
   void* stream;
 };
 
+// Forward with a per-output-channel decay r [B, T, H, dv] (real dtypes, d = 64).
+struct ChannelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* r;
+  const float* beta;
+  const float* S0;
+  void* out;
+  float* S_final;
+  int B, T, H, dtype;
+  void* stream;
+};
+
 hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, real dtypes
 hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only
 hipError_t launch_recurrent_step(const StepArgs& a);
@@ -85,5 +99,6 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+hipError_t launch_channel_decay(const ChannelArgs& a);
 
 }  // namespace gdn

@@ -2,9 +2,9 @@
 
 The raw entry points keep the C names and take integer device addresses:
 ``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_chunk_bwd``,
-``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
+``gdn_fwd_channel_decay``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
 ``gdn_chunk_bwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
-``chunk_fwd_prologue``, ``chunk_bwd`` and ``recurrent_step`` are conveniences for
+``chunk_fwd_prologue``, ``chunk_bwd``, ``fwd_channel_decay`` and ``recurrent_step`` are conveniences for
 torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
 ``data_ptr()`` and the current HIP stream, and raise on a non-OK status.  Every
 step of the computation runs in the HIP kernels; there is no fallback path.
@@ -22,7 +22,7 @@ GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
 GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
 
 EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_bwd_workspace_bytes",
-           "gdn_chunk_bwd", "gdn_recurrent_step", "gdn_status_str")
+           "gdn_chunk_bwd", "gdn_fwd_channel_decay", "gdn_recurrent_step", "gdn_status_str")
 
 _lib = None
 
@@ -54,6 +54,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     lib.gdn_chunk_bwd.argtypes = [vp] * 14 + [ci] * 6 + [vp, sz, vp]
     lib.gdn_chunk_bwd.restype = ci
+    lib.gdn_fwd_channel_decay.argtypes = [vp] * 8 + [ci] * 6 + [vp]
+    lib.gdn_fwd_channel_decay.restype = ci
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
     lib.gdn_recurrent_step.restype = ci
     lib.gdn_status_str.argtypes = [ci]
@@ -93,6 +95,10 @@ def gdn_chunk_bwd(q, k, v, alpha, beta, S0, grad_out, grad_S_final, grad_q, grad
     return int(load().gdn_chunk_bwd(q, k, v, alpha, beta, S0, grad_out, grad_S_final, grad_q, grad_k, grad_v,
                                     grad_alpha, grad_beta, grad_S0, B, T, H, dk, dv, dtype, workspace,
                                     workspace_bytes, stream))
+
+
+def gdn_fwd_channel_decay(q, k, v, r, beta, S0, out, S_final, B, T, H, dk, dv, dtype, stream) -> int:
+    return int(load().gdn_fwd_channel_decay(q, k, v, r, beta, S0, out, S_final, B, T, H, dk, dv, dtype, stream))
 
 
 def gdn_recurrent_step(q, k, v, alpha, beta, S, out, N, dk, dv, dtype, stream) -> int:
@@ -238,6 +244,37 @@ def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream
     if s != GDN_OK:
         raise GdnError(s)
     return gq, gk, gv, ga, gb, gS0
+
+
+def fwd_channel_decay(q, k, v, r, beta, S0=None, out=None, S_final=None, stream=None):
+    """Forward with a per-output-channel decay r [B,T,H,64] fp32 (one factor per token and value channel).
+    q, k, v [B,T,H,64] float32 or bfloat16; beta [B,T,H] fp32; S0 [B,H,64,64] fp32 or None.
+    Returns (out [B,T,H,64] in q's dtype, S_final [B,H,64,64] fp32)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd_channel_decay: tensors must live on a HIP device")
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(r, "r", (B, T, H, dv), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, T, H, dv), q.dtype, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    s = gdn_fwd_channel_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
+                              B, T, H, dk, dv, code, st)
+    if s != GDN_OK:
+        raise GdnError(s)
+    return out, S_final
 
 
 def recurrent_step(q, k, v, alpha, beta, S, out=None, stream=None):

@@ -142,6 +142,30 @@ def test_backward_empty_and_workspace_query():
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
 
 
+def channel(**kw):
+    args = dict(q=A, k=A, v=A, r=A, beta=A, S0=None, out=A, S_final=A, B=2, T=100, H=3, dk=64, dv=64,
+                dtype=gdn.GDN_BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_fwd_channel_decay(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), raw.GDN_ERR_DTYPE),
+    (dict(B=-2), raw.GDN_ERR_SHAPE),
+    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(r=None), raw.GDN_ERR_NULL),
+    (dict(out=None), raw.GDN_ERR_NULL),
+    (dict(r=A + 4), raw.GDN_ERR_ALIGN),
+])
+def test_channel_decay_argument_errors(kw, status):
+    assert channel(**kw) == status
+
+
+def test_channel_decay_empty_is_noop():
+    assert channel(H=0, q=None, k=None, v=None, r=None, beta=None, out=None, S_final=None) == raw.GDN_OK
+
+
 def test_workspace_query():
     assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
 
