@@ -12,9 +12,9 @@
 // one column: lane l of wave w owns column 16 w + l / 4 and rows
 // 16 (l % 4) .. + 15.  k^T s_j and q^T s_j are 16-term in-lane sums and two
 // DPP adds.  Keys and queries are read from global memory by every lane
-// (16 consecutive elements each), the next token's inputs while this token is
-// computed; there is no LDS and no barrier.  Waves are independent: one
-// workgroup of one wave per (chain, 16-column slice).
+// (16 consecutive elements each), four tokens ahead of their use; there is no
+// LDS and no barrier.  Waves are independent: one workgroup of one wave per
+// (chain, 16-column slice).
 #include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
@@ -93,24 +93,37 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
     return x;
   };
 
+  // One token on s; o is stored by the quad's first lane.
+  auto step = [&](const Tok& x, int t) {
+    float u = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) u += x.k[ii] * s[ii];
+    u = quad_sum(u);
+    const float y = x.be * (f32(x.v) - x.r * u);
+    float o = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) {
+      s[ii] = x.r * s[ii] + x.k[ii] * y;
+      o += x.q[ii] * s[ii];
+    }
+    o = quad_sum(o);
+    if (rq == 0) st(out + tok(t) * D + c, o);
+  };
+
+  // Inputs are loaded PF tokens ahead (a token takes well under a memory
+  // latency), in a ring of registers indexed at compile time; the loads are
+  // unconditional (clamped), so the compiler's in-order load counts are static.
+  constexpr int PF = 4;
   if (T > 0) {  // T = 0: the input buffers may be empty
-    Tok cur = load(0);
-    for (int t = 0; t < T; ++t) {
-      const Tok nxt = load(t + 1);
-      float u = 0.f;
+    Tok ring[PF];
 #pragma unroll
-      for (int ii = 0; ii < R; ++ii) u += cur.k[ii] * s[ii];
-      u = quad_sum(u);
-      const float y = cur.be * (f32(cur.v) - cur.r * u);
-      float o = 0.f;
+    for (int p = 0; p < PF; ++p) ring[p] = load(p);
+    for (int t = 0; t < T; t += PF) {
 #pragma unroll
-      for (int ii = 0; ii < R; ++ii) {
-        s[ii] = cur.r * s[ii] + cur.k[ii] * y;
-        o += cur.q[ii] * s[ii];
+      for (int p = 0; p < PF; ++p) {
+        if (t + p < T) step(ring[p], t + p);
+        ring[p] = load(t + p + PF);
       }
-      o = quad_sum(o);
-      if (rq == 0) st(out + tok(t) * D + c, o);
-      cur = nxt;
     }
   }
   if (Sf) {
