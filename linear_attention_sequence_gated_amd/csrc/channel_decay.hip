@@ -26,34 +26,10 @@ namespace gdn {
 namespace chd {
 
 using lane::quad_sum;
+using lane::Row;
 
 constexpr int D = 64;  // head dimension
 constexpr int R = 16;  // rows per lane
-
-typedef __attribute__((ext_vector_type(4))) unsigned int u32v4;
-typedef __attribute__((ext_vector_type(4))) float f32v4;
-
-// 16 consecutive elements from p (16-byte aligned), as stored.
-template <class IT> struct Row;
-template <> struct Row<float> {
-  f32v4 w[4];
-  __device__ __forceinline__ void load(const float* p) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const f32v4*>(p)[i];
-  }
-  __device__ __forceinline__ float operator[](int i) const { return w[i / 4][i % 4]; }
-};
-template <> struct Row<__hip_bfloat16> {
-  u32v4 w[2];
-  __device__ __forceinline__ void load(const __hip_bfloat16* p) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) w[i] = reinterpret_cast<const u32v4*>(p)[i];
-  }
-  __device__ __forceinline__ float operator[](int i) const {
-    const unsigned x = w[i / 8][(i % 8) / 2];
-    return __builtin_bit_cast(float, (i % 2) ? (x & 0xffff0000u) : (x << 16));
-  }
-};
 
 __device__ __forceinline__ float f32(float x) { return x; }
 __device__ __forceinline__ float f32(__hip_bfloat16 x) { return __bfloat162float(x); }

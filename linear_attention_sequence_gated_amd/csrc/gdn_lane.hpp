@@ -1,7 +1,8 @@
-// gdn_lane.hpp -- cross-lane sums within a wave (DPP), for the kernels that
-// keep one state column on a lane quad.
+// gdn_lane.hpp -- cross-lane sums within a wave (DPP) and 16-element row loads,
+// for the kernels that keep one state column on a lane quad.
 #pragma once
 
+#include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
 namespace gdn {
@@ -27,6 +28,31 @@ __device__ __forceinline__ float wave_sum(float x) {
          (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32)) +
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48)));
 }
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32v4;
+typedef __attribute__((ext_vector_type(4))) float f32v4;
+
+// 16 consecutive elements from p (16-byte aligned), as stored.
+template <class IT> struct Row;
+template <> struct Row<float> {
+  f32v4 w[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const f32v4*>(p)[i];
+  }
+  __device__ __forceinline__ float operator[](int i) const { return w[i / 4][i % 4]; }
+};
+template <> struct Row<__hip_bfloat16> {
+  u32v4 w[2];
+  __device__ __forceinline__ void load(const __hip_bfloat16* p) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] = reinterpret_cast<const u32v4*>(p)[i];
+  }
+  __device__ __forceinline__ float operator[](int i) const {
+    const unsigned x = w[i / 8][(i % 8) / 2];
+    return __builtin_bit_cast(float, (i % 2) ? (x & 0xffff0000u) : (x << 16));
+  }
+};
 
 }  // namespace lane
 }  // namespace gdn
