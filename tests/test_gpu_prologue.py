@@ -102,3 +102,19 @@ def test_prologue_full_size_sampled_chains():
     S_s = np.stack([S[b, h] for b, h in chains])[None]
     assert_close("prologue_full", "bf16", o_s, S_s, o_ref, S_ref)
     assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+def test_prologue_saturated_logits():
+    """Logits far in the tails: alpha ~ e^-40 (state wiped) or ~ 1, beta ~ 0 or ~ beta_scale; random tokens of
+    the sequence take each extreme, the rest stay as drawn."""
+    torch_dev()
+    inp = gen_raw_layer(2, 260, 2, 64, seed=41, s0_var=0.1)
+    rng = np.random.default_rng(4)
+    pick = rng.random(inp["a_logit"].shape)
+    inp["a_logit"] = np.where(pick < 0.1, 40.0, np.where(pick < 0.3, -40.0, inp["a_logit"])).astype(np.float32)
+    pick = rng.random(inp["b_logit"].shape)
+    inp["b_logit"] = np.where(pick < 0.15, 40.0, np.where(pick < 0.3, -40.0, inp["b_logit"])).astype(np.float32)
+    note("prologue saturated logits")
+    o, S = run_prologue(inp, 2.0)
+    o_ref, S_ref = oracle_prologue(inp, 2.0)
+    assert_close("prologue_saturated", "bf16", o, S, o_ref, S_ref)
