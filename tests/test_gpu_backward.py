@@ -102,3 +102,15 @@ def test_backward_full_size_sampled_chains():
     pick = [np.stack([g[b, :, h] for b, h in chains], axis=1)[None] for g in got[:5]]
     pick.append(np.stack([got[5][b, h] for b, h in chains])[None])
     assert_grads("bwd_full", pick, ref)
+
+
+def test_backward_extreme_gates():
+    """Gates at their extremes on random tokens: alpha = 1e-6 (state wiped) or 1, beta = 0 or 2 (a full
+    Householder reflection); the rest as drawn."""
+    inp, dO, dSf = _case(2, 150, 2, "f32", 77, True, True)
+    rng = np.random.default_rng(8)
+    pa, pb = rng.random(inp["alpha"].shape), rng.random(inp["beta"].shape)
+    inp["alpha"] = np.where(pa < 0.1, 1e-6, np.where(pa < 0.3, 1.0, inp["alpha"])).astype(np.float32)
+    inp["beta"] = np.where(pb < 0.15, 0.0, np.where(pb < 0.3, 2.0, inp["beta"])).astype(np.float32)
+    note("backward extreme gates")
+    assert_grads("bwd_extreme", run_bwd(inp, "f32", dO, dSf), oracle_bwd(inp, dO, dSf))
