@@ -23,6 +23,10 @@
  *     Triangular Solve", and section 5 (log-space factorisation of the decay);
  *   - the O(d^2) single-token step of gdn_recurrent_step: Sykra README,
  *     "Computational Complexity" table (inference step time O(d^2), fixed state).
+ * Around that forward: gdn_chunk_fwd_prologue folds the layer's input
+ * transforms (L2 norms, gate logits) into it; gdn_chunk_bwd returns its
+ * gradients; gdn_fwd_channel_decay replaces the scalar gate with a decay per
+ * value channel (DeltaPhase README, section 5).
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (memory the caller allocated on the
@@ -40,6 +44,7 @@
  *       GDN_F32  float32, GDN_BF16 bfloat16, GDN_C64 complex64 (interleaved
  *       re, im float32).  alpha and beta are always float32.  States (S0,
  *       S_final, S) are float32, or complex64 when dtype == GDN_C64.
+ *       Gradients from gdn_chunk_bwd are float32.
  *   - Every pointer must be 16-byte aligned.
  *   - Preconditions not checked on the device (violations give undefined,
  *     typically non-finite, results): 0 < alpha <= 1, 0 <= beta <= 2, finite
