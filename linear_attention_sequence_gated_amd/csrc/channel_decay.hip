@@ -12,7 +12,7 @@
 // one column: lane l of wave w owns column 16 w + l / 4 and rows
 // 16 (l % 4) .. + 15.  k^T s_j and q^T s_j are 16-term in-lane sums and two
 // DPP adds.  Keys and queries are read from global memory by every lane
-// (16 consecutive elements each), four tokens ahead of their use; there is no
+// (16 consecutive elements each), eight tokens ahead of their use; there is no
 // LDS and no barrier.  Waves are independent: one workgroup of one wave per
 // (chain, 16-column slice).
 #include <hip/hip_bf16.h>
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
   // Inputs are loaded PF tokens ahead (a token takes well under a memory
   // latency), in a ring of registers indexed at compile time; the loads are
   // unconditional (clamped), so the compiler's in-order load counts are static.
-  constexpr int PF = 4;
+  constexpr int PF = 8;
   if (T > 0) {  // T = 0: the input buffers may be empty
     Tok ring[PF];
 #pragma unroll
