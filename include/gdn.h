@@ -46,6 +46,10 @@
  *       S_final, S) are float32, or complex64 when dtype == GDN_C64.
  *       Gradients from gdn_chunk_bwd are float32.
  *   - Every pointer must be 16-byte aligned.
+ *   - Size limits (GDN_ERR_SHAPE otherwise): no tensor above 2^40 elements;
+ *     B * H below 2^20 for the chunk forwards, below 2^24 for the backward
+ *     and the channel-decay forward; N below 2^24 for the decode step.  These
+ *     keep every launch under 2^32 work-items.
  *   - Preconditions not checked on the device (violations give undefined,
  *     typically non-finite, results): 0 < alpha <= 1, 0 <= beta <= 2, finite
  *     inputs.  Inputs and outputs must not overlap, except that S_final may
@@ -192,17 +196,21 @@ int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *alph
                   size_t workspace_bytes, void *stream);
 
 /*
- * The forward with a per-output-channel decay in place of the scalar gate:
+ * The forward with a per-output-channel decay in place of the scalar gate,
+ * LaplacePhaseCore's gated-decay rule (DeltaPhase README, section 2: the
+ * memory is read through the key BEFORE it decays, and the error is written
+ * along the key; section 5: the decay diag(r_t) sits on the memory's output
+ * rows, one factor per value channel).  With S [dk, dv] (row = key dim),
+ * for every value channel j:
  *
- *   S_t = (I - beta_t k_t k_t^T) S_{t-1} diag(r_t) + beta_t k_t v_t^T,
- *   o_t = S_t^T q_t,
+ *   e_t[j] = v_t[j] - k_t^T s_j,   s_j <- r_t[j] s_j + beta_t k_t e_t[j],
+ *   o_t[j] = q_t^T s_j            (the updated state)
  *
- * where r_t holds one decay factor per value channel (DeltaPhase README,
- * section 5, LaplacePhaseCore: the decay diag(r_t) acts on the value channels
- * of the memory), applied to the Householder-updated state as the scalar gate
- * is in gdn_chunk_fwd.  With every r_t[j] = alpha_t it equals gdn_chunk_fwd.
+ * i.e. S_t = S_{t-1} diag(r_t) + beta_t k_t (v_t - S_{t-1}^T k_t)^T.  With
+ * every r_t[j] = 1 it is gdn_chunk_fwd at alpha = 1.  (With r < 1 it differs
+ * from gdn_chunk_fwd's ordering, where the gate also scales the erased part.)
  *
- *   q, k     [B, T, H, dk]  dtype    keys unit-norm for a stable update
+ *   q, k     [B, T, H, dk]  dtype    keys of norm <= 1 for a stable update
  *   v        [B, T, H, dv]  dtype
  *   r        [B, T, H, dv]  float32  decay per token and value channel, in (0, 1]
  *   beta     [B, T, H]      float32

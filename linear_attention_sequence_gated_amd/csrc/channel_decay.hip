@@ -1,17 +1,16 @@
 // channel_decay.hip -- the delta rule with a per-output-channel decay, real
 // data, d_k = d_v = 64 (fp32 or bf16 q, k, v; fp32 decay, beta and state).
 //
-// DeltaPhase README, section 5 (LaplacePhaseCore): the decay diag(r_t) acts on
-// the value channels of the memory.  With the state S [dk, dv] it scales the
-// columns, applied to the Householder-updated state:
-//   S_t = (I - beta_t k_t k_t^T) S_{t-1} diag(r_t) + beta_t k_t v_t^T,
-//   o_t = S_t^T q_t.
-// Column j of S evolves on its own:
-//   s_j <- r_j s_j + k (beta (v_j - r_j k^T s_j)),   o_j = q^T s_j,
-// so the kernel needs no communication between columns.  A lane quad holds
-// one column: lane l of wave w owns column 16 w + l / 4 and rows
-// 16 (l % 4) .. + 15.  k^T s_j and q^T s_j are 16-term in-lane sums and two
-// DPP adds.  Keys and queries are read from global memory by every lane
+// DeltaPhase README, section 2 (the gated-decay variant that LaplacePhaseCore
+// implements) and section 5 (the decay diag(r_t) on the memory's output rows):
+// the memory is read through the key before it decays, and the error is
+// written along the key.  With the state S [dk, dv] the output rows of the
+// memory are the columns of S, and column j evolves on its own:
+//   e_j = v_j - k^T s_j,   s_j <- r_j s_j + beta k e_j,   o_j = q^T s_j.
+// This token loop is the reference-shaped kernel for short or odd shapes.  A
+// lane quad holds one column: lane l of wave w owns column 16 w + l / 4 and
+// rows 16 (l % 4) .. + 15.  k^T s_j and q^T s_j are 16-term in-lane sums and
+// two DPP adds.  Keys and queries are read from global memory by every lane
 // (16 consecutive elements each), eight tokens ahead of their use; there is no
 // LDS and no barrier.  Waves are independent: one workgroup of one wave per
 // (chain, 16-column slice).
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
 #pragma unroll
     for (int ii = 0; ii < R; ++ii) u += x.k[ii] * s[ii];
     u = quad_sum(u);
-    const float y = x.be * (f32(x.v) - x.r * u);
+    const float y = x.be * (f32(x.v) - u);  // error from the undecayed state
     float o = 0.f;
 #pragma unroll
     for (int ii = 0; ii < R; ++ii) {

@@ -80,7 +80,10 @@ __global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, cons
   __shared__ __attribute__((aligned(16))) float kv[2][D], qv[2][D];  // k_t, q_t (double-buffered by token)
   __shared__ __attribute__((aligned(16))) float red[2][D * LDC];     // [column][row] products for the row sums
   __shared__ float rowp[2][NWV][D];                                  // per-wave partial row sums
-  __shared__ float scal[3][NWV];                                     // per-wave partial dbeta, dalpha, y . dO
+  // Per-wave partial dbeta, dalpha and y . dO, double-buffered by token: the
+  // other waves write the next token's partials before the first barrier of
+  // the next step, while wave 0 may still be reading this token's.
+  __shared__ float scal[2][3][NWV];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = 16 * w + (l >> 2), rq = l & 3, i0 = R * rq;
@@ -214,9 +217,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, cons
         const float da = wave_sum(dsp - lead * be * wc * u);
         const float yd = wave_sum(lead * y * doc);
         if (l == 0) {
-          scal[0][w] = db;
-          scal[1][w] = da;
-          scal[2][w] = yd;
+          scal[par][0][w] = db;
+          scal[par][1][w] = da;
+          scal[par][2][w] = yd;
         }
         // Row sums over the columns: sum_c S_{t-1}[i][c] dO_c and
         // sum_c (D[i][c] y_c - alpha beta S_{t-1}[i][c] w_c).
@@ -242,12 +245,12 @@ __global__ __launch_bounds__(256) void bwd_kernel(const IT* __restrict__ q, cons
         if (w == 0) {
           const float r1 = rowp[0][0][l] + rowp[0][1][l] + rowp[0][2][l] + rowp[0][3][l];
           const float r2 = rowp[1][0][l] + rowp[1][1][l] + rowp[1][2][l] + rowp[1][3][l];
-          const float ydo = scal[2][0] + scal[2][1] + scal[2][2] + scal[2][3];
+          const float ydo = scal[par][2][0] + scal[par][2][1] + scal[par][2][2] + scal[par][2][3];
           dq[r * D + l] = a * r1 + f32(cur.k) * ydo;  // cur.k is k_l here
           dk[r * D + l] = r2;
           if (l == 0) {
-            dbeta[r] = scal[0][0] + scal[0][1] + scal[0][2] + scal[0][3];
-            dalpha[r] = scal[1][0] + scal[1][1] + scal[1][2] + scal[1][3];
+            dbeta[r] = scal[par][0][0] + scal[par][0][1] + scal[par][0][2] + scal[par][0][3];
+            dalpha[r] = scal[par][1][0] + scal[par][1][1] + scal[par][1][2] + scal[par][1][3];
           }
         }
 #pragma unroll

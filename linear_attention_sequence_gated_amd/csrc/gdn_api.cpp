@@ -35,6 +35,16 @@ bool step_supported(int dtype, int dk, int dv) {
 // Largest element count any single tensor may have (keeps every index in range).
 constexpr long long kMaxElems = 1LL << 40;
 
+// Launch limits.  A launch may hold fewer than 2^32 work-items along x.  The
+// chunk kernels run at most 4096 threads per (batch, head) chain (eight
+// 512-thread workgroups), the backward and the channel-decay kernels 256, and
+// the decode kernel at most 256 per state.  Sizes past these bounds are argument errors,
+// reported before anything is launched.
+constexpr long long kMaxWorkItems = 1LL << 32;
+bool chains_fit(long long chains, long long threads_per_chain) {
+  return chains * threads_per_chain < kMaxWorkItems;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,6 +79,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems)
     return GDN_ERR_SHAPE;
   if (chunk != 64 || !chunk_supported(dtype, dk, dv)) return GDN_ERR_UNSUPPORTED;
+  if (!chains_fit((long long)B * H, 4096)) return GDN_ERR_SHAPE;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL;
   const void* ptrs[] = {q, k, v, alpha, beta, S0, out, S_final, workspace};
@@ -95,6 +106,7 @@ int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const fl
     return GDN_ERR_SHAPE;
   if (chunk != 64 || dtype != GDN_BF16 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
   if (!(beta_scale >= 0.f && beta_scale <= 2.f)) return GDN_ERR_SHAPE;
+  if (!chains_fit((long long)B * H, 4096)) return GDN_ERR_SHAPE;
   if ((long long)T * H * dk * 2 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !a_logit || !b_logit || !out)) return GDN_ERR_NULL;
@@ -120,7 +132,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
-      (long long)B * H >= (1LL << 31))
+      !chains_fit((long long)B * H, 256))
     return GDN_ERR_SHAPE;
   if (dtype == GDN_C64 || dk != 64 || dv != 64 || (long long)T * H * 4 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
@@ -145,7 +157,7 @@ int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const flo
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
-      (long long)B * H * 4 >= (1LL << 31))
+      !chains_fit((long long)B * H, 256))
     return GDN_ERR_SHAPE;
   if (dtype == GDN_C64 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
@@ -162,7 +174,7 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
                        void* S, void* out, int N, int dk, int dv, int dtype, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (N < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
-  if ((long long)N * dk * dv > kMaxElems) return GDN_ERR_SHAPE;
+  if ((long long)N * dk * dv > kMaxElems || !chains_fit(N, 256)) return GDN_ERR_SHAPE;
   if (!step_supported(dtype, dk, dv)) return GDN_ERR_UNSUPPORTED;
   if (N == 0) return GDN_OK;
   if (!q || !k || !v || !alpha || !beta || !S || !out) return GDN_ERR_NULL;

@@ -147,9 +147,9 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, chunk: int = 64, out=None, S_final=
     dv = v.shape[-1]
     code = _dtype_code(q)
     dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     if dev.type != "cuda":
         raise ValueError("chunk_fwd: tensors must live on a HIP device")
-    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     _check(k, "k", (B, T, H, dk), q.dtype, dev)
     _check(v, "v", (B, T, H, dv), q.dtype, dev)
     _check(alpha, "alpha", (B, T, H), torch.float32, dev)
@@ -184,9 +184,9 @@ def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=No
     dv = v.shape[-1]
     code = _dtype_code(q)
     dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     if dev.type != "cuda":
         raise ValueError("chunk_fwd_prologue: tensors must live on a HIP device")
-    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     _check(k, "k", (B, T, H, dk), q.dtype, dev)
     _check(v, "v", (B, T, H, dv), q.dtype, dev)
     _check(a_logit, "a_logit", (B, T, H), torch.float32, dev)
@@ -220,9 +220,10 @@ def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream
     dv = v.shape[-1]
     code = _dtype_code(q)
     dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     if dev.type != "cuda":
         raise ValueError("chunk_bwd: tensors must live on a HIP device")
-    for t, name, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)),
+    for t, name, shp in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)),
                          (grad_out, "grad_out", (B, T, H, dv))):
         _check(t, name, shp, q.dtype, dev)
     _check(alpha, "alpha", (B, T, H), torch.float32, dev)
@@ -255,6 +256,7 @@ def fwd_channel_decay(q, k, v, r, beta, S0=None, out=None, S_final=None, stream=
     dv = v.shape[-1]
     code = _dtype_code(q)
     dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
     if dev.type != "cuda":
         raise ValueError("fwd_channel_decay: tensors must live on a HIP device")
     _check(k, "k", (B, T, H, dk), q.dtype, dev)
@@ -284,6 +286,7 @@ def recurrent_step(q, k, v, alpha, beta, S, out=None, stream=None):
     dv = v.shape[-1]
     code = _dtype_code(q)
     dev = q.device
+    _check(q, "q", (N, dk), q.dtype, dev)
     if dev.type != "cuda":
         raise ValueError("recurrent_step: tensors must live on a HIP device")
     _check(k, "k", (N, dk), q.dtype, dev)

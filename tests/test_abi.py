@@ -53,6 +53,7 @@ def step(**kw):
     (dict(T=-5), raw.GDN_ERR_SHAPE),
     (dict(dk=0), raw.GDN_ERR_SHAPE),
     (dict(B=1 << 20, T=1 << 20, H=1 << 10), raw.GDN_ERR_SHAPE),
+    (dict(B=1 << 10, T=1, H=1 << 10), raw.GDN_ERR_SHAPE),  # 2^20 chains x 4096 threads: past the launch limit
     (dict(chunk=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=96, dv=96), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=128), raw.GDN_ERR_UNSUPPORTED),
@@ -117,6 +118,7 @@ def backward(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=5), raw.GDN_ERR_DTYPE),
     (dict(H=-1), raw.GDN_ERR_SHAPE),
+    (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
@@ -152,6 +154,7 @@ def channel(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), raw.GDN_ERR_DTYPE),
     (dict(B=-2), raw.GDN_ERR_SHAPE),
+    (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(r=None), raw.GDN_ERR_NULL),
@@ -173,6 +176,7 @@ def test_workspace_query():
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=3), raw.GDN_ERR_DTYPE),
     (dict(N=-1), raw.GDN_ERR_SHAPE),
+    (dict(N=1 << 24), raw.GDN_ERR_SHAPE),  # 2^24 states x 256 threads
     (dict(dk=48, dv=48), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),
     (dict(S=None), raw.GDN_ERR_NULL),
@@ -196,3 +200,20 @@ def test_torch_helper_rejects_bad_shapes_on_cpu():
         gdn.chunk_fwd(q.to(torch.float16), q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
     with pytest.raises(ValueError):
         gdn.recurrent_step(q[0, 0], q[0, 0], q[0, 0], torch.zeros(1), torch.zeros(1), torch.zeros(1, 64, 64))
+
+
+def test_torch_helpers_reject_non_contiguous_q():
+    """A transposed (non-contiguous) q is refused by every helper, not read as if it were dense."""
+    torch = pytest.importorskip("torch")
+    qt = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16).transpose(1, 2)  # [1, 4, 2, 64], strided
+    x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 4, 2)
+    for call in (lambda: gdn.chunk_fwd(qt, x, x, g, g),
+                 lambda: gdn.chunk_fwd_prologue(qt, x, x, g, g),
+                 lambda: gdn.chunk_bwd(qt, x, x, g, g, x),
+                 lambda: gdn.fwd_channel_decay(qt, x, x, torch.zeros(1, 4, 2, 64), g)):
+        with pytest.raises(ValueError, match="q: must be contiguous"):
+            call()
+    q2 = torch.zeros(64, 3, dtype=torch.bfloat16).t()  # [3, 64], strided
+    with pytest.raises(ValueError, match="q: must be contiguous"):
+        gdn.recurrent_step(q2, q2.contiguous(), q2.contiguous(), torch.zeros(3), torch.zeros(3), torch.zeros(3, 64, 64))

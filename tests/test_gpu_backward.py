@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from gdn_inputs import WORKLOADS, bf16_round, gen_chunk, gen_upstream_grads, gen_workload
-from gpu_util import note, take_chains, torch_dev, up
+from gpu_util import note, torch_dev, up
 
 pytestmark = pytest.mark.gpu
 
@@ -30,24 +30,29 @@ def oracle_bwd(inp, dO, dS):
     return recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp.get("S0"), dO, dS)
 
 
-def per_chain_rel(x, ref, name):
-    """Max over (b, h) chains of ||x - ref|| / ||ref||, over that chain's entries."""
+def per_chain_errors(x, ref, name):
+    """Max over (b, h) chains of ||x - ref|| / ||ref|| and of max|x - ref| / max|ref|, over that chain's entries."""
     x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
     if name == "dS0":
         xs, rs = x.reshape(-1, x.shape[-2] * x.shape[-1]), ref.reshape(-1, ref.shape[-2] * ref.shape[-1])
     else:  # [B, T, H, ...] -> chains
         xs = np.moveaxis(x, 2, 1).reshape(x.shape[0] * x.shape[2], -1)
         rs = np.moveaxis(ref, 2, 1).reshape(ref.shape[0] * ref.shape[2], -1)
+    if not len(xs) or not xs.shape[1]:
+        return 0.0, 0.0
     den = np.maximum(np.linalg.norm(rs, axis=1), 1e-30)
-    return float(np.max(np.linalg.norm(xs - rs, axis=1) / den)) if len(xs) else 0.0
+    norm = float(np.max(np.linalg.norm(xs - rs, axis=1) / den))
+    elem = float(np.max(np.abs(xs - rs).max(axis=1) / np.maximum(np.abs(rs).max(axis=1), 1e-30)))
+    return norm, elem
 
 
 def assert_grads(tag, got, ref):
-    errs = {n: per_chain_rel(g, r, n) for n, g, r in zip(NAMES, got, ref)}
-    print(f"[parity] {tag}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    errs = {n: per_chain_errors(g, r, n) for n, g, r in zip(NAMES, got, ref)}
+    print(f"[parity] {tag}: " + " ".join(f"{n}={e[0]:.2e}/{e[1]:.2e}" for n, e in errs.items())
+          + f" (norm / elem, tol {TOL:g})", flush=True)
     for n, g in zip(NAMES, got):
         assert np.isfinite(g).all(), (tag, n)
-    assert all(e <= TOL for e in errs.values()), (tag, errs)
+    assert all(e[0] <= TOL and e[1] <= TOL for e in errs.values()), (tag, errs)
 
 
 def _case(B, T, H, dtype, seed, s0, dS):
@@ -84,8 +89,10 @@ def test_backward_deterministic():
     assert all(np.array_equal(a, b) for a, b in zip(g1, g2))
 
 
-def test_backward_full_size_sampled_chains():
-    """The 8 x 2048 x 12 d64 bf16 layer, all chains on the GPU; sampled chains recomputed by the oracle."""
+@pytest.mark.timeout(600)
+def test_backward_full_size_all_chains():
+    """The 8 x 2048 x 12 d64 bf16 layer on the GPU; every chain recomputed by the oracle (two batch rows at a
+    time, to bound the oracle's memory for the states it keeps)."""
     w = WORKLOADS["sykra_layer_bf16"]
     inp = gen_workload(w)
     dO, dSf = gen_upstream_grads(w.B, w.T, w.H, w.dk, w.dv, seed=w.seed, with_dS=True)
@@ -94,14 +101,11 @@ def test_backward_full_size_sampled_chains():
     t0 = time.perf_counter()
     got = run_bwd(inp, "bf16", dO, dSf)
     print(f"[backward] full size call + copies {time.perf_counter() - t0:.3f} s", flush=True)
-    chains = [(0, 0), (5, 9)]
-    sub = take_chains(inp, chains)
-    dO_s = np.stack([dO[b, :, h] for b, h in chains], axis=1)[None]
-    dS_s = np.stack([dSf[b, h] for b, h in chains])[None]
-    ref = oracle_bwd(sub, dO_s, dS_s)
-    pick = [np.stack([g[b, :, h] for b, h in chains], axis=1)[None] for g in got[:5]]
-    pick.append(np.stack([got[5][b, h] for b, h in chains])[None])
-    assert_grads("bwd_full", pick, ref)
+    for b0 in range(0, w.B, 2):
+        sl = slice(b0, b0 + 2)
+        sub = {x: (None if inp[x] is None else inp[x][sl]) for x in inp}
+        ref = oracle_bwd(sub, dO[sl], dSf[sl])
+        assert_grads(f"bwd_full_rows{b0}-{b0 + 1}", [g[sl] for g in got], ref)
 
 
 def test_backward_extreme_gates():

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from gdn_inputs import WORKLOADS, gen_chunk, gen_decode, gen_decode_workload
-from gpu_util import TOL, chain_rel_errors, down, note, run_chunk, torch_dev, up
+from gpu_util import ELEM_TOL, TOL, chain_rel_errors, down, note, run_chunk, torch_dev, up
 
 pytestmark = pytest.mark.gpu
 
@@ -26,17 +26,24 @@ def run_steps(inp, dtype, steps=None):
 
 
 def check_steps(name, inp, dtype, outs, states):
+    """Every state after every step: relative norm error of o and S per state, and the elementwise
+    max|x - ref| / max|ref| per state (bounds as for the chunk forward)."""
     St = inp["S"].astype(np.complex128 if dtype == "c64" else np.float64)
-    worst_o = worst_s = 0.0
+    worst = dict(o=0.0, S=0.0, elem_o=0.0, elem_S=0.0)
     for t in range(len(outs)):
         o_ref, St = oracle.recurrent_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["alpha"][t], inp["beta"][t], St)
-        # per state, per step (states are independent)
-        eo = np.linalg.norm(outs[t] - o_ref, axis=1) / np.maximum(np.linalg.norm(o_ref, axis=1), 1e-30)
-        es = (np.linalg.norm((states[t] - St).reshape(len(St), -1), axis=1)
-              / np.linalg.norm(St.reshape(len(St), -1), axis=1))
-        worst_o, worst_s = max(worst_o, eo.max()), max(worst_s, es.max())
-    print(f"[parity] {name}: max state-step rel err o={worst_o:.3e} S={worst_s:.3e} (tol {TOL[dtype]:g})", flush=True)
-    assert worst_o <= TOL[dtype] and worst_s <= TOL[dtype], (worst_o, worst_s)
+        assert np.isfinite(outs[t]).all() and np.isfinite(states[t]).all(), (name, t)
+        N = len(St)
+        do, dS = outs[t] - o_ref, (states[t] - St).reshape(N, -1)
+        Sr = St.reshape(N, -1)
+        worst["o"] = max(worst["o"], (np.linalg.norm(do, axis=1) / np.maximum(np.linalg.norm(o_ref, axis=1), 1e-30)).max())
+        worst["S"] = max(worst["S"], (np.linalg.norm(dS, axis=1) / np.linalg.norm(Sr, axis=1)).max())
+        worst["elem_o"] = max(worst["elem_o"], (np.abs(do).max(axis=1) / np.maximum(np.abs(o_ref).max(axis=1), 1e-30)).max())
+        worst["elem_S"] = max(worst["elem_S"], (np.abs(dS).max(axis=1) / np.abs(Sr).max(axis=1)).max())
+    print(f"[parity] {name}: max state-step rel err o={worst['o']:.3e} S={worst['S']:.3e} "
+          f"elem o={worst['elem_o']:.3e} S={worst['elem_S']:.3e} (tol {TOL[dtype]:g} / {ELEM_TOL[dtype]:g})", flush=True)
+    assert worst["o"] <= TOL[dtype] and worst["S"] <= TOL[dtype], (name, worst)
+    assert worst["elem_o"] <= ELEM_TOL[dtype] and worst["elem_S"] <= ELEM_TOL[dtype], (name, worst)
 
 
 @pytest.mark.parametrize("dtype,d,N", [("bf16", 64, 300), ("bf16", 128, 37), ("f32", 64, 129), ("f32", 128, 5),

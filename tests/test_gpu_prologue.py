@@ -87,21 +87,15 @@ def test_prologue_row_rescaling():
     assert eo <= 1e-5 and es <= 1e-5
 
 
-def test_prologue_full_size_sampled_chains():
-    """The 8 x 2048 x 12 d64 layer from raw inputs, as the benchmark runs it; sampled chains vs the oracle."""
+def test_prologue_full_size_all_chains():
+    """The 8 x 2048 x 12 d64 layer from raw inputs, as the benchmark runs it; every chain vs the oracle."""
     torch_dev()
     w = WORKLOADS["sykra_layer_bf16_prologue"]
     inp = gen_workload(w)
     note("prologue full size sykra_layer_bf16_prologue")
     o, S = run_prologue(inp, 1.0)
-    chains = [(0, 0), (3, 7), (7, 11)]
-    sub = {key: np.stack([inp[key][b, :, h] for b, h in chains], axis=1)[None] for key in ("q", "k", "v", "a_logit", "b_logit")}
-    sub["S0"] = None
-    o_ref, S_ref = oracle_prologue(sub, 1.0)
-    o_s = np.stack([o[b, :, h] for b, h in chains], axis=1)[None]
-    S_s = np.stack([S[b, h] for b, h in chains])[None]
-    assert_close("prologue_full", "bf16", o_s, S_s, o_ref, S_ref)
-    assert np.isfinite(o).all() and np.isfinite(S).all()
+    o_ref, S_ref = oracle_prologue(inp, 1.0)
+    assert_close("prologue_full", "bf16", o, S, o_ref, S_ref)
 
 
 def test_prologue_saturated_logits():
