@@ -32,6 +32,14 @@ bool step_supported(int dtype, int dk, int dv) {
   }
 }
 
+// bf16 d = 64 / 128 run the two-launch path (factor pass, then state pass)
+// whenever one batch row of q, k, v and out is addressable with 32-bit buffer
+// offsets and the chunk count fits an int; larger rows take the fused kernel.
+bool two_path(int B, int T, int H, int dk, int dv, int dtype) {
+  if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128)) return false;
+  return (long long)T * H * dk * 2 < (1LL << 31) && (long long)B * H * ((T + 63) / 64) < (1LL << 30);
+}
+
 // Largest element count any single tensor may have (keeps every index in range).
 constexpr long long kMaxElems = 1LL << 40;
 
@@ -65,9 +73,19 @@ const char* gdn_status_str(int status) {
 
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (B < 0 || T < 0 || H < 0 || chunk != 64 || !chunk_supported(dtype, dk, dv)) return 0;
-  // The real kernels keep every intermediate on chip; the complex path hands
-  // per-chunk factors from one launch to the next.
+  // The complex path and the bf16 two-launch path hand per-chunk factors from
+  // one launch to the next; the fused kernels keep every intermediate on chip.
   if (dtype == GDN_C64) return gdn::chunk_cx_workspace_bytes(B, T, H);
+  if (two_path(B, T, H, dk, dv, dtype)) {
+    gdn::ChunkArgs a{};
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.dtype = dtype;
+    return gdn::chunk_two_workspace_bytes(a);
+  }
   return 0;
 }
 
@@ -89,10 +107,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::ChunkArgs a{q, k, v, alpha, beta, S0, out, S_final, B, T, H, dk, dv, dtype, stream};
-  // The pipelined bf16 kernel addresses one batch row of q/k/v/out with 32-bit
-  // buffer offsets; larger rows use the fused kernel.
-  const bool pipe_fits = (long long)T * H * (dk > dv ? dk : dv) * 2 < (1LL << 31);
-  if (dtype == GDN_BF16 && pipe_fits) return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (two_path(B, T, H, dk, dv, dtype)) return gdn::launch_chunk_two(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   if (dtype == GDN_C64) return gdn::launch_chunk_cx(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -90,7 +90,12 @@ struct ChannelArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a);   // fused kernel, real dtypes
-hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only
+hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 only (fused prologue)
+// bf16, d = 64 or 128: the chunk-parallel factor pass, then the state pass
+// (segmented for long sequences with few chains).  Per-chunk factors and the
+// segment maps go through `workspace`.
+size_t chunk_two_workspace_bytes(const ChunkArgs& a);
+hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace);
 hipError_t launch_recurrent_step(const StepArgs& a);
 // Complex64, head size 32: three launches (prep, state scan, output) that
 // exchange per-chunk intermediates through `workspace`.

@@ -76,6 +76,13 @@ def test_chunk_empty_is_noop():
     assert chunk(H=0) == raw.GDN_OK
 
 
+def test_chunk_bf16_needs_its_workspace():
+    need = gdn.gdn_chunk_fwd_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_BF16)
+    assert need == 2 * 3 * 2 * 6400
+    assert chunk(workspace=None, workspace_bytes=0) == raw.GDN_ERR_WORKSPACE
+    assert chunk(workspace=A, workspace_bytes=need - 1) == raw.GDN_ERR_WORKSPACE
+
+
 def prologue(**kw):
     args = dict(q=A, k=A, v=A, a_logit=A, b_logit=A, beta_scale=2.0, S0=None, chunk=64, out=A, S_final=A, B=2,
                 T=128, H=3, dk=64, dv=64, dtype=gdn.GDN_BF16, stream=None)
@@ -170,7 +177,15 @@ def test_channel_decay_empty_is_noop():
 
 
 def test_workspace_query():
-    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
+    # bf16: one 6400-byte factor record per (chain, chunk); fp32 keeps everything on chip
+    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 8 * 12 * 32 * 6400
+    assert gdn.gdn_chunk_fwd_workspace_bytes(2, 16384, 16, 128, 128, 64, gdn.GDN_BF16) == 2 * 16 * 256 * 6400
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 65, 1, 64, 64, 64, gdn.GDN_F32) == 0
+    assert gdn.gdn_chunk_fwd_workspace_bytes(2, 0, 3, 64, 64, 64, gdn.GDN_BF16) == 0
+    # a long sequence with few chains adds the segment maps and start states of the two-level scan
+    G = 16  # 1 chain x 8 slices: 15 x 16 map workgroups and 16 x 8 output workgroups fit 256 CUs
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 65536, 1, 128, 128, 64, gdn.GDN_BF16) == \
+        1024 * 6400 + G * (128 * 256 + 128 * 128) * 4
 
 
 @pytest.mark.parametrize("kw,status", [
