@@ -41,10 +41,13 @@ _CSRC = "linear_attention_sequence_gated_amd/csrc/"
 # Sources each measured kernel is compiled from; a counter summary is used only
 # while the hash of these files matches the one recorded with it.
 KERNEL_SOURCES = {
-    "chunk_pipe3_kernel": [_CSRC + "chunk_pipe.hip", _CSRC + "gdn_device.hpp"],
-    "chunk_pipe_kernel": [_CSRC + "chunk_pipe.hip", _CSRC + "gdn_device.hpp"],
+    "chunk_two": [_CSRC + "chunk_two.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
+    "chunk_pipe3_kernel": [_CSRC + "chunk_pipe.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
     "chunk_fwd_kernel": [_CSRC + "chunk_fwd.hip", _CSRC + "gdn_device.hpp"],
     "cx_prep_scan_out": [_CSRC + "chunk_cx.hip", _CSRC + "gdn_device.hpp"],
+    "decode_kernel": [_CSRC + "decode.hip", _CSRC + "gdn_device.hpp"],
+    "bwd_kernel": [_CSRC + "chunk_bwd.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
+    "channel_decay_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
 }
 
 
@@ -262,15 +265,16 @@ def main():
     tokens = w.B * w.T
     value = tokens * args.steps / wall
     achieved = wbytes / (avg_ms * 1e-3) / 1e9
-    # The library takes the pipelined kernels for bf16 whenever a chain's row offsets fit 32 bits:
-    # the three-stage one for d = 64, the two-stage one for d = 128.
-    pipe = w.dtype == "bf16" and w.T * w.H * max(w.dk, w.dv) * 2 < 2 ** 31
+    # bf16 calls that need a workspace run the two-launch path (a factor pass and a state pass, segmented
+    # for long sequences with few chains): d = 128, and d = 64 when the chains alone cannot fill the CUs.
+    # Other bf16 d = 64 calls and the fused prologue run the three-stage kernel; fp32 the fused kernel.
+    two = w.dtype == "bf16" and not pro and ws_bytes > 0
     if w.dtype == "c64":
         kernel, qual = "cx_prep_scan_out", "gdn::cx::"
-    elif pipe and w.dk == 64:
+    elif two:
+        kernel, qual = "chunk_two", "gdn::two::"
+    elif pro or (w.dtype == "bf16" and w.dk == 64):
         kernel, qual = "chunk_pipe3_kernel", "gdn::pipe3::"
-    elif pipe:
-        kernel, qual = "chunk_pipe_kernel", "gdn::pipe::"
     else:
         kernel, qual = "chunk_fwd_kernel", "gdn::"
     traffic = measured_traffic(kernel, args.workload)
@@ -296,6 +300,10 @@ def main():
                      "algorithmic_bytes_per_launch": wbytes, "kernel_avg_ms": avg_ms,
                      "kernel": qual + kernel},
     }
+    if two:
+        # The factor pass and the state pass of one call are priced together: achieved is the call's
+        # algorithmic bytes over the call's average duration (both launches and the gap between them).
+        result["roofline"]["kernel"] = "gdn::two::factor_kernel + state_kernel (one call)"
     if w.dtype == "c64":
         # Complex products run on fp32 matrix cores, which bind before HBM does.  The three
         # launches of one call (prep, state scan, output) are priced together.

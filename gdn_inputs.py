@@ -90,6 +90,9 @@ WORKLOADS = {
     "long_context_bf16": Workload(
         "long_context_bf16", "chunk", "bf16", B=2, T=16384, H=16, dk=128, dv=128, seed=2,
         alpha_mu=-5.0, s0_var=0.01, note="long context, d=128, slow decay, nonzero S0"),
+    "long_sequence_bf16": Workload(
+        "long_sequence_bf16", "chunk", "bf16", B=1, T=65536, H=12, dk=64, dv=64, seed=5,
+        note="the Sykra-shaped layer over one 65536-token sequence (the longest length DeltaPhase times)"),
     "deltaphase_c64": Workload(
         "deltaphase_c64", "chunk", "c64", B=4, T=4096, H=8, dk=32, dv=32, seed=3,
         beta_scale=2.0, note="complex phasor keys/queries, beta in (0, 2)"),

@@ -98,28 +98,30 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(const float (&a)[16], int g,
 #undef GDN_TWO_STEP
 
 // ------------------------------------------------------------- factor pass
-// One wave per (chain, chunk); waves of a workgroup are independent (no
-// barrier).  Chunk ids run over (batch, chunk, head), so the waves of one
-// workgroup read neighbouring heads' gates from the same cache lines.
+// One single-wave workgroup per (chain, chunk), 11.4 KB of LDS each, so a CU
+// holds a dozen of them and their load latencies overlap.  Chunk ids run over
+// (batch, chunk, head): neighbouring workgroups read neighbouring heads' gates
+// from the same cache lines.
 template <int DK>
 struct FactorCfg {
   static constexpr int NKP = DK / 32;
-  // per-wave fp32 scratch: g, beta, the rows of -A of the four diagonal
-  // blocks (16 x 20 each), and ten 16 x 17 transpose tiles
-  static constexpr int fG = 0, fB = 64, fDS = 128, fTR = fDS + 4 * 16 * 20, szW = fTR + 10 * 16 * 17;
+  // per-wave fp32 scratch: g, beta, and ten 16 x 17 transpose tiles (four
+  // for the diagonal blocks, six for the blocks below them).  The rows of -A of
+  // the four diagonal blocks (16 x 20 each) share the last six tiles: they are
+  // dead once the inverses are formed, before those tiles are written.
+  static constexpr int fG = 0, fB = 64, fTR = 128, fDS = fTR + 4 * 272, szW = fTR + 10 * 272;
+  static_assert(fDS + 4 * 16 * 20 <= szW, "diagonal-block rows fit the shared tiles");
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void factor_kernel(const __bf16* __restrict__ kg, const float* __restrict__ alpha,
-                                                     const float* __restrict__ beta, char* __restrict__ ws, int T,
-                                                     int H, int nch, int total) {
+__global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ kg, const float* __restrict__ alpha,
+                                                    const float* __restrict__ beta, char* __restrict__ ws, int T,
+                                                    int H, int nch, int total) {
   using Cf = FactorCfg<DK>;
   constexpr int NKP = Cf::NKP;
-  __shared__ __attribute__((aligned(16))) float sh[4 * Cf::szW];
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, g = l >> 4, c = l & 15;
-  const int id = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + w);
-  if (id >= total) return;  // whole wave; no barrier follows
-  float* const W = sh + w * Cf::szW;
+  __shared__ __attribute__((aligned(16))) float W[Cf::szW];
+  const int l = threadIdx.x & 63, g = l >> 4, c = l & 15;
+  const int id = blockIdx.x;
   const int h = id % H, bn = id / H, n = bn % nch, b = bn / nch;
   const int chain = b * H + h, t0 = n * 64;
   char* const rec = ws + ((size_t)chain * nch + n) * kRecBytes;
@@ -256,12 +258,17 @@ __global__ __launch_bounds__(256) void factor_kernel(const __bf16* __restrict__ 
 }
 
 // -------------------------------------------------------------- state pass
-// Key rows and query rows are staged in LDS unpadded, 16-byte pieces swizzled
-// so that the sixteen rows a 16-lane group reads at once fall on distinct
-// banks: piece u of row r sits at position u ^ sw(r).
+// Key rows and query rows are staged in LDS unpadded, 16-byte pieces swizzled:
+// piece u of row r sits at position u ^ sw(r).  Two read patterns must spread
+// over the 64 banks: a 16-lane group reading one piece of sixteen consecutive
+// rows (MFMA operands in row order), and the transposed reads of K, where a
+// 16-lane group reads pieces 4m .. 4m + 3 (one 8-byte half each) of four
+// consecutive rows 4g .. 4g + 3.  sw(r) rotates the bits of r so that both are
+// free of conflicts within 16 lanes (at d = 64 two rows share a 256-byte bank
+// window, told apart by r & 1).
 template <int DK> __device__ __forceinline__ int row_off(int r, int e) {
   constexpr int NU = DK / 8;
-  const int sw = DK == 64 ? ((r >> 1) & 7) : (r & 15);
+  const int sw = DK == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
   return r * DK + (((e >> 3) ^ sw) & (NU - 1)) * 8 + (e & 7);
 }
 
@@ -866,7 +873,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // segments' maps (dk more columns) once more.  That pays from G = 4 on, when
 // both launches still fit one workgroup per CU; each segment keeps at least 16
 // chunks.
-static int two_segments(const ChunkArgs& a) {
+int chunk_two_segments(const ChunkArgs& a) {
   const long nch = (a.T + 63) / 64, chains = (long)a.B * a.H;
   const long nv = a.dk == 64 ? 32 : 16;
   const long out_sl = a.dv / nv, map_sl = (a.dk + a.dv) / nv;
@@ -879,7 +886,7 @@ static int two_segments(const ChunkArgs& a) {
 size_t chunk_two_workspace_bytes(const ChunkArgs& a) {
   const size_t nch = (a.T + 63) / 64, chains = (size_t)a.B * a.H;
   size_t b = chains * nch * two::kRecBytes;
-  const int G = two_segments(a);
+  const int G = chunk_two_segments(a);
   if (G > 1) b += chains * G * ((size_t)a.dk * (a.dk + a.dv) + (size_t)a.dk * a.dv) * 4;
   return b;
 }
@@ -893,7 +900,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
   char* ws = static_cast<char*>(workspace);
   const long total = chains * nch;
   if (total > 0) {
-    const hipError_t e = launch_kernel(two::factor_kernel<DK>, dim3((unsigned)((total + 3) / 4)), dim3(256), st,
+    const hipError_t e = launch_kernel(two::factor_kernel<DK>, dim3((unsigned)total), dim3(64), st,
                                        static_cast<const __bf16*>(a.k), a.alpha, a.beta, ws, a.T, a.H, nch,
                                        (int)total);
     if (e != hipSuccess) return e;
@@ -910,7 +917,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
   s.H = a.H;
   s.DV = a.dv;
   s.nch = nch;
-  const int G = two_segments(a);
+  const int G = chunk_two_segments(a);
   s.G = G;
   s.SC = G > 1 ? (nch + G - 1) / G : max(nch, 1);
   if (G > 1) {

@@ -32,12 +32,30 @@ bool step_supported(int dtype, int dk, int dv) {
   }
 }
 
-// bf16 d = 64 / 128 run the two-launch path (factor pass, then state pass)
-// whenever one batch row of q, k, v and out is addressable with 32-bit buffer
-// offsets and the chunk count fits an int; larger rows take the fused kernel.
+// Kernels for bf16 whose rows are addressable with 32-bit buffer offsets (one
+// batch row of q, k, v and out under 2^31 bytes):
+//   d = 128: the two-launch path (factor pass, then state pass);
+//   d = 64: the three-stage pipelined kernel, unless the chains are too few to
+//   fill the CUs and the sequence is long: then the two-launch path with the
+//   segment-parallel two-level scan.
+// Rows past 32-bit offsets take the fused kernel.
+bool rows_fit(int T, int H, int dk) { return (long long)T * H * dk * 2 < (1LL << 31); }
+
+gdn::ChunkArgs shape_args(int B, int T, int H, int dk, int dv, int dtype) {
+  gdn::ChunkArgs a{};
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.dk = dk;
+  a.dv = dv;
+  a.dtype = dtype;
+  return a;
+}
+
 bool two_path(int B, int T, int H, int dk, int dv, int dtype) {
-  if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128)) return false;
-  return (long long)T * H * dk * 2 < (1LL << 31) && (long long)B * H * ((T + 63) / 64) < (1LL << 30);
+  if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128) || !rows_fit(T, H, dk)) return false;
+  if ((long long)B * H * ((T + 63) / 64) >= (1LL << 30)) return false;
+  return dk == 128 || gdn::chunk_two_segments(shape_args(B, T, H, dk, dv, dtype)) > 1;
 }
 
 // Largest element count any single tensor may have (keeps every index in range).
@@ -76,16 +94,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
   // The complex path and the bf16 two-launch path hand per-chunk factors from
   // one launch to the next; the fused kernels keep every intermediate on chip.
   if (dtype == GDN_C64) return gdn::chunk_cx_workspace_bytes(B, T, H);
-  if (two_path(B, T, H, dk, dv, dtype)) {
-    gdn::ChunkArgs a{};
-    a.B = B;
-    a.T = T;
-    a.H = H;
-    a.dk = dk;
-    a.dv = dv;
-    a.dtype = dtype;
-    return gdn::chunk_two_workspace_bytes(a);
-  }
+  if (two_path(B, T, H, dk, dv, dtype)) return gdn::chunk_two_workspace_bytes(shape_args(B, T, H, dk, dv, dtype));
   return 0;
 }
 
@@ -108,6 +117,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if ((long long)B * H == 0) return GDN_OK;
   gdn::ChunkArgs a{q, k, v, alpha, beta, S0, out, S_final, B, T, H, dk, dv, dtype, stream};
   if (two_path(B, T, H, dk, dv, dtype)) return gdn::launch_chunk_two(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (dtype == GDN_BF16 && dk == 64 && rows_fit(T, H, dk))
+    return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   if (dtype == GDN_C64) return gdn::launch_chunk_cx(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -95,6 +95,7 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 onl
 // (segmented for long sequences with few chains).  Per-chunk factors and the
 // segment maps go through `workspace`.
 size_t chunk_two_workspace_bytes(const ChunkArgs& a);
+int chunk_two_segments(const ChunkArgs& a);  // segments of the two-level scan (1: none)
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace);
 hipError_t launch_recurrent_step(const StepArgs& a);
 // Complex64, head size 32: three launches (prep, state scan, output) that

@@ -76,11 +76,18 @@ def test_chunk_empty_is_noop():
     assert chunk(H=0) == raw.GDN_OK
 
 
-def test_chunk_bf16_needs_its_workspace():
-    need = gdn.gdn_chunk_fwd_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_BF16)
+def test_chunk_bf16_d128_needs_its_workspace():
+    need = gdn.gdn_chunk_fwd_workspace_bytes(2, 128, 3, 128, 128, 64, gdn.GDN_BF16)
     assert need == 2 * 3 * 2 * 6400
-    assert chunk(workspace=None, workspace_bytes=0) == raw.GDN_ERR_WORKSPACE
-    assert chunk(workspace=A, workspace_bytes=need - 1) == raw.GDN_ERR_WORKSPACE
+    assert chunk(dk=128, dv=128, workspace=None, workspace_bytes=0) == raw.GDN_ERR_WORKSPACE
+    assert chunk(dk=128, dv=128, workspace=A, workspace_bytes=need - 1) == raw.GDN_ERR_WORKSPACE
+
+
+def test_long_sequence_few_chains_takes_the_segmented_scan():
+    # one 65536-token sequence of a 12-head d = 64 layer: 12 chains leave most CUs idle, so the call runs
+    # the two-level scan with 4 segments (factor records, segment maps [dk, dk + dv], start states)
+    need = gdn.gdn_chunk_fwd_workspace_bytes(1, 65536, 12, 64, 64, 64, gdn.GDN_BF16)
+    assert need == 12 * 1024 * 6400 + 12 * 4 * (64 * 128 + 64 * 64) * 4
 
 
 def prologue(**kw):
@@ -177,8 +184,9 @@ def test_channel_decay_empty_is_noop():
 
 
 def test_workspace_query():
-    # bf16: one 6400-byte factor record per (chain, chunk); fp32 keeps everything on chip
-    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 8 * 12 * 32 * 6400
+    # d = 64 bf16 with enough chains and fp32: the fused kernels keep everything on chip
+    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 2048, 12, 64, 64, 64, gdn.GDN_BF16) == 0
+    # d = 128 bf16: one 6400-byte factor record per (chain, chunk)
     assert gdn.gdn_chunk_fwd_workspace_bytes(2, 16384, 16, 128, 128, 64, gdn.GDN_BF16) == 2 * 16 * 256 * 6400
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 65, 1, 64, 64, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(2, 0, 3, 64, 64, 64, gdn.GDN_BF16) == 0

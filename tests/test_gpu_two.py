@@ -44,16 +44,16 @@ def decode_records(raw, chains, nch):
     return Tb, g
 
 
-@pytest.mark.parametrize("d,T", [(64, 150), (128, 77)])
-def test_factor_records_match_the_chunk_form(d, T):
+# (d, B, T, H): d = 128 always takes the two-launch path; d = 64 does for a long sequence with few chains.
+@pytest.mark.parametrize("d,B,T,H", [(128, 2, 150, 3), (128, 2, 77, 3), (64, 1, 4100, 1)])
+def test_factor_records_match_the_chunk_form(d, B, T, H):
     torch = torch_dev()
     import linear_attention_sequence_gated_amd as gdn
-    B, H = 2, 3
     inp = gen_chunk(B, T, H, d, d, dtype="bf16", seed=200 + d, beta_scale=2.0)
     note(f"two-pass factor records d={d} T={T}")
     nch = (T + 63) // 64
     need = gdn.gdn_chunk_fwd_workspace_bytes(B, T, H, d, d, 64, gdn.GDN_BF16)
-    assert need == B * H * nch * REC
+    assert need >= B * H * nch * REC  # records first, then (segmented scan) the segment maps
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     q, k, v = up(inp["q"], "bf16"), up(inp["k"], "bf16"), up(inp["v"], "bf16")
     a, b = up(inp["alpha"], "f32"), up(inp["beta"], "f32")
@@ -121,3 +121,21 @@ def test_segmented_scan_state_in_place():
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_chunk(inp)
     assert_close("segmented_alias", "bf16", down(o), down(S), o_ref, S_ref)
+
+
+def test_long_sequence_full_size_all_chains():
+    """The Sykra layer over one 65536-token sequence (12 chains of 1024 chunks), which takes the segmented scan
+    with 4 segments, in the benchmark's launch configuration; every chain against the oracle."""
+    torch = torch_dev()
+    from gdn_inputs import WORKLOADS, gen_workload
+    import linear_attention_sequence_gated_amd as gdn
+    w = WORKLOADS["long_sequence_bf16"]
+    inp = gen_workload(w)
+    need = gdn.gdn_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, 64, gdn.GDN_BF16)
+    assert need > w.B * w.H * (w.T // 64) * REC, "the long sequence must take the segmented scan"
+    note("segmented scan, long_sequence_bf16 full size")
+    o, S = gdn.chunk_fwd(up(inp["q"], "bf16"), up(inp["k"], "bf16"), up(inp["v"], "bf16"), up(inp["alpha"], "f32"),
+                         up(inp["beta"], "f32"), None)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_chunk(inp)
+    assert_close("full_long_sequence_bf16", "bf16", down(o), down(S), o_ref, S_ref)
