@@ -228,6 +228,31 @@ int gdn_fwd_channel_decay(const void *q, const void *k, const void *v, const flo
                           int dtype, void *stream);
 
 /*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as gdn_chunk_fwd, without the workspace: the
+ * call takes it from a fixed device array that the library keeps per device,
+ * from the first call on that device until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).
+ *
+ * Limit: GDN_NOALLOC_MAX_WORKSPACE bytes (128 MiB), compared with
+ * gdn_chunk_fwd_workspace_bytes(...) for the same sizes; a call that needs
+ * more returns GDN_ERR_WORKSPACE before anything is launched.  Calls that need
+ * no workspace (fp32, and bf16 d = 64 with enough chains) use none.
+ *
+ * All calls on one device share the array: calls that may overlap on one
+ * device (different streams, unordered host threads) race and give wrong
+ * results.  Order them (one stream) or use gdn_chunk_fwd with a workspace of
+ * your own.  Other errors as for gdn_chunk_fwd; GDN_ERR_HIP if the array's
+ * device address cannot be found.
+ */
+int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, const void *S0, int chunk, void *out, void *S_final,
+                          int B, int T, int H, int dk, int dv, int dtype, void *stream);
+#define GDN_NOALLOC_MAX_WORKSPACE ((size_t)128 << 20)
+
+/*
  * One single-token decode step on N independent states, in place.
  *
  *   q, k   [N, dk] dtype;  v [N, dv] dtype;  alpha, beta [N] float32

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "channel_decay.hip", "decode.hip", "gdn_api.cpp"]
+SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "channel_decay.hip", "decode.hip", "noalloc.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled for device code (the host pass warns that it

@@ -2,7 +2,8 @@
 
 The raw entry points keep the C names and take integer device addresses:
 ``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_chunk_bwd``,
-``gdn_fwd_channel_decay``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_workspace_bytes``,
+``gdn_fwd_channel_decay``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_noalloc``,
+``gdn_chunk_fwd_workspace_bytes``,
 ``gdn_chunk_bwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
 ``chunk_fwd_prologue``, ``chunk_bwd``, ``fwd_channel_decay`` and ``recurrent_step`` are conveniences for
 torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
@@ -20,9 +21,10 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE = 0, 1, 2, 3
 GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
 GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
+GDN_NOALLOC_MAX_WORKSPACE = 128 << 20  # include/gdn.h
 
 EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_bwd_workspace_bytes",
-           "gdn_chunk_bwd", "gdn_fwd_channel_decay", "gdn_recurrent_step", "gdn_status_str")
+           "gdn_chunk_bwd", "gdn_fwd_channel_decay", "gdn_recurrent_step", "gdn_status_str", "gdn_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -58,6 +60,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_fwd_channel_decay.restype = ci
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
     lib.gdn_recurrent_step.restype = ci
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = ci
     lib.gdn_status_str.argtypes = [ci]
     lib.gdn_status_str.restype = ctypes.c_char_p
     if path is None:
@@ -78,6 +82,11 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv
                   workspace, workspace_bytes, stream) -> int:
     return int(load().gdn_chunk_fwd(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype,
                                     workspace, workspace_bytes, stream))
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype, stream) -> int:
+    return int(load().gdn_chunk_fwd_noalloc(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H, dk, dv, dtype,
+                                            stream))
 
 
 def gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale, S0, chunk, out, S_final, B, T, H, dk, dv,

@@ -240,3 +240,16 @@ def test_torch_helpers_reject_non_contiguous_q():
     q2 = torch.zeros(64, 3, dtype=torch.bfloat16).t()  # [3, 64], strided
     with pytest.raises(ValueError, match="q: must be contiguous"):
         gdn.recurrent_step(q2, q2.contiguous(), q2.contiguous(), torch.zeros(3), torch.zeros(3), torch.zeros(3, 64, 64))
+
+
+def test_noalloc_rejects_sizes_past_its_scratch():
+    """gdn_chunk_fwd_noalloc refuses a call whose workspace exceeds its fixed scratch array, before any HIP call,
+    and reports argument errors as gdn_chunk_fwd does."""
+    args = dict(q=A, k=A, v=A, alpha=A, beta=A, S0=None, chunk=64, out=A, S_final=A, B=4, T=65536, H=16, dk=128,
+                dv=128, dtype=gdn.GDN_BF16, stream=None)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(4, 65536, 16, 128, 128, 64, gdn.GDN_BF16) > gdn.GDN_NOALLOC_MAX_WORKSPACE
+    assert gdn.gdn_chunk_fwd_noalloc(**args) == raw.GDN_ERR_WORKSPACE
+    assert gdn.gdn_chunk_fwd_noalloc(**dict(args, dtype=9)) == raw.GDN_ERR_DTYPE
+    assert gdn.gdn_chunk_fwd_noalloc(**dict(args, B=-1)) == raw.GDN_ERR_SHAPE
+    assert gdn.gdn_chunk_fwd_noalloc(**dict(args, B=0, q=None, k=None, v=None, alpha=None, beta=None, out=None,
+                                            S_final=None)) == raw.GDN_OK
