@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "decode_kernel": [_CSRC + "decode.hip", _CSRC + "gdn_device.hpp"],
     "bwd_kernel": [_CSRC + "chunk_bwd.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
+    "channel_chunk_kernel": [_CSRC + "channel_chunk.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
 }
 
 
@@ -555,7 +556,8 @@ def bench_channel(args, w, dev):
                    "input_copies_cycled": ncopies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": wbytes,
-                     "kernel_avg_ms": avg_ms, "kernel": "gdn::chd::channel_decay_kernel"},
+                     "kernel_avg_ms": avg_ms,
+                     "kernel": "gdn::chc::channel_chunk_kernel" if w.dtype == "bf16" else "gdn::chd::channel_decay_kernel"},
     }
     if not args.no_cpu:
         from oracle.channel_decay import channel_decay_fwd

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "channel_decay.hip", "decode.hip", "noalloc.hip", "gdn_api.cpp"]
+SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "channel_decay.hip", "channel_chunk.hip", "decode.hip", "noalloc.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled for device code (the host pass warns that it
@@ -25,9 +25,15 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source flags.  channel_chunk.hip rescales its matrix-core accumulators with
+# vector instructions every step; the VGPR form of the MFMA instructions keeps
+# them in VGPRs instead of copying them to and from AGPRs each time.
+EXTRA = {"channel_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

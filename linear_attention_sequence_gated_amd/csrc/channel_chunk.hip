@@ -1,0 +1,478 @@
+// channel_chunk.hip -- the per-output-channel decay forward in chunk form,
+// bf16 inputs, d_k = d_v = 64.
+//
+// The rule (DeltaPhase README, section 2: LaplacePhaseCore's gated-decay
+// variant, the error read from the undecayed memory; section 5: the decay
+// diag(r_t) on the memory's output rows, one factor per value channel), for
+// every value channel j of the state S [dk, dv]:
+//   s_j <- r_j s_j + k beta (v_j - k^T s_j),   o_j = q^T s_j.
+// Section 5's exact chunkwise scan: because the decay sits on the output side,
+// the coupling between the tokens of a chunk is the plain Gram K K^T, and the
+// decay between tokens u < t of channel j is the product of its factors in
+// between, so each channel needs its own unit lower-triangular solve.  With
+// S the state at the start of a sub-chunk of 16 tokens, w_t = beta_t e_t:
+//   w_t = beta_t (v_t - g'_t (K S)_t) - beta_t sum_{u<t} G_tu D'_tu w_u,
+//     G = K K^T, D'_tu = prod_{u<i<t} r_i, g'_t = prod_{i<t} r_i;
+//   o_t = g_t (Q S)_t + sum_{u<=t} P_tu D_tu w_u,
+//     P = Q K^T, D_tu = prod_{u<i<=t} r_i, g_t = prod_{i<=t} r_i;
+//   S <- diag(g_15) S + K^T (lambda * w),  lambda_u = prod_{u<i<=15} r_i.
+// The decay products are formed by Horner's rule inside the solves (each
+// earlier term is multiplied by r_u as token u passes), never as a ratio or
+// an exponential of a difference, so nothing overflows however small r is.
+//
+// One workgroup per (batch, head) chain, four waves:
+//   state wave   S [64 x 64] in matrix-core accumulators (keys in the key_row
+//                order of gdn_pipe.hpp); per sub-chunk n it applies the update
+//                of sub-chunk n - 1, then forms K_(n+1) S and Q_n S and the
+//                16 x 16 tiles G_(n+1), C_(n+1) = K_(n+1) K_n^T and P_n;
+//   solver wave  one lane per value channel: K S_n = g_15 (K_n S_(n-1)) +
+//                C_n (lambda * w)_(n-1) (the last term on the matrix cores),
+//                then the channel's forward substitution for w;
+//   output wave  one lane per channel: o of sub-chunk n - 1;
+//   loader wave  K, Q, V, r and beta of sub-chunk n + 2, through LDS.
+// Everything a role reads in step n was written in an earlier step; one
+// barrier per step.  The solver's substitution is the chain that carries the
+// state from sub-chunk to sub-chunk; the products that need only the old
+// state run on the state wave beside it.
+#include <hip/hip_bf16.h>
+
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+#include "gdn_pipe.hpp"
+
+namespace gdn {
+namespace chc {
+using namespace pipe;
+
+constexpr int D = 64, SC = 16;  // head dimension, tokens per sub-chunk
+constexpr int LDK = D + 8;      // bf16 row stride of the staged K and Q rows
+constexpr int LDT = SC + 4;     // fp32 stride of [channel][token] tables (16-byte rows, five 16-byte
+                                // banks apart: a 16-lane group reading or writing 16 bytes each hits 16 banks)
+constexpr int LDX = SC + 8;     // bf16 stride of the [channel][token] lambda * w table
+constexpr int NSLOT = 4;        // input slots: sub-chunks n - 1 .. n + 2
+
+struct Lay {
+  // input slot (bytes): K rows, Q rows [16][LDK] bf16; V^T, r^T [64][LDT] fp32; beta[16]
+  static constexpr int iK = 0, iQ = 16 * LDK * 2, iV = 2 * 16 * LDK * 2, iR = iV + 64 * LDT * 4, iB = iR + 64 * LDT * 4;
+  static constexpr int szIn = iB + 16 * 4;
+  // per-parity ring (bytes): Y^T = (K S)^T, QS^T [64][LDT] fp32; beta G^T [16][LDT] fp32 (column u of
+  // beta_t G_tu, t > u); P^T [16][LDT] fp32 (t >= u); C as bf16 A operands, 64 lanes x 8 bytes;
+  // (lambda w)^T [64][LDX] bf16; w^T [64][LDT] fp32; g_15 per channel [64] fp32
+  static constexpr int rY = 0, rQS = rY + 64 * LDT * 4, rG = rQS + 64 * LDT * 4, rP = rG + 16 * LDT * 4,
+                       rC = rP + 16 * LDT * 4, rXL = rC + 64 * 8, rW = rXL + 64 * LDX * 2, rGE = rW + 64 * LDT * 4;
+  static constexpr int szRing = rGE + 64 * 4;
+  static constexpr int oIn = 0, oRing = NSLOT * szIn, oCX = oRing + 2 * szRing;  // solver's own [64][LDT] scratch
+  static constexpr int bytes = oCX + 64 * LDT * 4;
+  static_assert(szIn % 16 == 0 && szRing % 16 == 0 && rC % 16 == 0 && rXL % 16 == 0 && rW % 16 == 0, "alignment");
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+struct Args {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* r;
+  const float* beta;
+  const float* S0;
+  __bf16* out;
+  float* Sf;
+  int T, H, nsub;
+};
+
+// Orders this wave's LDS writes before its later LDS reads in every lane.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Last step: nsub or nsub + 1, so that the loader's loop runs whole pairs of
+// steps (a loop with a conditional load path gets conservative wait counts).
+__device__ __forceinline__ int last_step(int nsub) { return nsub | 1; }
+
+// Steps n = -2 .. last_step(nsub), one barrier after each.
+template <class Step>
+__device__ __forceinline__ void run(int nsub, Step&& step) {
+  __builtin_assume(nsub >= 0);
+  const int last = last_step(nsub);
+  for (int n = -2; n <= last; ++n) {
+    step(n);
+    stage_barrier();
+  }
+}
+
+__device__ __forceinline__ void ld16(const float* p, float (&x)[SC]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(p)[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[4 * q + j] = v[j];
+  }
+}
+
+__device__ __forceinline__ char* in_slot(char* smem, int m) { return smem + Lay::oIn + (m & (NSLOT - 1)) * Lay::szIn; }
+__device__ __forceinline__ char* ring(char* smem, int m) { return smem + Lay::oRing + (m & 1) * Lay::szRing; }
+
+// ------------------------------------------------------------ state wave
+__device__ void state_role(const Args& a, int chain, char* smem, int l) {
+  const int g = l >> 4, c = l & 15;
+  f32x4 S[4][4];  // [dk block d][channel block T]; lane (g, c) holds keys key_row(d, g, j), channel 16T + c
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S[d][t][j] = a.S0 ? a.S0[((size_t)chain * D + key_row(d, g, j)) * D + 16 * t + c] : 0.f;
+  u32x2 sfr[4][4];
+  auto to_bf16 = [&]() {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sfr[d][t] = cvt4(S[d][t]);
+  };
+  // A operand: keys 32p + 8g .. + 7 of row c of a staged [16][LDK] matrix
+  auto row_piece = [&](const char* base, int p) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(base) + c * LDK + 32 * p + 8 * g);
+  };
+  to_bf16();
+  run(a.nsub, [&](int n) {
+    if (n < -1) return;
+    const bool upd = n >= 1 && n <= a.nsub;  // S_n from S_(n-1)
+    const bool cur = n >= 0 && n < a.nsub;   // Q_n S_n and P_n
+    const bool nxt = n + 1 < a.nsub;         // K_(n+1) S_n, G_(n+1), and C_(n+1) when n >= 0
+    // Every LDS read of the step first (reads issued after the step's first
+    // LDS write would each wait out the LDS latency).
+    u32x2 kt[4], xl[4];
+    float gs[4];
+    if (upd) {
+      const char* Rp = ring(smem, n - 1);
+      const __bf16* Kp = reinterpret_cast<const __bf16*>(in_slot(smem, n - 1) + Lay::iK);
+      const __bf16* XL = reinterpret_cast<const __bf16*>(Rp + Lay::rXL);
+      const float* ge = reinterpret_cast<const float*>(Rp + Lay::rGE);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)  // K^T rows in key_row order, tokens 4g .. 4g + 3
+        kt[d] = ld4_tr(Kp + (4 * g + (c >> 2)) * LDK + 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        xl[t] = *reinterpret_cast<const u32x2*>(XL + (16 * t + c) * LDX + 4 * g);
+        gs[t] = ge[16 * t + c];
+      }
+    }
+    const char* In = in_slot(smem, n);
+    const char* In1 = in_slot(smem, n + 1);
+    u32x4 q0, q1, k0, k1, n0, n1;
+    f32x4 bn;
+    if (cur) {
+      q0 = row_piece(In + Lay::iQ, 0);
+      q1 = row_piece(In + Lay::iQ, 1);
+      k0 = row_piece(In + Lay::iK, 0);
+      k1 = row_piece(In + Lay::iK, 1);
+    }
+    if (nxt) {
+      n0 = row_piece(In1 + Lay::iK, 0);
+      n1 = row_piece(In1 + Lay::iK, 1);
+      bn = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(In1 + Lay::iB) + 4 * g);
+    }
+    issue_fence();
+    if (upd) {  // S <- diag(g_15) S + K_(n-1)^T (lambda * w)_(n-1)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4 sv = S[d][t];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[j] *= gs[t];
+          S[d][t] = mma2(kt[d], z4(), xl[t], z4(), sv);
+        }
+      to_bf16();
+    }
+    // [16 tokens x 64 keys] rows (pieces a0, a1) times S, lane (g, c) of channel tile t
+    auto times_state = [&](const u32x4& a0, const u32x4& a1, int t) {
+      return mma32(a1, pair(sfr[2][t], sfr[3][t]), mma32(a0, pair(sfr[0][t], sfr[1][t]), zero4()));
+    };
+    f32x4 qs[4], y[4], P, G, C;
+    if (cur) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qs[t] = times_state(q0, q1, t);
+      P = mma32(k1, q1, mma32(k0, q0, zero4()));  // lane (g, c): k_(4g+j) . q_c = P[c][4g + j]
+    }
+    if (nxt) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = times_state(n0, n1, t);
+      G = mma32(n1, n1, mma32(n0, n0, zero4()));  // lane (g, c): k_(4g+j) . k_c
+      if (n >= 0) C = mma32(k1, n1, mma32(k0, n0, zero4()));  // lane (g, c): k_(n, 4g+j) . k_(n+1, c) = C[c][4g + j]
+    }
+    // ... then the writes, all transposed to [channel][token] or [u][t]
+    if (cur) {
+      char* const R = ring(smem, n);
+      float* QS = reinterpret_cast<float*>(R + Lay::rQS);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(QS + (16 * t + c) * LDT + 4 * g) = qs[t];
+      float* PT = reinterpret_cast<float*>(R + Lay::rP);  // P^T[u][t] = q_t . k_u for t >= u
+#pragma unroll
+      for (int j = 0; j < 4; ++j) PT[(4 * g + j) * LDT + c] = c >= 4 * g + j ? P[j] : 0.f;
+    }
+    if (nxt) {
+      char* const R1 = ring(smem, n + 1);
+      float* Y = reinterpret_cast<float*>(R1 + Lay::rY);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(Y + (16 * t + c) * LDT + 4 * g) = y[t];
+      // beta G^T[u][t] = beta_t k_t . k_u for t > u
+      float* GT = reinterpret_cast<float*>(R1 + Lay::rG);
+      *reinterpret_cast<f32x4*>(GT + c * LDT + 4 * g) =
+          f32x4{4 * g + 0 > c ? bn[0] * G[0] : 0.f, 4 * g + 1 > c ? bn[1] * G[1] : 0.f,
+                4 * g + 2 > c ? bn[2] * G[2] : 0.f, 4 * g + 3 > c ? bn[3] * G[3] : 0.f};
+      if (n >= 0) *reinterpret_cast<u32x2*>(R1 + Lay::rC + 8 * l) = cvt4(C);
+    }
+  });
+  if (a.Sf) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.Sf[((size_t)chain * D + key_row(d, g, j)) * D + 16 * t + c] = S[d][t][j];
+  }
+}
+
+// ----------------------------------------------------------- solver wave
+__device__ void solver_role(const Args& a, char* smem, int l) {
+  float* const CX = reinterpret_cast<float*>(smem + Lay::oCX);
+  float ge_prev = 1.f;  // g_15 of the previous sub-chunk (1 before the first)
+  run(a.nsub, [&](int n) {
+    if (n < 0 || n >= a.nsub) return;
+    const char* In = in_slot(smem, n);
+    char* const R = ring(smem, n);
+    const float* Vt = reinterpret_cast<const float*>(In + Lay::iV) + l * LDT;
+    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + l * LDT;
+    const float* be = reinterpret_cast<const float*>(In + Lay::iB);
+    const float* Yt = reinterpret_cast<const float*>(R + Lay::rY) + l * LDT;
+    const int g = l >> 4, c = l & 15;
+    // Every LDS read of the step first (the compiler keeps LDS reads below
+    // earlier LDS writes it cannot tell apart, so reads issued late would each
+    // wait out the LDS latency inside the substitution).
+    float yv[SC], rr[SC], vv[SC], bv[SC], gt[SC][SC];
+    ld16(Yt, yv);
+    ld16(Rt, rr);
+    ld16(Vt, vv);
+    ld16(be, bv);
+    const float* GT = reinterpret_cast<const float*>(R + Lay::rG);
+#pragma unroll
+    for (int u = 0; u < SC - 1; ++u) ld16(GT + u * LDT, gt[u]);  // column u of beta G (uniform: broadcast reads)
+    float ks[SC];
+    // the cross term C_n (lambda w)_(n-1) on the matrix cores, back through LDS to one lane per channel
+    if (n >= 1) {
+      const char* Rp = ring(smem, n - 1);
+      const u32x2 cA = *reinterpret_cast<const u32x2*>(R + Lay::rC + 8 * l);
+      const __bf16* XL = reinterpret_cast<const __bf16*>(Rp + Lay::rXL);
+      u32x2 xl[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xl[t] = *reinterpret_cast<const u32x2*>(XL + (16 * t + c) * LDX + 4 * g);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 x = mma2(cA, z4(), xl[t], z4(), zero4());  // lane (g, c): tokens 4g + j, channel 16t + c
+        *reinterpret_cast<f32x4*>(CX + (16 * t + c) * LDT + 4 * g) = x;
+      }
+      wave_sync_lds();
+      float cx[SC];
+      ld16(CX + l * LDT, cx);
+#pragma unroll
+      for (int t = 0; t < SC; ++t) ks[t] = ge_prev * yv[t] + cx[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < SC; ++t) ks[t] = yv[t];
+    }
+    // w_t = beta_t (v_t - g'_t (K S)_t) - sum_{u<t} beta_t G_tu D'_tu w_u, Horner over u
+    float w[SC], acc[SC];
+#pragma unroll
+    for (int t = 0; t < SC; ++t) acc[t] = 0.f;
+    float gp = 1.f;  // g'_t
+#pragma unroll
+    for (int u = 0; u < SC; ++u) {
+      w[u] = bv[u] * (vv[u] - gp * ks[u]) - acc[u];
+      gp *= rr[u];
+#pragma unroll
+      for (int t = u + 1; t < SC; ++t) acc[t] = acc[t] * rr[u] + gt[u][t] * w[u];
+    }
+    // lambda_u = prod_{u<i<=15} r_i; (lambda w) as bf16 B operands, w for the output, g_15
+    __bf16* XLn = reinterpret_cast<__bf16*>(R + Lay::rXL) + l * LDX;
+    float* Wn = reinterpret_cast<float*>(R + Lay::rW) + l * LDT;
+    float lam = 1.f, xl[SC];
+#pragma unroll
+    for (int u = SC - 1; u >= 0; --u) {
+      xl[u] = lam * w[u];
+      lam *= rr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < SC; u += 4) {
+      *reinterpret_cast<u32x2*>(XLn + u) = cvt4(f32x4{xl[u], xl[u + 1], xl[u + 2], xl[u + 3]});
+      Wn[u] = w[u];
+      Wn[u + 1] = w[u + 1];
+      Wn[u + 2] = w[u + 2];
+      Wn[u + 3] = w[u + 3];
+    }
+    reinterpret_cast<float*>(R + Lay::rGE)[l] = lam;
+    ge_prev = lam;
+  });
+}
+
+// ----------------------------------------------------------- output wave
+__device__ void output_role(const Args& a, int b, int h, char* smem, int l) {
+  const int H = a.H, T = a.T;
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(a.out + ((size_t)b * T * H + h) * D, span_bytes((size_t)T * H * D * 2, (size_t)h * D * 2));
+  const int rowO = H * D * 2;
+  run(a.nsub, [&](int n) {
+    const int m = n - 1;  // sub-chunk finished in this step
+    if (m < 0 || m >= a.nsub) return;
+    const char* In = in_slot(smem, m);
+    const char* R = ring(smem, m);
+    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + l * LDT;
+    const float* QS = reinterpret_cast<const float*>(R + Lay::rQS) + l * LDT;
+    const float* W = reinterpret_cast<const float*>(R + Lay::rW) + l * LDT;
+    const float* PT = reinterpret_cast<const float*>(R + Lay::rP);
+    float rr[SC], w[SC], qs[SC], y[SC], pt[SC][SC];
+    ld16(Rt, rr);
+    ld16(W, w);
+    ld16(QS, qs);
+#pragma unroll
+    for (int u = 0; u < SC; ++u) ld16(PT + u * LDT, pt[u]);  // column u of P (uniform over the lanes)
+#pragma unroll
+    for (int t = 0; t < SC; ++t) y[t] = 0.f;
+    // y_t = sum_{u<=t} P_tu D_tu w_u, Horner over u
+#pragma unroll
+    for (int u = 0; u < SC; ++u)
+#pragma unroll
+      for (int t = u; t < SC; ++t) y[t] = y[t] * rr[u] + pt[u][t] * w[u];
+    float gm = 1.f;
+#pragma unroll
+    for (int t = 0; t < SC; ++t) {
+      gm *= rr[t];
+      const float o = gm * qs[t] + y[t];
+      const unsigned short ob = __builtin_bit_cast(unsigned short, __float2bfloat16(o));
+      __builtin_amdgcn_raw_buffer_store_b16(ob, ro, 2 * l, (m * SC + t) * rowO, 0);
+    }
+  });
+}
+
+// ----------------------------------------------------------- loader wave
+// Sub-chunk m in step m - 2, from registers loaded two steps earlier.  Tokens past
+// T read k = q = v = 0, r = 1, beta = 0: the identity step.
+__device__ void loader_role(const Args& a, int b, int h, char* smem, int l) {
+  const int H = a.H, T = a.T;
+  const size_t tokbase = (size_t)b * T * H + h;
+  const uint32_t span = span_bytes((size_t)T * H * D * 2, (size_t)h * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + tokbase * D, span), rq = make_rsrc(a.q + tokbase * D, span),
+                               rv = make_rsrc(a.v + tokbase * D, span);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.r + tokbase * D, span_bytes((size_t)T * H * D * 4, (size_t)h * D * 4));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + tokbase, span_bytes((size_t)T * H * 4, (size_t)h * 4));
+  const int rowB = H * D * 2, rowF = H * D * 4;
+  // lane l: token l / 4 of the sub-chunk, channels / keys 16 (l % 4) .. + 15
+  const int tk = l >> 2, cq = 16 * (l & 3);
+  struct Set {
+    u32x4 k[2], q[2], v[2];
+    f32x4 r[4];
+    float be;
+  };
+  Set st[2];
+  auto load = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    const int t0 = m * SC;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int off = tk * rowB + 2 * (cq + 8 * e);
+      st[s].k[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, t0 * rowB, 0));
+      st[s].q[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, t0 * rowB, 0));
+      st[s].v[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, t0 * rowB, 0));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      st[s].r[e] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, tk * rowF + 4 * (cq + 4 * e), t0 * rowF, 0));
+    st[s].be = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (l & 15) * H * 4, t0 * H * 4, 0));
+  };
+  auto publish = [&](auto sc, int m) {
+    constexpr int s = decltype(sc)::value;
+    char* const In = in_slot(smem, m);
+    const bool live = m * SC + tk < T;
+    __bf16* K = reinterpret_cast<__bf16*>(In + Lay::iK);
+    __bf16* Q = reinterpret_cast<__bf16*>(In + Lay::iQ);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      *reinterpret_cast<u32x4*>(K + tk * LDK + cq + 8 * e) = st[s].k[e];
+      *reinterpret_cast<u32x4*>(Q + tk * LDK + cq + 8 * e) = st[s].q[e];
+    }
+    float* Vt = reinterpret_cast<float*>(In + Lay::iV);
+    float* Rt = reinterpret_cast<float*>(In + Lay::iR);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const unsigned wv = st[s].v[e][x];
+        Vt[(cq + 8 * e + 2 * x) * LDT + tk] = lo_f(wv);
+        Vt[(cq + 8 * e + 2 * x + 1) * LDT + tk] = hi_f(wv);
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) Rt[(cq + 4 * e + x) * LDT + tk] = live ? st[s].r[e][x] : 1.f;
+    if (l < 16) reinterpret_cast<float*>(In + Lay::iB)[l] = m * SC + l < T ? st[s].be : 0.f;
+  };
+  auto clampm = [&](int m) { return __builtin_amdgcn_readfirstlane(max(0, min(m, a.nsub - 1))); };
+  load(ic<0>{}, clampm(0));
+  issue_fence();
+  load(ic<1>{}, clampm(1));
+  issue_fence();
+  // Step n publishes sub-chunk n + 2 from set n & 1 and refills it with
+  // sub-chunk n + 4; whole pairs of steps (n = -2 .. last_step).
+  __builtin_assume(a.nsub >= 0);
+  const int last = last_step(a.nsub);
+  for (int n = -2; n <= last; n += 2) {
+    if (n + 2 < a.nsub) publish(ic<0>{}, n + 2);
+    issue_fence();
+    load(ic<0>{}, clampm(n + 4));
+    issue_fence();
+    stage_barrier();
+    if (n + 3 < a.nsub) publish(ic<1>{}, n + 3);
+    issue_fence();
+    load(ic<1>{}, clampm(n + 5));
+    issue_fence();
+    stage_barrier();
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void channel_chunk_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) char smem[Lay::bytes];
+  const int chain = blockIdx.x, b = chain / a.H, h = chain % a.H;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (w == 0)
+    state_role(a, chain, smem, l);
+  else if (w == 1)
+    solver_role(a, smem, l);
+  else if (w == 2)
+    output_role(a, b, h, smem, l);
+  else
+    loader_role(a, b, h, smem, l);
+}
+
+}  // namespace chc
+
+hipError_t launch_channel_chunk(const ChannelArgs& a) {
+  chc::Args x{};
+  x.q = static_cast<const __bf16*>(a.q);
+  x.k = static_cast<const __bf16*>(a.k);
+  x.v = static_cast<const __bf16*>(a.v);
+  x.r = a.r;
+  x.beta = a.beta;
+  x.S0 = a.S0;
+  x.out = static_cast<__bf16*>(a.out);
+  x.Sf = a.S_final;
+  x.T = a.T;
+  x.H = a.H;
+  x.nsub = (a.T + chc::SC - 1) / chc::SC;
+  return launch_kernel(chc::channel_chunk_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(256), (hipStream_t)a.stream,
+                       x);
+}
+
+}  // namespace gdn

@@ -193,6 +193,11 @@ int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const flo
     if (p && !aligned16(p)) return GDN_ERR_ALIGN;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::ChannelArgs a{q, k, v, r, beta, S0, out, S_final, B, T, H, dtype, stream};
+  // bf16: the chunk form (per-channel triangular solves, the state on the
+  // matrix cores) while rows are addressable with 32-bit buffer offsets;
+  // otherwise, and for fp32 inputs, the token loop.
+  if (dtype == GDN_BF16 && (long long)T * H * dk * 4 < (1LL << 31))
+    return gdn::launch_channel_chunk(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_channel_decay(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

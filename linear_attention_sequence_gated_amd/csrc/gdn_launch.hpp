@@ -105,6 +105,7 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
-hipError_t launch_channel_decay(const ChannelArgs& a);
+hipError_t launch_channel_decay(const ChannelArgs& a);  // token loop (fp32 inputs)
+hipError_t launch_channel_chunk(const ChannelArgs& a);  // chunk form on the matrix cores (bf16 inputs)
 
 }  // namespace gdn

@@ -1,5 +1,6 @@
 """Per-output-channel decay (gdn_fwd_channel_decay) on the GPU through the C ABI, against the fp64 oracle
-(oracle/channel_decay.py)."""
+(oracle/channel_decay.py).  bf16 inputs run the chunk form (16-token sub-chunks, one triangular solve per value
+channel); fp32 inputs the token loop."""
 import numpy as np
 import pytest
 
@@ -69,3 +70,43 @@ def test_channel_decay_full_size_all_chains():
     o, S = run(inp, "bf16")
     o_ref, S_ref = ref(inp)
     assert_close("chd_full", "bf16", o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33, 250])
+def test_channel_decay_chunk_form_lengths(T):
+    """bf16 (chunk form): lengths around the 16-token sub-chunk, with S0 given and S_final aliasing S0."""
+    inp = gen_channel_decay(2, T, 3, 64, dtype="bf16", seed=50 + T, s0_var=0.1)
+    note(f"channel decay chunk form T={T}")
+    o, S = run(inp, "bf16", alias=True)
+    o_ref, S_ref = ref(inp)
+    assert_close(f"chd_chunk_len{T}", "bf16", o, S, o_ref, S_ref)
+
+
+def test_channel_decay_chunk_form_extreme_decays():
+    """Decay factors at their extremes on random tokens and channels: r = 1e-6 (the channel is wiped) or 1 (kept),
+    beta at 0 or 2; the substitution forms decay products by Horner's rule, so nothing overflows."""
+    inp = gen_channel_decay(2, 300, 2, 64, dtype="bf16", seed=61, s0_var=0.1)
+    rng = np.random.default_rng(3)
+    pr, pb = rng.random(inp["r"].shape), rng.random(inp["beta"].shape)
+    inp["r"] = np.where(pr < 0.1, 1e-6, np.where(pr < 0.3, 1.0, inp["r"])).astype(np.float32)
+    inp["beta"] = np.where(pb < 0.1, 0.0, np.where(pb < 0.2, 2.0, inp["beta"])).astype(np.float32)
+    note("channel decay chunk form, extreme decays")
+    o, S = run(inp, "bf16")
+    o_ref, S_ref = ref(inp)
+    assert_close("chd_chunk_extreme", "bf16", o, S, o_ref, S_ref)
+
+
+def test_channel_decay_chunk_form_unit_decay_equals_delta_rule():
+    """bf16: r = 1 on every channel gives the chunk forward at alpha = 1 (two different kernels, each within the
+    bf16 bound of the oracle)."""
+    torch = torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    inp = gen_channel_decay(2, 190, 2, 64, dtype="bf16", seed=8, s0_var=0.1)
+    inp["r"] = np.ones_like(inp["r"])
+    ones = np.ones_like(inp["beta"])
+    note("channel decay chunk form r = 1 vs the chunk forward at alpha = 1")
+    o1, S1 = run(inp, "bf16")
+    o2, S2 = gdn.chunk_fwd(up(inp["q"], "bf16"), up(inp["k"], "bf16"), up(inp["v"], "bf16"), up(ones, "f32"),
+                           up(inp["beta"], "f32"), up(inp["S0"], "f32"))
+    torch.cuda.synchronize()
+    assert_close("chd_chunk_vs_delta_rule", "bf16", o1, S1, o2.float().cpu().numpy(), S2.cpu().numpy())
