@@ -8,22 +8,10 @@
 // bandwidth, vector-ALU issue (a wave64 instruction occupies its SIMD for four
 // cycles) and matrix-core issue -- are spread over the four SIMDs.
 //
-// Two kernels.  The three-stage kernel (namespace pipe3, d = 64, below) is
-// the one used at d = 64.  The two-stage kernel here runs d = 128: one
-// workgroup of 6 waves per (batch, head, 16 value columns), so a head's
-// columns are spread over eight CUs, with two barriers per chunk.  While the
-// CONSUMER wave runs chunk n out of LDS buffer n & 1, the five PRODUCER waves
-// fill buffer (n + 1) & 1 for chunk n + 1 from registers loaded from HBM a
-// chunk ahead:
-//
-//   consumer    16 value columns (one MFMA tile).
-//   row Gram    row blocks {0,1} / {2,3}: K and Q as whole rows from HBM,
-//               published to LDS in phase A (operands read back from there),
-//               tiles (i,i), (i+1,i), (i+1,i+1) of Q K^T and the sub-diagonal
-//               tile of K K^T, and the inverse of diagonal block i.
-//   lower Gram  row block i = 2 / 3: tiles (i,0), (i,1) of K K^T and Q K^T,
-//               and the inverse of diagonal block 1 / 3, in phase B.
-//   V wave      the V tile, gamma and lambda, in phase A.
+// The three-stage kernel below (namespace pipe3) runs bf16 at d = 64 with
+// enough chains to fill the CUs, and the fused input prologue.  Namespace pipe
+// holds its configuration, the consumer waves' state and the decayed-tile and
+// output helpers.
 //
 // With S the state at the chunk start, g the within-chunk prefix sum of
 // log alpha, gamma_r = exp(g_r), lambda_r = exp(g_C - g_r), Gamma_rs =
@@ -34,9 +22,8 @@
 // so beta only enters through the producer-built factors T_ii diag(beta_i);
 //     O  = gamma * (Q S) + lower(Q K^T * Gamma) Ut,
 //     S <- gamma_C S + K^T (lambda * Ut).
-// Diagonal blocks are inverted by row-owner forward substitution: lane (g, c)
-// owns row c of the inverse and each finished row is broadcast along the
-// 16-lane rows with DPP row_newbcast.
+// Diagonal blocks are inverted by row-owner forward substitution (each
+// finished row broadcast along the 16-lane rows with DPP row_newbcast).
 //
 // Global traffic uses buffer loads/stores whose range check implements the
 // ragged tail (rows >= T read as zero and are never written).  Decay factors
@@ -53,11 +40,8 @@
 namespace gdn {
 namespace pipe {
 
-
 template <int DK> struct Cfg {
-  // Value columns per workgroup: 32 at d = 64 (two consumer waves), 16 at
-  // d = 128 (one), so that a d = 128 layer has twice the workgroups to fill
-  // the CUs; the per-step work of a consumer and of the producers is the same.
+  // Value columns per workgroup: 32 at d = 64 (two consumer waves).
   static constexpr int NV = DK == 64 ? 32 : 16;
   static constexpr int NT = 1;               // 16-column tiles per consumer wave
   static constexpr int NCONS = NV / 16;      // consumer waves
@@ -98,16 +82,6 @@ struct Ctx {
 };
 
 // ---------------------------------------------------------------- producers
-// Per-token gates of chunk c0: g (log2 units, inclusive prefix of log2 alpha)
-// in lane l, written with beta to the wave's private table.
-__device__ __forceinline__ float gate_scan(float pa, float pb, int c0, int T, int l, float* PGT) {
-  const float a = (c0 + l < T) ? pa : 1.f;  // padding token: alpha = 1 (beta reads as 0)
-  const float x = wave_prefix_sum(__builtin_amdgcn_logf(a));
-  PGT[l] = x;
-  PGT[64 + l] = pb;
-  return x;
-}
-
 // Decay factors of diagonal block i: lane (g, c) gets Gamma[r][s] for r = 16i + c,
 // s = 16i + 4g + j, masked to 0 for s > r before the exponential.
 __device__ __forceinline__ f32x4 diag_gamma(const float* PGT, int i, int g, int c) {
@@ -118,54 +92,6 @@ __device__ __forceinline__ f32x4 diag_gamma(const float* PGT, int i, int g, int 
   for (int j = 0; j < 4; ++j) gm[j] = __builtin_amdgcn_exp2f(c >= 4 * g + j ? gr - gs[j] : -INFINITY);
   return gm;
 }
-
-// One forward-substitution step m for the four columns a lane owns:
-// t_j += row_bcast<m>(t_j) * a_m, fused into one DPP instruction per column.
-#define GDN_INV_STEP(M, A)                                                               \
-  "v_fmac_f32_dpp %0, %0, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
-  "v_fmac_f32_dpp %1, %1, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
-  "v_fmac_f32_dpp %2, %2, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"     \
-  "v_fmac_f32_dpp %3, %3, %" #A " row_newbcast:" #M " row_mask:0xf bank_mask:0xf\n"
-
-// T_ii diag(beta_i) for diagonal block i.  G is its Gram accumulator (lane
-// (g, c) holds k_s . k_r, r = 16i + c, s = 16i + 4g + j; K K^T is symmetric, so
-// it is also row c of the block) and gm its decay factors.  (I + A)^{-1} with
-// A = diag(beta) Gt_ii strictly lower is found by forward substitution: lane
-// (g, c) owns row c, and once row m is final it is broadcast along each row of
-// 16 lanes (DPP row_newbcast) and added, scaled by -A[c][m], to every later row.
-// The four column chains are interleaved, so each DPP source was written three
-// instructions earlier (two wait states are required); the leading s_nop covers
-// the instructions before the block.
-template <int DK>
-__device__ __forceinline__ void diag_inverse(const f32x4& G, const f32x4& gm, const float* PGT, float* ds, int i,
-                                             int g, int c, __bf16* dst) {
-  const float br = PGT[64 + 16 * i + c];
-  f32x4 na;  // -A[c][4g + j]
-#pragma unroll
-  for (int j = 0; j < 4; ++j) na[j] = c > 4 * g + j ? -br * gm[j] * G[j] : 0.f;
-  *reinterpret_cast<f32x4*>(ds + c * 20 + 4 * g) = na;
-  float a[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(ds + c * 20 + 4 * q);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
-  }
-  float t0 = c == 4 * g ? 1.f : 0.f, t1 = c == 4 * g + 1 ? 1.f : 0.f;
-  float t2 = c == 4 * g + 2 ? 1.f : 0.f, t3 = c == 4 * g + 3 ? 1.f : 0.f;
-  asm volatile("s_nop 1\n"
-               GDN_INV_STEP(0, 4) GDN_INV_STEP(1, 5) GDN_INV_STEP(2, 6) GDN_INV_STEP(3, 7) GDN_INV_STEP(4, 8)
-               GDN_INV_STEP(5, 9) GDN_INV_STEP(6, 10) GDN_INV_STEP(7, 11) GDN_INV_STEP(8, 12) GDN_INV_STEP(9, 13)
-               GDN_INV_STEP(10, 14) GDN_INV_STEP(11, 15) GDN_INV_STEP(12, 16) GDN_INV_STEP(13, 17)
-               GDN_INV_STEP(14, 18)
-               : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3)
-               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-                 "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]));
-  const f32x4 bs = *reinterpret_cast<const f32x4*>(PGT + 64 + 16 * i + 4 * g);
-  const f32x4 t{t0 * bs[0], t1 * bs[1], t2 * bs[2], t3 * bs[3]};
-  *reinterpret_cast<u32x2*>(dst + c * Cfg<DK>::LD16 + 4 * g) = cvt4(t);
-}
-#undef GDN_INV_STEP
 
 // Decayed Gram tile (row block i, column block j < i, so every r > s):
 // -Gt from the K K^T accumulator and P from the Q K^T accumulator.
@@ -192,259 +118,6 @@ __device__ __forceinline__ void diag_p_tile(const f32x4& P, const f32x4& gm, int
   using Cf = Cfg<DK>;
   const f32x4 pv{gm[0] * P[0], gm[1] * P[1], gm[2] * P[2], gm[3] * P[3]};
   *reinterpret_cast<u32x2*>(R + Cf::oP + tri(i, i) * Cf::szTile + c * Cf::LD16 + 4 * g) = cvt4(pv);
-}
-
-// One pipelined producer role: loads for chunk n + 2 are issued before chunk
-// n + 1 is processed; register set and stage buffer are chosen by parity.
-// Loads are unconditional (clamped to the last chunk; with no chunk at all the
-// zero buffer range drops them) and steps come in whole pairs, so the loop has
-// no conditional load path and the compiler keeps the next chunk's loads in
-// flight while this one is processed.  Each step has two barriers: the row
-// waves publish the chunk's K and Q rows in phase A, and the lower Gram waves
-// read them after the mid-step barrier, in phase B, instead of fetching them
-// from HBM again.  The consumers run the same barriers.
-template <class Load, class ProcA, class ProcB>
-__device__ __forceinline__ void producer_loop(int nch, Load&& load, ProcA&& procA, ProcB&& procB) {
-  // Clamped chunk index, kept in a scalar register: buffer-load offsets the
-  // compiler cannot prove uniform become per-lane loops.
-  auto clampc = [&](int m) { return __builtin_amdgcn_readfirstlane(max(0, min(m, nch - 1))); };
-  load(ic<0>{}, clampc(0));
-  issue_fence();
-  load(ic<1>{}, clampc(1));
-  issue_fence();
-  if (nch > 0) procA(ic<0>{}, 0);
-  stage_barrier();
-  if (nch > 0) procB(ic<0>{}, 0);
-  stage_barrier();
-  auto iter = [&](auto pc, int n) {
-    constexpr int par = decltype(pc)::value;
-    // Phase A first (it only moves registers of chunk n + 1 to LDS), so the
-    // mid-step barrier is not held up by issuing chunk n + 2's loads.
-    if (n + 1 < nch) procA(ic<par ^ 1>{}, n + 1);
-    issue_fence();
-    load(ic<par>{}, clampc(n + 2));
-    issue_fence();
-    stage_barrier();
-    if (n + 1 < nch) procB(ic<par ^ 1>{}, n + 1);
-    stage_barrier();
-  };
-  for (int n = 0; n < nch; n += 2) {
-    iter(ic<0>{}, n);
-    iter(ic<1>{}, n + 1);
-  }
-}
-
-// Row Gram waves of the two-stage kernel: row blocks b0 and b0 + 1 (b0 = 0 or 2).
-template <int DK>
-__device__ __forceinline__ void producer_rows(const Ctx& x, char* smem, int b0, int l) {
-  using Cf = Cfg<DK>;
-  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
-  const int wi = b0 >> 1;
-  float* const PGT = sf + Cf::fPGT + wi * Cf::szPGT;
-  float* const DS = sf + Cf::fDS + wi * Cf::szDS;
-  const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
-  const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanK = span_bytes((size_t)T * H * DK * 2, (size_t)x.h * DK * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(x.qg + tokbase * DK, spanK);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(x.kg + tokbase * DK, spanK);
-  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
-  const int rowK = H * DK * 2;
-  // Loads read whole rows (DK / 8 lanes of 16 bytes per row): load (e, p) gives
-  // lane l 16 bytes of row 16 b0 + RPI (e NKP + p) + l / NL.  Per-CU load
-  // throughput scales with the cache lines an instruction touches, and MFMA
-  // operand order (16 rows of 64 bytes per instruction) touches more.  The
-  // rows go to LDS row-major in phase A and the operands are read back from
-  // there in phase B.
-  constexpr int NL = DK / 8, RPI = 64 / NL;
-  static_assert(2 * NKP * RPI == 32, "the loads cover the wave's 32 rows");
-  int vofs[2][NKP], lofs[2][NKP];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      const int row = 16 * b0 + RPI * (e * NKP + p) + l / NL;
-      vofs[e][p] = row * rowK + 16 * (l % NL);
-      lofs[e][p] = row * LDK + 8 * (l % NL);
-    }
-
-  struct Set {
-    u32x4 k[2][NKP], q[2][NKP];
-    float a, b;
-  };
-  Set st[2];
-  auto load = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    const int c0 = n * 64;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        st[s].k[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vofs[e][p], c0 * rowK, 0));
-        st[s].q[e][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vofs[e][p], c0 * rowK, 0));
-      }
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
-  };
-  auto procA = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;  // register set == stage buffer == n & 1
-    const Set& S = st[s];
-    __bf16* const R = sb + s * Cf::szBuf;
-    // K and Q rows of both blocks, for this wave, the lower Gram waves and
-    // the consumers
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        *reinterpret_cast<u32x4*>(R + Cf::oK + lofs[e][p]) = S.k[e][p];
-        *reinterpret_cast<u32x4*>(R + Cf::oQ + lofs[e][p]) = S.q[e][p];
-      }
-  };
-  auto process = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    const Set& S = st[s];
-    __bf16* const R = sb + s * Cf::szBuf;
-    u32x4 kk[2][NKP], qq[2][NKP];  // MFMA operands: lane (g, c) holds row c, k = 32 p + 8 g .. + 7
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        const int o = (16 * (b0 + e) + c) * LDK + 32 * p + 8 * g;
-        kk[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
-        qq[e][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + o);
-      }
-    gate_scan(S.a, S.b, n * 64, T, l, PGT);
-    // accumulator [s][r]: s from the A operand (column block), r from the B
-    // operand (row block)
-    f32x4 Gd = zero4(), Go = zero4(), P0 = zero4(), P1 = zero4(), Po = zero4();
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      Gd = mma32(kk[0][p], kk[0][p], Gd);
-      P0 = mma32(kk[0][p], qq[0][p], P0);
-      Go = mma32(kk[0][p], kk[1][p], Go);
-      Po = mma32(kk[0][p], qq[1][p], Po);
-      P1 = mma32(kk[1][p], qq[1][p], P1);
-    }
-    offdiag_tiles<DK>(Go, Po, PGT, b0 + 1, b0, g, c, R);
-    const f32x4 gm0 = diag_gamma(PGT, b0, g, c), gm1 = diag_gamma(PGT, b0 + 1, g, c);
-    diag_p_tile<DK>(P0, gm0, b0, g, c, R);
-    diag_p_tile<DK>(P1, gm1, b0 + 1, g, c, R);
-    diag_inverse<DK>(Gd, gm0, PGT, DS, b0, g, c, R + Cf::oTP + b0 * Cf::szTile);
-  };
-  producer_loop(x.nchunks, load, procA, process);
-}
-
-// Lower Gram waves of the two-stage kernel: row block i = 2 / 3 below the
-// first two column blocks, tiles (i, 0) and (i, 1), and the inverse of
-// diagonal block 1 / 3, from the K and Q rows the row waves publish in phase A
-// of the same step.
-template <int DK>
-__device__ __forceinline__ void producer_lower(const Ctx& x, char* smem, int i, int l) {
-  using Cf = Cfg<DK>;
-  constexpr int NKP = Cf::NKP, LDK = Cf::LDK;
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
-  float* const PGT = sf + Cf::fPGT + i * Cf::szPGT;  // tables 2 and 3
-  float* const DS = sf + Cf::fDS + i * Cf::szDS;
-  const int g = l >> 4, c = l & 15, H = x.H, T = x.T;
-  const int id = i == 2 ? 1 : 3;  // diagonal block inverted here
-  const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)x.h * 4);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, spanG);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.beta + tokbase, spanG);
-  struct Set {
-    float a, b;
-  };
-  Set st[2];
-  auto load = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    const int c0 = n * 64;
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-    st[s].b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, c0 * H * 4, 0));
-  };
-  // Phase B: the chunk's K and Q rows, published by the row waves in phase A.
-  auto process = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    const Set& S = st[s];
-    __bf16* const R = sb + s * Cf::szBuf;
-    u32x4 k0[NKP], k1[NKP], ki[NKP], qi[NKP];
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      const int o = c * LDK + 32 * p + 8 * g;
-      k0[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + o);
-      k1[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * LDK + o);
-      ki[p] = *reinterpret_cast<const u32x4*>(R + Cf::oK + 16 * i * LDK + o);
-      qi[p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + o);
-    }
-    gate_scan(S.a, S.b, n * 64, T, l, PGT);
-    f32x4 G0 = zero4(), P0 = zero4(), G1 = zero4(), P1 = zero4(), Gd = zero4();
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-      G0 = mma32(k0[p], ki[p], G0);
-      P0 = mma32(k0[p], qi[p], P0);
-      G1 = mma32(k1[p], ki[p], G1);
-      P1 = mma32(k1[p], qi[p], P1);
-      const u32x4 kd = id == 1 ? k1[p] : ki[p];  // uniform choice
-      Gd = mma32(kd, kd, Gd);
-    }
-    offdiag_tiles<DK>(G0, P0, PGT, i, 0, g, c, R);
-    offdiag_tiles<DK>(G1, P1, PGT, i, 1, g, c, R);
-    diag_inverse<DK>(Gd, diag_gamma(PGT, id, g, c), PGT, DS, id, g, c, R + Cf::oTP + id * Cf::szTile);
-  };
-  producer_loop(x.nchunks, load, [](auto, int) {}, process);
-}
-
-// The 64 x NV V tile of the chunk (NVU 16-byte units per row, one per lane and
-// load), and gamma, lambda and gamma_C.
-template <int DK>
-__device__ __forceinline__ void producer_v(const Ctx& x, char* smem, int l) {
-  using Cf = Cfg<DK>;
-  constexpr int LDV = Cf::LDV, NVU = Cf::NVU;
-  __bf16* const sb = reinterpret_cast<__bf16*>(smem);
-  float* const sf = reinterpret_cast<float*>(smem + Cf::fBase);
-  const int H = x.H, T = x.T, DV = x.DV;
-  const size_t tokbase = (size_t)x.b * T * H + x.h;
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(x.vg + tokbase * DV + x.dv0, span_bytes((size_t)T * H * DV * 2, ((size_t)x.h * DV + x.dv0) * 2));
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.alpha + tokbase, span_bytes((size_t)T * H * 4, (size_t)x.h * 4));
-  const int rowV = H * DV * 2;
-  int vof[NVU], lof[NVU];
-#pragma unroll
-  for (int u = 0; u < NVU; ++u) {
-    const int unit = l + 64 * u, row = unit / NVU, cu = unit % NVU;
-    vof[u] = row * rowV + cu * 16;
-    lof[u] = row * LDV + cu * 8;
-  }
-  struct Set {
-    u32x4 v[NVU];
-    float a;
-  };
-  Set st[2];
-  auto load = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    const int c0 = n * 64;
-#pragma unroll
-    for (int u = 0; u < NVU; ++u)
-      st[s].v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vof[u], c0 * rowV, 0));
-    st[s].a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, c0 * H * 4, 0));
-  };
-  auto process = [&](auto sc, int n) {
-    constexpr int s = decltype(sc)::value;
-    __bf16* const R = sb + s * Cf::szBuf;
-#pragma unroll
-    for (int u = 0; u < NVU; ++u) *reinterpret_cast<u32x4*>(R + Cf::oV + lof[u]) = st[s].v[u];
-    const float a = (n * 64 + l < T) ? st[s].a : 1.f;
-    const float xg = wave_prefix_sum(__builtin_amdgcn_logf(a));
-    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xg), 63));
-    float* G = sf + Cf::fGate + s * Cf::szGate;
-    G[l] = __builtin_amdgcn_exp2f(xg);
-    G[64 + l] = __builtin_amdgcn_exp2f(gC - xg);
-    if (l == 63) G[128] = __builtin_amdgcn_exp2f(gC);
-  };
-  producer_loop(x.nchunks, load, process, [](auto, int) {});
 }
 
 // ---------------------------------------------------------------- output
@@ -564,13 +237,6 @@ struct Consumer {
     f32x4 lm[4];
     float gC;
   };
-  // Operands of the output: Q rows, gamma per token, the ten P tiles.
-  struct OutOps {
-    u32x4 qr[4][NKP];
-    u32x2 Pm[10];
-    float gm[4];
-  };
-
   // Ut = (I + A)^{-1} (diag(beta) V - diag(beta gamma) K S) of the chunk in
   // stage buffer R, block rows in order (after begin() on the same buffer):
   // Xf = Ut and XL = lambda * Ut as bf16 operands.  G holds gamma (G[0..63])
@@ -635,42 +301,6 @@ struct Consumer {
       }
   }
 
-  __device__ __forceinline__ void load_out(const __bf16* R, const float* G, OutOps& op) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int p = 0; p < NKP; ++p) op.qr[i][p] = *reinterpret_cast<const u32x4*>(R + Cf::oQ + 16 * i * LDK + 32 * p + offRow);
-      op.gm[i] = G[16 * i + c];  // gamma of token 16i + c
-    }
-#pragma unroll
-    for (int e = 0; e < 10; ++e) op.Pm[e] = ld4(R + Cf::oP + e * Cf::szTile + offT16);
-  }
-
-  // Output of chunk n from the state at its start (sfr) and Ut.
-  __device__ __forceinline__ void output(const OutOps& op, const u32x2 (&Xf)[4][NT], int n) {
-    const int c0 = n * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const f32x4 o = out_pu(out_qs<NKP>(sfr[t], op.qr[i], op.gm[i]), i, t, Xf, op.Pm);
-        __builtin_amdgcn_raw_buffer_store_b64(cvt4(o), ro, vofO + 32 * t, (c0 + 16 * i) * rowO, 0);
-      }
-  }
-
-  // Rest of chunk n (after begin() on the same stage buffer): the
-  // substitution, the state update and the output.
-  __device__ __forceinline__ void chunk(const __bf16* R, const float* G, int gCoff, int n) {
-    Upd u;
-    u32x2 Xf[4][NT], XL[4][NT];
-    solve(R, G, gCoff, u, Xf, XL, nullptr);
-    OutOps op;  // in flight during the state update
-    load_out(R, G, op);
-    issue_fence();
-    update(u, XL);
-    output(op, Xf, n);
-  }
-
   __device__ __forceinline__ void finish(const Ctx& x) {
     if (!x.Sfg) return;
 #pragma unroll
@@ -683,89 +313,6 @@ struct Consumer {
     }
   }
 };
-
-// Consumer wave(s) of the two-stage kernel.
-template <int DK>
-__device__ __forceinline__ void consumer(const Ctx& x, char* smem, int w, int l) {
-  using Cf = Cfg<DK>;
-  const __bf16* const sb = reinterpret_cast<const __bf16*>(smem);
-  const float* const sf = reinterpret_cast<const float*>(smem + Cf::fBase);
-  Consumer<DK> cs;
-  cs.init(x, w, l);
-  stage_barrier();  // prologue: chunk 0 staged (two barriers, as in every step)
-  stage_barrier();
-  auto body = [&](auto bufc, int n) {
-    constexpr int BUF = decltype(bufc)::value;
-    if (n < x.nchunks) cs.begin(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate);
-    stage_barrier();  // mid-step: the producers' phase A is done
-    if (n < x.nchunks) cs.chunk(sb + BUF * Cf::szBuf, sf + Cf::fGate + BUF * Cf::szGate, 128, n);
-    stage_barrier();
-  };
-  // whole pairs of steps, matching the producers' barrier count
-  for (int n = 0; n < x.nchunks; n += 2) {
-    body(ic<0>{}, n);
-    body(ic<1>{}, n + 1);
-  }
-  cs.finish(x);
-}
-
-template <int DK>
-__global__ __launch_bounds__(Cfg<DK>::kThreads, 1) void chunk_pipe_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
-                                                            const __bf16* __restrict__ vg,
-                                                            const float* __restrict__ alpha,
-                                                            const float* __restrict__ beta, const float* S0g,
-                                                            __bf16* __restrict__ outg, float* Sfg, int T, int H,
-                                                            int DV, int nslices) {
-  __shared__ __attribute__((aligned(16))) char smem[Cfg<DK>::bytes];
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // keep neighbours on one XCD
-  const int slice = bid % nslices, chain = bid / nslices;
-  Ctx x;
-  x.qg = qg;
-  x.kg = kg;
-  x.vg = vg;
-  x.alpha = alpha;
-  x.beta = beta;
-  x.S0g = S0g;
-  x.outg = outg;
-  x.Sfg = Sfg;
-  x.T = T;
-  x.H = H;
-  x.DV = DV;
-  x.b = chain / H;
-  x.h = chain % H;
-  x.chain = chain;
-  x.dv0 = slice * Cfg<DK>::NV;
-  x.nchunks = (T + 63) >> 6;
-  // The wave index is made explicitly uniform: role branches must be scalar
-  // branches, never exec-masked ones, because matrix-core instructions do not
-  // honour the exec mask.
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  // Waves are dealt to the four SIMDs in turn (wave w on SIMD w % 4).  With
-  // one consumer, the V wave (idle after phase A) shares its SIMD, and the
-  // four Gram waves, busy in phase B, get one each.
-  constexpr int NC = Cfg<DK>::NCONS;
-  if constexpr (NC == 1) {
-    if (w == 0)
-      consumer<DK>(x, smem, 0, l);
-    else if (w < 3)
-      producer_rows<DK>(x, smem, 2 * (w - 1), l);
-    else if (w == 4)
-      producer_v<DK>(x, smem, l);
-    else
-      producer_lower<DK>(x, smem, w == 3 ? 2 : 3, l);
-  } else {
-    if (w < NC)
-      consumer<DK>(x, smem, w, l);
-    else if (w < NC + 2)
-      producer_rows<DK>(x, smem, 2 * (w - NC), l);
-    else if (w < NC + 4)
-      producer_lower<DK>(x, smem, w - NC, l);
-    else
-      producer_v<DK>(x, smem, l);
-  }
-}
 
 }  // namespace pipe
 
@@ -1516,14 +1063,6 @@ __global__ __launch_bounds__(kThreads3, 1) void chunk_pipe3_kernel(const __bf16*
 
 }  // namespace pipe3
 
-template <int DK>
-static hipError_t launch_pipe_dk(const ChunkArgs& a) {
-  const int nslices = a.dv / pipe::Cfg<DK>::NV;
-  const long nblk = (long)a.B * a.H * nslices;
-  return launch_kernel(pipe::chunk_pipe_kernel<DK>, dim3((unsigned)nblk), dim3(pipe::Cfg<DK>::kThreads), (hipStream_t)a.stream, a.q, a.k,
-                       a.v, a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices);
-}
-
 hipError_t launch_chunk_pipe(const ChunkArgs& a) {
   if (a.dtype == kDtBF16 && a.dk == 64) {
     const int nslices = a.dv / pipe::Cfg<64>::NV;
@@ -1532,8 +1071,6 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a) {
     return launch_kernel(kern, dim3((unsigned)nblk), dim3(pipe3::kThreads3), (hipStream_t)a.stream, a.q, a.k, a.v,
                          a.alpha, a.beta, a.S0, a.out, a.S_final, a.T, a.H, a.dv, nslices, a.beta_scale);
   }
-  if (a.prologue) return hipErrorInvalidValue;
-  if (a.dtype == kDtBF16 && a.dk == 128) return launch_pipe_dk<128>(a);
   return hipErrorInvalidValue;
 }
 
