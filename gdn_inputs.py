@@ -105,6 +105,10 @@ WORKLOADS = {
     "sykra_layer_bf16_channel_decay": Workload(
         "sykra_layer_bf16_channel_decay", "channel", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="the Sykra-shaped layer with a decay per token and value channel (DeltaPhase section 5)"),
+    "laplace_c64_channel_decay": Workload(
+        "laplace_c64_channel_decay", "channel", "c64", B=4, T=4096, H=8, dk=32, dv=32, seed=6,
+        note="LaplacePhaseCore-shaped: complex keys e^{(sigma + i omega) dt} / sqrt(32), decay per token and "
+             "value channel (DeltaPhase section 5)"),
     "decode_4096x64": Workload(
         "decode_4096x64", "decode", "bf16", N=4096, dk=64, dv=64, steps=64, seed=4,
         s0_var=0.1, note="4096 independent 64x64 states, 64 single-token steps"),
@@ -182,7 +186,12 @@ def gen_channel_decay(B, T, H, d, dtype="bf16", seed=0, alpha_mu=-4.0, s0_var=No
     rng = np.random.default_rng(seed + 2000)
     logit = rng.normal(alpha_mu, 1.0, (B, T, H, d))
     r = np.exp(-(np.maximum(logit, 0.0) + np.log1p(np.exp(-np.abs(logit)))))
-    return dict(q=base["q"], k=base["k"], v=base["v"], r=r.astype(np.float32), beta=base["beta"], S0=base["S0"])
+    k = base["k"]
+    if dtype == "c64":
+        # LaplacePhaseCore-shaped keys e^{(sigma + i omega) dt} / sqrt(d): the unit phasors of gen_chunk times
+        # a per-element modulus e^{sigma dt} with sigma dt ~ U(-0.5, 0].
+        k = (k * np.exp(-rng.uniform(0.0, 0.5, k.shape))).astype(np.complex64)
+    return dict(q=base["q"], k=k, v=base["v"], r=r.astype(np.float32), beta=base["beta"], S0=base["S0"])
 
 
 def gen_workload(w: Workload, **overrides):

@@ -203,23 +203,27 @@ int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *alph
  * rows, one factor per value channel).  With S [dk, dv] (row = key dim),
  * for every value channel j:
  *
- *   e_t[j] = v_t[j] - k_t^T s_j,   s_j <- r_t[j] s_j + beta_t k_t e_t[j],
- *   o_t[j] = q_t^T s_j            (the updated state)
+ *   e_t[j] = v_t[j] - kr_t^T s_j,   s_j <- r_t[j] s_j + beta_t k_t e_t[j],
+ *   o_t[j] = qr_t^T s_j            (the updated state)
  *
- * i.e. S_t = S_{t-1} diag(r_t) + beta_t k_t (v_t - S_{t-1}^T k_t)^T.  With
- * every r_t[j] = 1 it is gdn_chunk_fwd at alpha = 1.  (With r < 1 it differs
- * from gdn_chunk_fwd's ordering, where the gate also scales the erased part.)
+ * with kr = k, qr = q for real data and kr = conj(k), qr = conj(q) for
+ * complex data (LaplacePhaseCore's keys are complex, e^{s dt}), i.e.
+ * S_t = S_{t-1} diag(r_t) + beta_t k_t (v_t - S_{t-1}^T kr_t)^T.  With every
+ * r_t[j] = 1 it is gdn_chunk_fwd at alpha = 1.  (With r < 1 it differs from
+ * gdn_chunk_fwd's ordering, where the gate also scales the erased part.)
  *
  *   q, k     [B, T, H, dk]  dtype    keys of norm <= 1 for a stable update
  *   v        [B, T, H, dv]  dtype
  *   r        [B, T, H, dv]  float32  decay per token and value channel, in (0, 1]
  *   beta     [B, T, H]      float32
- *   S0       [B, H, dk, dv] float32  may be NULL (zero)
+ *   S0       [B, H, dk, dv] state    may be NULL (zero)
  *   out      [B, T, H, dv]  dtype, written
- *   S_final  [B, H, dk, dv] float32, written; may be NULL, may equal S0
+ *   S_final  [B, H, dk, dv] state, written; may be NULL, may equal S0
  *
- * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0;
- * otherwise GDN_ERR_UNSUPPORTED.  fp32 arithmetic.  No workspace.  B * H == 0
+ * The state is float32 for real data and complex64 (interleaved re, im) for
+ * GDN_C64.  Supported: dtype GDN_F32 or GDN_BF16 with dk == dv == 64, or
+ * GDN_C64 with dk == dv == 32, any T >= 0; otherwise GDN_ERR_UNSUPPORTED.
+ * fp32 arithmetic.  No workspace.  B * H == 0
  * is a no-op; T == 0 copies S0 (or zeros) to S_final.  Errors as for
  * gdn_chunk_fwd.
  */

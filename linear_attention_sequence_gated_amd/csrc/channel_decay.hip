@@ -1,5 +1,7 @@
-// channel_decay.hip -- the delta rule with a per-output-channel decay, real
-// data, d_k = d_v = 64 (fp32 or bf16 q, k, v; fp32 decay, beta and state).
+// channel_decay.hip -- the delta rule with a per-output-channel decay, token
+// by token: real data with d_k = d_v = 64 (fp32 or bf16 q, k, v; fp32 decay,
+// beta and state) and complex data with d_k = d_v = 32 (complex64 q, k, v and
+// state; real decay and beta).
 //
 // DeltaPhase README, section 2 (the gated-decay variant that LaplacePhaseCore
 // implements) and section 5 (the decay diag(r_t) on the memory's output rows):
@@ -7,7 +9,7 @@
 // written along the key.  With the state S [dk, dv] the output rows of the
 // memory are the columns of S, and column j evolves on its own:
 //   e_j = v_j - k^T s_j,   s_j <- r_j s_j + beta k e_j,   o_j = q^T s_j.
-// This token loop is the reference-shaped kernel for short or odd shapes.  A
+// The real token loop serves fp32 inputs (bf16 takes the chunk form).  A
 // lane quad holds one column: lane l of wave w owns column 16 w + l / 4 and
 // rows 16 (l % 4) .. + 15.  k^T s_j and q^T s_j are 16-term in-lane sums and
 // two DPP adds.  Keys and queries are read from global memory by every lane
@@ -107,9 +109,109 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
   }
 }
 
+// Complex data, d_k = d_v = 32 (LaplacePhaseCore's keys are complex,
+// e^{s dt} with Re(s) <= 0; DeltaPhase README, section 5): the same rule with
+// the read through the conjugated key and query,
+//   e_j = v_j - sum_i conj(k_i) s_ij,   s_ij <- r_j s_ij + beta k_i e_j,
+//   o_j = sum_i conj(q_i) s_ij,
+// r real.  A lane pair holds one column: lane l owns column l / 2 and rows
+// 16 (l % 2) .. + 15, as (re, im) pairs; the column sums are 16-term in-lane
+// sums and one DPP add with the neighbouring lane.  One wave per chain.
+constexpr int DC = 32;
+
+__device__ __forceinline__ float pair_sum(float x) { return lane::dpp_add<lane::kQuadXor1>(x); }
+
+__global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float2* __restrict__ q, const float2* __restrict__ k,
+                                                               const float2* __restrict__ v, const float* __restrict__ r,
+                                                               const float* __restrict__ beta,
+                                                               const float2* __restrict__ S0, float2* __restrict__ out,
+                                                               float2* __restrict__ Sf, int T, int H) {
+  const int l = threadIdx.x, chain = blockIdx.x;
+  const int b = chain / H, h = chain % H;
+  const int c = l >> 1, i0 = R * (l & 1);
+  auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
+  float sr[R], si[R];
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii) {
+    const float2 x = S0 ? S0[((size_t)chain * DC + i0 + ii) * DC + c] : float2{0.f, 0.f};
+    sr[ii] = x.x;
+    si[ii] = x.y;
+  }
+  struct Tok {
+    float4 k[R / 2], q[R / 2];  // 16 complex values each, two per float4
+    float2 v;
+    float r, be;
+  };
+  auto load = [&](int t) {
+    Tok x;
+    const size_t rt = tok(max(0, min(t, T - 1)));
+#pragma unroll
+    for (int e = 0; e < R / 2; ++e) {
+      x.k[e] = reinterpret_cast<const float4*>(k + rt * DC + i0)[e];
+      x.q[e] = reinterpret_cast<const float4*>(q + rt * DC + i0)[e];
+    }
+    x.v = v[rt * DC + c];
+    x.r = r[rt * DC + c];
+    x.be = beta[rt];
+    return x;
+  };
+  auto step = [&](const Tok& x, int t) {
+    float ur = 0.f, ui = 0.f;  // sum_i conj(k_i) s_i
+#pragma unroll
+    for (int e = 0; e < R / 2; ++e) {
+      const float4 kk = x.k[e];
+      ur += kk.x * sr[2 * e] + kk.y * si[2 * e] + kk.z * sr[2 * e + 1] + kk.w * si[2 * e + 1];
+      ui += kk.x * si[2 * e] - kk.y * sr[2 * e] + kk.z * si[2 * e + 1] - kk.w * sr[2 * e + 1];
+    }
+    ur = pair_sum(ur);
+    ui = pair_sum(ui);
+    const float er = x.be * (x.v.x - ur), ei = x.be * (x.v.y - ui);  // beta e
+    float orr = 0.f, oi = 0.f;
+#pragma unroll
+    for (int e = 0; e < R / 2; ++e) {
+      const float4 kk = x.k[e], qq = x.q[e];
+      const float kr[2] = {kk.x, kk.z}, ki[2] = {kk.y, kk.w}, qr[2] = {qq.x, qq.z}, qi[2] = {qq.y, qq.w};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int ii = 2 * e + m;
+        const float nr = x.r * sr[ii] + (kr[m] * er - ki[m] * ei);
+        const float ni = x.r * si[ii] + (kr[m] * ei + ki[m] * er);
+        sr[ii] = nr;
+        si[ii] = ni;
+        orr += qr[m] * nr + qi[m] * ni;  // conj(q) s
+        oi += qr[m] * ni - qi[m] * nr;
+      }
+    }
+    orr = pair_sum(orr);
+    oi = pair_sum(oi);
+    if ((l & 1) == 0) out[tok(t) * DC + c] = float2{orr, oi};
+  };
+  constexpr int PF = 2;
+  if (T > 0) {
+    Tok ring[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[p] = load(p);
+    for (int t = 0; t < T; t += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        if (t + p < T) step(ring[p], t + p);
+        ring[p] = load(t + p + PF);
+      }
+    }
+  }
+  if (Sf) {
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) Sf[((size_t)chain * DC + i0 + ii) * DC + c] = float2{sr[ii], si[ii]};
+  }
+}
+
 }  // namespace chd
 
 hipError_t launch_channel_decay(const ChannelArgs& a) {
+  if (a.dtype == kDtC64)
+    return launch_kernel(chd::channel_decay_c64_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(64),
+                         (hipStream_t)a.stream, (const float2*)a.q, (const float2*)a.k, (const float2*)a.v, a.r, a.beta,
+                         (const float2*)a.S0, (float2*)a.out, (float2*)a.S_final, a.T, a.H);
   const dim3 grid((unsigned)((long)a.B * a.H * 4)), block(64);
   if (a.dtype == kDtBF16)
     return launch_kernel(chd::channel_decay_kernel<__hip_bfloat16>, grid, block, (hipStream_t)a.stream,

@@ -185,7 +185,7 @@ int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const flo
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
       !chains_fit((long long)B * H, 256))
     return GDN_ERR_SHAPE;
-  if (dtype == GDN_C64 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  if (dk != dv || (dtype == GDN_C64 ? dk != 32 : dk != 64)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !r || !beta || !out)) return GDN_ERR_NULL;
   const void* ptrs[] = {q, k, v, r, beta, S0, out, S_final};

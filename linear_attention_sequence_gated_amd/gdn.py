@@ -257,9 +257,10 @@ def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream
 
 
 def fwd_channel_decay(q, k, v, r, beta, S0=None, out=None, S_final=None, stream=None):
-    """Forward with a per-output-channel decay r [B,T,H,64] fp32 (one factor per token and value channel).
-    q, k, v [B,T,H,64] float32 or bfloat16; beta [B,T,H] fp32; S0 [B,H,64,64] fp32 or None.
-    Returns (out [B,T,H,64] in q's dtype, S_final [B,H,64,64] fp32)."""
+    """Forward with a per-output-channel decay r [B,T,H,d] fp32 (one factor per token and value channel).
+    q, k, v [B,T,H,d]: float32 or bfloat16 with d = 64, or complex64 with d = 32; beta [B,T,H] fp32;
+    S0 [B,H,d,d] (fp32, complex64 for complex data) or None.
+    Returns (out [B,T,H,d] in q's dtype, S_final [B,H,d,d] in the state's dtype)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -272,14 +273,15 @@ def fwd_channel_decay(q, k, v, r, beta, S0=None, out=None, S_final=None, stream=
     _check(v, "v", (B, T, H, dv), q.dtype, dev)
     _check(r, "r", (B, T, H, dv), torch.float32, dev)
     _check(beta, "beta", (B, T, H), torch.float32, dev)
+    sdt = _state_dtype(code)
     if S0 is not None:
-        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+        _check(S0, "S0", (B, H, dk, dv), sdt, dev)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     _check(out, "out", (B, T, H, dv), q.dtype, dev)
     if S_final is None:
-        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+        S_final = torch.empty((B, H, dk, dv), dtype=sdt, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), sdt, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     s = gdn_fwd_channel_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_final),
                               B, T, H, dk, dv, code, st)

@@ -106,7 +106,9 @@ def prologue(**kw):
     (dict(chunk=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_F32), raw.GDN_ERR_UNSUPPORTED),
-    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
+    (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(B=1, T=1 << 22, H=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(a_logit=None), raw.GDN_ERR_NULL),
     (dict(b_logit=None), raw.GDN_ERR_NULL),
@@ -135,7 +137,9 @@ def backward(**kw):
     (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
-    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
+    (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(B=1, T=1 << 22, H=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(grad_out=None), raw.GDN_ERR_NULL),
     (dict(grad_beta=None), raw.GDN_ERR_NULL),
@@ -170,7 +174,9 @@ def channel(**kw):
     (dict(B=-2), raw.GDN_ERR_SHAPE),
     (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
-    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
+    (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(r=None), raw.GDN_ERR_NULL),
     (dict(out=None), raw.GDN_ERR_NULL),
     (dict(r=A + 4), raw.GDN_ERR_ALIGN),

@@ -1,6 +1,6 @@
 """Per-output-channel decay (gdn_fwd_channel_decay) on the GPU through the C ABI, against the fp64 oracle
 (oracle/channel_decay.py).  bf16 inputs run the chunk form (16-token sub-chunks, one triangular solve per value
-channel); fp32 inputs the token loop."""
+channel); fp32 and complex64 (LaplacePhaseCore-shaped, d = 32) inputs the token loop."""
 import numpy as np
 import pytest
 
@@ -13,11 +13,12 @@ pytestmark = pytest.mark.gpu
 def run(inp, dtype, alias=False):
     torch = torch_dev()
     import linear_attention_sequence_gated_amd as gdn
-    S0 = up(inp["S0"], "f32") if inp.get("S0") is not None else None
+    sdt = "c64" if dtype == "c64" else "f32"
+    S0 = up(inp["S0"], sdt) if inp.get("S0") is not None else None
     o, S = gdn.fwd_channel_decay(up(inp["q"], dtype), up(inp["k"], dtype), up(inp["v"], dtype), up(inp["r"], "f32"),
                                  up(inp["beta"], "f32"), S0, S_final=S0 if alias else None)
     torch.cuda.synchronize()
-    return o.float().cpu().numpy(), S.cpu().numpy()
+    return (o.float() if o.dtype == torch.bfloat16 else o).cpu().numpy(), S.cpu().numpy()
 
 
 def ref(inp):
@@ -110,3 +111,49 @@ def test_channel_decay_chunk_form_unit_decay_equals_delta_rule():
                            up(inp["beta"], "f32"), up(inp["S0"], "f32"))
     torch.cuda.synchronize()
     assert_close("chd_chunk_vs_delta_rule", "bf16", o1, S1, o2.float().cpu().numpy(), S2.cpu().numpy())
+
+
+@pytest.mark.parametrize("B,T,H,s0", [(1, 50, 2, None), (2, 300, 3, 0.1)])
+def test_channel_decay_complex_small(B, T, H, s0):
+    inp = gen_channel_decay(B, T, H, 32, dtype="c64", seed=61 + T, s0_var=s0)
+    note(f"channel decay c64 B{B} T{T} H{H} s0={s0}")
+    o, S = run(inp, "c64")
+    o_ref, S_ref = ref(inp)
+    assert_close(f"chd_c64_{B}_{T}_{H}", "c64", o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("T", [0, 1, 3])
+def test_channel_decay_complex_lengths_and_alias(T):
+    inp = gen_channel_decay(2, T, 2, 32, dtype="c64", seed=70 + T, s0_var=0.5)
+    note(f"channel decay c64 T={T}, S_final aliasing S0")
+    o, S = run(inp, "c64", alias=True)
+    if T == 0:
+        assert np.array_equal(S, inp["S0"])
+        return
+    o_ref, S_ref = ref(inp)
+    assert_close(f"chd_c64_len{T}", "c64", o, S, o_ref, S_ref)
+
+
+def test_channel_decay_complex_unit_decay_equals_delta_rule():
+    """Complex data, r = 1: gdn_chunk_fwd's complex kernel at alpha = 1 computes the same rule."""
+    torch = torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    inp = gen_channel_decay(2, 200, 2, 32, dtype="c64", seed=4, s0_var=0.1)
+    inp["r"] = np.ones_like(inp["r"])
+    ones = np.ones_like(inp["beta"])
+    note("channel decay c64 r = 1 vs the complex chunk forward at alpha = 1")
+    o1, S1 = run(inp, "c64")
+    o2, S2 = gdn.chunk_fwd(up(inp["q"], "c64"), up(inp["k"], "c64"), up(inp["v"], "c64"), up(ones, "f32"),
+                           up(inp["beta"], "f32"), up(inp["S0"], "c64"))
+    torch.cuda.synchronize()
+    assert_close("chd_c64_vs_delta_rule", "c64", o1, S1, o2.cpu().numpy(), S2.cpu().numpy())
+
+
+def test_channel_decay_complex_full_size_all_chains():
+    """The 4 x 4096 x 8 complex d32 layer with LaplacePhaseCore-shaped keys; every chain vs the oracle."""
+    w = WORKLOADS["laplace_c64_channel_decay"]
+    inp = gen_workload(w)
+    note("channel decay c64 full size")
+    o, S = run(inp, "c64")
+    o_ref, S_ref = ref(inp)
+    assert_close("chd_c64_full", "c64", o, S, o_ref, S_ref)
