@@ -1,8 +1,9 @@
-"""Build libgdn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libgdn.so (HIP kernels + C ABI) and libgdn_peak.so (measured-peak
+loops for the benchmark's context figures) for gfx950 with hipcc, in-tree.
 
 Usage: ``python -m linear_attention_sequence_gated_amd.build``.  Objects go to
-``_build/`` at the repository root; the shared library is written next to this
-file so the Python binding finds it.
+``_build/`` at the repository root; the shared libraries are written next to
+this file so the Python binding finds them.
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+PEAK_LIB = os.path.join(PKG, "libgdn_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "channel_decay.hip", "channel_chunk.hip", "decode.hip", "noalloc.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,7 +31,10 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # Per-source flags.  channel_chunk.hip rescales its matrix-core accumulators with
 # vector instructions every step; the VGPR form of the MFMA instructions keeps
 # them in VGPRs instead of copying them to and from AGPRs each time.
-EXTRA = {"channel_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# peak.hip needs the same form for its loop of chained accumulations, or the
+# register allocator shuffles the accumulators through AGPR copies every round.
+EXTRA = {"channel_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
@@ -40,18 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {os.path.basename(lib)}:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    allsrc = SOURCES + PEAK_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(allsrc), 8)) as ex:
+        objs = dict(zip(allsrc, ex.map(_compile, allsrc)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAK_SOURCES], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 

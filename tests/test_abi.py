@@ -13,10 +13,36 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 A = 0x10000  # a 16-byte aligned fake address; validation rejects before any use
 
 
-def declared_functions():
-    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+def declared_functions(header="gdn.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["gdn.h", "gdn_peak.h"]
+
+
+def test_peak_library_exports_its_header():
+    """libgdn_peak.so (the benchmark's measured-peak loops) exports what include/gdn_peak.h declares and
+    rejects bad arguments without launching."""
+    import ctypes
+    from linear_attention_sequence_gated_amd import build as gbuild
+    lib = ctypes.CDLL(gbuild.PEAK_LIB)
+    names = declared_functions("gdn_peak.h")
+    assert names == ["gdn_peak_mfma_loop", "gdn_peak_read"]
+    fn = lib.gdn_peak_mfma_loop
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert fn(3, 10, 1, A, None) == -1
+    assert fn(0, 0, 1, A, None) == -1
+    assert fn(0, 10, 0, A, None) == -1
+    assert fn(1, 10, 1, None, None) == -1
+    rd = lib.gdn_peak_read
+    rd.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert rd(None, 1024, 1, A, None) == -1
+    assert rd(A + 4, 1024, 1, A, None) == -1
+    assert rd(A, 1024, 0, A, None) == -1
+    assert rd(A, 1024, 1, None, None) == -1
 
 
 def test_every_declared_symbol_is_exported():
