@@ -60,6 +60,8 @@ KERNEL_SOURCES = {
     "channel_decay_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_chunk_kernel": [_CSRC + "channel_chunk.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_c64_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
+    "chunk_grad": [_CSRC + "chunk_grad.hip", _CSRC + "chunk_two.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_lane.hpp",
+                   _CSRC + "gdn_device.hpp"],
 }
 FLUSH_BYTES = 1 << 30  # the cold protocol's cache-evicting fill
 
@@ -801,6 +803,7 @@ def bench_backward(args, w, dev):
     flops = backward_flops(w)
     tfs = flops / (avg_ms * 1e-3) / 1e12
     tok = w.B * w.T * w.H
+    # q, k, v, dO in; alpha, beta in; dq, dk, dv (fp32) and dalpha, dbeta out; dS_T in and dS0 out
     hbm_bytes = tok * (3 * w.dk * 2 + w.dv * 2 + 8) + tok * (2 * w.dk + w.dv) * 4 + tok * 8 + 2 * w.B * w.H * w.dk * w.dv * 4
     result = {
         "metric": f"tokens/sec gated-delta chunk bwd ({w.name})", "value": w.B * w.T * args.steps / wall,
@@ -816,7 +819,18 @@ def bench_backward(args, w, dev):
                      "hbm_achieved_GBs": hbm_bytes / (avg_ms * 1e-3) / 1e9, "kernel_avg_ms": avg_ms,
                      "kernel": "gdn::bwd::bwd_kernel"},
     }
-    add_context(result, args, step, stream, dev, "bwd_kernel", 1)
+    key = "bwd_kernel"
+    if w.dtype == "bf16":
+        # bf16 runs the chunk form on the matrix cores, four launches per call (the forward's factor and
+        # state passes, the adjoint scan, the chunk-parallel gradients): priced on its HBM bytes.
+        key = "chunk_grad"
+        achieved = hbm_bytes / (avg_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(key, w.name),
+                              "algorithmic_bytes_per_launch": hbm_bytes, "kernel_avg_ms": avg_ms,
+                              "kernel": "gdn::two::factor_kernel + state_kernel + gdn::grad::adj_kernel + "
+                                        "grad_kernel (one call)"}
+    add_context(result, args, step, stream, dev, key, 1)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_backward(inp, dO, dS, w)
     if args.calibrate_copy:

@@ -153,9 +153,12 @@ int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const fl
                            void *S_final, int B, int T, int H, int dk, int dv, int dtype, void *stream);
 
 /*
- * Bytes of workspace gdn_chunk_bwd needs: B * H * ceil(T / 8) * 64 * 64 * 4
- * (the forward state every 8 tokens).  0 for an unsupported combination or
- * T == 0.
+ * Bytes of workspace gdn_chunk_bwd needs.  bf16 (the chunk form): per
+ * (chain, 64-token chunk) two 6400-byte factor records, a bf16 start state and
+ * a bf16 end gradient (2 * 6400 + 2 * 64 * 64 * 2 bytes), plus the forward's
+ * segment maps when it splits long sequences (as gdn_chunk_fwd_workspace_bytes
+ * reports them).  fp32: B * H * ceil(T / 8) * 64 * 64 * 4 (the forward state
+ * every 8 tokens).  0 for an unsupported combination or T == 0.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
 
@@ -182,10 +185,15 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dt
  *                 that is 0)
  *
  * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0 with
- * T * H * 4 < 2^31; otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).  Arithmetic is fp32
- * throughout; bf16 inputs are read exactly.  The forward is recomputed inside
- * the call (checkpoints every 8 tokens in the workspace), so nothing from a
- * forward call is needed.  Gradient outputs must not alias any input.
+ * T * H * 4 < 2^31; otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).
+ * bf16 inputs take the chunk form on the matrix cores (the same chunking as
+ * gdn_chunk_fwd, run in reverse: the forward's chunk start states, then the
+ * gradient carried from the last chunk to the first, then every chunk's
+ * gradients at once), with bf16 operands and fp32 accumulation, like the
+ * forward.  fp32 inputs take a token-by-token reverse pass in fp32 throughout
+ * (checkpoints every 8 tokens).  The forward is recomputed inside the call, so
+ * nothing from a forward call is needed.  Gradient outputs must not alias any
+ * input.  alpha must be positive (the chunk form works with log alpha).
  * B * H == 0 is a no-op; T == 0 copies grad_S_final (or zeros) to grad_S0.
  * Errors as for gdn_chunk_fwd.
  */

@@ -39,17 +39,6 @@ namespace gdn {
 namespace two {
 using namespace pipe;
 
-// ------------------------------------------------------------ chunk records
-// One record per (chain, chunk) in the workspace:
-//   Tb as six 1 KB blocks of bf16 A operands of 16x16x32 products: block
-//   (i, p) holds, in lane L = 16 g + c, the 8 values Tb[16i + c][32p + 4g + j]
-//   and Tb[16i + c][32p + 16 + 4g + j] (j = 0..3), the k layout of mma32 with a
-//   pair of accumulator tiles as the B operand.  Blocks exist for p <= i / 2;
-//   their tiles above the diagonal block are zero.
-//   g[64] fp32, the inclusive prefix of log2 alpha over the chunk.
-constexpr int kRecTb = 0, kRecG = 6 * 1024, kRecBytes = kRecG + 64 * 4;
-__host__ __device__ constexpr int pblk(int i, int p) { return i < 2 ? i : 2 * i - 2 + p; }
-
 // Orders this wave's LDS writes before its later LDS reads in every lane (the
 // compiler treats each lane as a thread; see the three-stage kernel).
 __device__ __forceinline__ void wave_sync() {
@@ -115,8 +104,8 @@ struct FactorCfg {
 
 template <int DK>
 __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ kg, const float* __restrict__ alpha,
-                                                    const float* __restrict__ beta, char* __restrict__ ws, int T,
-                                                    int H, int nch, int total) {
+                                                    const float* __restrict__ beta, char* __restrict__ ws,
+                                                    char* __restrict__ wsT, int T, int H, int nch, int total) {
   using Cf = FactorCfg<DK>;
   constexpr int NKP = Cf::NKP;
   __shared__ __attribute__((aligned(16))) float W[Cf::szW];
@@ -255,23 +244,21 @@ __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ k
   tb[64 * pblk(2, 1)] = cvt8(TP[2], zero4());
   tb[64 * pblk(3, 0)] = cvt8(TA[3][0], TA[3][1]);
   tb[64 * pblk(3, 1)] = cvt8(TA[3][2], TP[3]);
+  if (wsT) {
+    // Tb^T: its A operand of block (i, k) is the B order of Tb block (k, i).
+    char* const recT = wsT + ((size_t)chain * nch + n) * kRecBytes;
+    u32x4* const tt = reinterpret_cast<u32x4*>(recT + kRecTb) + l;
+    tt[64 * qblk(0, 0)] = cvt8(TPb[0], Tb[1][0]);
+    tt[64 * qblk(0, 1)] = cvt8(Tb[2][0], Tb[3][0]);
+    tt[64 * qblk(1, 0)] = cvt8(zero4(), TPb[1]);
+    tt[64 * qblk(1, 1)] = cvt8(Tb[2][1], Tb[3][1]);
+    tt[64 * qblk(2, 1)] = cvt8(TPb[2], Tb[3][2]);
+    tt[64 * qblk(3, 1)] = cvt8(zero4(), TPb[3]);
+    reinterpret_cast<float*>(recT + kRecG)[l] = gl;
+  }
 }
 
 // -------------------------------------------------------------- state pass
-// Key rows and query rows are staged in LDS unpadded, 16-byte pieces swizzled:
-// piece u of row r sits at position u ^ sw(r).  Two read patterns must spread
-// over the 64 banks: a 16-lane group reading one piece of sixteen consecutive
-// rows (MFMA operands in row order), and the transposed reads of K, where a
-// 16-lane group reads pieces 4m .. 4m + 3 (one 8-byte half each) of four
-// consecutive rows 4g .. 4g + 3.  sw(r) rotates the bits of r so that both are
-// free of conflicts within 16 lanes (at d = 64 two rows share a 256-byte bank
-// window, told apart by r & 1).
-template <int DK> __device__ __forceinline__ int row_off(int r, int e) {
-  constexpr int NU = DK / 8;
-  const int sw = DK == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
-  return r * DK + (((e >> 3) ^ sw) & (NU - 1)) * 8 + (e & 7);
-}
-
 template <int DK, int NC>
 struct StateCfg {
   static constexpr int NV = 16 * NC;              // value columns per workgroup
@@ -310,6 +297,7 @@ struct StateArgs {
   float* Sf;           // [chains][DK][DV] or NULL
   float* seg_state;    // segmented scan: start states [chains][G][DK][DV] (output mode) or
                        // maps [chains][G][DK][DK + DV] (map mode)
+  __bf16* Sck;         // output mode, or NULL: every chunk's start state, bf16 [chains][nch][DK][DV]
   int T, H, DV, nch;
   int G, SC;           // segments per chain and chunks per segment (G = 1: one segment)
   int nseg;            // segments per chain in this launch's grid (G, or G - 1 in map mode)
@@ -443,6 +431,18 @@ struct Consumer2 {
     }
   }
 
+  // The state at the start of local chunk k (its bf16 operand copy) into the chunk-state array.
+  __device__ __forceinline__ void store_start(const StateArgs& a, const Seg& sg, int k) {
+    __bf16* const dst = a.Sck + ((size_t)sg.chain * a.nch + sg.n0 + k) * DK * a.DV + sg.dv0 + 16 * w + c;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned u = sfr[d][j >> 1];
+        dst[(size_t)key_row(d, g, j) * a.DV] = __builtin_bit_cast(__bf16, (unsigned short)((j & 1) ? u >> 16 : u));
+      }
+  }
+
   __device__ __forceinline__ void finish(const StateArgs& a, const Seg& sg) {
     float* dst = nullptr;
     size_t ld = a.DV, base = 0;
@@ -494,6 +494,7 @@ __device__ __forceinline__ void consumer_role(const StateArgs& a, const Seg& sg,
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
     if (k == -1) cs.publish_state(reinterpret_cast<unsigned*>(smem + Cf::oHS));  // start state of chunk 0
     if (k >= 0 && k < sg.nloc) {
+      if (out && a.Sck) cs.store_start(a, sg, k);
       unsigned* hu = out ? reinterpret_cast<unsigned*>(smem + Cf::oHU + (k & 1) * Cf::szHU) : nullptr;
       cs.chunk(smem + slot * Cf::szSlot, hu, sg.mcol);
       cs.publish_state(reinterpret_cast<unsigned*>(smem + Cf::oHS + ((k + 1) & 1) * Cf::szHS));
@@ -579,8 +580,10 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
     return;
   }
   const int H = a.H, T = a.T, DV = a.DV;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + ((size_t)sg.b * T * H + sg.h) * DV + sg.dv0,
-                                              span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2));
+  // No output array (the gradient pass's forward): every store is dropped by the empty range.
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(a.out + ((size_t)sg.b * T * H + sg.h) * DV + sg.dv0,
+                a.out ? span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2) : 0u);
   const int rowO = H * DV * 2, vofO = c * rowO + 8 * g;
   const int tok0 = sg.n0 * 64;
   f32x4 o[4][NC];
@@ -892,7 +895,7 @@ size_t chunk_two_workspace_bytes(const ChunkArgs& a) {
 }
 
 template <int DK, int NC>
-static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
+static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, __bf16* Sck) {
   using Cf = two::StateCfg<DK, NC>;
   const int nch = (a.T + 63) / 64;
   const long chains = (long)a.B * a.H;
@@ -901,7 +904,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
   const long total = chains * nch;
   if (total > 0) {
     const hipError_t e = launch_kernel(two::factor_kernel<DK>, dim3((unsigned)total), dim3(64), st,
-                                       static_cast<const __bf16*>(a.k), a.alpha, a.beta, ws, a.T, a.H, nch,
+                                       static_cast<const __bf16*>(a.k), a.alpha, a.beta, ws, wsT, a.T, a.H, nch,
                                        (int)total);
     if (e != hipSuccess) return e;
   }
@@ -913,6 +916,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
   s.S0 = static_cast<const float*>(a.S0);
   s.out = static_cast<__bf16*>(a.out);
   s.Sf = static_cast<float*>(a.S_final);
+  s.Sck = Sck;
   s.T = a.T;
   s.H = a.H;
   s.DV = a.dv;
@@ -941,8 +945,14 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace) {
 }
 
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace) {
-  if (a.dk == 64) return launch_two_dk<64, 2>(a, workspace);
-  if (a.dk == 128) return launch_two_dk<128, 1>(a, workspace);
+  if (a.dk == 64) return launch_two_dk<64, 2>(a, workspace, nullptr, nullptr);
+  if (a.dk == 128) return launch_two_dk<128, 1>(a, workspace, nullptr, nullptr);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_two_states(const ChunkArgs& a, void* workspace, void* recT, void* Sck) {
+  if (a.dk == 64) return launch_two_dk<64, 2>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
+  if (a.dk == 128) return launch_two_dk<128, 1>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
   return hipErrorInvalidValue;
 }
 

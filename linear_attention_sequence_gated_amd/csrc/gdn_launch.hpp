@@ -97,6 +97,10 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 onl
 size_t chunk_two_workspace_bytes(const ChunkArgs& a);
 int chunk_two_segments(const ChunkArgs& a);  // segments of the two-level scan (1: none)
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace);
+// The same forward for the gradient pass: also writes the Tb^T records to
+// `recT` and every chunk's start state (bf16 [chains][nch][dk][dv]) to `Sck`;
+// a.out may be NULL (no output written).
+hipError_t launch_chunk_two_states(const ChunkArgs& a, void* workspace, void* recT, void* Sck);
 hipError_t launch_recurrent_step(const StepArgs& a);
 // Complex64, head size 32: three launches (prep, state scan, output) that
 // exchange per-chunk intermediates through `workspace`.
@@ -105,6 +109,10 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+// bf16, d = 64, T > 0: the chunk form on the matrix cores (the forward's
+// factor and state passes, the adjoint scan, the chunk-parallel gradients).
+size_t chunk_grad_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk_grad(const BwdArgs& a);
 hipError_t launch_channel_decay(const ChannelArgs& a);  // token loop (fp32 inputs)
 hipError_t launch_channel_chunk(const ChannelArgs& a);  // chunk form on the matrix cores (bf16 inputs)
 

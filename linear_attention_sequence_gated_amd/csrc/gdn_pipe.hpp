@@ -1,8 +1,9 @@
 // gdn_pipe.hpp -- bf16 matrix-core helpers shared by the pipelined chunk
-// kernels (chunk_pipe.hip, chunk_two.hip): buffer resources and range-checked
-// loads, LDS barriers, fp32 <-> bf16 packing, 16x16x32 / 16x16x16 products,
-// wave prefix sums and broadcasts, and the key order of the state held in
-// matrix-core accumulators.
+// kernels (chunk_pipe.hip, chunk_two.hip, chunk_grad.hip): buffer resources
+// and range-checked loads, LDS barriers, fp32 <-> bf16 packing, 16x16x32 /
+// 16x16x16 products, wave prefix sums and broadcasts, the key order of the
+// state held in matrix-core accumulators, the chunk records of the two-launch
+// forward and the swizzled LDS row layout.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -126,6 +127,35 @@ __host__ __device__ constexpr int stri(int i, int j) { return i * (i - 1) / 2 + 
 // and 2p + 1 give lane group g the 8 consecutive keys 32p + 8g .. 32p + 8g + 7.
 // K S and Q S then read their K and Q operands as one 16-byte row piece.
 __host__ __device__ constexpr int key_row(int d, int g, int j) { return 32 * (d / 2) + 8 * g + 4 * (d % 2) + j; }
+
+// Chunk records of the two-launch forward, read again by the gradient pass.
+// One record per (chain, chunk) in the workspace:
+//   Tb as six 1 KB blocks of bf16 A operands of 16x16x32 products: block
+//   (i, p) holds, in lane L = 16 g + c, the 8 values Tb[16i + c][32p + 4g + j]
+//   and Tb[16i + c][32p + 16 + 4g + j] (j = 0..3), the k layout of mma32 with a
+//   pair of accumulator tiles as the B operand.  Blocks exist for p <= i / 2;
+//   their tiles above the diagonal block are zero.
+//   g[64] fp32, the inclusive prefix of log2 alpha over the chunk.
+constexpr int kRecTb = 0, kRecG = 6 * 1024, kRecBytes = kRecG + 64 * 4;
+__host__ __device__ constexpr int pblk(int i, int p) { return i < 2 ? i : 2 * i - 2 + p; }
+// The gradient pass also needs Tb^T, the upper-triangular transpose, as A
+// operands: a second record of the same size holds its six blocks (i, p), p
+// >= i / 2 (tiles left of the diagonal block zero), then the same g.
+__host__ __device__ constexpr int qblk(int i, int p) { return i < 2 ? 2 * i + p : i + 2; }
+
+// Key rows and query rows are staged in LDS unpadded, 16-byte pieces swizzled:
+// piece u of row r sits at position u ^ sw(r).  Two read patterns must spread
+// over the 64 banks: a 16-lane group reading one piece of sixteen consecutive
+// rows (MFMA operands in row order), and the transposed reads of K, where a
+// 16-lane group reads pieces 4m .. 4m + 3 (one 8-byte half each) of four
+// consecutive rows 4g .. 4g + 3.  sw(r) rotates the bits of r so that both are
+// free of conflicts within 16 lanes (at d = 64 two rows share a 256-byte bank
+// window, told apart by r & 1).
+template <int DK> __device__ __forceinline__ int row_off(int r, int e) {
+  constexpr int NU = DK / 8;
+  const int sw = DK == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  return r * DK + (((e >> 3) ^ sw) & (NU - 1)) * 8 + (e & 7);
+}
 
 }  // namespace pipe
 }  // namespace gdn

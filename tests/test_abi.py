@@ -182,7 +182,9 @@ def test_backward_empty_and_workspace_query():
     assert backward(B=0, q=None, k=None, v=None, alpha=None, beta=None, grad_out=None, grad_q=None, grad_k=None,
                     grad_v=None, grad_alpha=None, grad_beta=None, grad_S0=None, workspace=None,
                     workspace_bytes=0) == raw.GDN_OK
-    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_BF16) == 2 * 3 * 16 * 64 * 64 * 4
+    # bf16: the matrix-core path -- two 6400-byte records, a bf16 start state and a bf16 end gradient per chunk
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_BF16) == 2 * 3 * 2 * (2 * 6400 + 2 * 8192)
+    # fp32: the token-by-token kernel -- the state every 8 tokens
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == 2 * 3 * 17 * 64 * 64 * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
