@@ -43,13 +43,6 @@ namespace gdn {
 namespace grad {
 using namespace pipe;
 
-// Orders this wave's LDS writes before its later LDS reads in every lane.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ float bf_at(const u32x2& v, int j) { return j & 1 ? hi_f(v[j >> 1]) : lo_f(v[j >> 1]); }
 
 // Sum over the lane's row of 16 (every lane of the row receives it).

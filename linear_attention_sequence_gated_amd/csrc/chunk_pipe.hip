@@ -648,6 +648,8 @@ __device__ __forceinline__ void gram_rows(const Ctx& x, char* smem, int b0, int 
         *reinterpret_cast<u32x4*>(R + Cf::oK + lofs[e][p]) = S.k[e][p];
         *reinterpret_cast<u32x4*>(R + Cf::oQ + lofs[e][p]) = S.q[e][p];
       }
+    // The operands below come from rows other lanes of this wave just wrote.
+    wave_sync();
     u32x4 kk[2][NKP], qq[2][NKP];  // MFMA operands: lane (g, c) holds row c, k = 32 p + 8 g .. + 7
 #pragma unroll
     for (int e = 0; e < 2; ++e)
