@@ -323,27 +323,38 @@ __device__ __forceinline__ void adj_consumer(const AdjArgs& a, int chain, int dv
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // chunk k
     if (k < 0 || k >= a.nch) return;
     const int n = a.nch - 1 - k;
-    // The gradient at the end of chunk n, for the gradient pass.
-    __bf16* const dst = a.dSck + ((size_t)chain * a.nch + n) * DK * a.DV + col;
+    // The gradient at the end of chunk n, for the gradient pass (32-bit
+    // offsets through a buffer resource, formed here).
+    {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(a.dSck + ((size_t)chain * a.nch + n) * DK * a.DV + dv0 + 16 * w, (uint32_t)(DK * a.DV * 2));
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+      for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned u = sfr[d][j >> 1];
-        dst[(size_t)key_row(d, g, j) * a.DV] = __builtin_bit_cast(__bf16, (unsigned short)((j & 1) ? u >> 16 : u));
-      }
+        for (int j = 0; j < 4; ++j) {
+          const unsigned u = sfr[d][j >> 1];
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)((j & 1) ? u >> 16 : u), rs,
+                                                (key_row(d, g, j) * a.DV + c) * 2, 0, 0);
+        }
+    }
     const char* const R = smem + slot * Cf::szSlot;
     const __bf16* const Rb = reinterpret_cast<const __bf16*>(R);
     const float* const Gt = reinterpret_cast<const float*>(R + Cf::oGt);
     const float* const E = reinterpret_cast<const float*>(smem + Cf::oE + (k & 1) * Cf::szE);
-    u32x4 kr[4][NKP];
+    // At d = 128 the K rows are read per 16-row block and half of the update's
+    // K^T operands after the Tb^T product (register budget, as in the forward).
+    constexpr int KRB = DK == 128 ? 1 : 4, KTB = DK == 128 ? 4 : NDT;
+    auto krow = [&](int i, u32x4 (&dst)[NKP]) {
+#pragma unroll
+      for (int p = 0; p < NKP; ++p)
+        dst[p] = *reinterpret_cast<const u32x4*>(Rb + Cf::oK / 2 + row_off<DK>(16 * i + c, 32 * p + 8 * g));
+    };
+    u32x4 kr[KRB][NKP];
     u32x2 dd[4];
     f32x4 gm[4], lm[4], ee[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int p = 0; p < NKP; ++p)
-        kr[i][p] = *reinterpret_cast<const u32x4*>(Rb + Cf::oK / 2 + row_off<DK>(16 * i + c, 32 * p + 8 * g));
+      if (i < KRB) krow(i, kr[i < KRB ? i : 0]);
       dd[i] = ld4_tr(Rb + Cf::oV / 2 + (16 * i + 4 * g + (c >> 2)) * Cf::LDV + 16 * w + 4 * (c & 3));
       gm[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gGam + 16 * i + 4 * g);
       lm[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gLam + 16 * i + 4 * g);
@@ -357,26 +368,58 @@ __device__ __forceinline__ void adj_consumer(const AdjArgs& a, int chain, int dv
     u32x2 du[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      u32x4 ki[NKP];
+      if (i < KRB) {
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) ki[p] = kr[i < KRB ? i : 0][p];
+      } else {
+        krow(i, ki);
+      }
       f32x4 z = zero4();
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) z = mma32(kr[i][p], pair(sfr[2 * p], sfr[2 * p + 1]), z);
+      for (int p = 0; p < NKP; ++p) z = mma32(ki[p], pair(sfr[2 * p], sfr[2 * p + 1]), z);
       f32x4 x;
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = ee[i][j] + lm[i][j] * z[j];
       du[i] = cvt4(x);
     }
-    // Update operands, in flight during the Tb^T product: K^T and Q^T in the
-    // key order of the accumulators.
-    u32x2 kt[NDT][4], qt[NDT][4];
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
+    // The update's Q side needs only dO: dS <- gamma_C dS + Q^T (gamma dO) runs
+    // while the Tb^T product is formed (Q^T read in the key order of the
+    // accumulators, one key block at a time).
+    const float gC = Gt[Cf::gGC];
+    {
+      u32x2 W1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int off = row_off<DK>(16 * i + 4 * g + (c >> 2), 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3));
-        kt[d][i] = ld4_tr(Rb + Cf::oK / 2 + off);
-        qt[d][i] = ld4_tr(Rb + Cf::oQ / 2 + off);
+        f32x4 x1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x1[j] = gm[i][j] * bf_at(dd[i], j);
+        W1[i] = cvt4(x1);
       }
-    const float gC = Gt[Cf::gGC];
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) {
+        u32x2 qt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          qt[i] = ld4_tr(Rb + Cf::oQ / 2 +
+                         row_off<DK>(16 * i + 4 * g + (c >> 2), 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3)));
+        f32x4 sd = S[d];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sd[j] *= gC;
+        sd = mma2(qt[0], qt[1], W1[0], W1[1], sd);
+        S[d] = mma2(qt[2], qt[3], W1[2], W1[3], sd);
+      }
+    }
+    // K^T operands of the update, in flight during the Tb^T product.
+    auto ktr = [&](int d, u32x2 (&dst)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[i] = ld4_tr(Rb + Cf::oK / 2 +
+                        row_off<DK>(16 * i + 4 * g + (c >> 2), 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3)));
+    };
+    u32x2 kt[KTB][4];
+#pragma unroll
+    for (int d = 0; d < KTB; ++d) ktr(d, kt[d]);
     issue_fence();
     // dX = Tb^T dU (block row i sums k blocks i .. 3)
     const u32x4 d01 = pair(du[0], du[1]), d23 = pair(du[2], du[3]);
@@ -385,28 +428,26 @@ __device__ __forceinline__ void adj_consumer(const AdjArgs& a, int chain, int dv
     X[1] = mma32(tt[qblk(1, 1)], d23, mma32(tt[qblk(1, 0)], d01, zero4()));
     X[2] = mma32(tt[qblk(2, 1)], d23, zero4());
     X[3] = mma32(tt[qblk(3, 1)], d23, zero4());
-    u32x2 W1[4], W2[4];
+    u32x2 W2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x4 x1, x2;
+      f32x4 x2;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x1[j] = gm[i][j] * bf_at(dd[i], j);
-        x2[j] = -gm[i][j] * X[i][j];
-      }
-      W1[i] = cvt4(x1);
+      for (int j = 0; j < 4; ++j) x2[j] = -gm[i][j] * X[i][j];
       W2[i] = cvt4(x2);
     }
-    // dS <- gamma_C dS + Q^T (gamma dO) - K^T (gamma dX)
+    // ... - K^T (gamma dX)
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
-      f32x4 sd = S[d];
+      u32x2 kd[4];
+      if (d < KTB) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sd[j] *= gC;
-      sd = mma2(qt[d][0], qt[d][1], W1[0], W1[1], sd);
-      sd = mma2(qt[d][2], qt[d][3], W1[2], W1[3], sd);
-      sd = mma2(kt[d][0], kt[d][1], W2[0], W2[1], sd);
-      sd = mma2(kt[d][2], kt[d][3], W2[2], W2[3], sd);
+        for (int i = 0; i < 4; ++i) kd[i] = kt[d < KTB ? d : 0][i];
+      } else {
+        ktr(d, kd);
+      }
+      f32x4 sd = mma2(kd[0], kd[1], W2[0], W2[1], S[d]);
+      sd = mma2(kd[2], kd[3], W2[2], W2[3], sd);
       S[d] = sd;
       sfr[d] = cvt4(sd);
     }
@@ -490,39 +531,71 @@ struct GradArgs {
   float* dalpha;
   float* dbeta;
   int T, H, nch;
+  // d = 128 only: the hand-off between its two launches, per (chain, chunk):
+  // U and dX (bf16 [64][128]) and the value-side dg terms (fp32 [64])
+  __bf16* Uw;
+  __bf16* Xw;
+  float* dgA;
 };
 
 __device__ __forceinline__ __bf16* mat(char* smem, int m) { return reinterpret_cast<__bf16*>(smem + m * GradCfg::MAT); }
 
+// LDS matrices of W bf16 columns with swizzled rows (row_off<W>).
 // A or B operand piece: 8 consecutive elements of row r from column e0.
+template <int W = 64>
 __device__ __forceinline__ u32x4 rowp(const __bf16* M, int r, int e0) {
-  return *reinterpret_cast<const u32x4*>(M + row_off<64>(r, e0));
+  return *reinterpret_cast<const u32x4*>(M + row_off<W>(r, e0));
 }
 // Column piece: M[r0 + e][c0 + c] for e = 0..7 in lane (g, c) (r0 may depend
 // on g), through two transposed reads.
+template <int W = 64>
 __device__ __forceinline__ u32x4 colp(const __bf16* M, int r0, int c0, int c) {
-  const u32x2 lo = ld4_tr(M + row_off<64>(r0 + (c >> 2), c0 + 4 * (c & 3)));
-  const u32x2 hi = ld4_tr(M + row_off<64>(r0 + 4 + (c >> 2), c0 + 4 * (c & 3)));
+  const u32x2 lo = ld4_tr(M + row_off<W>(r0 + (c >> 2), c0 + 4 * (c & 3)));
+  const u32x2 hi = ld4_tr(M + row_off<W>(r0 + 4 + (c >> 2), c0 + 4 * (c & 3)));
   return pair(lo, hi);
 }
 // Accumulator-layout piece: M[r0 + 4g + j][c0 + c], j = 0..3.
+template <int W = 64>
 __device__ __forceinline__ u32x2 accp(const __bf16* M, int r0, int c0, int g, int c) {
-  return ld4_tr(M + row_off<64>(r0 + 4 * g + (c >> 2), c0 + 4 * (c & 3)));
+  return ld4_tr(M + row_off<W>(r0 + 4 * g + (c >> 2), c0 + 4 * (c & 3)));
 }
 // Stores an accumulator tile (rows r0 + 4g + j, column c0 + c) as bf16.
+template <int W = 64>
 __device__ __forceinline__ void st_acc(__bf16* M, int r0, int c0, int g, int c, const f32x4& v) {
   const u32x2 b = cvt4(v);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    M[row_off<64>(r0 + 4 * g + j, c0 + c)] =
+    M[row_off<W>(r0 + 4 * g + j, c0 + c)] =
         __builtin_bit_cast(__bf16, (unsigned short)((j & 1) ? b[j >> 1] >> 16 : b[j >> 1]));
 }
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // Decay 2^(g_t - g_u) for token t of block J and token u of block I, J > I,
-// from the tables (rows t of the lane: 4g + r in block J, or one row per lane).
+// from the tables ge (3 x 64) and fs (64).
+__device__ __forceinline__ float cross_decay(const float* ge, const float* fs, int I, int t, int u) {
+  return ge[64 * I + t] * fs[u];
+}
 __device__ __forceinline__ float cross_decay(const float* F, int I, int t, int u) {
-  return F[GradCfg::fGe + 64 * I + t] * F[GradCfg::fFs + u];
+  return cross_decay(F + GradCfg::fGe, F + GradCfg::fFs, I, t, u);
+}
+
+// Gate tables of a chunk, by one wave from its g (log2 prefix, lane t):
+// g, gamma, lambda, fs and ge (3 x 64) at the given offsets of F.  Returns g_C.
+__device__ __forceinline__ float gate_tables(float* F, float gl, int l, int oG, int oGam, int oLam, int oFs, int oGe) {
+  auto at = [&](int src_lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), src_lane));
+  };
+  const float e0 = at(15), e1 = at(31), e2 = at(47), gC = at(63);
+  const int blk = l >> 4;
+  const float gend = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gC;
+  F[oG + l] = gl;
+  F[oGam + l] = __builtin_amdgcn_exp2f(gl);
+  F[oLam + l] = __builtin_amdgcn_exp2f(gC - gl);
+  F[oFs + l] = __builtin_amdgcn_exp2f(gend - gl);
+  F[oGe + l] = __builtin_amdgcn_exp2f(blk > 0 ? gl - e0 : -INFINITY);
+  F[oGe + 64 + l] = __builtin_amdgcn_exp2f(blk > 1 ? gl - e1 : -INFINITY);
+  F[oGe + 128 + l] = __builtin_amdgcn_exp2f(blk > 2 ? gl - e2 : -INFINITY);
+  return gC;
 }
 
 __global__ __launch_bounds__(256, 2) void grad_kernel(GradArgs a) {
@@ -963,41 +1036,591 @@ __global__ __launch_bounds__(256, 2) void grad_kernel(GradArgs a) {
   }
 }
 
-}  // namespace grad
-
-// Workspace of the matrix-core gradient path (bf16, d = 64): the forward's
-// two-launch workspace (records, and the segment maps when it segments), then
-// the Tb^T records, the chunk start states and the chunk end gradients.
-struct GradLayout {
-  size_t fwd, recT, sck, dsck, total;
+// ------------------------------------------------ gradient pass at d = 128
+// The d = 64 workgroup holds K, Q, V, dO, S, dS', U, dX and the C x C
+// factors at once (79 KB).  At d = 128 the two states alone take 64 KB, so the
+// pass runs as two launches per (chain, chunk), handing U, dX (bf16) and the
+// value-side dg terms over through the workspace:
+//   cols: phases 0 and 1, eight waves (one per 16 value columns): dV, dbeta;
+//   rows: phases 2 to 4, four waves: dQ, dK, dalpha.  There the S and dS'
+//         rows are B operands read straight from global memory (16 contiguous
+//         bytes each), and only 64-column matrices sit in LDS.
+struct Grad128Cfg {
+  static constexpr int D = 128;
+  static constexpr int MAT = 64 * D * 2;  // a 64 x 128 bf16 matrix
+  // cols launch (bytes): K, Q, V, dO; S, dS' (128 x 128); phase 0 operand blocks (PT, GT, GL)
+  static constexpr int cK = 0, cQ = MAT, cV = 2 * MAT, cO = 3 * MAT, cS = 4 * MAT, cDS = 6 * MAT, cBL = 8 * MAT;
+  static constexpr int cF = cBL + 3 * 8192;
+  // fp32 arrays: g, beta, gamma, lambda, fs, ge[3]; per-wave dg and dbeta partials; Z.U and <dS', S> per wave
+  static constexpr int fG = 0, fB = 64, fGam = 128, fLam = 192, fFs = 256, fGe = 320, fDG = 512, fDB = fDG + 512,
+                       fZS = fDB + 512, fSS = fZS + 8, szF = fSS + 8;
+  static constexpr int cBytes = cF + szF * 4;
+  // rows launch (bytes): K, Q, dO, U, dX (64 x 128), D1 and D2 + D2^T (64 x 64)
+  static constexpr int rK = 0, rQ = MAT, rO = 2 * MAT, rU = 3 * MAT, rX = 4 * MAT, rD1 = 5 * MAT, rM2 = rD1 + 8192,
+                       rF = rM2 + 8192;
+  // fp32 arrays: g, gamma, lambda, fs, ge[3], the cols launch's dg terms, column partials [4][64], row sums
+  static constexpr int hG = 0, hGam = 64, hLam = 128, hFs = 192, hGe = 256, hDA = 448, hCP = 512, hRP = 768,
+                       szH = 832;
+  static constexpr int rBytes = rF + szH * 4;
+  static_assert(cBytes <= 160 * 1024 && rBytes <= 160 * 1024, "LDS budget");
 };
 
-static GradLayout grad_layout(int B, int T, int H) {
+__global__ __launch_bounds__(512, 1) void grad_cols_kernel(GradArgs a) {
+  using Cf = Grad128Cfg;
+  constexpr int D = Cf::D;
+  __shared__ __attribute__((aligned(16))) char smem[Cf::cBytes];
+  float* const F = reinterpret_cast<float*>(smem + Cf::cF);
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.T, H = a.H, nch = a.nch;
+  const int id = blockIdx.x;
+  const int h = id % H, bn = id / H, n = bn % nch, b = bn / nch;
+  const int chain = b * H + h, t0 = n * 64;
+  const size_t tokbase = (size_t)b * T * H + h, ck = (size_t)chain * nch + n;
+  const int rowB = H * D * 2;
+  const uint32_t spanR = span_bytes((size_t)T * H * D * 2, (size_t)h * D * 2);
+  const char* const rec = a.rec + ck * kRecBytes;
+  const char* const recT = a.recT + ck * kRecBytes;
+  auto M = [&](int off) { return reinterpret_cast<__bf16*>(smem + off); };
+
+  // ---- loads
+  {
+    const __bf16* src[4] = {a.k, a.q, a.v, a.dO};
+    const int dst[4] = {Cf::cK, Cf::cQ, Cf::cV, Cf::cO};
+    u32x4 x[4][2], st[2][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src[m] + tokbase * D, spanR);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int unit = tid + 512 * u, row = unit >> 4, pc = unit & 15;
+        x[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, row * rowB + 16 * pc, t0 * rowB, 0));
+      }
+    }
+    const u32x4* ss[2] = {reinterpret_cast<const u32x4*>(a.Sck + ck * D * D),
+                          reinterpret_cast<const u32x4*>(a.dSck + ck * D * D)};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st[m][u] = ss[m][tid + 512 * u];
+    if (w == 0) {
+      const float gl = reinterpret_cast<const float*>(rec + kRecG)[l];
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + tokbase, span_bytes((size_t)T * H * 4, (size_t)h * 4));
+      F[Cf::fB + l] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, t0 * H * 4, 0));
+      gate_tables(F, gl, l, Cf::fG, Cf::fGam, Cf::fLam, Cf::fFs, Cf::fGe);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int unit = tid + 512 * u, row = unit >> 4, pc = unit & 15;
+        *reinterpret_cast<u32x4*>(M(dst[m]) + row_off<D>(row, 8 * pc)) = x[m][u];
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int unit = tid + 512 * u, row = unit >> 4, pc = unit & 15;
+        *reinterpret_cast<u32x4*>(M(m == 0 ? Cf::cS : Cf::cDS) + row_off<D>(row, 8 * pc)) = st[m][u];
+      }
+  }
+  __syncthreads();
+
+  const __bf16* const mK = M(Cf::cK);
+  const __bf16* const mQ = M(Cf::cQ);
+  const __bf16* const mO = M(Cf::cO);
+  const float* const gt = F + Cf::fG;
+  const float gC = gt[63];
+  auto blob = [&](int which, int i, int p) {
+    return reinterpret_cast<u32x4*>(smem + Cf::cBL + which * 8192 + (i * 2 + p) * 1024) + l;
+  };
+
+  // ---- phase 0: waves 0-3 P^T of block row w, waves 4-7 Gt^T and Gt of block row w - 4
+  {
+    const int I = w & 3;
+    const bool pwave = w < 4;
+    u32x4 kI[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) kI[p] = rowp<D>(mK, 16 * I + c, 32 * p + 8 * g);
+    const float gu = gt[16 * I + c];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x2 h0[2], h1[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int J = 2 * p + hh;
+        h0[hh] = h1[hh] = z4();
+        const __bf16* const src = pwave ? mQ : mK;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) acc = mma32(rowp<D>(src, 16 * J + c, 32 * kp + 8 * g), kI[kp], acc);
+        const f32x4 gj = ld4f(gt + 16 * J + 4 * g);
+        if (J >= I) {  // P^T / Gt^T block (I, J): t = 16J + 4g + r, u = 16I + c
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * J + 4 * g + r, u = 16 * I + c;
+            const float m = J > I ? cross_decay(F + Cf::fGe, F + Cf::fFs, I, t, u)
+                                  : __builtin_amdgcn_exp2f(t >= u ? gj[r] - gu : -INFINITY);
+            v[r] = (pwave || t > u) ? acc[r] * m : 0.f;
+          }
+          h0[hh] = cvt4(v);
+        }
+        if (!pwave && J <= I) {  // Gt block (I, J): t = 16I + c, u = 16J + 4g + r (G symmetric)
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + c, u = 16 * J + 4 * g + r;
+            const float m = I > J ? cross_decay(F + Cf::fGe, F + Cf::fFs, J, t, u)
+                                  : __builtin_amdgcn_exp2f(t > u ? gu - gj[r] : -INFINITY);
+            v[r] = acc[r] * m;
+          }
+          h1[hh] = cvt4(v);
+        }
+      }
+      if (pwave) {
+        *blob(0, I, p) = pair(h0[0], h0[1]);
+      } else {
+        *blob(1, I, p) = pair(h0[0], h0[1]);
+        *blob(2, I, p) = pair(h1[0], h1[1]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: value columns cw .. cw + 15
+  const int cw = 16 * w;
+  f32x4 U[4], DX[4];
+  {
+    const __bf16* const mS = M(Cf::cS);
+    const __bf16* const mDS = M(Cf::cDS);
+    u32x4 sB[4], dsB[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      sB[p] = colp<D>(mS, 32 * p + 8 * g, cw, c);
+      dsB[p] = colp<D>(mDS, 32 * p + 8 * g, cw, c);
+    }
+    {
+      float ss = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += lo_f(sB[p][e]) * lo_f(dsB[p][e]) + hi_f(sB[p][e]) * hi_f(dsB[p][e]);
+      ss = lane::wave_sum(ss);
+      if (l == 0) F[Cf::fSS + w] = ss;
+    }
+    u32x2 oB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oB[i] = accp<D>(mO, 16 * i, cw, g, c);
+    float dgr[4][4];
+    f32x4 KS[4], X[4];
+    u32x2 ub[4];
+    {
+      u32x2 xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x2 vB = accp<D>(M(Cf::cV), 16 * i, cw, g, c);
+        f32x4 qs = zero4(), ks = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          qs = mma32(rowp<D>(mQ, 16 * i + c, 32 * p + 8 * g), sB[p], qs);
+          ks = mma32(rowp<D>(mK, 16 * i + c, 32 * p + 8 * g), sB[p], ks);
+        }
+        const f32x4 gm = ld4f(F + Cf::fGam + 16 * i + 4 * g);
+        KS[i] = ks;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dgr[i][j] = gm[j] * qs[j] * bf_at(oB[i], j);
+          X[i][j] = bf_at(vB, j) - gm[j] * ks[j];
+        }
+        xb[i] = cvt4(X[i]);
+      }
+      u32x4 tb[6];
+#pragma unroll
+      for (int e = 0; e < 6; ++e) tb[e] = reinterpret_cast<const u32x4*>(rec + kRecTb + e * 1024)[l];
+      const u32x4 x01 = pair(xb[0], xb[1]), x23 = pair(xb[2], xb[3]);
+      U[0] = mma32(tb[pblk(0, 0)], x01, zero4());
+      U[1] = mma32(tb[pblk(1, 0)], x01, zero4());
+      U[2] = mma32(tb[pblk(2, 1)], x23, mma32(tb[pblk(2, 0)], x01, zero4()));
+      U[3] = mma32(tb[pblk(3, 1)], x23, mma32(tb[pblk(3, 0)], x01, zero4()));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ub[i] = cvt4(U[i]);
+    }
+    f32x4 dU[4], Z[4];
+    {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 z = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) z = mma32(rowp<D>(mK, 16 * i + c, 32 * p + 8 * g), dsB[p], z);
+        const f32x4 lm = ld4f(F + Cf::fLam + 16 * i + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Z[i][j] = lm[j] * z[j];
+      }
+      const u32x4 o01 = pair(oB[0], oB[1]), o23 = pair(oB[2], oB[3]);
+      dU[0] = mma32(*blob(0, 0, 1), o23, mma32(*blob(0, 0, 0), o01, Z[0]));
+      dU[1] = mma32(*blob(0, 1, 1), o23, mma32(*blob(0, 1, 0), o01, Z[1]));
+      dU[2] = mma32(*blob(0, 2, 1), o23, Z[2]);
+      dU[3] = mma32(*blob(0, 3, 1), o23, Z[3]);
+    }
+    u32x2 dxb[4];
+    float zsum = 0.f;
+    {
+      u32x2 dub[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dub[i] = cvt4(dU[i]);
+      u32x4 tt[6];
+#pragma unroll
+      for (int e = 0; e < 6; ++e) tt[e] = reinterpret_cast<const u32x4*>(recT + kRecTb + e * 1024)[l];
+      const u32x4 d01 = pair(dub[0], dub[1]), d23 = pair(dub[2], dub[3]);
+      DX[0] = mma32(tt[qblk(0, 1)], d23, mma32(tt[qblk(0, 0)], d01, zero4()));
+      DX[1] = mma32(tt[qblk(1, 1)], d23, mma32(tt[qblk(1, 0)], d01, zero4()));
+      DX[2] = mma32(tt[qblk(2, 1)], d23, zero4());
+      DX[3] = mma32(tt[qblk(3, 1)], d23, zero4());
+      const __amdgpu_buffer_rsrc_t rdv =
+          make_rsrc(a.dv + tokbase * D + cw, span_bytes((size_t)T * H * D * 4, ((size_t)h * D + cw) * 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dxb[i] = cvt4(DX[i]);
+        const f32x4 gm = ld4f(F + Cf::fGam + 16 * i + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * i + 4 * g + j;
+          const float dvv = DX[i][j];  // through a scalar (see the d = 64 kernel)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, dvv), rdv, r * H * D * 4 + 4 * c,
+                                                t0 * H * D * 4, 0);
+          const float zu = Z[i][j] * U[i][j];
+          zsum += zu;
+          dgr[i][j] -= gm[j] * KS[i][j] * dvv + zu;
+        }
+      }
+    }
+    {
+      const u32x4 x01 = pair(dxb[0], dxb[1]), x23 = pair(dxb[2], dxb[3]);
+      const u32x4 u01 = pair(ub[0], ub[1]), u23 = pair(ub[2], ub[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 t = mma32(*blob(1, i, 1), x23, mma32(*blob(1, i, 0), x01, zero4()));
+        const f32x4 rr = mma32(*blob(2, i, 1), u23, mma32(*blob(2, i, 0), u01, zero4()));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * i + 4 * g + j;
+          const float db = row16_sum((dU[i][j] - t[j]) * (X[i][j] - rr[j]));
+          const float dg = row16_sum(dgr[i][j]);
+          if (c == 0) {
+            F[Cf::fDB + 64 * w + r] = db;
+            F[Cf::fDG + 64 * w + r] = dg;
+          }
+        }
+      }
+      zsum = lane::wave_sum(zsum);
+      if (l == 0) F[Cf::fZS + w] = zsum;
+    }
+  }
+  __syncthreads();  // V and dO are dead: U and dX go through their space to the workspace
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st_acc<D>(M(Cf::cV), 16 * i, cw, g, c, U[i]);
+    st_acc<D>(M(Cf::cO), 16 * i, cw, g, c, DX[i]);
+  }
+  __syncthreads();
+  {
+    u32x4* const uw = reinterpret_cast<u32x4*>(a.Uw + ck * 64 * D);
+    u32x4* const xw = reinterpret_cast<u32x4*>(a.Xw + ck * 64 * D);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int unit = tid + 512 * u, row = unit >> 4, pc = unit & 15;
+      uw[unit] = *reinterpret_cast<const u32x4*>(M(Cf::cV) + row_off<D>(row, 8 * pc));
+      xw[unit] = *reinterpret_cast<const u32x4*>(M(Cf::cO) + row_off<D>(row, 8 * pc));
+    }
+  }
+  if (w == 0) {
+    const int t = l;
+    float dg = 0.f, db = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      dg += F[Cf::fDG + 64 * v + t];
+      db += F[Cf::fDB + 64 * v + t];
+    }
+    if (t == 63) {
+      float ss = 0.f, zt = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        ss += F[Cf::fSS + v];
+        zt += F[Cf::fZS + v];
+      }
+      dg += __builtin_amdgcn_exp2f(gC) * ss + zt;
+    }
+    a.dgA[ck * 64 + t] = dg;
+    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)h * 4);
+    const __amdgpu_buffer_rsrc_t rdb = make_rsrc(a.dbeta + tokbase, spanG);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, db), rdb, t * H * 4, t0 * H * 4, 0);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void grad_rows_kernel(GradArgs a) {
+  using Cf = Grad128Cfg;
+  constexpr int D = Cf::D;
+  __shared__ __attribute__((aligned(16))) char smem[Cf::rBytes];
+  float* const F = reinterpret_cast<float*>(smem + Cf::rF);
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.T, H = a.H, nch = a.nch;
+  const int id = blockIdx.x;
+  const int h = id % H, bn = id / H, n = bn % nch, b = bn / nch;
+  const int chain = b * H + h, t0 = n * 64;
+  const size_t tokbase = (size_t)b * T * H + h, ck = (size_t)chain * nch + n;
+  const int rowB = H * D * 2;
+  const uint32_t spanR = span_bytes((size_t)T * H * D * 2, (size_t)h * D * 2);
+  const char* const rec = a.rec + ck * kRecBytes;
+  auto M = [&](int off) { return reinterpret_cast<__bf16*>(smem + off); };
+
+  // ---- loads: K, Q, dO rows; U and dX from the cols launch; its dg terms
+  {
+    const __bf16* src[3] = {a.k, a.q, a.dO};
+    const int dst[3] = {Cf::rK, Cf::rQ, Cf::rO};
+    u32x4 x[3][4], y[2][4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src[m] + tokbase * D, spanR);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int unit = tid + 256 * u, row = unit >> 4, pc = unit & 15;
+        x[m][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, row * rowB + 16 * pc, t0 * rowB, 0));
+      }
+    }
+    const u32x4* hw[2] = {reinterpret_cast<const u32x4*>(a.Uw + ck * 64 * D),
+                          reinterpret_cast<const u32x4*>(a.Xw + ck * 64 * D)};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[m][u] = hw[m][tid + 256 * u];
+    if (w == 0) {
+      const float gl = reinterpret_cast<const float*>(rec + kRecG)[l];
+      gate_tables(F, gl, l, Cf::hG, Cf::hGam, Cf::hLam, Cf::hFs, Cf::hGe);
+      F[Cf::hDA + l] = a.dgA[ck * 64 + l];
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int unit = tid + 256 * u, row = unit >> 4, pc = unit & 15;
+        *reinterpret_cast<u32x4*>(M(dst[m]) + row_off<D>(row, 8 * pc)) = x[m][u];
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int unit = tid + 256 * u, row = unit >> 4, pc = unit & 15;
+        *reinterpret_cast<u32x4*>(M(m == 0 ? Cf::rU : Cf::rX) + row_off<D>(row, 8 * pc)) = y[m][u];
+      }
+  }
+  __syncthreads();
+
+  const __bf16* const mK = M(Cf::rK);
+  const __bf16* const mQ = M(Cf::rQ);
+  const __bf16* const mO = M(Cf::rO);
+  const __bf16* const mU = M(Cf::rU);
+  const __bf16* const mX = M(Cf::rX);
+  const float* const gt = F + Cf::hG;
+
+  // ---- phase 2: token rows 16I .. 16I + 15, I = w
+  {
+    const int I = w;
+    __bf16* const mD1 = M(Cf::rD1);
+    __bf16* const mM2 = M(Cf::rM2);
+    u32x4 oR[4], xR[4], qI[4], kI[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      oR[p] = rowp<D>(mO, 16 * I + c, 32 * p + 8 * g);
+      xR[p] = rowp<D>(mX, 16 * I + c, 32 * p + 8 * g);
+      qI[p] = rowp<D>(mQ, 16 * I + c, 32 * p + 8 * g);
+      kI[p] = rowp<D>(mK, 16 * I + c, 32 * p + 8 * g);
+    }
+    const f32x4 gI = ld4f(gt + 16 * I + 4 * g);
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > I) {
+        st_acc<64>(mD1, 16 * I, 16 * J, g, c, zero4());
+        if (g == 0) F[Cf::hCP + 64 * w + 16 * J + c] = 0.f;
+        continue;
+      }
+      f32x4 dP = zero4(), dG = zero4(), P = zero4(), G = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x4 uJ = rowp<D>(mU, 16 * J + c, 32 * p + 8 * g);
+        const u32x4 kJ = rowp<D>(mK, 16 * J + c, 32 * p + 8 * g);
+        dP = mma32(oR[p], uJ, dP);
+        dG = mma32(xR[p], uJ, dG);
+        P = mma32(qI[p], kJ, P);
+        G = mma32(kI[p], kJ, G);
+      }
+      const float gu = gt[16 * J + c];
+      f32x4 d1, d2;
+      float cs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 16 * I + 4 * g + r, uj = 16 * J + c;
+        const float m = I > J ? cross_decay(F + Cf::hGe, F + Cf::hFs, J, ti, uj)
+                              : __builtin_amdgcn_exp2f(ti >= uj ? gI[r] - gu : -INFINITY);
+        const float ms = ti > uj ? m : 0.f;
+        d1[r] = dP[r] * m;
+        d2[r] = -dG[r] * ms;
+        const float e = d1[r] * P[r] + d2[r] * G[r];
+        rs[r] += e;
+        cs += e;
+      }
+      cs = col4_sum(cs);
+      if (g == 0) F[Cf::hCP + 64 * w + 16 * J + c] = cs;
+      st_acc<64>(mD1, 16 * I, 16 * J, g, c, d1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 16 * I + 4 * g + r, uj = 16 * J + c;
+        const __bf16 val = __builtin_bit_cast(__bf16, (unsigned short)(cvt2(d2[r], 0.f) & 0xffffu));
+        if (J < I || ti > uj) {
+          mM2[row_off<64>(ti, uj)] = val;
+          mM2[row_off<64>(uj, ti)] = val;
+        } else if (ti == uj) {
+          mM2[row_off<64>(ti, uj)] = __builtin_bit_cast(__bf16, (unsigned short)0);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = row16_sum(rs[r]);
+      if (c == 0) F[Cf::hRP + 16 * I + 4 * g + r] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: key columns 32w .. 32w + 31, two 16-column blocks
+  {
+    const __bf16* const mD1 = M(Cf::rD1);
+    const __bf16* const mM2 = M(Cf::rM2);
+    const __bf16* const Sg = a.Sck + ck * D * D;
+    const __bf16* const dSg = a.dSck + ck * D * D;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kw = 32 * w + 16 * kb;
+      u32x4 kB[2], qB[2], sR[4], dsR[4];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        kB[p] = colp<D>(mK, 32 * p + 8 * g, kw, c);
+        qB[p] = colp<D>(mQ, 32 * p + 8 * g, kw, c);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {  // rows kw + c of S and dS', value columns 32p + 8g .. + 7
+        sR[p] = *reinterpret_cast<const u32x4*>(Sg + (size_t)(kw + c) * D + 32 * p + 8 * g);
+        dsR[p] = *reinterpret_cast<const u32x4*>(dSg + (size_t)(kw + c) * D + 32 * p + 8 * g);
+      }
+      const __amdgpu_buffer_rsrc_t rdq =
+          make_rsrc(a.dq + tokbase * D + kw, span_bytes((size_t)T * H * D * 4, ((size_t)h * D + kw) * 4));
+      const __amdgpu_buffer_rsrc_t rdk =
+          make_rsrc(a.dk + tokbase * D + kw, span_bytes((size_t)T * H * D * 4, ((size_t)h * D + kw) * 4));
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 q1 = zero4(), q2 = zero4(), k1 = zero4(), k3 = zero4(), k4 = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          q1 = mma32(rowp<64>(mD1, 16 * I + c, 32 * p + 8 * g), kB[p], q1);
+          k1 = mma32(colp<64>(mD1, 32 * p + 8 * g, 16 * I, c), qB[p], k1);
+          k1 = mma32(rowp<64>(mM2, 16 * I + c, 32 * p + 8 * g), kB[p], k1);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          q2 = mma32(rowp<D>(mO, 16 * I + c, 32 * p + 8 * g), sR[p], q2);
+          k3 = mma32(rowp<D>(mU, 16 * I + c, 32 * p + 8 * g), dsR[p], k3);
+          k4 = mma32(rowp<D>(mX, 16 * I + c, 32 * p + 8 * g), sR[p], k4);
+        }
+        const f32x4 gm = ld4f(F + Cf::hGam + 16 * I + 4 * g), lm = ld4f(F + Cf::hLam + 16 * I + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * I + 4 * g + j;
+          const float dqv = q1[j] + gm[j] * q2[j];
+          const float dkv = k1[j] + lm[j] * k3[j] - gm[j] * k4[j];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, dqv), rdq, r * H * D * 4 + 4 * c,
+                                                t0 * H * D * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, dkv), rdk, r * H * D * 4 + 4 * c,
+                                                t0 * H * D * 4, 0);
+        }
+      }
+    }
+  }
+
+  // ---- phase 4: dg, d ln alpha as suffix sums, dalpha
+  __syncthreads();
+  if (w == 0) {
+    const int t = l;
+    float dg = F[Cf::hDA + t] + F[Cf::hRP + t];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dg -= F[Cf::hCP + 64 * v + t];
+    const float pre = wave_prefix_sum(dg);
+    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), 63));
+    const float dla = tot - pre + dg;
+    const uint32_t spanG = span_bytes((size_t)T * H * 4, (size_t)h * 4);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.alpha + tokbase, spanG);
+    const float al = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, t * H * 4, t0 * H * 4, 0));
+    const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.dalpha + tokbase, spanG);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, dla / al), rda, t * H * 4, t0 * H * 4, 0);
+  }
+}
+
+}  // namespace grad
+
+// Workspace of the matrix-core gradient path: the forward's two-launch
+// workspace (records, and the segment maps when it segments), then the Tb^T
+// records, the chunk start states and the chunk end gradients (bf16, D x D);
+// at D = 128 also U, dX and the value-side dg terms for the second half of the
+// gradient pass.
+struct GradLayout {
+  size_t fwd, recT, sck, dsck, uw, xw, dga, total;
+};
+
+static GradLayout grad_layout(int B, int T, int H, int D) {
   ChunkArgs f{};
   f.B = B;
   f.T = T;
   f.H = H;
-  f.dk = 64;
-  f.dv = 64;
+  f.dk = D;
+  f.dv = D;
   f.dtype = kDtBF16;
-  const size_t chains = (size_t)B * H, nch = (size_t)(T + 63) / 64;
+  const size_t chains = (size_t)B * H, nch = (size_t)(T + 63) / 64, cn = chains * nch;
   GradLayout L;
   L.fwd = (chunk_two_workspace_bytes(f) + 255) & ~(size_t)255;
   L.recT = L.fwd;
-  L.sck = L.recT + chains * nch * pipe::kRecBytes;
-  L.dsck = L.sck + chains * nch * 64 * 64 * 2;
-  L.total = L.dsck + chains * nch * 64 * 64 * 2;
+  L.sck = L.recT + cn * pipe::kRecBytes;
+  L.dsck = L.sck + cn * D * D * 2;
+  L.uw = L.dsck + cn * D * D * 2;
+  L.xw = L.uw + (D == 128 ? cn * 64 * D * 2 : 0);
+  L.dga = L.xw + (D == 128 ? cn * 64 * D * 2 : 0);
+  L.total = L.dga + (D == 128 ? cn * 64 * 4 : 0);
   return L;
 }
 
-size_t chunk_grad_workspace_bytes(int B, int T, int H) { return T > 0 ? grad_layout(B, T, H).total : 0; }
+size_t chunk_grad_workspace_bytes(int B, int T, int H, int D) { return T > 0 ? grad_layout(B, T, H, D).total : 0; }
+
+namespace grad {
+// T = 0: dS0 = dS_T (or zero).  One thread per element.
+__global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+}  // namespace grad
 
 hipError_t launch_chunk_grad(const BwdArgs& a) {
-  const GradLayout L = grad_layout(a.B, a.T, a.H);
-  char* const ws = static_cast<char*>(a.workspace);
   hipStream_t st = (hipStream_t)a.stream;
-  const int nch = (a.T + 63) / 64;
+  const int D = a.D;
   const long chains = (long)a.B * a.H;
+  if (a.T == 0) {
+    if (!a.dS0) return hipSuccess;
+    const size_t n = (size_t)chains * D * D;
+    return launch_kernel(grad::copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a.dS_final,
+                         a.dS0, n);
+  }
+  const GradLayout L = grad_layout(a.B, a.T, a.H, D);
+  char* const ws = static_cast<char*>(a.workspace);
+  const int nch = (a.T + 63) / 64;
   ChunkArgs f{};
   f.q = a.q;
   f.k = a.k;
@@ -1010,8 +1633,8 @@ hipError_t launch_chunk_grad(const BwdArgs& a) {
   f.B = a.B;
   f.T = a.T;
   f.H = a.H;
-  f.dk = 64;
-  f.dv = 64;
+  f.dk = D;
+  f.dv = D;
   f.dtype = kDtBF16;
   f.stream = a.stream;
   hipError_t e = launch_chunk_two_states(f, ws, ws + L.recT, ws + L.sck);
@@ -1026,10 +1649,15 @@ hipError_t launch_chunk_grad(const BwdArgs& a) {
   j.dS0 = a.dS0;
   j.T = a.T;
   j.H = a.H;
-  j.DV = 64;
+  j.DV = D;
   j.nch = nch;
-  using ACf = grad::AdjCfg<64, 2>;
-  e = launch_kernel(grad::adj_kernel<64, 2>, dim3((unsigned)(chains * (64 / ACf::NV))), dim3(ACf::kThreads), st, j);
+  if (D == 64) {
+    using ACf = grad::AdjCfg<64, 2>;
+    e = launch_kernel(grad::adj_kernel<64, 2>, dim3((unsigned)(chains * (D / ACf::NV))), dim3(ACf::kThreads), st, j);
+  } else {
+    using ACf = grad::AdjCfg<128, 1>;
+    e = launch_kernel(grad::adj_kernel<128, 1>, dim3((unsigned)(chains * (D / ACf::NV))), dim3(ACf::kThreads), st, j);
+  }
   if (e != hipSuccess) return e;
   grad::GradArgs gr{};
   gr.q = static_cast<const __bf16*>(a.q);
@@ -1050,7 +1678,14 @@ hipError_t launch_chunk_grad(const BwdArgs& a) {
   gr.T = a.T;
   gr.H = a.H;
   gr.nch = nch;
-  return launch_kernel(grad::grad_kernel, dim3((unsigned)(chains * nch)), dim3(256), st, gr);
+  const dim3 grid((unsigned)(chains * nch));
+  if (D == 64) return launch_kernel(grad::grad_kernel, grid, dim3(256), st, gr);
+  gr.Uw = reinterpret_cast<__bf16*>(ws + L.uw);
+  gr.Xw = reinterpret_cast<__bf16*>(ws + L.xw);
+  gr.dgA = reinterpret_cast<float*>(ws + L.dga);
+  e = launch_kernel(grad::grad_cols_kernel, grid, dim3(512), st, gr);
+  if (e != hipSuccess) return e;
+  return launch_kernel(grad::grad_rows_kernel, grid, dim3(256), st, gr);
 }
 
 }  // namespace gdn

@@ -346,11 +346,12 @@ struct Consumer2 {
       }
   }
 
+  // The state's bf16 operands, also handed to the output wave when hs is given.
   __device__ __forceinline__ void publish_state(unsigned* hs) {
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
       sfr[d] = cvt4(S[d]);
-      *reinterpret_cast<u32x2*>(hs + 2 * ((w * NDT + d) * 64 + l)) = sfr[d];
+      if (hs) *reinterpret_cast<u32x2*>(hs + 2 * ((w * NDT + d) * 64 + l)) = sfr[d];
     }
   }
 
@@ -358,14 +359,22 @@ struct Consumer2 {
   __device__ __forceinline__ void chunk(const char* R, unsigned* hu, bool mzero) {
     const __bf16* const Rb = reinterpret_cast<const __bf16*>(R);
     const float* const Gt = reinterpret_cast<const float*>(R + Cf::oGt);
-    u32x4 kr[4][NKP];
+    // At d = 128 the K rows are read one 16-row block at a time and half of the
+    // update's K^T operands after the Tb product: with everything held at once
+    // the consumer needs more than its 256 registers and spills every step.
+    constexpr int KRB = DK == 128 ? 1 : 4;    // row blocks of K read ahead of the K S products
+    constexpr int KTB = DK == 128 ? 4 : NDT;  // key blocks of K^T read ahead of the Tb product
+    u32x4 kr[KRB][NKP];
     u32x2 vv[4];
     f32x4 gg[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    auto krow = [&](int i, u32x4 (&dst)[NKP]) {
 #pragma unroll
       for (int p = 0; p < NKP; ++p)
-        kr[i][p] = *reinterpret_cast<const u32x4*>(Rb + Cf::oK / 2 + row_off<DK>(16 * i + c, 32 * p + 8 * g));
+        dst[p] = *reinterpret_cast<const u32x4*>(Rb + Cf::oK / 2 + row_off<DK>(16 * i + c, 32 * p + 8 * g));
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < KRB) krow(i, kr[i]);
       vv[i] = ld4_tr(Rb + Cf::oV / 2 + (16 * i + 4 * g + (c >> 2)) * Cf::LDV + 16 * w + 4 * (c & 3));
       gg[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gGam + 16 * i + 4 * g);
     }
@@ -377,9 +386,16 @@ struct Consumer2 {
     u32x2 xb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      u32x4 ki[NKP];
+      if (i < KRB) {
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) ki[p] = kr[i < KRB ? i : 0][p];
+      } else {
+        krow(i, ki);
+      }
       f32x4 acc = zero4();
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) acc = mma32(kr[i][p], pair(sfr[2 * p], sfr[2 * p + 1]), acc);
+      for (int p = 0; p < NKP; ++p) acc = mma32(ki[p], pair(sfr[2 * p], sfr[2 * p + 1]), acc);
       f32x4 x;
       const u32x2 v = vv[i];
       const float v0 = mzero ? 0.f : lo_f(v[0]), v1 = mzero ? 0.f : hi_f(v[0]);
@@ -391,13 +407,15 @@ struct Consumer2 {
       xb[i] = cvt4(x);
     }
     // Operands of the update, in flight during the Tb product.
-    u32x2 kt[NDT][4];
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
+    auto ktr = [&](int d, u32x2 (&dst)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        kt[d][i] = ld4_tr(Rb + Cf::oK / 2 +
-                          row_off<DK>(16 * i + 4 * g + (c >> 2), 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3)));
+        dst[i] = ld4_tr(Rb + Cf::oK / 2 +
+                        row_off<DK>(16 * i + 4 * g + (c >> 2), 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3)));
+    };
+    u32x2 kt[KTB][4];
+#pragma unroll
+    for (int d = 0; d < KTB; ++d) ktr(d, kt[d]);
     f32x4 lm[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lm[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gLam + 16 * i + 4 * g);
@@ -422,24 +440,35 @@ struct Consumer2 {
     // S <- gamma_C S + K^T (lambda * Ut)
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
+      u32x2 kd[4];
+      if (d < KTB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kd[i] = kt[d < KTB ? d : 0][i];
+      } else {
+        ktr(d, kd);
+      }
       f32x4 sd = S[d];
 #pragma unroll
       for (int j = 0; j < 4; ++j) sd[j] *= gC;
-      sd = mma2(kt[d][0], kt[d][1], XL[0], XL[1], sd);
-      sd = mma2(kt[d][2], kt[d][3], XL[2], XL[3], sd);
+      sd = mma2(kd[0], kd[1], XL[0], XL[1], sd);
+      sd = mma2(kd[2], kd[3], XL[2], XL[3], sd);
       S[d] = sd;
     }
   }
 
-  // The state at the start of local chunk k (its bf16 operand copy) into the chunk-state array.
+  // The state at the start of local chunk k (its bf16 operand copy) into the
+  // chunk-state array, through a buffer resource with 32-bit offsets formed
+  // here (64-bit per-element addresses held across the loop would spill).
   __device__ __forceinline__ void store_start(const StateArgs& a, const Seg& sg, int k) {
-    __bf16* const dst = a.Sck + ((size_t)sg.chain * a.nch + sg.n0 + k) * DK * a.DV + sg.dv0 + 16 * w + c;
+    const size_t base = ((size_t)sg.chain * a.nch + sg.n0 + k) * DK * a.DV + sg.dv0 + 16 * w;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.Sck + base, (uint32_t)(DK * a.DV * 2));
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const unsigned u = sfr[d][j >> 1];
-        dst[(size_t)key_row(d, g, j) * a.DV] = __builtin_bit_cast(__bf16, (unsigned short)((j & 1) ? u >> 16 : u));
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)((j & 1) ? u >> 16 : u), rs,
+                                              (key_row(d, g, j) * a.DV + c) * 2, 0, 0);
       }
   }
 
@@ -489,15 +518,17 @@ __device__ __forceinline__ void consumer_role(const StateArgs& a, const Seg& sg,
   using Cf = StateCfg<DK, NC>;
   Consumer2<DK, NC> cs;
   cs.init(a, sg, w, l);
-  const bool out = a.mode == kOut;
+  // Output mode without an output array (the gradient pass's forward, which
+  // keeps only the chunk states): nothing is handed to the output wave.
+  const bool out = a.mode == kOut, form = out && a.out;
   run_steps2(sg.nloc, [&](auto pc, int k) {
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
-    if (k == -1) cs.publish_state(reinterpret_cast<unsigned*>(smem + Cf::oHS));  // start state of chunk 0
+    if (k == -1) cs.publish_state(form ? reinterpret_cast<unsigned*>(smem + Cf::oHS) : nullptr);  // chunk 0's start
     if (k >= 0 && k < sg.nloc) {
       if (out && a.Sck) cs.store_start(a, sg, k);
-      unsigned* hu = out ? reinterpret_cast<unsigned*>(smem + Cf::oHU + (k & 1) * Cf::szHU) : nullptr;
+      unsigned* hu = form ? reinterpret_cast<unsigned*>(smem + Cf::oHU + (k & 1) * Cf::szHU) : nullptr;
       cs.chunk(smem + slot * Cf::szSlot, hu, sg.mcol);
-      cs.publish_state(reinterpret_cast<unsigned*>(smem + Cf::oHS + ((k + 1) & 1) * Cf::szHS));
+      cs.publish_state(form ? reinterpret_cast<unsigned*>(smem + Cf::oHS + ((k + 1) & 1) * Cf::szHS) : nullptr);
     }
   });
   cs.finish(a, sg);
@@ -510,10 +541,10 @@ __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* 
   using Cf = StateCfg<DK, NC>;
   constexpr int NKP = Cf::NKP;
   const int g = l >> 4, c = l & 15;
-  const bool out = a.mode == kOut;
+  const bool form = a.mode == kOut && a.out;
   run_steps2(sg.nloc, [&](auto pc, int k) {
     constexpr int slot = (decltype(pc)::value + 1) % 3;
-    if (!out || k < 0 || k >= sg.nloc) return;
+    if (!form || k < 0 || k >= sg.nloc) return;
     const char* R = smem + slot * Cf::szSlot;
     const __bf16* const Rb = reinterpret_cast<const __bf16*>(R);
     const float* const Gt = reinterpret_cast<const float*>(R + Cf::oGt);
@@ -575,15 +606,13 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
   using Cf = StateCfg<DK, NC>;
   constexpr int NKP = Cf::NKP, NDT = Cf::NDT;
   const int g = l >> 4, c = l & 15;
-  if (a.mode != kOut) {
+  if (a.mode != kOut || !a.out) {
     run_steps2(sg.nloc, [&](auto, int) {});
     return;
   }
   const int H = a.H, T = a.T, DV = a.DV;
-  // No output array (the gradient pass's forward): every store is dropped by the empty range.
-  const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(a.out + ((size_t)sg.b * T * H + sg.h) * DV + sg.dv0,
-                a.out ? span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + ((size_t)sg.b * T * H + sg.h) * DV + sg.dv0,
+                                              span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2));
   const int rowO = H * DV * 2, vofO = c * rowO + 8 * g;
   const int tok0 = sg.n0 * 64;
   f32x4 o[4][NC];

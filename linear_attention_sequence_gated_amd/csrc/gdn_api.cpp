@@ -58,11 +58,12 @@ bool two_path(int B, int T, int H, int dk, int dv, int dtype) {
   return dk == 128 || gdn::chunk_two_segments(shape_args(B, T, H, dk, dv, dtype)) > 1;
 }
 
-// The backward's matrix-core path: bf16, d = 64, T > 0, rows addressable with
-// 32-bit offsets (fp32 gradient rows included) and the chunk grid in range.
-// Other real inputs take the token-by-token kernel (fp32 throughout).
+// The backward's matrix-core path: bf16, d = 64 (T > 0) or 128 (any T), rows
+// addressable with 32-bit offsets (fp32 gradient rows included) and the chunk
+// grid in range.  fp32 inputs take the token-by-token kernel (fp32
+// throughout, d = 64).
 bool grad_path(int B, int T, int H, int dk, int dv, int dtype) {
-  if (dtype != GDN_BF16 || dk != 64 || dv != 64 || T <= 0) return false;
+  if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128) || (dk == 64 && T <= 0)) return false;
   if ((long long)T * H * dk * 4 >= (1LL << 31)) return false;
   return (long long)B * H * ((T + 63) / 64) < (1LL << 30);
 }
@@ -156,8 +157,9 @@ int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const fl
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
-  if (B < 0 || T < 0 || H < 0 || (dtype != GDN_F32 && dtype != GDN_BF16) || dk != 64 || dv != 64) return 0;
-  if (grad_path(B, T, H, dk, dv, dtype)) return gdn::chunk_grad_workspace_bytes(B, T, H);
+  if (B < 0 || T < 0 || H < 0 || (dtype != GDN_F32 && dtype != GDN_BF16)) return 0;
+  if (grad_path(B, T, H, dk, dv, dtype)) return gdn::chunk_grad_workspace_bytes(B, T, H, dk);
+  if (dk != 64 || dv != 64) return 0;
   return gdn::chunk_bwd_workspace_bytes(B, T, H);
 }
 
@@ -170,7 +172,9 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
       !chains_fit((long long)B * H, 256))
     return GDN_ERR_SHAPE;
-  if (dtype == GDN_C64 || dk != 64 || dv != 64 || (long long)T * H * 4 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
+  const bool mfma = grad_path(B, T, H, dk, dv, dtype);
+  if (dtype == GDN_C64 || (!mfma && (dk != 64 || dv != 64 || (long long)T * H * 4 >= (1LL << 31))))
+    return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v || !grad_alpha ||
                  !grad_beta))
@@ -179,12 +183,12 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
                         grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_S0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-  const bool mfma = grad_path(B, T, H, dk, dv, dtype);
-  const size_t need = mfma ? gdn::chunk_grad_workspace_bytes(B, T, H) : gdn::chunk_bwd_workspace_bytes(B, T, H);
+  const size_t need = mfma ? gdn::chunk_grad_workspace_bytes(B, T, H, dk) : gdn::chunk_bwd_workspace_bytes(B, T, H);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::BwdArgs a{q,      k,      v,      alpha,      beta,      S0,      grad_out, grad_S_final, grad_q, grad_k,
                  grad_v, grad_alpha, grad_beta, grad_S0, workspace, B, T, H, dtype, stream};
+  a.D = dk;
   if (mfma) return gdn::launch_chunk_grad(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -73,6 +73,7 @@ struct BwdArgs {
   void* workspace;
   int B, T, H, dtype;
   void* stream;
+  int D = 64;  // dk = dv
 };
 
 // Forward with a per-output-channel decay r [B, T, H, dv] (real dtypes, d = 64).
@@ -109,9 +110,10 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
-// bf16, d = 64, T > 0: the chunk form on the matrix cores (the forward's
+// bf16, d = 64 or 128: the chunk form on the matrix cores (the forward's
 // factor and state passes, the adjoint scan, the chunk-parallel gradients).
-size_t chunk_grad_workspace_bytes(int B, int T, int H);
+// T = 0 copies dS_final (or zeros) to dS0.
+size_t chunk_grad_workspace_bytes(int B, int T, int H, int D);
 hipError_t launch_chunk_grad(const BwdArgs& a);
 hipError_t launch_channel_decay(const ChannelArgs& a);  // token loop (fp32 inputs)
 hipError_t launch_channel_chunk(const ChannelArgs& a);  // chunk form on the matrix cores (bf16 inputs)

@@ -161,7 +161,8 @@ def backward(**kw):
     (dict(dtype=5), raw.GDN_ERR_DTYPE),
     (dict(H=-1), raw.GDN_ERR_SHAPE),
     (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
-    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),              # fp32: d = 64 only
+    (dict(dtype=gdn.GDN_BF16, dk=128, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
@@ -184,6 +185,10 @@ def test_backward_empty_and_workspace_query():
                     workspace_bytes=0) == raw.GDN_OK
     # bf16: the matrix-core path -- two 6400-byte records, a bf16 start state and a bf16 end gradient per chunk
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_BF16) == 2 * 3 * 2 * (2 * 6400 + 2 * 8192)
+    # bf16 d = 128: also U and dX (bf16 64 x 128) and 64 fp32 dg terms per chunk
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 128, 128, gdn.GDN_BF16) == \
+        2 * 3 * 2 * (2 * 6400 + 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2 + 64 * 4)
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 128, 128, gdn.GDN_BF16) == 0
     # fp32: the token-by-token kernel -- the state every 8 tokens
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == 2 * 3 * 17 * 64 * 64 * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0

@@ -58,9 +58,9 @@ def assert_grads(tag, got, ref, dtype):
     assert all(e[0] <= tol and e[1] <= tol for e in errs.values()), (tag, errs)
 
 
-def _case(B, T, H, dtype, seed, s0, dS):
-    inp = gen_chunk(B, T, H, 64, 64, dtype=dtype, seed=seed, s0_var=0.1 if s0 else None)
-    dO, dSf = gen_upstream_grads(B, T, H, 64, 64, seed=seed, with_dS=dS)
+def _case(B, T, H, dtype, seed, s0, dS, d=64):
+    inp = gen_chunk(B, T, H, d, d, dtype=dtype, seed=seed, s0_var=0.1 if s0 else None)
+    dO, dSf = gen_upstream_grads(B, T, H, d, d, seed=seed, with_dS=dS)
     if dtype == "bf16":
         dO = bf16_round(dO)
     return inp, dO, dSf
@@ -121,3 +121,33 @@ def test_backward_extreme_gates():
     inp["beta"] = np.where(pb < 0.15, 0.0, np.where(pb < 0.3, 2.0, inp["beta"])).astype(np.float32)
     note("backward extreme gates")
     assert_grads("bwd_extreme", run_bwd(inp, "f32", dO, dSf), oracle_bwd(inp, dO, dSf), "f32")
+
+
+@pytest.mark.parametrize("B,T,H,s0,dS", [(1, 20, 2, False, False), (2, 77, 3, True, True), (1, 200, 2, True, False)])
+def test_backward_d128(B, T, H, s0, dS):
+    """bf16 d = 128: the chunk form with its gradient pass in two launches (value columns, then rows and keys)."""
+    inp, dO, dSf = _case(B, T, H, "bf16", 21 + T, s0, dS, d=128)
+    note(f"backward d128 B{B} T{T} H{H} S0={s0} dS={dS}")
+    assert_grads(f"bwd_d128_{B}_{T}_{H}", run_bwd(inp, "bf16", dO, dSf), oracle_bwd(inp, dO, dSf), "bf16")
+
+
+@pytest.mark.parametrize("T", [0, 1, 64, 65, 130])
+def test_backward_d128_lengths(T):
+    inp, dO, dSf = _case(2, T, 2, "bf16", 40 + T, True, True, d=128)
+    note(f"backward d128 lengths T={T}")
+    got = run_bwd(inp, "bf16", dO, dSf)
+    if T == 0:  # only dS0 = dS_T
+        assert np.array_equal(got[5], dSf)
+        return
+    assert_grads(f"bwd_d128_len{T}", got, oracle_bwd(inp, dO, dSf), "bf16")
+
+
+@pytest.mark.timeout(600)
+def test_backward_d128_long():
+    """A longer d = 128 case, 16 chunks per chain, with the long-context gate recipe (alpha logits ~ N(-5, 1))
+    and S0 given; every chain against the oracle."""
+    inp = gen_chunk(1, 1000, 4, 128, 128, dtype="bf16", seed=2, alpha_mu=-5.0, s0_var=0.01)
+    dO, dSf = gen_upstream_grads(1, 1000, 4, 128, 128, seed=2, with_dS=True)
+    dO = bf16_round(dO)
+    note("backward d128 long")
+    assert_grads("bwd_d128_long", run_bwd(inp, "bf16", dO, dSf), oracle_bwd(inp, dO, dSf), "bf16")
