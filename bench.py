@@ -829,7 +829,8 @@ def bench_backward(args, w, dev):
                               "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(key, w.name),
                               "algorithmic_bytes_per_launch": hbm_bytes, "kernel_avg_ms": avg_ms,
                               "kernel": "gdn::two::factor_kernel + state_kernel + gdn::grad::adj_kernel + "
-                                        "grad_kernel (one call)"}
+                                        + ("grad_kernel" if w.dk == 64 else "grad_cols_kernel + grad_rows_kernel")
+                                        + " (one call)"}
     add_context(result, args, step, stream, dev, key, 1)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_backward(inp, dO, dS, w)
@@ -839,11 +840,13 @@ def bench_backward(args, w, dev):
 
 
 def cpu_baseline_backward(inp, dO, dS, w, budget_s: float = 12.0):
-    """The oracle's reverse-mode gradients (NumPy fp64, as they stand) on a sample of chains."""
+    """The oracle's reverse-mode gradients (NumPy fp64, as they stand) on a sample of chains (and, for long
+    sequences, of their first 2048 tokens: the oracle keeps every state)."""
     from oracle.backward import recurrent_bwd
-    chains = [(0, 0), (3, 7)]
-    sub = {x: np.stack([inp[x][b, :, h] for b, h in chains], axis=1)[None] for x in ("q", "k", "v", "alpha", "beta")}
-    dO_s = np.stack([dO[b, :, h] for b, h in chains], axis=1)[None]
+    chains = [(0, 0), (w.B - 1, w.H - 1)]
+    tt = min(w.T, 2048)
+    sub = {x: np.stack([inp[x][b, :tt, h] for b, h in chains], axis=1)[None] for x in ("q", "k", "v", "alpha", "beta")}
+    dO_s = np.stack([dO[b, :tt, h] for b, h in chains], axis=1)[None]
     dS_s = np.stack([dS[b, h] for b, h in chains])[None]
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -852,9 +855,9 @@ def cpu_baseline_backward(inp, dO, dS, w, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 50:
             break
-    tokens = reps * w.T * len(chains) / w.H  # a token is all H heads of one position
+    tokens = reps * tt * len(chains) / w.H  # a token is all H heads of one position
     return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(chains)} of {w.B * w.H} chains x {w.T} tokens, NumPy fp64 token loop (one thread), "
+            "sample": f"{len(chains)} of {w.B * w.H} chains x {tt} tokens, NumPy fp64 token loop (one thread), "
                       f"repeated {reps}x in {el:.1f} s; tokens counted as chains x T / H"}
 
 

@@ -102,6 +102,10 @@ WORKLOADS = {
     "sykra_layer_bf16_bwd": Workload(
         "sykra_layer_bf16_bwd", "backward", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="gradients of the Sykra-shaped layer (inputs as sykra_layer_bf16, upstream dO, dS_T ~ N(0,1))"),
+    "long_context_bf16_bwd": Workload(
+        "long_context_bf16_bwd", "backward", "bf16", B=2, T=16384, H=16, dk=128, dv=128, seed=2,
+        alpha_mu=-5.0, s0_var=0.01,
+        note="gradients of the long-context d=128 layer (inputs as long_context_bf16, upstream dO, dS_T ~ N(0,1))"),
     "sykra_layer_bf16_channel_decay": Workload(
         "sykra_layer_bf16_channel_decay", "channel", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="the Sykra-shaped layer with a decay per token and value channel (DeltaPhase section 5)"),
