@@ -345,6 +345,38 @@ PROFILE_PASSES = {
 }
 
 
+def run_profiles(root: str, workload: str, passes) -> int:
+    """Run the named PROFILE_PASSES for one workload, one child process at a time, from the repository root with
+    TMPDIR=/tmp, each under a 240 s limit (the whole process group is killed past it); output under
+    root/<workload>.  Returns the first non-zero status, else 0."""
+    import shlex
+    import signal
+    import subprocess
+    d = os.path.join(root, workload)
+    os.makedirs(d, exist_ok=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name in passes:
+        cmd = PROFILE_PASSES[name].format(d=d, w=workload)
+        out = os.path.join(d, "bench.json" if name == "trace" else name + ".out")
+        err = os.path.join(d, name + ".err")
+        print(f"[profile] {workload} {name}: {cmd}", flush=True)
+        t0 = time.time()
+        with open(out, "w") as fo, open(err, "w") as fe:
+            p = subprocess.Popen(shlex.split(cmd), stdin=subprocess.DEVNULL, stdout=fo, stderr=fe, cwd=ROOT, env=env,
+                                 start_new_session=True)
+            try:
+                rc = p.wait(timeout=240)
+            except subprocess.TimeoutExpired:
+                os.killpg(p.pid, signal.SIGKILL)
+                p.wait()
+                rc = 124
+        print(f"[profile] {workload} {name}: status {rc} after {time.time() - t0:.0f} s", flush=True)
+        if rc != 0:
+            print(open(err).read()[-2000:], flush=True)
+            return rc
+    return 0
+
+
 def _csv_rows(path, pattern):
     import csv
     import glob
@@ -397,7 +429,8 @@ def write_profile(workload: str, d: str) -> str:
             continue
         extra = f" > {dd}/bench.json" if name == "trace" else ""
         lines.append("    timeout -s KILL 240 " + cmd.format(d=dd, w=workload) + extra)
-    lines.append("")
+    lines += ["", f"(`python3 bench.py --run-profiles {os.path.dirname(dd)} --workload {workload}` runs the same passes "
+              "in turn.)", ""]
 
     # Kernel trace.
     tr = [r for r in _csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv")]
@@ -534,6 +567,9 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / matrix-core peak loops")
     ap.add_argument("--profile-commands", metavar="ROOT",
                     help="print the rocprofv3 passes for --workload, writing under ROOT/<workload>")
+    ap.add_argument("--run-profiles", metavar="ROOT",
+                    help="run the rocprofv3 passes named by --passes for --workload, writing under ROOT/<workload>")
+    ap.add_argument("--passes", default=",".join(PROFILE_PASSES), help="comma-separated passes for --run-profiles")
     ap.add_argument("--write-profile", metavar="DIR",
                     help="summarise the rocprofv3 passes under DIR into profiles/<kernel>_<workload>.md")
     args = ap.parse_args()
@@ -545,6 +581,8 @@ def main():
         for name, cmd in PROFILE_PASSES.items():
             print(name + "\t" + cmd.format(d=d, w=args.workload) + (f" > {d}/bench.json" if name == "trace" else ""))
         return
+    if args.run_profiles:
+        sys.exit(run_profiles(args.run_profiles, args.workload, [p for p in args.passes.split(",") if p]))
     if args.write_profile:
         print(write_profile(args.workload, args.write_profile))
         return
