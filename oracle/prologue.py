@@ -8,7 +8,10 @@ Per token t and head h the layer forms, from raw projections:
 
 * q_t / max(||q_t||, eps) and k_t / max(||k_t||, eps): L2 normalisation over
   the key dimension (the unit-norm keys and queries of the input recipe; a
-  zero row stays zero);
+  zero row stays zero).  For complex rows the norm is the Hermitian one,
+  ||x||^2 = sum |x_i|^2, the length of x read as a real vector of twice the
+  size (DeltaPhase README, section 2: the keys are unit phasors, so a key
+  of d phasors has norm sqrt(d));
 * beta_t = beta_scale * sigmoid(b_t): DeltaPhase README, section 1 "Extended
   Householder Beta Range" (beta_scale = 2 there; 1 gives the (0, 1) range);
 * alpha_t = exp(-softplus(a_t)): the data-dependent forget gate of the Sykra
@@ -25,10 +28,17 @@ import numpy as np
 EPS = 1e-12
 
 
+def _widen(x) -> np.ndarray:
+    """fp64, or complex128 for complex input."""
+    x = np.asarray(x)
+    return x.astype(np.complex128 if np.iscomplexobj(x) else np.float64)
+
+
 def l2_normalise(x, eps: float = EPS) -> np.ndarray:
-    """Rows of the last axis scaled to unit L2 norm; rows with norm below eps are divided by eps."""
-    x = np.asarray(x, dtype=np.float64)
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    """Rows of the last axis scaled to unit L2 norm (Hermitian for complex rows); rows with norm below eps are
+    divided by eps."""
+    x = _widen(x)
+    n = np.sqrt(np.sum(np.abs(x) ** 2, axis=-1, keepdims=True))
     return x / np.maximum(n, eps)
 
 
@@ -54,9 +64,10 @@ def prologue(q, k, a_logit, b_logit, beta_scale: float = 1.0):
 def prologue_fwd(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=None, threads: int = 0):
     """The layer forward from raw inputs: the transforms above, then the recurrence.
 
-    Returns (o, S_final) in fp64, as ``oracle.recurrent_fwd`` does.
+    Real or complex q, k, v (the gates are real either way).  Returns (o, S_final) in fp64 or complex128, as
+    ``oracle.recurrent_fwd`` does.
     """
     from . import recurrent_fwd
     qh, kh, alpha, beta = prologue(q, k, a_logit, b_logit, beta_scale)
-    o, S, _ = recurrent_fwd(qh, kh, np.asarray(v, dtype=np.float64), alpha, beta, S0, threads=threads)
+    o, S, _ = recurrent_fwd(qh, kh, _widen(v), alpha, beta, S0, threads=threads)
     return o, S

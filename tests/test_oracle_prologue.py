@@ -1,14 +1,18 @@
 """Pins for the oracle's input transforms (oracle/prologue.py), and mutants they must catch.
 
-The transforms are L2 normalisation of q and k over the key dimension,
+The transforms are L2 normalisation of q and k over the key dimension (Hermitian
+for complex rows),
 beta = beta_scale * sigmoid(b) and alpha = exp(-softplus(a)).  The pins check
 them against closed forms (special values, an exact hand-worked token),
 invariants (per-row rescaling of the raw q and k) and an identity
 (exp(-softplus(a)) = 1 / (1 + e^a)) that rebuilds logits from given gates and
-must reproduce the plain oracle.  Each mutant plants one plausible mistake in a
+must reproduce the plain oracle; complex rows are pinned by unit phasors (norm
+sqrt(d)), by the real vector a complex row stands for, and by the phase a
+rescaled complex query puts on the output.  Each mutant plants one plausible mistake in a
 copy of the transforms; some pin must reject it.  CPU only.
 """
 import types
+import warnings
 
 import numpy as np
 import pytest
@@ -21,7 +25,8 @@ def _impl(prologue_fn):
     """A transforms implementation (prologue, prologue_fwd) built on `prologue_fn`."""
     def prologue_fwd(q, k, v, a, b, beta_scale=1.0, S0=None):
         qh, kh, alpha, beta = prologue_fn(q, k, a, b, beta_scale)
-        o, S, _ = oracle.recurrent_fwd(qh, kh, np.asarray(v, np.float64), alpha, beta, S0, threads=1)
+        v = np.asarray(v, np.complex128 if np.iscomplexobj(v) else np.float64)
+        o, S, _ = oracle.recurrent_fwd(qh, kh, v, alpha, beta, S0, threads=1)
         return o, S
     return types.SimpleNamespace(prologue=prologue_fn, prologue_fwd=prologue_fwd)
 
@@ -109,8 +114,46 @@ def pin_logits_from_gates(impl):
         assert np.linalg.norm(S1 - S2) <= 1e-12 * np.linalg.norm(S2)
 
 
+def _craw(rng, B, T, H, d):
+    q = (rng.normal(size=(B, T, H, d)) + 1j * rng.normal(size=(B, T, H, d))) * rng.uniform(0.2, 5.0, (B, T, H, 1))
+    k = (rng.normal(size=(B, T, H, d)) + 1j * rng.normal(size=(B, T, H, d))) * rng.uniform(0.2, 5.0, (B, T, H, 1))
+    v = rng.normal(size=(B, T, H, d)) + 1j * rng.normal(size=(B, T, H, d))
+    return q, k, v
+
+
+def pin_complex_phasor_rows(impl):
+    """Rows of d unit phasors e^{i theta} (the DeltaPhase keys) have Hermitian norm sqrt(d), so they normalise to
+    e^{i theta} / sqrt(d) exactly; a general complex row normalises to the same unit vector as the real vector
+    (Re x, Im x) it stands for."""
+    rng = np.random.default_rng(21)
+    d = 8
+    th = rng.uniform(-np.pi, np.pi, size=(1, 3, 2, d))
+    ph = np.exp(1j * th)
+    _, kh, _, _ = impl.prologue(ph, ph, np.zeros((1, 3, 2)), np.zeros((1, 3, 2)), 2.0)
+    assert np.allclose(kh, ph / np.sqrt(d), atol=1e-15, rtol=0)
+    q, k, _ = _craw(rng, 1, 4, 2, 5)
+    qh, _, _, _ = impl.prologue(q, k, np.zeros((1, 4, 2)), np.zeros((1, 4, 2)), 1.0)
+    r = np.concatenate([q.real, q.imag], axis=-1)
+    rh = r / np.linalg.norm(r, axis=-1, keepdims=True)
+    assert np.allclose(np.concatenate([qh.real, qh.imag], axis=-1), rh, atol=1e-14, rtol=0)
+
+
+def pin_complex_query_phase(impl):
+    """Multiplying each raw complex query row by its own nonzero complex factor c rescales the output row by
+    conj(c / |c|) (the readout uses the conjugated query) and leaves the final state unchanged."""
+    rng = np.random.default_rng(23)
+    q, k, v = _craw(rng, 1, 10, 2, 4)
+    a = rng.normal(-2.0, 1.0, size=(1, 10, 2))
+    b = rng.normal(0.0, 1.0, size=(1, 10, 2))
+    c = rng.normal(size=(1, 10, 2, 1)) + 1j * rng.normal(size=(1, 10, 2, 1))
+    o1, S1 = impl.prologue_fwd(q, k, v, a, b, 2.0)
+    o2, S2 = impl.prologue_fwd(q * c, k, v, a, b, 2.0)
+    assert np.linalg.norm(o2 - np.conj(c / np.abs(c)) * o1) <= 1e-12 * np.linalg.norm(o1)
+    assert np.linalg.norm(S2 - S1) <= 1e-12 * np.linalg.norm(S1)
+
+
 PINS = [pin_special_values, pin_unit_rows, pin_handworked_token, pin_row_rescaling_invariance,
-        pin_logits_from_gates]
+        pin_logits_from_gates, pin_complex_phasor_rows, pin_complex_query_phase]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -121,6 +164,18 @@ def test_prologue_pin(pin):
 def _norm_axis(x, axis):
     x = np.asarray(x, np.float64)
     return x / np.maximum(np.sqrt(np.sum(x * x, axis=axis, keepdims=True)), pro.EPS)
+
+
+def _square_norm(x):
+    """x / sqrt(sum x_i^2) without the modulus (the real formula applied to complex rows)."""
+    x = np.asarray(x)
+    return x / np.maximum(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)), pro.EPS)
+
+
+def _real_part_norm(x):
+    """Complex rows divided by the norm of their real parts only."""
+    x = np.asarray(x)
+    return x / np.maximum(np.sqrt(np.sum(np.real(x) ** 2, axis=-1, keepdims=True)), pro.EPS)
 
 
 def _mut(**over):
@@ -147,13 +202,16 @@ MUTANTS = {
     "beta_sigmoid_negated": _mut(beta=lambda b, s: s * pro.sigmoid(-np.asarray(b))),
     "beta_scale_dropped": _mut(beta=lambda b, s: pro.sigmoid(b)),
     "beta_scale_squared": _mut(beta=lambda b, s: s * s * pro.sigmoid(b)),
+    "complex_norm_without_modulus": _mut(q=lambda q: _square_norm(q), k=lambda k: _square_norm(k)),
+    "complex_norm_real_part_only": _mut(q=lambda q: _real_part_norm(q), k=lambda k: _real_part_norm(k)),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_prologue_mutant_caught(name):
     impl = MUTANTS[name]
-    with np.errstate(all="ignore"):
+    with np.errstate(all="ignore"), warnings.catch_warnings():
+        warnings.simplefilter("ignore", np.exceptions.ComplexWarning)
         caught = []
         for pin in PINS:
             try:
