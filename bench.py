@@ -8,7 +8,8 @@ chain), on inputs already resident in HBM.  The default workload is the
 Sykra-shaped layer (B=8, T=2048, H=12, d=64, chunk 64, bf16 q/k/v);
 ``--workload sykra_layer_bf16_prologue`` runs the same layer from raw inputs
 through gdn_chunk_fwd_prologue (q, k normalised and the gates formed from their
-logits inside the kernel).  To keep
+logits on the device; ``long_context_bf16_prologue``, ``deltaphase_c64_prologue``
+and ``single_head_f32_prologue`` do the same for the other shapes).  To keep
 the 256 MB Infinity Cache from serving a step's inputs, the timed loop cycles
 through enough independent copies of the inputs (>= 1 GiB in total) that each
 step reads data not touched for several steps.
@@ -631,7 +632,8 @@ def main():
     # serving loop would, so host-side checks do not open gaps between launches.
     code = {"bf16": gdn.GDN_BF16, "f32": gdn.GDN_F32, "c64": gdn.GDN_C64}[w.dtype]
     lib = gdn.load()
-    ws_bytes = gdn.gdn_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, code)
+    ws_query = gdn.gdn_chunk_fwd_prologue_workspace_bytes if pro else gdn.gdn_chunk_fwd_workspace_bytes
+    ws_bytes = ws_query(w.B, w.T, w.H, w.dk, w.dv, w.chunk, code)
     # One workspace serves every copy: the calls are ordered on one stream.
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_ptr = ws.data_ptr() if ws_bytes else None
@@ -643,7 +645,7 @@ def main():
                                    out=d["out"], S_final=d["S"], stream=stream.cuda_stream)
             calls.append((ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["a_logit"]), ptr(d["b_logit"]), w.beta_scale,
                           ptr(d["S0"]), w.chunk, ptr(d["out"]), ptr(d["S"]), w.B, w.T, w.H, w.dk, w.dv, code,
-                          stream.cuda_stream))
+                          ws_ptr, ws_bytes, stream.cuda_stream))
         else:
             gdn.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], out=d["out"], S_final=d["S"],
                           stream=stream.cuda_stream)
@@ -666,13 +668,14 @@ def main():
     achieved = wbytes / (avg_ms * 1e-3) / 1e9
     # bf16 calls that need a workspace run the two-launch path (a factor pass and a state pass, segmented
     # for long sequences with few chains): d = 128, and d = 64 when the chains alone cannot fill the CUs.
-    # Other bf16 d = 64 calls and the fused prologue run the three-stage kernel; fp32 the fused kernel.
-    two = w.dtype == "bf16" and not pro and ws_bytes > 0
+    # Other bf16 d = 64 calls, with or without the prologue, run the three-stage kernel; fp32 the fused
+    # kernel.  The fp32 and complex64 prologues add a pass over the rows ahead of the forward.
+    two = w.dtype == "bf16" and ws_bytes > 0
     if w.dtype == "c64":
         kernel, qual = "cx_prep_scan_out", "gdn::cx::"
     elif two:
         kernel, qual = "chunk_two", "gdn::two::"
-    elif pro or (w.dtype == "bf16" and w.dk == 64):
+    elif w.dtype == "bf16" and w.dk == 64:
         kernel, qual = "chunk_pipe3_kernel", "gdn::pipe3::"
     else:
         kernel, qual = "chunk_fwd_kernel", "gdn::"
@@ -689,8 +692,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": ("synthetic (seeded; raw q/k rows N(0,1) x U(0.25,4), N(0,1) v, logits b ~ N(0,1), a ~ N(-4,1); "
-                 "normalisation and gates inside the kernel)" if pro else
+        "data": (("synthetic (seeded; raw q/k rows of unit phasors x U(0.25,4), complex normal v, "
+                  if w.dtype == "c64" else "synthetic (seeded; raw q/k rows N(0,1) x U(0.25,4), N(0,1) v, ")
+                 + f"logits b ~ N(0,1), a ~ N({w.alpha_mu:g},1); normalisation and gates on the device)" if pro else
                  "synthetic (seeded; unit-norm q/k, N(0,1) v, sigmoid beta, exp(-softplus) alpha)"),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
                    "S0": inp["S0"] is not None, "input_copies_cycled": ncopies},

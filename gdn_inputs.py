@@ -99,6 +99,15 @@ WORKLOADS = {
     "sykra_layer_bf16_prologue": Workload(
         "sykra_layer_bf16_prologue", "prologue", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="the Sykra-shaped layer from raw inputs: q, k not normalised, gate logits a, b"),
+    "long_context_bf16_prologue": Workload(
+        "long_context_bf16_prologue", "prologue", "bf16", B=2, T=16384, H=16, dk=128, dv=128, seed=2,
+        alpha_mu=-5.0, s0_var=0.01, note="the long-context d=128 layer from raw inputs"),
+    "deltaphase_c64_prologue": Workload(
+        "deltaphase_c64_prologue", "prologue", "c64", B=4, T=4096, H=8, dk=32, dv=32, seed=3, beta_scale=2.0,
+        note="the complex phasor layer from raw inputs: phasor rows of any modulus, beta = 2 sigmoid(b)"),
+    "single_head_f32_prologue": Workload(
+        "single_head_f32_prologue", "prologue", "f32", B=1, T=256, H=1, dk=64, dv=64, seed=0,
+        note="one fp32 head from raw inputs"),
     "sykra_layer_bf16_bwd": Workload(
         "sykra_layer_bf16_bwd", "backward", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="gradients of the Sykra-shaped layer (inputs as sykra_layer_bf16, upstream dO, dS_T ~ N(0,1))"),
@@ -158,18 +167,34 @@ def gen_chunk(B, T, H, dk, dv, dtype="f32", seed=0, alpha_mu=-4.0, beta_scale=1.
                 alpha=alpha.astype(np.float32), beta=beta.astype(np.float32), S0=S0)
 
 
-def gen_raw_layer(B, T, H, d, seed=0, alpha_mu=-4.0, s0_var=None):
-    """Raw bf16 q, k, v and fp32 logits for the fused-prologue entry point.
+def gen_raw_layer(B, T, H, d, seed=0, alpha_mu=-4.0, s0_var=None, dtype="bf16"):
+    """Raw q, k, v and fp32 logits for the fused-prologue entry point.
 
-    Returns dict q, k, v (bf16 values in float32 arrays), a_logit, b_logit, S0 (None if absent)."""
+    Real dtypes: q, k ~ N(0, 1) rows, each row scaled by its own U(0.25, 4) factor (not normalised), v ~ N(0, 1).
+    Complex: q, k rows of unit phasors e^{i theta}, theta ~ U(0, 2 pi), each row scaled by its own U(0.25, 4)
+    factor (the transforms normalise them to e^{i theta} / sqrt(d)), v complex normal.  Logits b ~ N(0, 1),
+    a ~ N(alpha_mu, 1).  Returns dict q, k, v (values in stored precision), a_logit, b_logit, S0 (None if
+    absent)."""
     rng = np.random.default_rng(seed)
-    q = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
-    k = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
-    v = rng.normal(0.0, 1.0, (B, T, H, d))
+    if dtype == "c64":
+        q = np.exp(1j * rng.uniform(0.0, 2.0 * np.pi, (B, T, H, d))) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+        k = np.exp(1j * rng.uniform(0.0, 2.0 * np.pi, (B, T, H, d))) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+        v = rng.normal(0.0, np.sqrt(0.5), (B, T, H, d)) + 1j * rng.normal(0.0, np.sqrt(0.5), (B, T, H, d))
+    else:
+        q = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+        k = rng.normal(0.0, 1.0, (B, T, H, d)) * rng.uniform(0.25, 4.0, (B, T, H, 1))
+        v = rng.normal(0.0, 1.0, (B, T, H, d))
     b = rng.normal(0.0, 1.0, (B, T, H))
     a = rng.normal(alpha_mu, 1.0, (B, T, H))
-    S0 = rng.normal(0.0, np.sqrt(s0_var), (B, H, d, d)).astype(np.float32) if s0_var is not None else None
-    return dict(q=_store(q, "bf16"), k=_store(k, "bf16"), v=_store(v, "bf16"), a_logit=a.astype(np.float32),
+    S0 = None
+    if s0_var is not None:
+        sd = np.sqrt(s0_var)
+        if dtype == "c64":
+            S0 = (rng.normal(0.0, sd * np.sqrt(0.5), (B, H, d, d))
+                  + 1j * rng.normal(0.0, sd * np.sqrt(0.5), (B, H, d, d))).astype(np.complex64)
+        else:
+            S0 = rng.normal(0.0, sd, (B, H, d, d)).astype(np.float32)
+    return dict(q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype), a_logit=a.astype(np.float32),
                 b_logit=b.astype(np.float32), S0=S0)
 
 
@@ -208,7 +233,7 @@ def gen_workload(w: Workload, **overrides):
                                  alpha_mu=p["alpha_mu"], s0_var=p["s0_var"])
     if w.kind == "prologue":
         return gen_raw_layer(p["B"], p["T"], p["H"], p["dk"], seed=p["seed"], alpha_mu=p["alpha_mu"],
-                             s0_var=p["s0_var"])
+                             s0_var=p["s0_var"], dtype=p["dtype"])
     return gen_chunk(**p)
 
 

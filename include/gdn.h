@@ -122,12 +122,25 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *alph
                   int dv, int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace gdn_chunk_fwd_prologue needs for these sizes (0:
+ * workspace may be NULL; 0 also for unsupported arguments).  bf16: 0 where
+ * gdn_chunk_fwd needs no workspace; otherwise (the two-launch path) what
+ * gdn_chunk_fwd needs plus B * H * ceil(T / 64) * 512 bytes, the inverse key
+ * and query norms handed from the first launch to the second.  GDN_F32 and GDN_C64: the
+ * transformed q and k (B * T * H rows of 256 bytes each) and the two gates
+ * (B * T * H floats each), each rounded up to 256 bytes, plus, for GDN_C64,
+ * what gdn_chunk_fwd needs.  Ownership and sharing as for gdn_chunk_fwd.
+ */
+size_t gdn_chunk_fwd_prologue_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/*
  * gdn_chunk_fwd for a layer's raw projections, with its input transforms
- * computed inside the kernel:
+ * applied on the device:
  *
  *   q_t <- q_t / max(|q_t|, 1e-12),  k_t <- k_t / max(|k_t|, 1e-12)
  *          (L2 over the key dimension, per token and head; the unit-norm keys
- *          and queries the chunkwise form is usually run on)
+ *          and queries the chunkwise form is usually run on; for complex
+ *          rows the Hermitian norm, sum over i of |q_i|^2)
  *   beta_t  = beta_scale * sigmoid(b_t)
  *          (DeltaPhase README, section 1 "Extended Householder Beta Range":
  *          beta_scale = 2 gives beta in (0, 2); 1 gives (0, 1))
@@ -135,22 +148,35 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *alph
  *          (the data-dependent forget gate of the Sykra README, "Architectural
  *          Highlights", as a logistic map of a logit into (0, 1))
  *
- *   q, k      [B, T, H, dk]  bfloat16   raw queries and keys
- *   v         [B, T, H, dv]  bfloat16   values
+ *   q, k      [B, T, H, dk]  dtype      raw queries and keys
+ *   v         [B, T, H, dv]  dtype      values
  *   a_logit   [B, T, H]      float32    forget-gate logits
  *   b_logit   [B, T, H]      float32    write-strength logits
  *   beta_scale                          finite, 0 <= beta_scale <= 2
- *   S0, chunk, out, S_final, B, T, H, dk, dv, stream: as for gdn_chunk_fwd.
+ *   workspace  device memory of at least
+ *              gdn_chunk_fwd_prologue_workspace_bytes(...) bytes, or NULL when
+ *              that is 0
+ *   S0, chunk, out, S_final, B, T, H, dk, dv, dtype, stream: as for
+ *   gdn_chunk_fwd.
  *
- * Supported: dtype == GDN_BF16, dk == dv == 64, chunk == 64, and each batch
- * row of q, k, v, out under 2^31 bytes; otherwise GDN_ERR_UNSUPPORTED.  No
- * workspace.  The normalisation is folded into the arithmetic (1/|k| and 1/|q|
- * scale the Gram tiles and the per-token gates), so q and k are read once, as
- * stored.
+ * Supported: the shapes gdn_chunk_fwd supports (bf16 d = 64 or 128, fp32
+ * d = 64, complex64 d = 32; dk == dv; chunk == 64), except bf16 shapes with a
+ * batch row of q, k, v or out of 2^31 bytes or more, and bf16 d = 128 grids of
+ * 2^30 chunks or more (GDN_ERR_UNSUPPORTED).
+ *
+ * bf16 fuses the transforms into the forward's kernels, so q, k and the
+ * logits are read once, as stored, and the rows are never rewritten: 1/|k|
+ * and 1/|q| scale the Gram tiles, the decay factors and the per-token gates
+ * (on the two-launch path, d = 128 and long d = 64 sequences, the first
+ * launch forms both and the second reads them).  fp32 and complex64
+ * run one extra pass over the rows that writes the transformed q, k and gates
+ * to the workspace; there alpha is kept at or above 2^-126 (a logit above 87
+ * already gives a gate that wipes the state).
  */
 int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const float *a_logit,
                            const float *b_logit, float beta_scale, const void *S0, int chunk, void *out,
-                           void *S_final, int B, int T, int H, int dk, int dv, int dtype, void *stream);
+                           void *S_final, int B, int T, int H, int dk, int dv, int dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of workspace gdn_chunk_bwd needs.  bf16 (the chunk form): per

@@ -94,18 +94,27 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(const float (&a)[16], int g,
 template <int DK>
 struct FactorCfg {
   static constexpr int NKP = DK / 32;
-  // per-wave fp32 scratch: g, beta, and ten 16 x 17 transpose tiles (four
-  // for the diagonal blocks, six for the blocks below them).  The rows of -A of
+  // per-wave fp32 scratch: g, beta, ten 16 x 17 transpose tiles (four for
+  // the diagonal blocks, six for the blocks below them), and 1/|k| (fused
+  // prologue).  The rows of -A of
   // the four diagonal blocks (16 x 20 each) share the last six tiles: they are
   // dead once the inverses are formed, before those tiles are written.
-  static constexpr int fG = 0, fB = 64, fTR = 128, fDS = fTR + 4 * 272, szW = fTR + 10 * 272;
+  static constexpr int fG = 0, fB = 64, fTR = 128, fDS = fTR + 4 * 272, fR = fTR + 10 * 272, szW = fR + 64;
   static_assert(fDS + 4 * 16 * 20 <= szW, "diagonal-block rows fit the shared tiles");
 };
 
-template <int DK>
+// PRO: the layer's input transforms are fused in.  k and q are raw: the
+// inverse row norms r = 1 / max(|k|, 1e-12) scale the Gram tiles (K^ K^^T =
+// diag(r) K K^T diag(r) for the normalised keys K^), and r and the queries'
+// p = 1 / max(|q|, 1e-12) go to rpw[chunk][2][64] for the state pass, which
+// folds them into its gates; alpha and beta hold the logits a and b,
+// alpha = exp(-softplus(a)), beta = bscale * sigmoid(b).
+template <int DK, bool PRO>
 __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ kg, const float* __restrict__ alpha,
                                                     const float* __restrict__ beta, char* __restrict__ ws,
-                                                    char* __restrict__ wsT, int T, int H, int nch, int total) {
+                                                    char* __restrict__ wsT, int T, int H, int nch, int total,
+                                                    float bscale, const __bf16* __restrict__ qg,
+                                                    float* __restrict__ rpw) {
   using Cf = FactorCfg<DK>;
   constexpr int NKP = Cf::NKP;
   __shared__ __attribute__((aligned(16))) float W[Cf::szW];
@@ -131,11 +140,51 @@ __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ k
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (16 * i + c) * rowK + 2 * (32 * p + 8 * g), t0 * rowK, 0));
   const float av = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, l * H * 4, t0 * H * 4, 0));
   const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, l * H * 4, t0 * H * 4, 0));
+  const bool live = t0 + l < T;
 
-  // Gates: padding tokens take alpha = 1 (beta reads as 0 there).
-  const float gl = wave_prefix_sum(__builtin_amdgcn_logf(t0 + l < T ? av : 1.f));
+  if constexpr (PRO) {
+    // Inverse norms of the lane's four key rows 16 i + c and of the same
+    // query rows: its pieces 4p + g are summed over p here and over g across
+    // lanes (xor 16, xor 32).
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + tokbase * DK, span_bytes((size_t)T * H * DK * 2, (size_t)h * DK * 2));
+    float* const rp = rpw + ((size_t)chain * nch + n) * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) {
+        sk += piece_sumsq(kr[i][p]);
+        sq += piece_sumsq(__builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * i + c) * rowK + 2 * (32 * p + 8 * g), t0 * rowK, 0)));
+      }
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 32);
+      sq += __shfl_xor(sq, 32);
+      const float r = inv_row_norm(sk);
+      if (g == 0) {
+        W[Cf::fR + 16 * i + c] = r;
+        rp[16 * i + c] = r;
+        rp[64 + 16 * i + c] = inv_row_norm(sq);
+      }
+    }
+  }
+
+  // Gates: padding tokens take alpha = 1 and beta = 0.  From logits,
+  // log2 alpha = -softplus(a) / ln 2 = -(max(u, 0) + log2(1 + 2^-|u|)) with
+  // u = a log2(e), and beta = bscale / (1 + 2^(-b log2(e))).
+  float la, bt;
+  if constexpr (PRO) {
+    const float u = av * 1.4426950408889634f;
+    la = live ? -(fmaxf(u, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(u)))) : 0.f;
+    bt = live ? bscale * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-bv * 1.4426950408889634f)) : 0.f;
+  } else {
+    la = __builtin_amdgcn_logf(live ? av : 1.f);
+    bt = bv;
+  }
+  const float gl = wave_prefix_sum(la);
   W[Cf::fG + l] = gl;
-  W[Cf::fB + l] = bv;
+  W[Cf::fB + l] = bt;
   reinterpret_cast<float*>(rec + kRecG)[l] = gl;
 
   // Lower Gram tiles: lane (g, c) of G[i][k] holds (K K^T)[16i + c][16k + 4g + j].
@@ -149,6 +198,18 @@ __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ k
       for (int p = 0; p < NKP; ++p) G[i][k] = mma32(kr[k][p], kr[i][p], G[i][k]);
     }
   wave_sync();
+  if constexpr (PRO) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ri = W[Cf::fR + 16 * i + c];
+#pragma unroll
+      for (int k = 0; k <= i; ++k) {
+        const f32x4 rs = *reinterpret_cast<const f32x4*>(W + Cf::fR + 16 * k + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) G[i][k][j] *= ri * rs[j];
+      }
+    }
+  }
 
   // Rows of -A for the diagonal blocks, through LDS to the row owners.
 #pragma unroll
@@ -272,8 +333,14 @@ struct StateCfg {
   static constexpr int oK = 0, oQ = 64 * DK * 2, oV = 2 * 64 * DK * 2, oTb = oV + 64 * LDV * 2, oGt = oTb + 6 * 1024;
   // gate table (floats): gamma, lambda, g, fs (decay to the end of the
   // token's 16-block), ge[3][64] (decay from the end of block k to the
-  // token), gamma_C
-  static constexpr int gGam = 0, gLam = 64, gG = 128, gFs = 192, gGe = 256, gGC = 448, szG = 452;
+  // token), gamma_C, gamma for the output, and g + log2 p and g - log2 r
+  // for the P tiles' diagonal blocks.  With the prologue fused in, the
+  // inverse row norms r of the keys and p of the queries (from the factor
+  // pass) are folded in here: the consumers' gamma and lambda, and fs, carry
+  // r, the output's gamma and ge carry p, so no wave of the step multiplies
+  // by them itself.
+  static constexpr int gGam = 0, gLam = 64, gG = 128, gFs = 192, gGe = 256, gGC = 448, gGO = 452, gGq = 516,
+                       gGk = 580, szG = 644;
   static constexpr int szSlot = oGt + szG * 4;
   static constexpr int oP = 3 * szSlot, szP = 6 * 1024;  // P ring, two slots
   // hand-off to the output wave, two slots each: Ut (NC x 4 tiles) and the
@@ -298,6 +365,7 @@ struct StateArgs {
   float* seg_state;    // segmented scan: start states [chains][G][DK][DV] (output mode) or
                        // maps [chains][G][DK][DK + DV] (map mode)
   __bf16* Sck;         // output mode, or NULL: every chunk's start state, bf16 [chains][nch][DK][DV]
+  const float* rp;     // fused prologue: 1 / |k| and 1 / |q| per token, [chains][nch][2][64]
   int T, H, DV, nch;
   int G, SC;           // segments per chain and chunks per segment (G = 1: one segment)
   int nseg;            // segments per chain in this launch's grid (G, or G - 1 in map mode)
@@ -536,7 +604,7 @@ __device__ __forceinline__ void consumer_role(const StateArgs& a, const Seg& sg,
 
 // P tiles of chunk k: lane (g, c) of tile (i, kk) holds P[16i + c][16kk + 4g + j]
 // = q_(16i+c) . k_(16kk+4g+j) Gamma, A order, written in pairs like Tb.
-template <int DK, int NC>
+template <int DK, int NC, bool PRO>
 __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
   using Cf = StateCfg<DK, NC>;
   constexpr int NKP = Cf::NKP;
@@ -559,10 +627,11 @@ __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* 
       }
     float gr[4], ger[4][3];
     f32x4 gsv[4], fsv[4];
+    constexpr int oGr = PRO ? Cf::gGq : Cf::gG, oGs = PRO ? Cf::gGk : Cf::gG;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      gr[i] = Gt[Cf::gG + 16 * i + c];
-      gsv[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gG + 16 * i + 4 * g);
+      gr[i] = Gt[oGr + 16 * i + c];
+      gsv[i] = *reinterpret_cast<const f32x4*>(Gt + oGs + 16 * i + 4 * g);
       fsv[i] = *reinterpret_cast<const f32x4*>(Gt + Cf::gFs + 16 * i + 4 * g);
 #pragma unroll
       for (int kb = 0; kb < 3; ++kb) ger[i][kb] = Gt[Cf::gGe + kb * 64 + 16 * i + c];
@@ -601,7 +670,7 @@ __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* 
 //   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{k <= i} Ut_k^T P_ik^T.
 // In step k it finishes chunk k - 1 (the P Ut term) and starts chunk k (the
 // Q S term, from the start state the consumers handed over).
-template <int DK, int NC>
+template <int DK, int NC, bool PRO>
 __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
   using Cf = StateCfg<DK, NC>;
   constexpr int NKP = Cf::NKP, NDT = Cf::NDT;
@@ -632,7 +701,7 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
 #pragma unroll
       for (int p = 0; p < NKP; ++p)
         qr[i][p] = *reinterpret_cast<const u32x4*>(Rb + Cf::oQ / 2 + row_off<DK>(16 * i + c, 32 * p + 8 * g));
-      gm[i] = Gt[Cf::gGam + 16 * i + c];
+      gm[i] = Gt[Cf::gGO + 16 * i + c];
     }
     issue_fence();
 #pragma unroll
@@ -682,7 +751,7 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
 // unconditional (clamped chunk index; range-checked buffer loads read rows
 // past T as zero), so the loop has one load path and the compiler's wait
 // counts stay three steps deep.
-template <int DK, int NC, int ROLE>
+template <int DK, int NC, int ROLE, bool PRO>
 __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
   using Cf = StateCfg<DK, NC>;
   const int H = a.H, T = a.T, DV = a.DV, nloc = sg.nloc;
@@ -763,8 +832,11 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
     }
     struct Set {
       u32x4 v[NVL], tb[6];
-      float gv;
+      float gv, rk, pq;
     };
+    // fused prologue: the factor pass's 1 / |k| and 1 / |q| per token of the segment's chunks
+    const __amdgpu_buffer_rsrc_t rn =
+        make_rsrc(PRO ? a.rp + ((size_t)sg.chain * a.nch + sg.n0) * 128 : nullptr, PRO ? (uint32_t)nloc * 512 : 0u);
     Set st[3];
     auto load = [&](auto sc, int m) {
       constexpr int s = decltype(sc)::value;
@@ -777,6 +849,10 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
         st[s].tb[e] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, kRecTb + e * 1024 + l * 16, m * kRecBytes, 0));
       st[s].gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, kRecG + 4 * l, m * kRecBytes, 0));
+      if constexpr (PRO) {
+        st[s].rk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, 4 * l, m * 512, 0));
+        st[s].pq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, 256 + 4 * l, m * 512, 0));
+      }
     };
     load(ic<0>{}, clampc(0, nloc));
     issue_fence();
@@ -802,13 +878,20 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
         const float e0 = at(15), e1 = at(31), e2 = at(47), gC = at(63);
         const int blk = l >> 4;
         const float gend = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gC;
-        Gt[Cf::gGam + l] = __builtin_amdgcn_exp2f(gl);
-        Gt[Cf::gLam + l] = __builtin_amdgcn_exp2f(gC - gl);
+        const float gam = __builtin_amdgcn_exp2f(gl);
+        const float rk = PRO ? st[ph].rk : 1.f, pq = PRO ? st[ph].pq : 1.f;
+        Gt[Cf::gGam + l] = gam * rk;
+        Gt[Cf::gLam + l] = __builtin_amdgcn_exp2f(gC - gl) * rk;
+        Gt[Cf::gGO + l] = gam * pq;
         Gt[Cf::gG + l] = gl;
-        Gt[Cf::gFs + l] = __builtin_amdgcn_exp2f(gend - gl);
-        Gt[Cf::gGe + l] = __builtin_amdgcn_exp2f(blk > 0 ? gl - e0 : -INFINITY);
-        Gt[Cf::gGe + 64 + l] = __builtin_amdgcn_exp2f(blk > 1 ? gl - e1 : -INFINITY);
-        Gt[Cf::gGe + 128 + l] = __builtin_amdgcn_exp2f(blk > 2 ? gl - e2 : -INFINITY);
+        Gt[Cf::gFs + l] = __builtin_amdgcn_exp2f(gend - gl) * rk;
+        if constexpr (PRO) {
+          Gt[Cf::gGq + l] = gl + __builtin_amdgcn_logf(pq);
+          Gt[Cf::gGk + l] = gl - __builtin_amdgcn_logf(rk);
+        }
+        Gt[Cf::gGe + l] = __builtin_amdgcn_exp2f(blk > 0 ? gl - e0 : -INFINITY) * pq;
+        Gt[Cf::gGe + 64 + l] = __builtin_amdgcn_exp2f(blk > 1 ? gl - e1 : -INFINITY) * pq;
+        Gt[Cf::gGe + 128 + l] = __builtin_amdgcn_exp2f(blk > 2 ? gl - e2 : -INFINITY) * pq;
         if (l == 63) Gt[Cf::gGC] = __builtin_amdgcn_exp2f(gC);
       }
       issue_fence();
@@ -817,7 +900,7 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
   }
 }
 
-template <int DK, int NC>
+template <int DK, int NC, bool PRO>
 __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(StateArgs a) {
   using Cf = StateCfg<DK, NC>;
   __shared__ __attribute__((aligned(16))) char smem[Cf::bytes];
@@ -847,15 +930,15 @@ __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(
   if (w < NC)
     consumer_role<DK, NC>(a, sg, smem, w, l);
   else if (w == Cf::wP)
-    p_role<DK, NC>(a, sg, smem, l);
+    p_role<DK, NC, PRO>(a, sg, smem, l);
   else if (w == Cf::wO)
-    out_role<DK, NC>(a, sg, smem, l);
+    out_role<DK, NC, PRO>(a, sg, smem, l);
   else if (w == Cf::wL)
-    load_role<DK, NC, 0>(a, sg, smem, l);
+    load_role<DK, NC, 0, PRO>(a, sg, smem, l);
   else if (w == Cf::wL + 1)
-    load_role<DK, NC, 1>(a, sg, smem, l);
+    load_role<DK, NC, 1, PRO>(a, sg, smem, l);
   else if constexpr (Cf::NLOAD > 2)
-    load_role<DK, NC, 2>(a, sg, smem, l);
+    load_role<DK, NC, 2, PRO>(a, sg, smem, l);
 }
 
 // Start states of the segments: S_(s+1) = M_s S_s + B_s for s = 0 .. G - 2,
@@ -923,8 +1006,15 @@ size_t chunk_two_workspace_bytes(const ChunkArgs& a) {
   return b;
 }
 
-template <int DK, int NC>
+size_t chunk_two_prologue_workspace_bytes(const ChunkArgs& a) {
+  return chunk_two_workspace_bytes(a) + (size_t)a.B * a.H * ((a.T + 63) / 64) * 2 * 64 * 4;
+}
+
+template <int DK, int NC, bool PRO>
 static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, __bf16* Sck) {
+  // fused prologue: 1 / |k| and 1 / |q| per token after the records and segment maps
+  float* const rp = PRO ? reinterpret_cast<float*>(static_cast<char*>(workspace) + chunk_two_workspace_bytes(a))
+                        : nullptr;
   using Cf = two::StateCfg<DK, NC>;
   const int nch = (a.T + 63) / 64;
   const long chains = (long)a.B * a.H;
@@ -932,9 +1022,9 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
   char* ws = static_cast<char*>(workspace);
   const long total = chains * nch;
   if (total > 0) {
-    const hipError_t e = launch_kernel(two::factor_kernel<DK>, dim3((unsigned)total), dim3(64), st,
+    const hipError_t e = launch_kernel(two::factor_kernel<DK, PRO>, dim3((unsigned)total), dim3(64), st,
                                        static_cast<const __bf16*>(a.k), a.alpha, a.beta, ws, wsT, a.T, a.H, nch,
-                                       (int)total);
+                                       (int)total, a.beta_scale, static_cast<const __bf16*>(a.q), rp);
     if (e != hipSuccess) return e;
   }
   two::StateArgs s{};
@@ -946,6 +1036,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
   s.out = static_cast<__bf16*>(a.out);
   s.Sf = static_cast<float*>(a.S_final);
   s.Sck = Sck;
+  s.rp = rp;
   s.T = a.T;
   s.H = a.H;
   s.DV = a.dv;
@@ -959,7 +1050,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
     s.mode = two::kMap;
     s.nseg = G - 1;
     s.seg_state = maps;
-    hipError_t e = launch_kernel(two::state_kernel<DK, NC>, dim3((unsigned)(chains * (G - 1) * ((DK + a.dv) / Cf::NV))),
+    hipError_t e = launch_kernel(two::state_kernel<DK, NC, PRO>, dim3((unsigned)(chains * (G - 1) * ((DK + a.dv) / Cf::NV))),
                                  dim3(Cf::kThreads), st, s);
     if (e != hipSuccess) return e;
     e = launch_kernel(two::combine_kernel<DK>, dim3((unsigned)(chains * (a.dv / 16))), dim3(256), st,
@@ -969,19 +1060,27 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
   }
   s.mode = two::kOut;
   s.nseg = G;
-  return launch_kernel(two::state_kernel<DK, NC>, dim3((unsigned)(chains * G * (a.dv / Cf::NV))),
+  return launch_kernel(two::state_kernel<DK, NC, PRO>, dim3((unsigned)(chains * G * (a.dv / Cf::NV))),
                        dim3(Cf::kThreads), st, s);
 }
 
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace) {
-  if (a.dk == 64) return launch_two_dk<64, 2>(a, workspace, nullptr, nullptr);
-  if (a.dk == 128) return launch_two_dk<128, 1>(a, workspace, nullptr, nullptr);
+  if (a.prologue) {
+    if (a.dk == 64) return launch_two_dk<64, 2, true>(a, workspace, nullptr, nullptr);
+    if (a.dk == 128) return launch_two_dk<128, 1, true>(a, workspace, nullptr, nullptr);
+    return hipErrorInvalidValue;
+  }
+  if (a.dk == 64) return launch_two_dk<64, 2, false>(a, workspace, nullptr, nullptr);
+  if (a.dk == 128) return launch_two_dk<128, 1, false>(a, workspace, nullptr, nullptr);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_two_states(const ChunkArgs& a, void* workspace, void* recT, void* Sck) {
-  if (a.dk == 64) return launch_two_dk<64, 2>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
-  if (a.dk == 128) return launch_two_dk<128, 1>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
+  if (a.prologue) return hipErrorInvalidValue;
+  if (a.dk == 64)
+    return launch_two_dk<64, 2, false>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
+  if (a.dk == 128)
+    return launch_two_dk<128, 1, false>(a, workspace, static_cast<char*>(recT), static_cast<__bf16*>(Sck));
   return hipErrorInvalidValue;
 }
 

@@ -133,27 +133,57 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   return gdn::launch_chunk_fwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_chunk_fwd_prologue_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (B < 0 || T < 0 || H < 0 || chunk != 64 || !chunk_supported(dtype, dk, dv)) return 0;
+  // bf16: the transforms are fused into the forward's own kernels; the
+  // two-launch path also hands 1 / |k| per token from its factor pass to its
+  // state pass.  fp32 and complex64: a pass over the rows writes the
+  // transformed q, k and the gates for the forward to read.
+  if (dtype == GDN_BF16)
+    return two_path(B, T, H, dk, dv, dtype) ? gdn::chunk_two_prologue_workspace_bytes(shape_args(B, T, H, dk, dv, dtype))
+                                            : 0;
+  size_t b = gdn::prologue_rows_workspace_bytes((long)B * T * H);
+  if (dtype == GDN_C64) b += gdn::chunk_cx_workspace_bytes(B, T, H);
+  return b;
+}
+
 int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const float* a_logit,
                            const float* b_logit, float beta_scale, const void* S0, int chunk, void* out,
-                           void* S_final, int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+                           void* S_final, int B, int T, int H, int dk, int dv, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems)
     return GDN_ERR_SHAPE;
-  if (chunk != 64 || dtype != GDN_BF16 || dk != 64 || dv != 64) return GDN_ERR_UNSUPPORTED;
+  if (chunk != 64 || !chunk_supported(dtype, dk, dv)) return GDN_ERR_UNSUPPORTED;
   if (!(beta_scale >= 0.f && beta_scale <= 2.f)) return GDN_ERR_SHAPE;
   if (!chains_fit((long long)B * H, 4096)) return GDN_ERR_SHAPE;
-  if ((long long)T * H * dk * 2 >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
+  // bf16 runs on the buffer-resource kernels only (rows under 2^31 bytes; at
+  // d = 128 the two-launch path).
+  const bool two = two_path(B, T, H, dk, dv, dtype);
+  if (dtype == GDN_BF16 && (!rows_fit(T, H, dk) || (dk == 128 && !two))) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !a_logit || !b_logit || !out)) return GDN_ERR_NULL;
-  const void* ptrs[] = {q, k, v, a_logit, b_logit, S0, out, S_final};
+  const void* ptrs[] = {q, k, v, a_logit, b_logit, S0, out, S_final, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+  const size_t need = gdn_chunk_fwd_prologue_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::ChunkArgs a{q, k, v, a_logit, b_logit, S0, out, S_final, B, T, H, dk, dv, dtype, stream};
   a.prologue = 1;
   a.beta_scale = beta_scale;
-  return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (dtype == GDN_BF16) {
+    if (two) return gdn::launch_chunk_two(a, workspace) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return gdn::launch_chunk_pipe(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  gdn::ChunkArgs f{};
+  if (gdn::launch_prologue_rows(a, workspace, &f) != hipSuccess) return GDN_ERR_HIP;
+  if (dtype == GDN_C64) {
+    void* cx = static_cast<char*>(workspace) + gdn::prologue_rows_workspace_bytes((long)B * T * H);
+    return gdn::launch_chunk_cx(f, cx) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  return gdn::launch_chunk_fwd(f) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {

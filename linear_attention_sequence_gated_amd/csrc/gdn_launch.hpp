@@ -35,8 +35,8 @@ struct ChunkArgs {
   void* S_final;
   int B, T, H, dk, dv, dtype;
   void* stream;
-  // Fused prologue (d64 bf16 pipelined kernel only): q and k raw, alpha and
-  // beta hold the logits a and b; beta = beta_scale * sigmoid(b).
+  // Fused prologue (bf16 pipelined and two-launch kernels): q and k raw,
+  // alpha and beta hold the logits a and b; beta = beta_scale * sigmoid(b).
   int prologue = 0;
   float beta_scale = 1.f;
 };
@@ -96,6 +96,7 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a);  // pipelined kernel, bf16 onl
 // (segmented for long sequences with few chains).  Per-chunk factors and the
 // segment maps go through `workspace`.
 size_t chunk_two_workspace_bytes(const ChunkArgs& a);
+size_t chunk_two_prologue_workspace_bytes(const ChunkArgs& a);  // + 1 / |k|, 1 / |q| per token
 int chunk_two_segments(const ChunkArgs& a);  // segments of the two-level scan (1: none)
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace);
 // The same forward for the gradient pass: also writes the Tb^T records to
@@ -105,6 +106,11 @@ hipError_t launch_chunk_two_states(const ChunkArgs& a, void* workspace, void* re
 hipError_t launch_recurrent_step(const StepArgs& a);
 // Complex64, head size 32: three launches (prep, state scan, output) that
 // exchange per-chunk intermediates through `workspace`.
+// Input transforms of the layer for the fp32 and complex64 forwards (rows of
+// 64 floats): normalised q, k and the gates written to the workspace; *fwd
+// receives `a` with q, k, alpha, beta pointing there.
+size_t prologue_rows_workspace_bytes(long rows);
+hipError_t launch_prologue_rows(const ChunkArgs& a, void* workspace, ChunkArgs* fwd);
 size_t chunk_cx_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.

@@ -91,6 +91,40 @@ template <int M> __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + M, 0xf, 0xf, true));
 }
 
+// Input transforms of a layer (L2 normalisation of query and key rows), for
+// kernels that read the rows in 16-byte pieces of eight bf16 values: the
+// squared norm of a piece (fp32 sum of squares), and the inverse norm
+// 1 / max(|x|, 1e-12) from a row's squared norm.
+__device__ __forceinline__ float piece_sumsq(const u32x4& p) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = lo_f(p[e]), b = hi_f(p[e]);
+    s = __builtin_fmaf(a, a, s);
+    s = __builtin_fmaf(b, b, s);
+  }
+  return s;
+}
+__device__ __forceinline__ float inv_row_norm(float sq) { return __builtin_amdgcn_rsqf(fmaxf(sq, 1e-24f)); }
+// Sum over NU consecutive lanes (NU = 8 or 16, aligned) that hold the pieces
+// of one row.  Lane partners by DPP: xor 1 and xor 2 (quad_perm), then the
+// half-row mirror (lane i ^ 7) and the row mirror (lane i ^ 15); once the
+// partial sums agree within quads (and half-rows), those mirrors read the same
+// values as xor 4 (and xor 8), so every lane of the group ends with the same
+// total.
+template <int NU> __device__ __forceinline__ float row_piece_sum(float s) {
+  static_assert(NU == 8 || NU == 16, "8 or 16 pieces per row");
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value, 0xf,
+                                                              0xf, true));
+  };
+  s += dpp(s, ic<0xB1>{});   // quad_perm [1, 0, 3, 2]
+  s += dpp(s, ic<0x4E>{});   // quad_perm [2, 3, 0, 1]
+  s += dpp(s, ic<0x141>{});  // row_half_mirror
+  if constexpr (NU == 16) s += dpp(s, ic<0x140>{});  // row_mirror
+  return s;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ u32x2 z4() { return u32x2{0u, 0u}; }
 

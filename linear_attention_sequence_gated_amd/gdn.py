@@ -3,7 +3,7 @@
 The raw entry points keep the C names and take integer device addresses:
 ``gdn_chunk_fwd``, ``gdn_chunk_fwd_prologue``, ``gdn_chunk_bwd``,
 ``gdn_fwd_channel_decay``, ``gdn_recurrent_step``, ``gdn_chunk_fwd_noalloc``,
-``gdn_chunk_fwd_workspace_bytes``,
+``gdn_chunk_fwd_workspace_bytes``, ``gdn_chunk_fwd_prologue_workspace_bytes``,
 ``gdn_chunk_bwd_workspace_bytes``, ``gdn_status_str``.  ``chunk_fwd``,
 ``chunk_fwd_prologue``, ``chunk_bwd``, ``fwd_channel_decay`` and ``recurrent_step`` are conveniences for
 torch tensors: they check dtypes and shapes, allocate outputs with torch, pass
@@ -23,7 +23,8 @@ GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 4, 5, 6, 7
 GDN_F32, GDN_BF16, GDN_C64 = 0, 1, 2
 GDN_NOALLOC_MAX_WORKSPACE = 128 << 20  # include/gdn.h
 
-EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_bwd_workspace_bytes",
+EXPORTS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_prologue_workspace_bytes",
+           "gdn_chunk_fwd_prologue", "gdn_chunk_bwd_workspace_bytes",
            "gdn_chunk_bwd", "gdn_fwd_channel_decay", "gdn_recurrent_step", "gdn_status_str", "gdn_chunk_fwd_noalloc")
 
 _lib = None
@@ -49,8 +50,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = ci
+    lib.gdn_chunk_fwd_prologue_workspace_bytes.argtypes = [ci] * 7
+    lib.gdn_chunk_fwd_prologue_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, ci, vp, vp, ci, ci, ci, ci, ci,
-                                           ci, vp]
+                                           ci, vp, sz, vp]
     lib.gdn_chunk_fwd_prologue.restype = ci
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [ci] * 6
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
@@ -89,10 +92,14 @@ def gdn_chunk_fwd_noalloc(q, k, v, alpha, beta, S0, chunk, out, S_final, B, T, H
                                             stream))
 
 
+def gdn_chunk_fwd_prologue_workspace_bytes(B, T, H, dk, dv, chunk, dtype) -> int:
+    return int(load().gdn_chunk_fwd_prologue_workspace_bytes(B, T, H, dk, dv, chunk, dtype))
+
+
 def gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale, S0, chunk, out, S_final, B, T, H, dk, dv,
-                           dtype, stream) -> int:
+                           dtype, workspace, workspace_bytes, stream) -> int:
     return int(load().gdn_chunk_fwd_prologue(q, k, v, a_logit, b_logit, float(beta_scale), S0, chunk, out, S_final,
-                                             B, T, H, dk, dv, dtype, stream))
+                                             B, T, H, dk, dv, dtype, workspace, workspace_bytes, stream))
 
 
 def gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, dtype) -> int:
@@ -185,8 +192,9 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, chunk: int = 64, out=None, S_final=
 def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=None, chunk: int = 64, out=None,
                        S_final=None, stream=None):
     """Chunked forward from raw projections: q and k are L2-normalised per row, alpha = exp(-softplus(a_logit))
-    and beta = beta_scale * sigmoid(b_logit), all inside the kernel.  q, k, v [B,T,H,64] bfloat16; a_logit,
-    b_logit [B,T,H] float32.  Returns (out [B,T,H,64], S_final [B,H,64,64] float32).
+    and beta = beta_scale * sigmoid(b_logit), all on the device.  q, k, v [B,T,H,d] in any supported dtype
+    (bfloat16 d 64 or 128, float32 d 64, complex64 d 32); a_logit, b_logit [B,T,H] float32.  The workspace is
+    allocated here with torch.  Returns (out [B,T,H,d], S_final [B,H,d,d], float32 or complex64).
     """
     import torch
     B, T, H, dk = q.shape
@@ -209,9 +217,11 @@ def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=No
     if S_final is None:
         S_final = torch.empty((B, H, dk, dv), dtype=sdt, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), sdt, dev)
+    ws_bytes = gdn_chunk_fwd_prologue_workspace_bytes(B, T, H, dk, dv, chunk, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     s = gdn_chunk_fwd_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(a_logit), _ptr(b_logit), beta_scale, _ptr(S0), chunk,
-                               _ptr(out), _ptr(S_final), B, T, H, dk, dv, code, st)
+                               _ptr(out), _ptr(S_final), B, T, H, dk, dv, code, _ptr(ws), ws_bytes, st)
     if s != GDN_OK:
         raise GdnError(s)
     return out, S_final

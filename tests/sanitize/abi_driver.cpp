@@ -61,11 +61,21 @@ int main() {
          GDN_ERR_WORKSPACE);
 
   // gdn_chunk_fwd_prologue
-  expect("pro scale", gdn_chunk_fwd_prologue(A, A, A, F, F, 3.f, nullptr, 64, A, A, 1, 64, 1, 64, 64, GDN_BF16, nullptr),
+  expect("pro scale", gdn_chunk_fwd_prologue(A, A, A, F, F, 3.f, nullptr, 64, A, A, 1, 64, 1, 64, 64, GDN_BF16, nullptr,
+                                             0, nullptr),
          GDN_ERR_SHAPE);
   expect("pro null", gdn_chunk_fwd_prologue(A, nullptr, A, F, F, 1.f, nullptr, 64, A, A, 1, 64, 1, 64, 64, GDN_BF16,
-                                            nullptr),
+                                            nullptr, 0, nullptr),
          GDN_ERR_NULL);
+  expect("pro workspace", gdn_chunk_fwd_prologue(A, A, A, F, F, 1.f, nullptr, 64, A, A, 1, 64, 1, 32, 32, GDN_C64,
+                                                 A, 64, nullptr),
+         GDN_ERR_WORKSPACE);
+  expect("pro f32 d128", gdn_chunk_fwd_prologue(A, A, A, F, F, 1.f, nullptr, 64, A, A, 1, 64, 1, 128, 128, GDN_F32,
+                                                nullptr, 0, nullptr),
+         GDN_ERR_UNSUPPORTED);
+  for (int dt : {GDN_F32, GDN_BF16, GDN_C64})
+    for (int d : {32, 64, 128})
+      for (int T : {0, 1, 64, 65, 100000}) (void)gdn_chunk_fwd_prologue_workspace_bytes(3, T, 7, d, d, 64, dt);
 
   // gdn_chunk_bwd
   expect("bwd dtype", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 64, 64, 7,

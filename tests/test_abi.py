@@ -118,7 +118,7 @@ def test_long_sequence_few_chains_takes_the_segmented_scan():
 
 def prologue(**kw):
     args = dict(q=A, k=A, v=A, a_logit=A, b_logit=A, beta_scale=2.0, S0=None, chunk=64, out=A, S_final=A, B=2,
-                T=128, H=3, dk=64, dv=64, dtype=gdn.GDN_BF16, stream=None)
+                T=128, H=3, dk=64, dv=64, dtype=gdn.GDN_BF16, workspace=None, workspace_bytes=0, stream=None)
     args.update(kw)
     return gdn.gdn_chunk_fwd_prologue(**args)
 
@@ -130,8 +130,10 @@ def prologue(**kw):
     (dict(beta_scale=2.5), raw.GDN_ERR_SHAPE),
     (dict(beta_scale=float("nan")), raw.GDN_ERR_SHAPE),
     (dict(chunk=32), raw.GDN_ERR_UNSUPPORTED),
-    (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
-    (dict(dtype=gdn.GDN_F32), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128), raw.GDN_ERR_WORKSPACE),                # d128 runs the two-launch path
+    (dict(dtype=gdn.GDN_F32), raw.GDN_ERR_WORKSPACE),             # fp32: the row pass writes to the workspace
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32), raw.GDN_ERR_WORKSPACE),
+    (dict(dtype=gdn.GDN_F32, dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),  # fp32: d = 64 only
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
     (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
@@ -143,6 +145,23 @@ def prologue(**kw):
 ])
 def test_prologue_argument_errors(kw, status):
     assert prologue(**kw) == status
+
+
+def test_prologue_workspace_sizes():
+    """bf16 needs what the plain forward needs, plus 1/|k| and 1/|q| per token (512 bytes per chunk) on the
+    two-launch path;
+    fp32 and complex64 hold the transformed q, k (256-byte rows) and the two gates, each rounded up to 256 bytes,
+    and complex64 adds the forward's own workspace."""
+    rows = 2 * 128 * 3
+    rowpass = 2 * (rows * 256) + 2 * ((rows * 4 + 255) // 256 * 256)
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 128, 128, 64, gdn.GDN_BF16) == 2 * 3 * 2 * (6400 + 512)
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_F32) == rowpass
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 32, 32, 64, gdn.GDN_C64) == rowpass + 2 * 3 * 2 * 57600
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_C64) == 0   # unsupported
+    need = gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_F32)
+    assert prologue(dtype=gdn.GDN_F32, workspace=A, workspace_bytes=need - 1) == raw.GDN_ERR_WORKSPACE
+    assert prologue(dtype=gdn.GDN_F32, workspace=A + 8, workspace_bytes=need) == raw.GDN_ERR_ALIGN
 
 
 def test_prologue_empty_is_noop():
