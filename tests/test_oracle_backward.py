@@ -3,7 +3,10 @@
 The gradients are pinned to something other than their own derivation:
 * central finite differences, in fp64, of the C oracle's forward (the token
   loop itself) for the scalar  L = sum(o * dO) + sum(S_T * dS_T), along a
-  random direction in each input separately;
+  random direction in each input separately; for complex data the same with
+  L = Re sum(conj(dO) o) + Re sum(conj(dS_T) S_T), along a real and an
+  imaginary direction in each complex input (the gradient's real and
+  imaginary parts);
 * the closed form at beta = 0, where S_t = gamma_t S0 and o_t = gamma_t S0^T q_t;
 * T = 0, where the only gradient is dS0 = dS_T.
 Each mutant plants one plausible mistake in a copy of the source (a dropped
@@ -52,6 +55,39 @@ def pin_finite_differences(fn):
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (name, fd, an)
 
 
+def _cinputs(seed, B=1, T=6, H=2, dk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    c = lambda *sh: rng.normal(size=sh) + 1j * rng.normal(size=sh)  # noqa: E731
+    x = dict(q=c(B, T, H, dk), k=c(B, T, H, dk) / np.sqrt(2 * dk), v=c(B, T, H, dv),
+             alpha=rng.uniform(0.4, 0.95, size=(B, T, H)), beta=rng.uniform(0.2, 1.8, size=(B, T, H)),
+             S0=c(B, H, dk, dv))
+    up = dict(dO=c(B, T, H, dv), dS=c(B, H, dk, dv))
+    return x, up
+
+
+def _closs(x, up):
+    o, S, _ = oracle.recurrent_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], threads=1)
+    return float(np.real(np.sum(np.conj(up["dO"]) * o) + np.sum(np.conj(up["dS"]) * S)))
+
+
+def pin_finite_differences_complex(fn):
+    """For complex inputs the gradient is dL/dRe + i dL/dIm: along a real direction D the loss moves by
+    Re sum(conj(grad) D), along an imaginary one i D by Re sum(conj(grad) i D); the real gates as before."""
+    for seed in (3, 4):
+        x, up = _cinputs(seed)
+        grads = dict(zip(NAMES, fn(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], up["dO"], up["dS"])))
+        rng = np.random.default_rng(200 + seed)
+        for name in NAMES:
+            dirs = [1.0, 1j] if np.iscomplexobj(x[name]) else [1.0]
+            for ph in dirs:
+                D = rng.normal(size=x[name].shape) * ph
+                eps = 1e-6
+                fd = (_closs(dict(x, **{name: x[name] + eps * D}), up)
+                      - _closs(dict(x, **{name: x[name] - eps * D}), up)) / (2 * eps)
+                an = float(np.real(np.sum(np.conj(grads[name]) * D)))
+                assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (name, ph, fd, an)
+
+
 def pin_beta_zero_closed_form(fn):
     """beta = 0: S_t = gamma_t S0, so dq_t = gamma_t S0 dO_t, dS0 = sum_t gamma_t q_t dO_t^T + gamma_T dS_T,
     dalpha_t = sum_{s >= t} (gamma_s / alpha_t) q_s^T S0 dO_s + (gamma_T / alpha_t) <S0, dS_T>,
@@ -89,7 +125,7 @@ def pin_empty_sequence(fn):
     assert np.array_equal(out[5], up["dS"])
 
 
-PINS = [pin_finite_differences, pin_beta_zero_closed_form, pin_empty_sequence]
+PINS = [pin_finite_differences, pin_finite_differences_complex, pin_beta_zero_closed_form, pin_empty_sequence]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -99,21 +135,31 @@ def test_backward_pin(pin):
 
 MUTATIONS = {
     "readout_gradient_dropped": ("D = G + qt[..., :, None] * dot[..., None, :]", "D = G + 0 * qt[..., :, None]"),
-    "dq_from_previous_state": ('dq[:, t] = np.einsum("bhij,bhj->bhi", St, dot)',
-                               'dq[:, t] = np.einsum("bhij,bhj->bhi", Sp, dot)'),
-    "dalpha_from_new_state": ("np.sum(D * (Sp - b", "np.sum(D * (St - b"),
+    "dq_from_previous_state": ('dq[:, t] = np.einsum("bhij,bhj->bhi", St, cj(dot))',
+                               'dq[:, t] = np.einsum("bhij,bhj->bhi", Sp, cj(dot))'),
+    "dalpha_from_new_state": ("np.sum(cj(D) * (Sp - b", "np.sum(cj(D) * (St - b"),
     "carry_without_alpha": ("G = a[..., None, None] * (D", "G = (D"),
     "carry_without_rank_one": ("G = a[..., None, None] * (D - b[..., None, None] * kt[..., :, None] * w[..., None, :])",
                                "G = a[..., None, None] * D"),
-    "dk_second_term_sign": ('- (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, w)',
-                            '+ (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, w)'),
+    "dk_second_term_sign": ('- (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, cj(w))',
+                            '+ (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, cj(w))'),
     "dbeta_without_alpha": ("(vt - a[..., None] * u)", "(vt - u)"),
     "dv_without_beta": ("dv_[:, t] = b[..., None] * w", "dv_[:, t] = w"),
-    "w_from_carry_only": ('w = np.einsum("bhij,bhi->bhj", D, kt)', 'w = np.einsum("bhij,bhi->bhj", G, kt)'),
-    "u_from_new_state": ('u = np.einsum("bhij,bhi->bhj", Sp, kt)', 'u = np.einsum("bhij,bhi->bhj", St, kt)'),
+    "w_from_carry_only": ('w = np.einsum("bhij,bhi->bhj", D, cj(kt))', 'w = np.einsum("bhij,bhi->bhj", G, cj(kt))'),
+    "u_from_new_state": ('u = np.einsum("bhij,bhi->bhj", Sp, cj(kt))', 'u = np.einsum("bhij,bhi->bhj", St, cj(kt))'),
     "y_without_beta": ("y = b[..., None] * vt", "y = vt"),
-    "dk_transposed_state": ('- (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, w)',
-                            '- (a * b)[..., None] * np.einsum("bhji,bhj->bhi", Sp[..., :, :dv], w[..., :dk])'),
+    "dk_transposed_state": ('- (a * b)[..., None] * np.einsum("bhij,bhj->bhi", Sp, cj(w))',
+                            '- (a * b)[..., None] * np.einsum("bhji,bhj->bhi", Sp[..., :, :dv], cj(w)[..., :dk])'),
+    # complex only: a conjugation dropped or added
+    "forward_readout_unconjugated": ('u = np.einsum("bhij,bhi->bhj", S, cj(kt))',
+                                     'u = np.einsum("bhij,bhi->bhj", S, kt)'),
+    "w_unconjugated_key": ('w = np.einsum("bhij,bhi->bhj", D, cj(kt))', 'w = np.einsum("bhij,bhi->bhj", D, kt)'),
+    "dq_unconjugated_upstream": ('St, cj(dot))', 'St, dot)'),
+    "dk_unconjugated_y": ('np.einsum("bhij,bhj->bhi", D, cj(y))', 'np.einsum("bhij,bhj->bhi", D, y)'),
+    "dk_unconjugated_w": ('np.einsum("bhij,bhj->bhi", Sp, cj(w)))', 'np.einsum("bhij,bhj->bhi", Sp, w))'),
+    "dbeta_unconjugated_w": ("np.real(np.sum(cj(w) *", "np.real(np.sum(w *"),
+    "dalpha_unconjugated_D": ("np.real(np.sum(cj(D) *", "np.real(np.sum(D *"),
+    "carry_conjugated_w": ("kt[..., :, None] * w[..., None, :])", "kt[..., :, None] * cj(w)[..., None, :])"),
 }
 
 
