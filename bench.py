@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
     "cx_prep_scan_out": [_CSRC + "chunk_cx.hip", _CSRC + "gdn_device.hpp"],
     "decode_kernel": [_CSRC + "decode.hip", _CSRC + "gdn_device.hpp"],
     "bwd_kernel": [_CSRC + "chunk_bwd.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
+    "bwd_cx_kernel": [_CSRC + "bwd_cx.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_chunk_kernel": [_CSRC + "channel_chunk.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_c64_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
@@ -799,7 +800,7 @@ def backward_flops(w) -> float:
     """Vector flops of the backward per call: one forward recompute (u = S^T k and the rank-one update,
     5 d^2 per token-head) and the reverse step (D, u, w, <D, S>, the two row sums and the carried
     gradient, 17 d^2), i.e. 22 d^2 per token-head.  The checkpoint pass's second forward is not counted."""
-    return 22.0 * w.dk * w.dv * w.B * w.T * w.H
+    return 22.0 * w.dk * w.dv * w.B * w.T * w.H * (4 if w.dtype == "c64" else 1)
 
 
 def bench_backward(args, w, dev):
@@ -810,12 +811,15 @@ def bench_backward(args, w, dev):
     import linear_attention_sequence_gated_amd as gdn
     from gdn_inputs import bf16_round, gen_upstream_grads, gen_workload
     inp = gen_workload(w)
-    dO, dS = gen_upstream_grads(w.B, w.T, w.H, w.dk, w.dv, seed=w.seed, with_dS=True)
-    dO = bf16_round(dO)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    code = gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32
+    cx = w.dtype == "c64"
+    dO, dS = gen_upstream_grads(w.B, w.T, w.H, w.dk, w.dv, seed=w.seed, with_dS=True, dtype="c64" if cx else "f32")
+    if w.dtype == "bf16":
+        dO = bf16_round(dO)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "c64": torch.complex64}[w.dtype]
+    code = {"bf16": gdn.GDN_BF16, "f32": gdn.GDN_F32, "c64": gdn.GDN_C64}[w.dtype]
     ncopies = args.copies or 2
-    f32 = dict(dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.complex64 if cx else torch.float32, device=dev)
+    g32 = dict(dtype=torch.float32, device=dev)
     sets = []
     for _ in range(ncopies):
         d = {x: torch.from_numpy(inp[x]).to(dev).to(tdt) for x in ("q", "k", "v")}
@@ -823,8 +827,8 @@ def bench_backward(args, w, dev):
         d["dO"], d["dS"] = torch.from_numpy(dO).to(dev).to(tdt), torch.from_numpy(dS).to(dev)
         sets.append(d)
     outs = [torch.empty((w.B, w.T, w.H, w.dk), **f32), torch.empty((w.B, w.T, w.H, w.dk), **f32),
-            torch.empty((w.B, w.T, w.H, w.dv), **f32), torch.empty((w.B, w.T, w.H), **f32),
-            torch.empty((w.B, w.T, w.H), **f32), torch.empty((w.B, w.H, w.dk, w.dv), **f32)]
+            torch.empty((w.B, w.T, w.H, w.dv), **f32), torch.empty((w.B, w.T, w.H), **g32),
+            torch.empty((w.B, w.T, w.H), **g32), torch.empty((w.B, w.H, w.dk, w.dv), **f32)]
     ws_bytes = gdn.gdn_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, code)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -846,12 +850,17 @@ def bench_backward(args, w, dev):
     tfs = flops / (avg_ms * 1e-3) / 1e12
     tok = w.B * w.T * w.H
     # q, k, v, dO in; alpha, beta in; dq, dk, dv (fp32) and dalpha, dbeta out; dS_T in and dS0 out
-    hbm_bytes = tok * (3 * w.dk * 2 + w.dv * 2 + 8) + tok * (2 * w.dk + w.dv) * 4 + tok * 8 + 2 * w.B * w.H * w.dk * w.dv * 4
+    eb = {"bf16": 2, "f32": 4, "c64": 8}[w.dtype]
+    gb = 8 if cx else 4
+    hbm_bytes = (tok * (2 * w.dk * eb + 2 * w.dv * eb + 8) + tok * (2 * w.dk + w.dv) * gb + tok * 8
+                 + 2 * w.B * w.H * w.dk * w.dv * gb)
     result = {
         "metric": f"tokens/sec gated-delta chunk bwd ({w.name})", "value": w.B * w.T * args.steps / wall,
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded; inputs as sykra_layer_bf16, upstream gradients N(0,1))",
+        "dtype": w.dtype,
+        "data": ("synthetic (seeded; inputs as deltaphase_c64, complex normal upstream gradients)" if cx else
+                 "synthetic (seeded; inputs as the forward workload, upstream gradients N(0,1))"),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
                    "input_copies_cycled": ncopies, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
@@ -859,9 +868,11 @@ def bench_backward(args, w, dev):
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": hbm_bytes,
                      "hbm_achieved_GBs": hbm_bytes / (avg_ms * 1e-3) / 1e9, "kernel_avg_ms": avg_ms,
-                     "kernel": "gdn::bwd::bwd_kernel"},
+                     "kernel": "gdn::bwdcx::bwd_cx_kernel" if cx else "gdn::bwd::bwd_kernel"},
     }
-    key = "bwd_kernel"
+    key = "bwd_cx_kernel" if cx else "bwd_kernel"
+    if cx:
+        result["roofline"]["traffic"] = measured_traffic(key, w.name)
     if w.dtype == "bf16":
         # bf16 runs the chunk form on the matrix cores, four launches per call (the forward's factor and
         # state passes, the adjoint scan, the chunk-parallel gradients): priced on its HBM bytes.

@@ -115,6 +115,9 @@ WORKLOADS = {
         "long_context_bf16_bwd", "backward", "bf16", B=2, T=16384, H=16, dk=128, dv=128, seed=2,
         alpha_mu=-5.0, s0_var=0.01,
         note="gradients of the long-context d=128 layer (inputs as long_context_bf16, upstream dO, dS_T ~ N(0,1))"),
+    "deltaphase_c64_bwd": Workload(
+        "deltaphase_c64_bwd", "backward", "c64", B=4, T=4096, H=8, dk=32, dv=32, seed=3, beta_scale=2.0,
+        note="gradients of the complex phasor layer (inputs as deltaphase_c64, complex upstream dO, dS_T)"),
     "sykra_layer_bf16_channel_decay": Workload(
         "sykra_layer_bf16_channel_decay", "channel", "bf16", B=8, T=2048, H=12, dk=64, dv=64, seed=1,
         note="the Sykra-shaped layer with a decay per token and value channel (DeltaPhase section 5)"),
@@ -198,10 +201,17 @@ def gen_raw_layer(B, T, H, d, seed=0, alpha_mu=-4.0, s0_var=None, dtype="bf16"):
                 b_logit=b.astype(np.float32), S0=S0)
 
 
-def gen_upstream_grads(B, T, H, dk, dv, seed=0, with_dS=True):
+def gen_upstream_grads(B, T, H, dk, dv, seed=0, with_dS=True, dtype="f32"):
     """Upstream gradients for the backward: dO ~ N(0, 1) [B, T, H, dv] stored in fp32 (cast to the
-    forward's dtype by the caller) and, if asked, dS_T ~ N(0, 1) [B, H, dk, dv] fp32."""
+    forward's dtype by the caller) and, if asked, dS_T ~ N(0, 1) [B, H, dk, dv] fp32.  dtype 'c64': complex
+    normal, real and imaginary parts N(0, 1/2) each, stored as complex64."""
     rng = np.random.default_rng(seed + 1000)
+    if dtype == "c64":
+        s = np.sqrt(0.5)
+        dO = (rng.normal(0.0, s, (B, T, H, dv)) + 1j * rng.normal(0.0, s, (B, T, H, dv))).astype(np.complex64)
+        dS = ((rng.normal(0.0, s, (B, H, dk, dv)) + 1j * rng.normal(0.0, s, (B, H, dk, dv))).astype(np.complex64)
+              if with_dS else None)
+        return dO, dS
     dO = rng.normal(0.0, 1.0, (B, T, H, dv)).astype(np.float32)
     dS = rng.normal(0.0, 1.0, (B, H, dk, dv)).astype(np.float32) if with_dS else None
     return dO, dS

@@ -184,15 +184,19 @@ int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const fl
  * a bf16 end gradient (2 * 6400 + 2 * 64 * 64 * 2 bytes), plus the forward's
  * segment maps when it splits long sequences (as gdn_chunk_fwd_workspace_bytes
  * reports them).  fp32: B * H * ceil(T / 8) * 64 * 64 * 4 (the forward state
- * every 8 tokens).  0 for an unsupported combination or T == 0.
+ * every 8 tokens).  complex64 (d = 32): B * H * ceil(T / 8) * 32 * 32 * 8.  0
+ * for an unsupported combination or T == 0.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
 
 /*
- * Reverse-mode gradients of gdn_chunk_fwd for real data: given the gradients
- * grad_out of out and grad_S_final of S_final, the gradients of
+ * Reverse-mode gradients of gdn_chunk_fwd: given the gradients grad_out of
+ * out and grad_S_final of S_final, the gradients of the real loss
  * sum(out * grad_out) + sum(S_final * grad_S_final) with respect to q, k, v,
- * alpha, beta and S0.  The forward is the recurrence of DeltaPhase README
+ * alpha, beta and S0.  For complex data the loss is
+ * Re sum(conj(grad_out) out) + Re sum(conj(grad_S_final) S_final), and the
+ * gradient of a complex value z is dL/dRe(z) + i dL/dIm(z) (the upstream
+ * gradients are given the same way); alpha and beta stay real.  The forward is the recurrence of DeltaPhase README
  * section 2 with the data-dependent forget gate of the Sykra README
  * ("Architectural Highlights"), applied to the whole Householder-updated
  * state, as for gdn_chunk_fwd; the gradients follow it token by token in
@@ -202,22 +206,27 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dt
  *   q, k, v, alpha, beta, S0   the forward's inputs, as for gdn_chunk_fwd
  *                              (S0 may be NULL: zero)
  *   grad_out      [B, T, H, dv]  dtype     gradient of out
- *   grad_S_final  [B, H, dk, dv] float32   gradient of S_final (NULL: zero)
- *   grad_q, grad_k [B, T, H, dk], grad_v [B, T, H, dv]   float32, written
+ *   grad_S_final  [B, H, dk, dv] float32 (complex64 for GDN_C64)   gradient
+ *                 of S_final (NULL: zero)
+ *   grad_q, grad_k [B, T, H, dk], grad_v [B, T, H, dv]   float32 (complex64
+ *                 for GDN_C64), written
  *   grad_alpha, grad_beta [B, T, H]                      float32, written
- *   grad_S0       [B, H, dk, dv] float32, written (NULL: not computed)
+ *   grad_S0       [B, H, dk, dv] float32 (complex64 for GDN_C64), written
+ *                 (NULL: not computed)
+ *   (for GDN_C64 the float pointers hold complex64 as interleaved re, im)
  *   workspace     device memory of at least gdn_chunk_bwd_workspace_bytes(...)
  *                 bytes, owned by the caller, overwritten (may be NULL when
  *                 that is 0)
  *
- * Supported: dtype GDN_F32 or GDN_BF16, dk == dv == 64, any T >= 0 with
- * T * H * 4 < 2^31; otherwise GDN_ERR_UNSUPPORTED (GDN_C64 included).
+ * Supported: GDN_F32 with dk == dv == 64, GDN_BF16 with dk == dv == 64 or
+ * 128, GDN_C64 with dk == dv == 32, any T >= 0 with T * H * 4 < 2^31;
+ * otherwise GDN_ERR_UNSUPPORTED.
  * bf16 inputs take the chunk form on the matrix cores (the same chunking as
  * gdn_chunk_fwd, run in reverse: the forward's chunk start states, then the
  * gradient carried from the last chunk to the first, then every chunk's
  * gradients at once), with bf16 operands and fp32 accumulation, like the
- * forward.  fp32 inputs take a token-by-token reverse pass in fp32 throughout
- * (checkpoints every 8 tokens).  The forward is recomputed inside the call, so
+ * forward.  fp32 and complex64 inputs take a token-by-token reverse pass in
+ * fp32 throughout (checkpoints every 8 tokens).  The forward is recomputed inside the call, so
  * nothing from a forward call is needed.  Gradient outputs must not alias any
  * input.  alpha must be positive (the chunk form works with log alpha).
  * B * H == 0 is a no-op; T == 0 copies grad_S_final (or zeros) to grad_S0.

@@ -187,7 +187,9 @@ int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const fl
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
-  if (B < 0 || T < 0 || H < 0 || (dtype != GDN_F32 && dtype != GDN_BF16)) return 0;
+  if (B < 0 || T < 0 || H < 0) return 0;
+  if (dtype == GDN_C64) return dk == 32 && dv == 32 ? gdn::chunk_bwd_cx_workspace_bytes(B, T, H) : 0;
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
   if (grad_path(B, T, H, dk, dv, dtype)) return gdn::chunk_grad_workspace_bytes(B, T, H, dk);
   if (dk != 64 || dv != 64) return 0;
   return gdn::chunk_bwd_workspace_bytes(B, T, H);
@@ -203,8 +205,9 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
       !chains_fit((long long)B * H, 256))
     return GDN_ERR_SHAPE;
   const bool mfma = grad_path(B, T, H, dk, dv, dtype);
-  if (dtype == GDN_C64 || (!mfma && (dk != 64 || dv != 64 || (long long)T * H * 4 >= (1LL << 31))))
-    return GDN_ERR_UNSUPPORTED;
+  const bool cx = dtype == GDN_C64;
+  if ((long long)T * H * 4 >= (1LL << 31) && !mfma) return GDN_ERR_UNSUPPORTED;
+  if (cx ? (dk != 32 || dv != 32) : (!mfma && (dk != 64 || dv != 64))) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;
   if (tokens && (!q || !k || !v || !alpha || !beta || !grad_out || !grad_q || !grad_k || !grad_v || !grad_alpha ||
                  !grad_beta))
@@ -213,12 +216,15 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
                         grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_S0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-  const size_t need = mfma ? gdn::chunk_grad_workspace_bytes(B, T, H, dk) : gdn::chunk_bwd_workspace_bytes(B, T, H);
+  const size_t need = cx     ? gdn::chunk_bwd_cx_workspace_bytes(B, T, H)
+                      : mfma ? gdn::chunk_grad_workspace_bytes(B, T, H, dk)
+                             : gdn::chunk_bwd_workspace_bytes(B, T, H);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if ((long long)B * H == 0) return GDN_OK;
   gdn::BwdArgs a{q,      k,      v,      alpha,      beta,      S0,      grad_out, grad_S_final, grad_q, grad_k,
                  grad_v, grad_alpha, grad_beta, grad_S0, workspace, B, T, H, dtype, stream};
   a.D = dk;
+  if (cx) return gdn::launch_chunk_bwd_cx(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   if (mfma) return gdn::launch_chunk_grad(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -53,8 +53,9 @@ struct StepArgs {
   void* stream;
 };
 
-// Reverse-mode gradients of the chunk forward (real dtypes, d = 64); all
-// gradient outputs are fp32.  dS_final, S0 and dS0 may be NULL.
+// Reverse-mode gradients of the chunk forward; gradient outputs are fp32
+// (complex64 for complex data, as float pairs).  dS_final, S0 and dS0 may be
+// NULL.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -116,6 +117,10 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+// Complex data, d = 32 (pointers hold complex64 as float pairs; alpha, beta
+// and their gradients real).
+size_t chunk_bwd_cx_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk_bwd_cx(const BwdArgs& a);
 // bf16, d = 64 or 128: the chunk form on the matrix cores (the forward's
 // factor and state passes, the adjoint scan, the chunk-parallel gradients).
 // T = 0 copies dS_final (or zeros) to dS0.

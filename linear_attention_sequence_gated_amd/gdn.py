@@ -228,11 +228,13 @@ def chunk_fwd_prologue(q, k, v, a_logit, b_logit, beta_scale: float = 1.0, S0=No
 
 
 def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream=None):
-    """Gradients of sum(out * grad_out) + sum(S_final * grad_S_final) for chunk_fwd's forward (real data, d = 64).
+    """Gradients of sum(out * grad_out) + sum(S_final * grad_S_final) for chunk_fwd's forward (for complex data
+    Re sum(conj(grad_out) out) + Re sum(conj(grad_S_final) S_final), gradients dL/dRe + i dL/dIm).
 
-    q, k, v, grad_out [B,T,H,64] float32 or bfloat16 (one dtype); alpha, beta [B,T,H] float32; S0 and
-    grad_S_final [B,H,64,64] float32 or None.  Returns fp32 (grad_q, grad_k, grad_v, grad_alpha, grad_beta,
-    grad_S0).  The workspace is allocated here with torch.
+    q, k, v, grad_out [B,T,H,d]: float32 (d 64), bfloat16 (d 64 or 128) or complex64 (d 32), one dtype;
+    alpha, beta [B,T,H] float32; S0 and grad_S_final [B,H,d,d] float32 (complex64 for complex data) or None.
+    Returns (grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_S0): float32, complex64 for the complex
+    ones of complex data.  The workspace is allocated here with torch.
     """
     import torch
     B, T, H, dk = q.shape
@@ -247,14 +249,16 @@ def chunk_bwd(q, k, v, alpha, beta, grad_out, S0=None, grad_S_final=None, stream
         _check(t, name, shp, q.dtype, dev)
     _check(alpha, "alpha", (B, T, H), torch.float32, dev)
     _check(beta, "beta", (B, T, H), torch.float32, dev)
+    gdt = _state_dtype(code)
     if S0 is not None:
-        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+        _check(S0, "S0", (B, H, dk, dv), gdt, dev)
     if grad_S_final is not None:
-        _check(grad_S_final, "grad_S_final", (B, H, dk, dv), torch.float32, dev)
+        _check(grad_S_final, "grad_S_final", (B, H, dk, dv), gdt, dev)
+    g = dict(dtype=gdt, device=dev)
+    gq, gk, gv = torch.empty((B, T, H, dk), **g), torch.empty((B, T, H, dk), **g), torch.empty((B, T, H, dv), **g)
     f32 = dict(dtype=torch.float32, device=dev)
-    gq, gk, gv = torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dv), **f32)
     ga, gb = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
-    gS0 = torch.empty((B, H, dk, dv), **f32)
+    gS0 = torch.empty((B, H, dk, dv), **g)
     ws_bytes = gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, code)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream

@@ -81,17 +81,20 @@ int main() {
   expect("bwd dtype", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 64, 64, 7,
                                     A, 1 << 20, nullptr),
          GDN_ERR_DTYPE);
-  expect("bwd c64", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 32, 32, GDN_C64,
-                                  A, 1 << 20, nullptr),
+  expect("bwd c64 d64", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 64, 64,
+                                      GDN_C64, A, 1 << 20, nullptr),
          GDN_ERR_UNSUPPORTED);
+  expect("bwd c64 workspace", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 32,
+                                            32, GDN_C64, A, 16, nullptr),
+         GDN_ERR_WORKSPACE);
   expect("bwd null", gdn_chunk_bwd(A, A, A, F, F, nullptr, nullptr, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 1, 64, 1, 64, 64,
                                    GDN_F32, A, 1 << 20, nullptr),
          GDN_ERR_NULL);
   expect("bwd workspace", gdn_chunk_bwd(A, A, A, F, F, nullptr, A, nullptr, Fw, Fw, Fw, Fw, Fw, Fw, 2, 640, 3, 128, 128,
                                         GDN_BF16, A, 16, nullptr),
          GDN_ERR_WORKSPACE);
-  for (int dt : {GDN_F32, GDN_BF16})
-    for (int d : {64, 128})
+  for (int dt : {GDN_F32, GDN_BF16, GDN_C64})
+    for (int d : {32, 64, 128})
       for (int T : {0, 1, 64, 65, 100000}) (void)gdn_chunk_bwd_workspace_bytes(3, T, 7, d, d, dt);
 
   // gdn_fwd_channel_decay

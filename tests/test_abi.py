@@ -187,6 +187,9 @@ def backward(**kw):
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
     (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(B=1, T=1 << 22, H=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32, B=1, T=1 << 22, H=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32, workspace=None), raw.GDN_ERR_WORKSPACE),
+    (dict(dtype=gdn.GDN_C64, dk=32, dv=32, workspace_bytes=2 * 3 * 16 * 32 * 32 * 8 - 1), raw.GDN_ERR_WORKSPACE),
     (dict(grad_out=None), raw.GDN_ERR_NULL),
     (dict(grad_beta=None), raw.GDN_ERR_NULL),
     (dict(alpha=None), raw.GDN_ERR_NULL),
@@ -212,6 +215,8 @@ def test_backward_empty_and_workspace_query():
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == 2 * 3 * 17 * 64 * 64 * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
+    # complex64 d = 32: the token-by-token kernel -- the complex state every 8 tokens
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 32, 32, gdn.GDN_C64) == 2 * 3 * 17 * 32 * 32 * 8
 
 
 def channel(**kw):

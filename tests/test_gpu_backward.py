@@ -10,9 +10,9 @@ from gpu_util import note, torch_dev, up
 
 pytestmark = pytest.mark.gpu
 
-# fp32 inputs: the token-by-token kernel, fp32 arithmetic on exactly-read inputs.  bf16 inputs: the chunk form
-# on the matrix cores, bf16 operands with fp32 accumulation (as in the forward).
-TOLS = {"f32": 1e-4, "bf16": 5e-2}
+# fp32 and complex64 inputs: the token-by-token kernels, fp32 arithmetic on exactly-read inputs.  bf16 inputs:
+# the chunk form on the matrix cores, bf16 operands with fp32 accumulation (as in the forward).
+TOLS = {"f32": 1e-4, "bf16": 5e-2, "c64": 1e-4}
 NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")
 
 
@@ -34,7 +34,8 @@ def oracle_bwd(inp, dO, dS):
 
 def per_chain_errors(x, ref, name):
     """Max over (b, h) chains of ||x - ref|| / ||ref|| and of max|x - ref| / max|ref|, over that chain's entries."""
-    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    cplx = np.iscomplexobj(x) or np.iscomplexobj(ref)
+    x, ref = (np.asarray(y, np.complex128 if cplx else np.float64) for y in (x, ref))
     if name == "dS0":
         xs, rs = x.reshape(-1, x.shape[-2] * x.shape[-1]), ref.reshape(-1, ref.shape[-2] * ref.shape[-1])
     else:  # [B, T, H, ...] -> chains
@@ -59,8 +60,9 @@ def assert_grads(tag, got, ref, dtype):
 
 
 def _case(B, T, H, dtype, seed, s0, dS, d=64):
-    inp = gen_chunk(B, T, H, d, d, dtype=dtype, seed=seed, s0_var=0.1 if s0 else None)
-    dO, dSf = gen_upstream_grads(B, T, H, d, d, seed=seed, with_dS=dS)
+    inp = gen_chunk(B, T, H, d, d, dtype=dtype, seed=seed, s0_var=0.1 if s0 else None,
+                    beta_scale=2.0 if dtype == "c64" else 1.0)
+    dO, dSf = gen_upstream_grads(B, T, H, d, d, seed=seed, with_dS=dS, dtype="c64" if dtype == "c64" else "f32")
     if dtype == "bf16":
         dO = bf16_round(dO)
     return inp, dO, dSf
@@ -151,3 +153,47 @@ def test_backward_d128_long():
     dO = bf16_round(dO)
     note("backward d128 long")
     assert_grads("bwd_d128_long", run_bwd(inp, "bf16", dO, dSf), oracle_bwd(inp, dO, dSf), "bf16")
+
+
+# Complex data, d = 32 (the phasor memory): the token-by-token kernel in fp32, gradients dL/dRe + i dL/dIm.
+@pytest.mark.parametrize("B,T,H,s0,dS", [(1, 20, 2, False, False), (2, 77, 3, True, True), (1, 200, 2, True, False)])
+def test_backward_complex(B, T, H, s0, dS):
+    inp, dO, dSf = _case(B, T, H, "c64", 31 + T, s0, dS, d=32)
+    note(f"backward complex B{B} T{T} H{H} S0={s0} dS={dS}")
+    assert_grads(f"bwd_c64_{B}_{T}_{H}", run_bwd(inp, "c64", dO, dSf), oracle_bwd(inp, dO, dSf), "c64")
+
+
+@pytest.mark.parametrize("T", [0, 1, 7, 8, 9, 65])
+def test_backward_complex_lengths(T):
+    inp, dO, dSf = _case(2, T, 2, "c64", 50 + T, True, True, d=32)
+    note(f"backward complex lengths T={T}")
+    got = run_bwd(inp, "c64", dO, dSf)
+    if T == 0:  # only dS0 = dS_T
+        assert np.array_equal(got[5], dSf)
+        return
+    assert_grads(f"bwd_c64_len{T}", got, oracle_bwd(inp, dO, dSf), "c64")
+
+
+def test_backward_complex_extreme_gates():
+    """Complex data with gates at their extremes on random tokens: alpha = 1e-6 or 1, beta = 0 or 2."""
+    inp, dO, dSf = _case(2, 150, 2, "c64", 78, True, True, d=32)
+    rng = np.random.default_rng(9)
+    pa, pb = rng.random(inp["alpha"].shape), rng.random(inp["beta"].shape)
+    inp["alpha"] = np.where(pa < 0.1, 1e-6, np.where(pa < 0.3, 1.0, inp["alpha"])).astype(np.float32)
+    inp["beta"] = np.where(pb < 0.15, 0.0, np.where(pb < 0.3, 2.0, inp["beta"])).astype(np.float32)
+    note("backward complex extreme gates")
+    assert_grads("bwd_c64_extreme", run_bwd(inp, "c64", dO, dSf), oracle_bwd(inp, dO, dSf), "c64")
+
+
+@pytest.mark.timeout(600)
+def test_backward_complex_full_size_all_chains():
+    """The 4 x 4096 x 8 complex phasor layer; every chain recomputed by the oracle (one batch row at a time)."""
+    w = WORKLOADS["deltaphase_c64_bwd"]
+    inp = gen_workload(w)
+    dO, dSf = gen_upstream_grads(w.B, w.T, w.H, w.dk, w.dv, seed=w.seed, with_dS=True, dtype="c64")
+    note("backward full size deltaphase_c64_bwd")
+    got = run_bwd(inp, "c64", dO, dSf)
+    for b0 in range(w.B):
+        sl = slice(b0, b0 + 1)
+        sub = {x: (None if inp[x] is None else inp[x][sl]) for x in inp}
+        assert_grads(f"bwd_c64_full_row{b0}", [g[sl] for g in got], oracle_bwd(sub, dO[sl], dSf[sl]), "c64")
