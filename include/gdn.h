@@ -183,9 +183,11 @@ int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const fl
  * (chain, 64-token chunk) two 6400-byte factor records, a bf16 start state and
  * a bf16 end gradient (2 * 6400 + 2 * 64 * 64 * 2 bytes), plus the forward's
  * segment maps when it splits long sequences (as gdn_chunk_fwd_workspace_bytes
- * reports them).  fp32: B * H * ceil(T / 8) * 64 * 64 * 4 (the forward state
- * every 8 tokens).  complex64 (d = 32): B * H * ceil(T / 8) * 32 * 32 * 8.  0
- * for an unsupported combination or T == 0.
+ * reports them).  fp32 (d = 64) and complex64 (d = 32): the forward state
+ * every 8 tokens, B * H * ceil(T / 8) * d * d * e bytes (e = 4 or 8), plus the
+ * shares of dq, dk, dalpha and dbeta from each of the d / 8 column groups,
+ * (d / 8) * B * T * H * (2 * d * e + 8) bytes.  0 for an unsupported
+ * combination.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
 
@@ -226,7 +228,9 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dt
  * gradient carried from the last chunk to the first, then every chunk's
  * gradients at once), with bf16 operands and fp32 accumulation, like the
  * forward.  fp32 and complex64 inputs take a token-by-token reverse pass in
- * fp32 throughout (checkpoints every 8 tokens).  The forward is recomputed inside the call, so
+ * fp32 throughout (checkpoints every 8 tokens), split by groups of 8 state
+ * columns (the columns evolve independently; a second launch adds the
+ * groups' shares of dq, dk, dalpha and dbeta).  The forward is recomputed inside the call, so
  * nothing from a forward call is needed.  Gradient outputs must not alias any
  * input.  alpha must be positive (the chunk form works with log alpha).
  * B * H == 0 is a no-op; T == 0 copies grad_S_final (or zeros) to grad_S0.

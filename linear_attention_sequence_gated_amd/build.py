@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 PEAK_LIB = os.path.join(PKG, "libgdn_peak.so")
 PEAK_SOURCES = ["peak.hip"]
-SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "bwd_cx.hip", "chunk_grad.hip", "channel_decay.hip", "channel_chunk.hip", "decode.hip", "noalloc.hip", "prologue.hip", "gdn_api.cpp"]
+SOURCES = ["chunk_fwd.hip", "chunk_pipe.hip", "chunk_two.hip", "chunk_cx.hip", "chunk_bwd.hip", "tok_bwd.hip", "chunk_grad.hip", "channel_decay.hip", "channel_chunk.hip", "decode.hip", "noalloc.hip", "prologue.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled for device code (the host pass warns that it

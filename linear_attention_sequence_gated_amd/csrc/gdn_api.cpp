@@ -188,9 +188,10 @@ int gdn_chunk_fwd_prologue(const void* q, const void* k, const void* v, const fl
 
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
   if (B < 0 || T < 0 || H < 0) return 0;
-  if (dtype == GDN_C64) return dk == 32 && dv == 32 ? gdn::chunk_bwd_cx_workspace_bytes(B, T, H) : 0;
+  if (dtype == GDN_C64) return dk == 32 && dv == 32 ? gdn::tok_bwd_workspace_bytes(B, T, H, true) : 0;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
   if (grad_path(B, T, H, dk, dv, dtype)) return gdn::chunk_grad_workspace_bytes(B, T, H, dk);
+  if (dtype == GDN_F32) return dk == 64 && dv == 64 ? gdn::tok_bwd_workspace_bytes(B, T, H, false) : 0;
   if (dk != 64 || dv != 64) return 0;
   return gdn::chunk_bwd_workspace_bytes(B, T, H);
 }
@@ -216,7 +217,11 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
                         grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_S0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-  const size_t need = cx     ? gdn::chunk_bwd_cx_workspace_bytes(B, T, H)
+  // complex64 and fp32: the token-by-token pass split by column groups; bf16:
+  // the chunk form (the token kernel only for T == 0 and rows past 32-bit
+  // offsets)
+  const bool tok = cx || dtype == GDN_F32;
+  const size_t need = tok    ? gdn::tok_bwd_workspace_bytes(B, T, H, cx)
                       : mfma ? gdn::chunk_grad_workspace_bytes(B, T, H, dk)
                              : gdn::chunk_bwd_workspace_bytes(B, T, H);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
@@ -224,7 +229,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   gdn::BwdArgs a{q,      k,      v,      alpha,      beta,      S0,      grad_out, grad_S_final, grad_q, grad_k,
                  grad_v, grad_alpha, grad_beta, grad_S0, workspace, B, T, H, dtype, stream};
   a.D = dk;
-  if (cx) return gdn::launch_chunk_bwd_cx(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (tok) return gdn::launch_tok_bwd(a, cx) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   if (mfma) return gdn::launch_chunk_grad(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

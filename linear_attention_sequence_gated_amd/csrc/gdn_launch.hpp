@@ -117,10 +117,11 @@ hipError_t launch_chunk_cx(const ChunkArgs& a, void* workspace);
 // Backward: forward checkpoints every 8 tokens in `workspace`.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
-// Complex data, d = 32 (pointers hold complex64 as float pairs; alpha, beta
+// Token-by-token reverse pass split by column groups: fp32 data (d = 64) or
+// complex64 data (d = 32; pointers hold complex64 as float pairs, alpha, beta
 // and their gradients real).
-size_t chunk_bwd_cx_workspace_bytes(int B, int T, int H);
-hipError_t launch_chunk_bwd_cx(const BwdArgs& a);
+size_t tok_bwd_workspace_bytes(int B, int T, int H, bool complex_data);
+hipError_t launch_tok_bwd(const BwdArgs& a, bool complex_data);
 // bf16, d = 64 or 128: the chunk form on the matrix cores (the forward's
 // factor and state passes, the adjoint scan, the chunk-parallel gradients).
 // T = 0 copies dS_final (or zeros) to dS0.

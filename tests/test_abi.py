@@ -211,12 +211,15 @@ def test_backward_empty_and_workspace_query():
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 128, 128, gdn.GDN_BF16) == \
         2 * 3 * 2 * (2 * 6400 + 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2 + 64 * 4)
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 128, 128, gdn.GDN_BF16) == 0
-    # fp32: the token-by-token kernel -- the state every 8 tokens
-    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == 2 * 3 * 17 * 64 * 64 * 4
+    # fp32: the token-by-token pass in 8 column groups -- the state every 8 tokens, and each group's share
+    # of dq, dk (64 floats each) and of dalpha, dbeta per token-head
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 64, 64, gdn.GDN_F32) == \
+        2 * 3 * 17 * 64 * 64 * 4 + 8 * (2 * 129 * 3) * (2 * 64 + 2) * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
-    # complex64 d = 32: the token-by-token kernel -- the complex state every 8 tokens
-    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 32, 32, gdn.GDN_C64) == 2 * 3 * 17 * 32 * 32 * 8
+    # complex64 d = 32: the same in 4 column groups, complex values
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 32, 32, gdn.GDN_C64) == \
+        2 * 3 * 17 * 32 * 32 * 8 + 4 * (2 * 129 * 3) * (2 * 32 * 2 + 2) * 4
 
 
 def channel(**kw):
