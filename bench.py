@@ -58,7 +58,7 @@ KERNEL_SOURCES = {
     "cx_prep_scan_out": [_CSRC + "chunk_cx.hip", _CSRC + "gdn_device.hpp"],
     "decode_kernel": [_CSRC + "decode.hip", _CSRC + "gdn_device.hpp"],
     "bwd_kernel": [_CSRC + "chunk_bwd.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
-    "bwd_cx_kernel": [_CSRC + "bwd_cx.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
+    "tok_bwd": [_CSRC + "tok_bwd.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
     "channel_chunk_kernel": [_CSRC + "channel_chunk.hip", _CSRC + "gdn_pipe.hpp", _CSRC + "gdn_device.hpp"],
     "channel_decay_c64_kernel": [_CSRC + "channel_decay.hip", _CSRC + "gdn_lane.hpp", _CSRC + "gdn_device.hpp"],
@@ -864,15 +864,13 @@ def bench_backward(args, w, dev):
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
                    "input_copies_cycled": ncopies, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": measured_traffic("bwd_kernel", w.name),
+                     "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": measured_traffic("tok_bwd", w.name),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": hbm_bytes,
                      "hbm_achieved_GBs": hbm_bytes / (avg_ms * 1e-3) / 1e9, "kernel_avg_ms": avg_ms,
-                     "kernel": "gdn::bwdcx::bwd_cx_kernel" if cx else "gdn::bwd::bwd_kernel"},
+                     "kernel": "gdn::tbwd::tok_bwd_kernel + tok_bwd_sum_kernel (one call)"},
     }
-    key = "bwd_cx_kernel" if cx else "bwd_kernel"
-    if cx:
-        result["roofline"]["traffic"] = measured_traffic(key, w.name)
+    key = "tok_bwd"
     if w.dtype == "bf16":
         # bf16 runs the chunk form on the matrix cores, four launches per call (the forward's factor and
         # state passes, the adjoint scan, the chunk-parallel gradients): priced on its HBM bytes.

@@ -1,5 +1,7 @@
 // chunk_bwd.hip -- reverse-mode gradients of the gated delta rule, real data,
-// d_k = d_v = 64 (fp32 or bf16 inputs, fp32 arithmetic and gradients).
+// d_k = d_v = 64, bf16 inputs, fp32 arithmetic and gradients: the token-loop
+// pass for the bf16 calls the chunk form does not take (T == 0, and layers
+// whose gradient rows pass 32-bit offsets).
 //
 // Per (batch, head) chain the forward is u_t = S_{t-1}^T k_t,
 // S_t = alpha_t (S_{t-1} - beta_t k_t u_t^T) + beta_t k_t v_t^T and
@@ -273,15 +275,12 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H) {
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
+  if (a.dtype != kDtBF16) return hipErrorInvalidValue;  // fp32 runs the column-group pass
   const dim3 grid((unsigned)((long)a.B * a.H)), block(bwd::NWV * 64);
-  if (a.dtype == kDtBF16)
-    return launch_kernel(bwd::bwd_kernel<__hip_bfloat16>, grid, block, (hipStream_t)a.stream,
-                         (const __hip_bfloat16*)a.q, (const __hip_bfloat16*)a.k, (const __hip_bfloat16*)a.v, a.alpha,
-                         a.beta, a.S0, (const __hip_bfloat16*)a.dout, a.dS_final, a.dq, a.dk, a.dv, a.dalpha, a.dbeta,
-                         a.dS0, (float*)a.workspace, a.T, a.H);
-  return launch_kernel(bwd::bwd_kernel<float>, grid, block, (hipStream_t)a.stream, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, a.alpha, a.beta, a.S0, (const float*)a.dout, a.dS_final,
-                       a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dS0, (float*)a.workspace, a.T, a.H);
+  return launch_kernel(bwd::bwd_kernel<__hip_bfloat16>, grid, block, (hipStream_t)a.stream,
+                       (const __hip_bfloat16*)a.q, (const __hip_bfloat16*)a.k, (const __hip_bfloat16*)a.v, a.alpha,
+                       a.beta, a.S0, (const __hip_bfloat16*)a.dout, a.dS_final, a.dq, a.dk, a.dv, a.dalpha, a.dbeta,
+                       a.dS0, (float*)a.workspace, a.T, a.H);
 }
 
 }  // namespace gdn
