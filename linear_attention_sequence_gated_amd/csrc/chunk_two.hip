@@ -944,38 +944,62 @@ __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(
 // Start states of the segments: S_(s+1) = M_s S_s + B_s for s = 0 .. G - 2,
 // with S_0 = S0 (or zero).  One workgroup per (chain, 16 value columns); the
 // sixteen columns are carried through the segments in fp32, one thread per
-// (key row, column) entry.
+// (key row, column) entry.  Each map's M block is staged in LDS with 16-byte
+// loads, the next one loaded into registers while the current one is applied.
 template <int DK>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ S0, const float* __restrict__ maps,
                                                       float* __restrict__ starts, int G, int DV) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int NF4 = DK * DK / 4 / 256;  // float4 of an M block per thread
+  constexpr int NR = DK / 16;             // rows per thread
+  __shared__ __attribute__((aligned(16))) float Ms[DK][DK + 4];
   __shared__ float cur[DK][17];
   const int nsl = DV / 16, chain = blockIdx.x / nsl, col0 = (blockIdx.x % nsl) * 16;
-  const int tid = threadIdx.x, cc = tid & 15;
+  const int tid = threadIdx.x, cc = tid & 15, r0 = tid >> 4;
   const int LD = DK + DV;
-  for (int r = tid >> 4; r < DK; r += 16) {
+  for (int r = r0; r < DK; r += 16) {
     const float s = S0 ? S0[((size_t)chain * DK + r) * DV + col0 + cc] : 0.f;
     cur[r][cc] = s;
     starts[(((size_t)chain * G) * DK + r) * DV + col0 + cc] = s;
   }
-  __syncthreads();
-  for (int s = 0; s + 1 < G; ++s) {
+  f4 m[NF4];
+  float bc[NR];
+  auto load_map = [&](int s) {
     const float* M = maps + ((size_t)chain * G + s) * DK * LD;
-    float nxt[DK / 16];
 #pragma unroll
-    for (int q = 0; q < DK / 16; ++q) {
-      const int r = (tid >> 4) + 16 * q;
-      float acc = M[(size_t)r * LD + DK + col0 + cc];  // B_s
-      for (int e = 0; e < DK; ++e) acc += M[(size_t)r * LD + e] * cur[e][cc];
-      nxt[q] = acc;
+    for (int u = 0; u < NF4; ++u) {
+      const int idx = tid + 256 * u, r = idx / (DK / 4), c4 = idx % (DK / 4);
+      m[u] = *reinterpret_cast<const f4*>(M + (size_t)r * LD + 4 * c4);
     }
-    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < DK / 16; ++q) {
-      const int r = (tid >> 4) + 16 * q;
-      cur[r][cc] = nxt[q];
-      starts[(((size_t)chain * G + s + 1) * DK + r) * DV + col0 + cc] = nxt[q];
+    for (int q = 0; q < NR; ++q) bc[q] = M[(size_t)(r0 + 16 * q) * LD + DK + col0 + cc];  // B_s
+  };
+  if (G > 1) load_map(0);
+  for (int s = 0; s + 1 < G; ++s) {
+    __syncthreads();  // cur written, and the previous block's readers done
+#pragma unroll
+    for (int u = 0; u < NF4; ++u) {
+      const int idx = tid + 256 * u, r = idx / (DK / 4), c4 = idx % (DK / 4);
+      *reinterpret_cast<f4*>(&Ms[r][4 * c4]) = m[u];
     }
+    float acc[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) acc[q] = bc[q];
     __syncthreads();
+    if (s + 2 < G) load_map(s + 1);
+#pragma unroll 8
+    for (int e = 0; e < DK; ++e) {
+      const float ce = cur[e][cc];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) acc[q] += Ms[r0 + 16 * q][e] * ce;
+    }
+    __syncthreads();  // every thread has read cur
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int r = r0 + 16 * q;
+      cur[r][cc] = acc[q];
+      starts[(((size_t)chain * G + s + 1) * DK + r) * DV + col0 + cc] = acc[q];
+    }
   }
 }
 
@@ -985,17 +1009,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Segments of the two-level scan.  With G segments a chain takes about
 // 2 nch / G chunk steps (maps of segments 0 .. G - 2 at once, then every
 // segment's output at once) instead of nch, at the cost of running the
-// segments' maps (dk more columns) once more.  That pays from G = 4 on, when
-// both launches still fit one workgroup per CU; each segment keeps at least 16
-// chunks.
+// segments' maps (dk more columns) once more, and at d = 64 of the factor
+// pass that the single-launch kernel does not need.  Every workgroup holds a
+// CU of its own (LDS), so a launch of more than 256 workgroups runs in rounds.
+// G (2 .. 16, at least 16 chunks per segment) minimises the modelled step
+// count: chunks per segment x (rounds of the map launch + rounds of the output
+// launch), plus the combine's G steps and the factor pass (about 235 chunks in
+// one step time on the whole chip); it is taken only when it saves a fifth of
+// the single-segment count.
 int chunk_two_segments(const ChunkArgs& a) {
   const long nch = (a.T + 63) / 64, chains = (long)a.B * a.H;
   const long nv = a.dk == 64 ? 32 : 16;
   const long out_sl = a.dv / nv, map_sl = (a.dk + a.dv) / nv;
+  constexpr long kCU = 256;
+  auto rounds = [](long wg) { return (wg + kCU - 1) / kCU; };
+  const long factor = a.dk == 64 ? chains * nch / 235 : 0;
+  const long base = nch * rounds(chains * out_sl);
+  long best_cost = base;
   int best = 1;
-  for (int G = 4; G <= 16; G *= 2)
-    if (chains * (G - 1) * map_sl <= 256 && chains * G * out_sl <= 256 && nch >= 16L * G) best = G;
-  return best;
+  for (int G = 2; G <= 16; ++G) {
+    const long sc = (nch + G - 1) / G;
+    if (sc < 16) break;
+    const long cost = sc * (rounds(chains * (G - 1) * map_sl) + rounds(chains * G * out_sl)) + G + factor;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = G;
+    }
+  }
+  return 5 * best_cost < 4 * base ? best : 1;
 }
 
 size_t chunk_two_workspace_bytes(const ChunkArgs& a) {

@@ -111,9 +111,10 @@ def test_chunk_bf16_d128_needs_its_workspace():
 
 def test_long_sequence_few_chains_takes_the_segmented_scan():
     # one 65536-token sequence of a 12-head d = 64 layer: 12 chains leave most CUs idle, so the call runs
-    # the two-level scan with 4 segments (factor records, segment maps [dk, dk + dv], start states)
+    # the two-level scan with 10 segments (factor records, segment maps [dk, dk + dv], start states): 103
+    # chunks per segment, the map launch in two rounds of the 256 CUs and the output launch in one
     need = gdn.gdn_chunk_fwd_workspace_bytes(1, 65536, 12, 64, 64, 64, gdn.GDN_BF16)
-    assert need == 12 * 1024 * 6400 + 12 * 4 * (64 * 128 + 64 * 64) * 4
+    assert need == 12 * 1024 * 6400 + 12 * 10 * (64 * 128 + 64 * 64) * 4
 
 
 def prologue(**kw):

@@ -87,7 +87,7 @@ def test_factor_records_match_the_chunk_form(d, B, T, H):
 # Shapes that take the segmented scan (one or two chains, long sequences) and their segment counts.
 SEGMENTED = [
     ("d128_T4100_one_chain", 1, 4100, 1, 128, 0.01),   # 65 chunks: 4 segments of 17, 17, 17, 14
-    ("d128_T8192_two_chains", 2, 8192, 1, 128, None),  # 128 chunks: 4 segments
+    ("d128_T8192_two_chains", 2, 8192, 1, 128, None),  # 128 chunks: 8 segments of 16
     ("d64_T16400_one_chain", 1, 16400, 1, 64, 0.1),    # 257 chunks: 16 segments, ragged last chunk
 ]
 
@@ -125,7 +125,7 @@ def test_segmented_scan_state_in_place():
 
 def test_long_sequence_full_size_all_chains():
     """The Sykra layer over one 65536-token sequence (12 chains of 1024 chunks), which takes the segmented scan
-    with 4 segments, in the benchmark's launch configuration; every chain against the oracle."""
+    with 10 segments, in the benchmark's launch configuration; every chain against the oracle."""
     torch = torch_dev()
     from gdn_inputs import WORKLOADS, gen_workload
     import linear_attention_sequence_gated_amd as gdn
