@@ -114,94 +114,154 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
 // the read through the conjugated key and query,
 //   e_j = v_j - sum_i conj(k_i) s_ij,   s_ij <- r_j s_ij + beta k_i e_j,
 //   o_j = sum_i conj(q_i) s_ij,
-// r real.  A lane pair holds one column: lane l owns column l / 2 and rows
-// 16 (l % 2) .. + 15, as (re, im) pairs; the column sums are 16-term in-lane
-// sums and one DPP add with the neighbouring lane.  One wave per chain.
+// r real.  The columns are independent, so each chain runs as four waves of
+// 8 columns (one 64-thread workgroup each): lane l owns column 8 g + l / 8 of
+// its group g and rows 4 (l % 8) .. + 3, as (re, im) pairs; the column sums are
+// 4-term in-lane sums and an 8-lane DPP sum.  Each wave stages its inputs in
+// LDS a block of 8 tokens ahead (k and q rows, its columns of v and r, beta),
+// so the memory latency hides behind the previous block's steps.
 constexpr int DC = 32;
+constexpr int CG = 8;    // columns per wave
+constexpr int RC = 4;    // rows per lane
+constexpr int NGC = DC / CG;
+constexpr int BT = 8;    // tokens per staged block
 
-__device__ __forceinline__ float pair_sum(float x) { return lane::dpp_add<lane::kQuadXor1>(x); }
+// Sum over the 8 consecutive lanes of a column: xor 1, xor 2 (quad_perm),
+// then the half-row mirror, which reads the xor-4 partner's value once the
+// quads agree.
+template <int ctrl> __device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  return v + dpp_mov<0x141>(v);
+}
 
-__global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float2* __restrict__ q, const float2* __restrict__ k,
-                                                               const float2* __restrict__ v, const float* __restrict__ r,
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct CxBlk {
+  float k[BT][2 * DC], q[BT][2 * DC], v[BT][2 * CG], r[BT][CG], be[BT];
+};
+
+__global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                               const float* __restrict__ v, const float* __restrict__ r,
                                                                const float* __restrict__ beta,
-                                                               const float2* __restrict__ S0, float2* __restrict__ out,
-                                                               float2* __restrict__ Sf, int T, int H) {
-  const int l = threadIdx.x, chain = blockIdx.x;
-  const int b = chain / H, h = chain % H;
-  const int c = l >> 1, i0 = R * (l & 1);
+                                                               const float* __restrict__ S0, float* __restrict__ out,
+                                                               float* __restrict__ Sf, int T, int H) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) CxBlk buf[2];
+  const int l = threadIdx.x;
+  const int grp = blockIdx.x % NGC, chain = blockIdx.x / NGC, b = chain / H, h = chain % H;
+  const int cl = l >> 3, c = grp * CG + cl, i0 = RC * (l & 7);
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
-  float sr[R], si[R];
+  float sr[RC], si[RC];
 #pragma unroll
-  for (int ii = 0; ii < R; ++ii) {
-    const float2 x = S0 ? S0[((size_t)chain * DC + i0 + ii) * DC + c] : float2{0.f, 0.f};
-    sr[ii] = x.x;
-    si[ii] = x.y;
+  for (int ii = 0; ii < RC; ++ii) {
+    const size_t e = ((size_t)chain * DC + i0 + ii) * DC + c;
+    sr[ii] = S0 ? S0[2 * e] : 0.f;
+    si[ii] = S0 ? S0[2 * e + 1] : 0.f;
   }
-  struct Tok {
-    float4 k[R / 2], q[R / 2];  // 16 complex values each, two per float4
-    float2 v;
-    float r, be;
+  // A block's inputs in registers: k and q rows (512 floats each: 2 float4 per
+  // lane), v of the group's columns (128 floats: 2 per lane), r (64: 1 per
+  // lane), beta (lanes 0 .. 7).  Tokens past T read token T - 1 (never used).
+  struct Regs {
+    f4 k[2], q[2];
+    float v[2], r, be;
   };
-  auto load = [&](int t) {
-    Tok x;
-    const size_t rt = tok(max(0, min(t, T - 1)));
+  auto load_block = [&](int blk) {
+    Regs x;
+    const int t0 = blk * BT;
 #pragma unroll
-    for (int e = 0; e < R / 2; ++e) {
-      x.k[e] = reinterpret_cast<const float4*>(k + rt * DC + i0)[e];
-      x.q[e] = reinterpret_cast<const float4*>(q + rt * DC + i0)[e];
+    for (int u = 0; u < 2; ++u) {
+      const int f = (l + 64 * u) * 4, m = f / (2 * DC), e = f % (2 * DC);
+      const size_t rt = tok(min(t0 + m, T - 1));
+      x.k[u] = *reinterpret_cast<const f4*>(k + rt * 2 * DC + e);
+      x.q[u] = *reinterpret_cast<const f4*>(q + rt * 2 * DC + e);
     }
-    x.v = v[rt * DC + c];
-    x.r = r[rt * DC + c];
-    x.be = beta[rt];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = l + 64 * u, m = f / (2 * CG), e = f % (2 * CG);
+      x.v[u] = v[tok(min(t0 + m, T - 1)) * 2 * DC + 2 * grp * CG + e];
+    }
+    {
+      const int m = l / CG, e = l % CG;
+      x.r = r[tok(min(t0 + m, T - 1)) * DC + grp * CG + e];
+    }
+    x.be = beta[tok(min(t0 + (l & 7), T - 1))];
     return x;
   };
-  auto step = [&](const Tok& x, int t) {
-    float ur = 0.f, ui = 0.f;  // sum_i conj(k_i) s_i
+  auto store_block = [&](const Regs& x, CxBlk& B) {
 #pragma unroll
-    for (int e = 0; e < R / 2; ++e) {
-      const float4 kk = x.k[e];
-      ur += kk.x * sr[2 * e] + kk.y * si[2 * e] + kk.z * sr[2 * e + 1] + kk.w * si[2 * e + 1];
-      ui += kk.x * si[2 * e] - kk.y * sr[2 * e] + kk.z * si[2 * e + 1] - kk.w * sr[2 * e + 1];
+    for (int u = 0; u < 2; ++u) {
+      const int f = (l + 64 * u) * 4, m = f / (2 * DC), e = f % (2 * DC);
+      *reinterpret_cast<f4*>(&B.k[m][e]) = x.k[u];
+      *reinterpret_cast<f4*>(&B.q[m][e]) = x.q[u];
     }
-    ur = pair_sum(ur);
-    ui = pair_sum(ui);
-    const float er = x.be * (x.v.x - ur), ei = x.be * (x.v.y - ui);  // beta e
-    float orr = 0.f, oi = 0.f;
 #pragma unroll
-    for (int e = 0; e < R / 2; ++e) {
-      const float4 kk = x.k[e], qq = x.q[e];
-      const float kr[2] = {kk.x, kk.z}, ki[2] = {kk.y, kk.w}, qr[2] = {qq.x, qq.z}, qi[2] = {qq.y, qq.w};
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int ii = 2 * e + m;
-        const float nr = x.r * sr[ii] + (kr[m] * er - ki[m] * ei);
-        const float ni = x.r * si[ii] + (kr[m] * ei + ki[m] * er);
-        sr[ii] = nr;
-        si[ii] = ni;
-        orr += qr[m] * nr + qi[m] * ni;  // conj(q) s
-        oi += qr[m] * ni - qi[m] * nr;
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int f = l + 64 * u, m = f / (2 * CG), e = f % (2 * CG);
+      B.v[m][e] = x.v[u];
     }
-    orr = pair_sum(orr);
-    oi = pair_sum(oi);
-    if ((l & 1) == 0) out[tok(t) * DC + c] = float2{orr, oi};
+    B.r[l / CG][l % CG] = x.r;
+    if (l < BT) B.be[l] = x.be;
   };
-  constexpr int PF = 2;
-  if (T > 0) {
-    Tok ring[PF];
+  const int nblk = (T + BT - 1) / BT;
+  if (nblk > 0) {
+    Regs x = load_block(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+      CxBlk& B = buf[blk & 1];
+      wave_sync();  // the block two back has been read
+      store_block(x, B);
+      wave_sync();
+      if (blk + 1 < nblk) x = load_block(blk + 1);
+      const int mend = min(BT, T - blk * BT);
 #pragma unroll
-    for (int p = 0; p < PF; ++p) ring[p] = load(p);
-    for (int t = 0; t < T; t += PF) {
+      for (int m = 0; m < BT; ++m) {
+        if (m < mend) {
+          const f4 ka = *reinterpret_cast<const f4*>(&B.k[m][2 * i0]), kb = *reinterpret_cast<const f4*>(&B.k[m][2 * i0 + 4]);
+          const f4 qa = *reinterpret_cast<const f4*>(&B.q[m][2 * i0]), qb = *reinterpret_cast<const f4*>(&B.q[m][2 * i0 + 4]);
+          const float kr[RC] = {ka.x, ka.z, kb.x, kb.z}, ki[RC] = {ka.y, ka.w, kb.y, kb.w};
+          const float qr[RC] = {qa.x, qa.z, qb.x, qb.z}, qi[RC] = {qa.y, qa.w, qb.y, qb.w};
+          const float rr = B.r[m][cl], be = B.be[m];
+          const float vr = B.v[m][2 * cl], vi = B.v[m][2 * cl + 1];
+          float ur = 0.f, ui = 0.f;  // sum_i conj(k_i) s_i
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        if (t + p < T) step(ring[p], t + p);
-        ring[p] = load(t + p + PF);
+          for (int ii = 0; ii < RC; ++ii) {
+            ur += kr[ii] * sr[ii] + ki[ii] * si[ii];
+            ui += kr[ii] * si[ii] - ki[ii] * sr[ii];
+          }
+          ur = sum8(ur);
+          ui = sum8(ui);
+          const float er = be * (vr - ur), ei = be * (vi - ui);  // beta e
+          float orr = 0.f, oi = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < RC; ++ii) {
+            const float nr = rr * sr[ii] + (kr[ii] * er - ki[ii] * ei);
+            const float ni = rr * si[ii] + (kr[ii] * ei + ki[ii] * er);
+            sr[ii] = nr;
+            si[ii] = ni;
+            orr += qr[ii] * nr + qi[ii] * ni;  // conj(q) s
+            oi += qr[ii] * ni - qi[ii] * nr;
+          }
+          orr = sum8(orr);
+          oi = sum8(oi);
+          if ((l & 7) == 0) *reinterpret_cast<float2*>(out + (tok(blk * BT + m) * DC + c) * 2) = float2{orr, oi};
+        }
       }
     }
   }
   if (Sf) {
 #pragma unroll
-    for (int ii = 0; ii < R; ++ii) Sf[((size_t)chain * DC + i0 + ii) * DC + c] = float2{sr[ii], si[ii]};
+    for (int ii = 0; ii < RC; ++ii) {
+      const size_t e = ((size_t)chain * DC + i0 + ii) * DC + c;
+      Sf[2 * e] = sr[ii];
+      Sf[2 * e + 1] = si[ii];
+    }
   }
 }
 
@@ -209,9 +269,9 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float2* __r
 
 hipError_t launch_channel_decay(const ChannelArgs& a) {
   if (a.dtype == kDtC64)
-    return launch_kernel(chd::channel_decay_c64_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(64),
-                         (hipStream_t)a.stream, (const float2*)a.q, (const float2*)a.k, (const float2*)a.v, a.r, a.beta,
-                         (const float2*)a.S0, (float2*)a.out, (float2*)a.S_final, a.T, a.H);
+    return launch_kernel(chd::channel_decay_c64_kernel, dim3((unsigned)((long)a.B * a.H * chd::NGC)), dim3(64),
+                         (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.r, a.beta,
+                         (const float*)a.S0, (float*)a.out, (float*)a.S_final, a.T, a.H);
   const dim3 grid((unsigned)((long)a.B * a.H * 4)), block(64);
   if (a.dtype == kDtBF16)
     return launch_kernel(chd::channel_decay_kernel<__hip_bfloat16>, grid, block, (hipStream_t)a.stream,
