@@ -156,7 +156,12 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
   typedef float f4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) CxBlk buf[2];
   const int l = threadIdx.x;
-  const int grp = blockIdx.x % NGC, chain = blockIdx.x / NGC, b = chain / H, h = chain % H;
+  // The hardware deals consecutive blocks to the eight XCDs in turn; remap so
+  // that a chain's groups share an XCD and its k and q rows are fetched once
+  // into that XCD's L2.
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int grp = bid % NGC, chain = bid / NGC, b = chain / H, h = chain % H;
   const int cl = l >> 3, c = grp * CG + cl, i0 = RC * (l & 7);
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
   float sr[RC], si[RC];

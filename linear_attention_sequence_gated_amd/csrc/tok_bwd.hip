@@ -135,12 +135,16 @@ __global__ __launch_bounds__(64) void tok_bwd_kernel(const float* __restrict__ q
   __shared__ __attribute__((aligned(16))) Blk<CX> buf[2];
   __shared__ __attribute__((aligned(16))) float red[2][NCW][D * W + 4];  // [product][column][row] for the row sums
   const int l = threadIdx.x;
-  const int grp = blockIdx.x % NG, chain = blockIdx.x / NG, b = chain / H, h = chain % H;
+  // A chain's groups on one XCD (the hardware deals consecutive blocks to the
+  // eight XCDs in turn), so its k and q rows are fetched once into that L2.
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int grp = bid % NG, chain = bid / NG, b = chain / H, h = chain % H;
   const int cl = l >> 3, c = grp * NCW + cl, rq = l & 7, i0 = R * rq;
   const int nsub = (T + SUB - 1) / SUB;
   const size_t ntok = (size_t)(gridDim.x / NG) * T;
   // checkpoints of this group's columns: [nsub][NCW][D]
-  float* const ck = ckpt + (size_t)blockIdx.x * nsub * NCW * D * W;
+  float* const ck = ckpt + (size_t)bid * nsub * NCW * D * W;
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
   const size_t gbase = (size_t)b * T * H + h;
   const __amdgpu_buffer_rsrc_t ra = gate_rsrc(alpha + gbase, (size_t)T * H * 4, (size_t)h * 4);
