@@ -20,16 +20,21 @@
 // earlier term is multiplied by r_u as token u passes), never as a ratio or
 // an exponential of a difference, so nothing overflows however small r is.
 //
-// One workgroup per (batch, head) chain, four waves:
-//   state wave   S [64 x 64] in matrix-core accumulators (keys in the key_row
-//                order of gdn_pipe.hpp); per sub-chunk n it applies the update
-//                of sub-chunk n - 1, then forms K_(n+1) S and Q_n S and the
-//                16 x 16 tiles G_(n+1), C_(n+1) = K_(n+1) K_n^T and P_n;
-//   solver wave  one lane per value channel: K S_n = g_15 (K_n S_(n-1)) +
-//                C_n (lambda * w)_(n-1) (the last term on the matrix cores),
-//                then the channel's forward substitution for w;
-//   output wave  one lane per channel: o of sub-chunk n - 1;
+// One workgroup per (batch, head) chain, seven waves:
+//   state waves  (two, 32 channels each) S [64 x 32] in matrix-core
+//                accumulators (keys in the key_row order of gdn_pipe.hpp); per
+//                sub-chunk n they apply the update of sub-chunk n - 1, then
+//                form K_(n+1) S and Q_n S, and between them the 16 x 16 tiles
+//                P_n (wave 0), G_(n+1) and C_(n+1) = K_(n+1) K_n^T (wave 1);
+//   solver waves (two) a lane pair per value channel: K S_n = g_15 (K_n
+//                S_(n-1)) + C_n (lambda * w)_(n-1) (the last term on the
+//                matrix cores), then the channel's forward substitution for w,
+//                the pair splitting the running sums by token parity;
+//   output waves (two) a lane pair per channel: o of sub-chunk n - 1;
 //   loader wave  K, Q, V, r and beta of sub-chunk n + 2, through LDS.
+// A wave issues one vector instruction per 4 cycles whatever its active
+// lanes, so the per-channel substitution and sums, one lane per channel in
+// one wave, were issue-bound; two lanes per channel halve each lane's share.
 // Everything a role reads in step n was written in an earlier step; one
 // barrier per step.  The solver's substitution is the chain that carries the
 // state from sub-chunk to sub-chunk; the products that need only the old
@@ -56,7 +61,8 @@ struct Lay {
   static constexpr int iK = 0, iQ = 16 * LDK * 2, iV = 2 * 16 * LDK * 2, iR = iV + 64 * LDT * 4, iB = iR + 64 * LDT * 4;
   static constexpr int szIn = iB + 16 * 4;
   // per-parity ring (bytes): Y^T = (K S)^T, QS^T [64][LDT] fp32; beta G^T [16][LDT] fp32 (column u of
-  // beta_t G_tu, t > u); P^T [16][LDT] fp32 (t >= u); C as bf16 A operands, 64 lanes x 8 bytes;
+  // beta_t G_tu, t > u); P^T [16][LDT] fp32 (t >= u) -- both with the tokens of row u in parity order,
+  // t = 2 i + h at position 8 h + i; C as bf16 A operands, 64 lanes x 8 bytes;
   // (lambda w)^T [64][LDX] bf16; w^T [64][LDT] fp32; g_15 per channel [64] fp32
   static constexpr int rY = 0, rQS = rY + 64 * LDT * 4, rG = rQS + 64 * LDT * 4, rP = rG + 16 * LDT * 4,
                        rC = rP + 16 * LDT * 4, rXL = rC + 64 * 8, rW = rXL + 64 * LDX * 2, rGE = rW + 64 * LDT * 4;
@@ -113,23 +119,27 @@ __device__ __forceinline__ void ld16(const float* p, float (&x)[SC]) {
 __device__ __forceinline__ char* in_slot(char* smem, int m) { return smem + Lay::oIn + (m & (NSLOT - 1)) * Lay::szIn; }
 __device__ __forceinline__ char* ring(char* smem, int m) { return smem + Lay::oRing + (m & 1) * Lay::szRing; }
 
-// ------------------------------------------------------------ state wave
-__device__ void state_role(const Args& a, int chain, char* smem, int l) {
+// Position of token t in a parity-ordered row of a [u][t] table.
+__device__ __forceinline__ int par_pos(int t) { return 8 * (t & 1) + (t >> 1); }
+
+// ------------------------------------------------------------ state waves
+// Wave sw owns channel tiles 2 sw and 2 sw + 1.
+__device__ void state_role(const Args& a, int chain, char* smem, int l, int sw) {
   const int g = l >> 4, c = l & 15;
-  f32x4 S[4][4];  // [dk block d][channel block T]; lane (g, c) holds keys key_row(d, g, j), channel 16T + c
+  f32x4 S[4][2];  // [dk block d][own channel tile tt]; lane (g, c) holds keys key_row(d, g, j), channel 16T + c
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        S[d][t][j] = a.S0 ? a.S0[((size_t)chain * D + key_row(d, g, j)) * D + 16 * t + c] : 0.f;
-  u32x2 sfr[4][4];
+        S[d][tt][j] = a.S0 ? a.S0[((size_t)chain * D + key_row(d, g, j)) * D + 16 * (2 * sw + tt) + c] : 0.f;
+  u32x2 sfr[4][2];
   auto to_bf16 = [&]() {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sfr[d][t] = cvt4(S[d][t]);
+      for (int tt = 0; tt < 2; ++tt) sfr[d][tt] = cvt4(S[d][tt]);
   };
   // A operand: keys 32p + 8g .. + 7 of row c of a staged [16][LDK] matrix
   auto row_piece = [&](const char* base, int p) {
@@ -143,8 +153,8 @@ __device__ void state_role(const Args& a, int chain, char* smem, int l) {
     const bool nxt = n + 1 < a.nsub;         // K_(n+1) S_n, G_(n+1), and C_(n+1) when n >= 0
     // Every LDS read of the step first (reads issued after the step's first
     // LDS write would each wait out the LDS latency).
-    u32x2 kt[4], xl[4];
-    float gs[4];
+    u32x2 kt[4], xl[2];
+    float gs[2];
     if (upd) {
       const char* Rp = ring(smem, n - 1);
       const __bf16* Kp = reinterpret_cast<const __bf16*>(in_slot(smem, n - 1) + Lay::iK);
@@ -154,9 +164,10 @@ __device__ void state_role(const Args& a, int chain, char* smem, int l) {
       for (int d = 0; d < 4; ++d)  // K^T rows in key_row order, tokens 4g .. 4g + 3
         kt[d] = ld4_tr(Kp + (4 * g + (c >> 2)) * LDK + 32 * (d / 2) + 4 * (d % 2) + 8 * (c & 3));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        xl[t] = *reinterpret_cast<const u32x2*>(XL + (16 * t + c) * LDX + 4 * g);
-        gs[t] = ge[16 * t + c];
+      for (int tt = 0; tt < 2; ++tt) {
+        const int ch = 16 * (2 * sw + tt) + c;
+        xl[tt] = *reinterpret_cast<const u32x2*>(XL + ch * LDX + 4 * g);
+        gs[tt] = ge[ch];
       }
     }
     const char* In = in_slot(smem, n);
@@ -179,125 +190,156 @@ __device__ void state_role(const Args& a, int chain, char* smem, int l) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f32x4 sv = S[d][t];
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 sv = S[d][tt];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sv[j] *= gs[t];
-          S[d][t] = mma2(kt[d], z4(), xl[t], z4(), sv);
+          for (int j = 0; j < 4; ++j) sv[j] *= gs[tt];
+          S[d][tt] = mma2(kt[d], z4(), xl[tt], z4(), sv);
         }
       to_bf16();
     }
-    // [16 tokens x 64 keys] rows (pieces a0, a1) times S, lane (g, c) of channel tile t
-    auto times_state = [&](const u32x4& a0, const u32x4& a1, int t) {
-      return mma32(a1, pair(sfr[2][t], sfr[3][t]), mma32(a0, pair(sfr[0][t], sfr[1][t]), zero4()));
+    // [16 tokens x 64 keys] rows (pieces a0, a1) times S, lane (g, c) of own channel tile tt
+    auto times_state = [&](const u32x4& a0, const u32x4& a1, int tt) {
+      return mma32(a1, pair(sfr[2][tt], sfr[3][tt]), mma32(a0, pair(sfr[0][tt], sfr[1][tt]), zero4()));
     };
-    f32x4 qs[4], y[4], P, G, C;
+    f32x4 qs[2], y[2], P, G, C;
     if (cur) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) qs[t] = times_state(q0, q1, t);
-      P = mma32(k1, q1, mma32(k0, q0, zero4()));  // lane (g, c): k_(4g+j) . q_c = P[c][4g + j]
+      for (int tt = 0; tt < 2; ++tt) qs[tt] = times_state(q0, q1, tt);
+      if (sw == 0) P = mma32(k1, q1, mma32(k0, q0, zero4()));  // lane (g, c): k_(4g+j) . q_c = P[c][4g + j]
     }
     if (nxt) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) y[t] = times_state(n0, n1, t);
-      G = mma32(n1, n1, mma32(n0, n0, zero4()));  // lane (g, c): k_(4g+j) . k_c
-      if (n >= 0) C = mma32(k1, n1, mma32(k0, n0, zero4()));  // lane (g, c): k_(n, 4g+j) . k_(n+1, c) = C[c][4g + j]
+      for (int tt = 0; tt < 2; ++tt) y[tt] = times_state(n0, n1, tt);
+      if (sw == 1) {
+        G = mma32(n1, n1, mma32(n0, n0, zero4()));  // lane (g, c): k_(4g+j) . k_c
+        if (n >= 0) C = mma32(k1, n1, mma32(k0, n0, zero4()));  // lane (g, c): k_(n, 4g+j) . k_(n+1, c) = C[c][4g + j]
+      }
     }
     // ... then the writes, all transposed to [channel][token] or [u][t]
     if (cur) {
       char* const R = ring(smem, n);
       float* QS = reinterpret_cast<float*>(R + Lay::rQS);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(QS + (16 * t + c) * LDT + 4 * g) = qs[t];
-      float* PT = reinterpret_cast<float*>(R + Lay::rP);  // P^T[u][t] = q_t . k_u for t >= u
+      for (int tt = 0; tt < 2; ++tt)
+        *reinterpret_cast<f32x4*>(QS + (16 * (2 * sw + tt) + c) * LDT + 4 * g) = qs[tt];
+      if (sw == 0) {
+        float* PT = reinterpret_cast<float*>(R + Lay::rP);  // P^T[u][t] = q_t . k_u for t >= u, t in parity order
 #pragma unroll
-      for (int j = 0; j < 4; ++j) PT[(4 * g + j) * LDT + c] = c >= 4 * g + j ? P[j] : 0.f;
+        for (int j = 0; j < 4; ++j) PT[(4 * g + j) * LDT + par_pos(c)] = c >= 4 * g + j ? P[j] : 0.f;
+      }
     }
     if (nxt) {
       char* const R1 = ring(smem, n + 1);
       float* Y = reinterpret_cast<float*>(R1 + Lay::rY);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(Y + (16 * t + c) * LDT + 4 * g) = y[t];
-      // beta G^T[u][t] = beta_t k_t . k_u for t > u
-      float* GT = reinterpret_cast<float*>(R1 + Lay::rG);
-      *reinterpret_cast<f32x4*>(GT + c * LDT + 4 * g) =
-          f32x4{4 * g + 0 > c ? bn[0] * G[0] : 0.f, 4 * g + 1 > c ? bn[1] * G[1] : 0.f,
-                4 * g + 2 > c ? bn[2] * G[2] : 0.f, 4 * g + 3 > c ? bn[3] * G[3] : 0.f};
-      if (n >= 0) *reinterpret_cast<u32x2*>(R1 + Lay::rC + 8 * l) = cvt4(C);
+      for (int tt = 0; tt < 2; ++tt)
+        *reinterpret_cast<f32x4*>(Y + (16 * (2 * sw + tt) + c) * LDT + 4 * g) = y[tt];
+      if (sw == 1) {
+        // beta G^T[u][t] = beta_t k_t . k_u for t > u (row u = c, tokens 4g + j in parity order)
+        float* GT = reinterpret_cast<float*>(R1 + Lay::rG) + c * LDT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) GT[par_pos(4 * g + j)] = 4 * g + j > c ? bn[j] * G[j] : 0.f;
+        if (n >= 0) *reinterpret_cast<u32x2*>(R1 + Lay::rC + 8 * l) = cvt4(C);
+      }
     }
   });
   if (a.Sf) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a.Sf[((size_t)chain * D + key_row(d, g, j)) * D + 16 * t + c] = S[d][t][j];
+        for (int j = 0; j < 4; ++j)
+          a.Sf[((size_t)chain * D + key_row(d, g, j)) * D + 16 * (2 * sw + tt) + c] = S[d][tt][j];
   }
 }
 
-// ----------------------------------------------------------- solver wave
-__device__ void solver_role(const Args& a, char* smem, int l) {
+// Value of the lane pair's other lane (quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float pair_other(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+}
+
+// ----------------------------------------------------------- solver waves
+// Wave sv: lanes 2 m + h hold channel 32 sv + m; lane h keeps the running sums
+// of the tokens t = 2 i + h.
+__device__ void solver_role(const Args& a, char* smem, int l, int sv) {
   float* const CX = reinterpret_cast<float*>(smem + Lay::oCX);
+  const int ch = 32 * sv + (l >> 1), h = l & 1;
   float ge_prev = 1.f;  // g_15 of the previous sub-chunk (1 before the first)
   run(a.nsub, [&](int n) {
     if (n < 0 || n >= a.nsub) return;
     const char* In = in_slot(smem, n);
     char* const R = ring(smem, n);
-    const float* Vt = reinterpret_cast<const float*>(In + Lay::iV) + l * LDT;
-    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + l * LDT;
+    const float* Vt = reinterpret_cast<const float*>(In + Lay::iV) + ch * LDT;
+    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + ch * LDT;
     const float* be = reinterpret_cast<const float*>(In + Lay::iB);
-    const float* Yt = reinterpret_cast<const float*>(R + Lay::rY) + l * LDT;
+    const float* Yt = reinterpret_cast<const float*>(R + Lay::rY) + ch * LDT;
     const int g = l >> 4, c = l & 15;
     // Every LDS read of the step first (the compiler keeps LDS reads below
     // earlier LDS writes it cannot tell apart, so reads issued late would each
     // wait out the LDS latency inside the substitution).
-    float yv[SC], rr[SC], vv[SC], bv[SC], gt[SC][SC];
+    float yv[SC], rr[SC], vv[SC], bv[SC], gt[SC][SC / 2];
     ld16(Yt, yv);
     ld16(Rt, rr);
     ld16(Vt, vv);
     ld16(be, bv);
     const float* GT = reinterpret_cast<const float*>(R + Lay::rG);
 #pragma unroll
-    for (int u = 0; u < SC - 1; ++u) ld16(GT + u * LDT, gt[u]);  // column u of beta G (uniform: broadcast reads)
+    for (int u = 0; u < SC - 1; ++u) {  // row u of beta G, this lane's parity (uniform: broadcast reads)
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(GT + u * LDT + 8 * h);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(GT + u * LDT + 8 * h + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gt[u][j] = a0[j];
+        gt[u][4 + j] = a1[j];
+      }
+    }
     float ks[SC];
-    // the cross term C_n (lambda w)_(n-1) on the matrix cores, back through LDS to one lane per channel
+    // the cross term C_n (lambda w)_(n-1) on the matrix cores (this wave's two channel tiles), back through
+    // LDS to the lane pairs
     if (n >= 1) {
       const char* Rp = ring(smem, n - 1);
       const u32x2 cA = *reinterpret_cast<const u32x2*>(R + Lay::rC + 8 * l);
       const __bf16* XL = reinterpret_cast<const __bf16*>(Rp + Lay::rXL);
-      u32x2 xl[4];
+      u32x2 xl[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xl[t] = *reinterpret_cast<const u32x2*>(XL + (16 * t + c) * LDX + 4 * g);
+      for (int tt = 0; tt < 2; ++tt)
+        xl[tt] = *reinterpret_cast<const u32x2*>(XL + (16 * (2 * sv + tt) + c) * LDX + 4 * g);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4 x = mma2(cA, z4(), xl[t], z4(), zero4());  // lane (g, c): tokens 4g + j, channel 16t + c
-        *reinterpret_cast<f32x4*>(CX + (16 * t + c) * LDT + 4 * g) = x;
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 x = mma2(cA, z4(), xl[tt], z4(), zero4());  // lane (g, c): tokens 4g + j, channel 16T + c
+        *reinterpret_cast<f32x4*>(CX + (16 * (2 * sv + tt) + c) * LDT + 4 * g) = x;
       }
       wave_sync_lds();
       float cx[SC];
-      ld16(CX + l * LDT, cx);
+      ld16(CX + ch * LDT, cx);
 #pragma unroll
       for (int t = 0; t < SC; ++t) ks[t] = ge_prev * yv[t] + cx[t];
     } else {
 #pragma unroll
       for (int t = 0; t < SC; ++t) ks[t] = yv[t];
     }
-    // w_t = beta_t (v_t - g'_t (K S)_t) - sum_{u<t} beta_t G_tu D'_tu w_u, Horner over u
-    float w[SC], acc[SC];
+    // w_t = beta_t (v_t - g'_t (K S)_t) - sum_{u<t} beta_t G_tu D'_tu w_u, Horner over u.  The sum for
+    // token t runs in lane h = t % 2 (local index t / 2); w_u comes from that lane to both.
+    float w[SC], acc[SC / 2];
 #pragma unroll
-    for (int t = 0; t < SC; ++t) acc[t] = 0.f;
+    for (int i = 0; i < SC / 2; ++i) acc[i] = 0.f;
     float gp = 1.f;  // g'_t
 #pragma unroll
     for (int u = 0; u < SC; ++u) {
-      w[u] = bv[u] * (vv[u] - gp * ks[u]) - acc[u];
+      const float mine = bv[u] * (vv[u] - gp * ks[u]) - acc[u >> 1];
+      const float other = pair_other(mine);
+      w[u] = (u & 1) == h ? mine : other;
       gp *= rr[u];
+      // tokens 2 i + h > u (the lane's entry at t = u, if any, is spent: updating it is harmless)
 #pragma unroll
-      for (int t = u + 1; t < SC; ++t) acc[t] = acc[t] * rr[u] + gt[u][t] * w[u];
+      for (int i = (u + 1) >> 1; i < SC / 2; ++i) acc[i] = acc[i] * rr[u] + gt[u][i] * w[u];
     }
-    // lambda_u = prod_{u<i<=15} r_i; (lambda w) as bf16 B operands, w for the output, g_15
-    __bf16* XLn = reinterpret_cast<__bf16*>(R + Lay::rXL) + l * LDX;
-    float* Wn = reinterpret_cast<float*>(R + Lay::rW) + l * LDT;
+    // lambda_u = prod_{u<i<=15} r_i; (lambda w) as bf16 B operands, w for the output, g_15; lane h
+    // writes tokens 8 h .. 8 h + 7
+    __bf16* XLn = reinterpret_cast<__bf16*>(R + Lay::rXL) + ch * LDX;
+    float* Wn = reinterpret_cast<float*>(R + Lay::rW) + ch * LDT;
     float lam = 1.f, xl[SC];
 #pragma unroll
     for (int u = SC - 1; u >= 0; --u) {
@@ -306,52 +348,64 @@ __device__ void solver_role(const Args& a, char* smem, int l) {
     }
 #pragma unroll
     for (int u = 0; u < SC; u += 4) {
+      if ((u >> 3) != h) continue;
       *reinterpret_cast<u32x2*>(XLn + u) = cvt4(f32x4{xl[u], xl[u + 1], xl[u + 2], xl[u + 3]});
-      Wn[u] = w[u];
-      Wn[u + 1] = w[u + 1];
-      Wn[u + 2] = w[u + 2];
-      Wn[u + 3] = w[u + 3];
+      *reinterpret_cast<f32x4*>(Wn + u) = f32x4{w[u], w[u + 1], w[u + 2], w[u + 3]};
     }
-    reinterpret_cast<float*>(R + Lay::rGE)[l] = lam;
+    if (h == 0) reinterpret_cast<float*>(R + Lay::rGE)[ch] = lam;
     ge_prev = lam;
   });
 }
 
-// ----------------------------------------------------------- output wave
-__device__ void output_role(const Args& a, int b, int h, char* smem, int l) {
+// ----------------------------------------------------------- output waves
+// Wave so: lanes 2 m + h hold channel 32 so + m and the tokens t = 2 i + h.
+__device__ void output_role(const Args& a, int b, int h_, char* smem, int l, int so) {
   const int H = a.H, T = a.T;
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(a.out + ((size_t)b * T * H + h) * D, span_bytes((size_t)T * H * D * 2, (size_t)h * D * 2));
+      make_rsrc(a.out + ((size_t)b * T * H + h_) * D, span_bytes((size_t)T * H * D * 2, (size_t)h_ * D * 2));
   const int rowO = H * D * 2;
+  const int ch = 32 * so + (l >> 1), h = l & 1;
   run(a.nsub, [&](int n) {
     const int m = n - 1;  // sub-chunk finished in this step
     if (m < 0 || m >= a.nsub) return;
     const char* In = in_slot(smem, m);
     const char* R = ring(smem, m);
-    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + l * LDT;
-    const float* QS = reinterpret_cast<const float*>(R + Lay::rQS) + l * LDT;
-    const float* W = reinterpret_cast<const float*>(R + Lay::rW) + l * LDT;
+    const float* Rt = reinterpret_cast<const float*>(In + Lay::iR) + ch * LDT;
+    const float* QS = reinterpret_cast<const float*>(R + Lay::rQS) + ch * LDT;
+    const float* W = reinterpret_cast<const float*>(R + Lay::rW) + ch * LDT;
     const float* PT = reinterpret_cast<const float*>(R + Lay::rP);
-    float rr[SC], w[SC], qs[SC], y[SC], pt[SC][SC];
+    float rr[SC], w[SC], qs[SC], y[SC / 2], pt[SC][SC / 2];
     ld16(Rt, rr);
     ld16(W, w);
     ld16(QS, qs);
 #pragma unroll
-    for (int u = 0; u < SC; ++u) ld16(PT + u * LDT, pt[u]);  // column u of P (uniform over the lanes)
+    for (int u = 0; u < SC; ++u) {  // row u of P^T, this lane's parity (uniform over the lanes of a parity)
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(PT + u * LDT + 8 * h);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(PT + u * LDT + 8 * h + 4);
 #pragma unroll
-    for (int t = 0; t < SC; ++t) y[t] = 0.f;
-    // y_t = sum_{u<=t} P_tu D_tu w_u, Horner over u
+      for (int j = 0; j < 4; ++j) {
+        pt[u][j] = a0[j];
+        pt[u][4 + j] = a1[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SC / 2; ++i) y[i] = 0.f;
+    // y_t = sum_{u<=t} P_tu D_tu w_u, Horner over u, for this lane's tokens t = 2 i + h >= u
 #pragma unroll
     for (int u = 0; u < SC; ++u)
 #pragma unroll
-      for (int t = u; t < SC; ++t) y[t] = y[t] * rr[u] + pt[u][t] * w[u];
+      for (int i = u >> 1; i < SC / 2; ++i) {
+        const float nxt = y[i] * rr[u] + pt[u][i] * w[u];
+        y[i] = (2 * i + h >= u) ? nxt : y[i];
+      }
     float gm = 1.f;
 #pragma unroll
     for (int t = 0; t < SC; ++t) {
       gm *= rr[t];
-      const float o = gm * qs[t] + y[t];
+      if ((t & 1) != h) continue;
+      const float o = gm * qs[t] + y[t >> 1];
       const unsigned short ob = __builtin_bit_cast(unsigned short, __float2bfloat16(o));
-      __builtin_amdgcn_raw_buffer_store_b16(ob, ro, 2 * l, (m * SC + t) * rowO, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(ob, ro, 2 * ch, (m * SC + t) * rowO, 0);
     }
   });
 }
@@ -442,16 +496,18 @@ __device__ void loader_role(const Args& a, int b, int h, char* smem, int l) {
   }
 }
 
-__global__ __launch_bounds__(256, 1) void channel_chunk_kernel(Args a) {
+constexpr int kThreads = 7 * 64;
+
+__global__ __launch_bounds__(kThreads, 1) void channel_chunk_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[Lay::bytes];
   const int chain = blockIdx.x, b = chain / a.H, h = chain % a.H;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  if (w == 0)
-    state_role(a, chain, smem, l);
-  else if (w == 1)
-    solver_role(a, smem, l);
-  else if (w == 2)
-    output_role(a, b, h, smem, l);
+  if (w < 2)
+    state_role(a, chain, smem, l, w);
+  else if (w < 4)
+    solver_role(a, smem, l, w - 2);
+  else if (w < 6)
+    output_role(a, b, h, smem, l, w - 4);
   else
     loader_role(a, b, h, smem, l);
 }
@@ -471,8 +527,8 @@ hipError_t launch_channel_chunk(const ChannelArgs& a) {
   x.T = a.T;
   x.H = a.H;
   x.nsub = (a.T + chc::SC - 1) / chc::SC;
-  return launch_kernel(chc::channel_chunk_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(256), (hipStream_t)a.stream,
-                       x);
+  return launch_kernel(chc::channel_chunk_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(chc::kThreads),
+                       (hipStream_t)a.stream, x);
 }
 
 }  // namespace gdn
