@@ -47,7 +47,7 @@
  *       Gradients from gdn_chunk_bwd are float32.
  *   - Every pointer must be 16-byte aligned.
  *   - Size limits (GDN_ERR_SHAPE otherwise): no tensor above 2^40 elements;
- *     B * H below 2^20 for the chunk forwards, below 2^24 for the backward
+ *     B * H below 2^20 for the chunk forwards, below 2^23 for the backward
  *     and the channel-decay forward; N below 2^24 for the decode step.  These
  *     keep every launch under 2^32 work-items.
  *   - Preconditions not checked on the device (violations give undefined,
@@ -162,7 +162,7 @@ size_t gdn_chunk_fwd_prologue_workspace_bytes(int B, int T, int H, int dk, int d
  * Supported: the shapes gdn_chunk_fwd supports (bf16 d = 64 or 128, fp32
  * d = 64, complex64 d = 32; dk == dv; chunk == 64), except bf16 shapes with a
  * batch row of q, k, v or out of 2^31 bytes or more, and bf16 d = 128 grids of
- * 2^30 chunks or more (GDN_ERR_UNSUPPORTED).
+ * 2^26 chunks (B * H * ceil(T / 64)) or more (GDN_ERR_UNSUPPORTED).
  *
  * bf16 fuses the transforms into the forward's kernels, so q, k and the
  * logits are read once, as stored, and the rows are never rewritten: 1/|k|

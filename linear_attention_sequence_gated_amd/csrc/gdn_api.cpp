@@ -54,18 +54,19 @@ gdn::ChunkArgs shape_args(int B, int T, int H, int dk, int dv, int dtype) {
 
 bool two_path(int B, int T, int H, int dk, int dv, int dtype) {
   if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128) || !rows_fit(T, H, dk)) return false;
-  if ((long long)B * H * ((T + 63) / 64) >= (1LL << 30)) return false;
+  // the factor pass runs 64 threads per chunk
+  if ((long long)B * H * ((T + 63) / 64) * 64 >= (1LL << 32)) return false;
   return dk == 128 || gdn::chunk_two_segments(shape_args(B, T, H, dk, dv, dtype)) > 1;
 }
 
 // The backward's matrix-core path: bf16, d = 64 (T > 0) or 128 (any T), rows
 // addressable with 32-bit offsets (fp32 gradient rows included) and the chunk
-// grid in range.  fp32 inputs take the token-by-token kernel (fp32
+// grid (512 threads per chunk at d = 128) in range.  fp32 inputs take the token-by-token kernel (fp32
 // throughout, d = 64).
 bool grad_path(int B, int T, int H, int dk, int dv, int dtype) {
   if (dtype != GDN_BF16 || dk != dv || (dk != 64 && dk != 128) || (dk == 64 && T <= 0)) return false;
   if ((long long)T * H * dk * 4 >= (1LL << 31)) return false;
-  return (long long)B * H * ((T + 63) / 64) < (1LL << 30);
+  return (long long)B * H * ((T + 63) / 64) * 512 < (1LL << 32);
 }
 
 // Largest element count any single tensor may have (keeps every index in range).
@@ -73,8 +74,11 @@ constexpr long long kMaxElems = 1LL << 40;
 
 // Launch limits.  A launch may hold fewer than 2^32 work-items along x.  The
 // chunk kernels run at most 4096 threads per (batch, head) chain (eight
-// 512-thread workgroups), the backward and the channel-decay kernels 256, and
-// the decode kernel at most 256 per state.  Sizes past these bounds are argument errors,
+// 512-thread workgroups), the backward and the channel-decay kernels at most
+// 512 (the fp32 token backward: eight 64-lane column groups; the bf16
+// channel-decay chunk form: 448), and the decode kernel at most 256 per state.
+// The grids that scale with the chunk count are bounded where their path is
+// chosen.  Sizes past these bounds are argument errors,
 // reported before anything is launched.
 constexpr long long kMaxWorkItems = 1LL << 32;
 bool chains_fit(long long chains, long long threads_per_chain) {
@@ -203,7 +207,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alph
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
-      !chains_fit((long long)B * H, 256))
+      !chains_fit((long long)B * H, 512))
     return GDN_ERR_SHAPE;
   const bool mfma = grad_path(B, T, H, dk, dv, dtype);
   const bool cx = dtype == GDN_C64;
@@ -240,7 +244,7 @@ int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const flo
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
-      !chains_fit((long long)B * H, 256))
+      !chains_fit((long long)B * H, 512))
     return GDN_ERR_SHAPE;
   if (dk != dv || (dtype == GDN_C64 ? dk != 32 : dk != 64)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;

@@ -21,6 +21,9 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
     int i = 0;
     ((ptrs[i++] = static_cast<void*>(&v)), ...);
   }, vals);
+  // fewer than 2^32 work-items along x: the argument checks keep every launch
+  // inside this; a grid past it is refused rather than truncated
+  if ((unsigned long long)grid.x * block.x >= (1ULL << 32)) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
 }
 

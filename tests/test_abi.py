@@ -139,6 +139,9 @@ def prologue(**kw):
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
     (dict(dtype=gdn.GDN_C64, dk=32, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(B=1, T=1 << 22, H=64), raw.GDN_ERR_UNSUPPORTED),
+    # d128 factor grid: 2^26 chunks x 64 threads reach the launch limit; one chunk fewer per chain still fits
+    (dict(B=1 << 10, T=1 << 18, H=16, dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(B=1 << 10, T=(1 << 18) - 64, H=16, dk=128, dv=128), raw.GDN_ERR_WORKSPACE),
     (dict(a_logit=None), raw.GDN_ERR_NULL),
     (dict(b_logit=None), raw.GDN_ERR_NULL),
     (dict(q=A + 8), raw.GDN_ERR_ALIGN),
@@ -180,8 +183,11 @@ def backward(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=5), raw.GDN_ERR_DTYPE),
     (dict(H=-1), raw.GDN_ERR_SHAPE),
-    (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
+    (dict(B=1 << 11, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^23 chains x 512 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),              # fp32: d = 64 only
+    # bf16 d128 gradient grid: 2^23 chunks x 512 threads reach the launch limit; one chunk fewer per chain fits
+    (dict(dtype=gdn.GDN_BF16, B=1 << 10, T=1 << 15, H=16, dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_BF16, B=1 << 10, T=(1 << 15) - 64, H=16, dk=128, dv=128), raw.GDN_ERR_WORKSPACE),
     (dict(dtype=gdn.GDN_BF16, dk=128, dv=64), raw.GDN_ERR_UNSUPPORTED),
     (dict(dk=64, dv=32), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
@@ -233,7 +239,7 @@ def channel(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), raw.GDN_ERR_DTYPE),
     (dict(B=-2), raw.GDN_ERR_SHAPE),
-    (dict(B=1 << 12, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^24 chains x 256 threads
+    (dict(B=1 << 11, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^23 chains x 512 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
