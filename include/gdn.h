@@ -47,9 +47,9 @@
  *       Gradients from gdn_chunk_bwd are float32.
  *   - Every pointer must be 16-byte aligned.
  *   - Size limits (GDN_ERR_SHAPE otherwise): no tensor above 2^40 elements;
- *     B * H below 2^20 for the chunk forwards, below 2^23 for the backward
- *     and the channel-decay forward; N below 2^24 for the decode step.  These
- *     keep every launch under 2^32 work-items.
+ *     B * H below 2^20 for the chunk forwards, below 2^23 for the backward,
+ *     below 2^22 for the channel-decay forward; N below 2^24 for the decode
+ *     step.  These keep every launch under 2^32 work-items.
  *   - Preconditions not checked on the device (violations give undefined,
  *     typically non-finite, results): 0 < alpha <= 1, 0 <= beta <= 2, finite
  *     inputs.  Inputs and outputs must not overlap, except that S_final may

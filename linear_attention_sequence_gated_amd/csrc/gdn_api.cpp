@@ -74,9 +74,10 @@ constexpr long long kMaxElems = 1LL << 40;
 
 // Launch limits.  A launch may hold fewer than 2^32 work-items along x.  The
 // chunk kernels run at most 4096 threads per (batch, head) chain (eight
-// 512-thread workgroups), the backward and the channel-decay kernels at most
-// 512 (the fp32 token backward: eight 64-lane column groups; the bf16
-// channel-decay chunk form: 448), and the decode kernel at most 256 per state.
+// 512-thread workgroups), the backward kernels at most 512 (the fp32 token
+// backward: eight 64-lane column groups), the channel-decay kernels at most
+// 1024 (the bf16 chunk form: two 448-thread workgroups), and the decode
+// kernel at most 256 per state.
 // The grids that scale with the chunk count are bounded where their path is
 // chosen.  Sizes past these bounds are argument errors,
 // reported before anything is launched.
@@ -244,7 +245,7 @@ int gdn_fwd_channel_decay(const void* q, const void* k, const void* v, const flo
   if (dtype != GDN_F32 && dtype != GDN_BF16 && dtype != GDN_C64) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
   if ((long long)B * T * H * (dk > dv ? dk : dv) > kMaxElems || (long long)B * H * dk * dv > kMaxElems ||
-      !chains_fit((long long)B * H, 512))
+      !chains_fit((long long)B * H, 1024))
     return GDN_ERR_SHAPE;
   if (dk != dv || (dtype == GDN_C64 ? dk != 32 : dk != 64)) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long long)B * T * H > 0;

@@ -239,7 +239,7 @@ def channel(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), raw.GDN_ERR_DTYPE),
     (dict(B=-2), raw.GDN_ERR_SHAPE),
-    (dict(B=1 << 11, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^23 chains x 512 threads
+    (dict(B=1 << 10, T=1, H=1 << 12), raw.GDN_ERR_SHAPE),  # 2^22 chains x 1024 threads
     (dict(dk=128, dv=128), raw.GDN_ERR_UNSUPPORTED),
     (dict(dtype=gdn.GDN_C64), raw.GDN_ERR_UNSUPPORTED),         # complex: d = 32 only
     (dict(dk=32, dv=32), raw.GDN_ERR_UNSUPPORTED),                # real: d = 64 only
