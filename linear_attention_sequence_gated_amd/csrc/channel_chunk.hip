@@ -137,6 +137,31 @@ __device__ __forceinline__ char* ring(char* smem, int m) { return smem + Lay::oR
 // Position of token t in a quad-ordered row: lane h of a quad finds its tokens
 // t = 4 i + h at 4 h + i.
 __device__ __forceinline__ int quad_pos(int t) { return 4 * (t & 3) + (t >> 2); }
+// Position of token t in a row of the triangular G and P tables: lane h finds
+// token 4 i + h at 4 h + 3 - i, so the entries a row holds for tokens at or
+// after a block (i >= i0) are the first 4 - i0 floats of the lane's piece,
+// and the lanes read only those.
+__device__ __forceinline__ int tri_pos(int t) { return 4 * (t & 3) + 3 - (t >> 2); }
+
+// dst[i] for i = I0 .. 3 from the lane's piece p of a triangular-table row
+// (dst[i] = p[3 - i]); one 16-, 12-, 8- or 4-byte read.
+template <int I0>
+__device__ __forceinline__ void ld_tri(const float* p, float (&dst)[4]) {
+  typedef float f32x3 __attribute__((ext_vector_type(3)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (I0 == 0) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    dst[3] = x[0], dst[2] = x[1], dst[1] = x[2], dst[0] = x[3];
+  } else if constexpr (I0 == 1) {
+    const f32x3 x = *reinterpret_cast<const f32x3*>(p);
+    dst[3] = x[0], dst[2] = x[1], dst[1] = x[2];
+  } else if constexpr (I0 == 2) {
+    const f32x2 x = *reinterpret_cast<const f32x2*>(p);
+    dst[3] = x[0], dst[2] = x[1];
+  } else {
+    dst[3] = p[0];
+  }
+}
 
 // ------------------------------------------------------------ state waves
 // Wave sw owns channel tile sw of the slice (channels dv0 + 16 sw .. + 15).
@@ -220,7 +245,7 @@ __device__ void state_role(const Args& a, int chain, int dv0, char* smem, int l,
       }
     }
     // ... then the writes, all transposed to [channel][token] or [u][t], tokens in quad order
-    // (token 4g + j at position 4j + g)
+    // (token 4g + j at position 4j + g) or, in the G and P tables, triangular order
     if (cur) {
       char* const R = ring(smem, n);
       float* QS = reinterpret_cast<float*>(R + Lay::rQS) + chs * LDT;
@@ -229,7 +254,7 @@ __device__ void state_role(const Args& a, int chain, int dv0, char* smem, int l,
       if (sw == 0) {
         float* PT = reinterpret_cast<float*>(R + Lay::rP);  // P^T[u][t] = q_t . k_u for t >= u
 #pragma unroll
-        for (int j = 0; j < 4; ++j) PT[(4 * g + j) * LDT + quad_pos(c)] = c >= 4 * g + j ? P[j] : 0.f;
+        for (int j = 0; j < 4; ++j) PT[(4 * g + j) * LDT + tri_pos(c)] = c >= 4 * g + j ? P[j] : 0.f;
       }
     }
     if (nxt) {
@@ -241,7 +266,7 @@ __device__ void state_role(const Args& a, int chain, int dv0, char* smem, int l,
         // beta G^T[u][t] = beta_t k_t . k_u for t > u (row u = c, tokens 4g + j)
         float* GT = reinterpret_cast<float*>(R1 + Lay::rG) + c * LDT;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) GT[4 * j + g] = 4 * g + j > c ? bn[j] * G[j] : 0.f;
+        for (int j = 0; j < 4; ++j) GT[tri_pos(4 * g + j)] = 4 * g + j > c ? bn[j] * G[j] : 0.f;
         if (n >= 0) *reinterpret_cast<u32x2*>(R1 + Lay::rC + 8 * l) = cvt4(C);
       }
     }
@@ -292,13 +317,12 @@ __device__ void solver_role(const Args& a, char* smem, int l, int sv) {
     const f32x4 yv = ld4f(reinterpret_cast<const float*>(R + Lay::rY) + ch * LDT + 4 * h);
     const f32x4 vv = ld4f(reinterpret_cast<const float*>(In + Lay::iV) + ch * LDT + 4 * h);
     const f32x4 bv = ld4f(reinterpret_cast<const float*>(In + Lay::iBq) + 4 * h);
-    const float* GT = reinterpret_cast<const float*>(R + Lay::rG);
-#pragma unroll
-    for (int u = 0; u < SC - 1; ++u) {  // row u of beta G, this lane's tokens (uniform over a quad position)
-      const f32x4 r4 = ld4f(GT + u * LDT + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gt[u][j] = r4[j];
-    }
+    const float* GT = reinterpret_cast<const float*>(R + Lay::rG) + 4 * h;
+    // row u of beta G, this lane's tokens after u (uniform over a quad position)
+    unroll16<0>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < SC - 1) ld_tri<((u + 1) >> 2)>(GT + u * LDT, gt[u]);
+    });
     f32x4 ks;
     // the cross term C_n (lambda w)_(n-1) on the matrix cores (this wave's channel tile), back through LDS
     // to the lane quads
@@ -372,12 +396,11 @@ __device__ void output_role(const Args& a, int b, int h_, int dv0, char* smem, i
     ld16(reinterpret_cast<const float*>(In + Lay::iR) + ch * LDT, rr);
     ld16(reinterpret_cast<const float*>(R + Lay::rW) + ch * LDT, w);
     const f32x4 qs = ld4f(reinterpret_cast<const float*>(R + Lay::rQS) + ch * LDT + 4 * h);
-#pragma unroll
-    for (int u = 0; u < SC; ++u) {  // row u of P^T, this lane's tokens (uniform over a quad position)
-      const f32x4 r4 = ld4f(PT + u * LDT + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pt[u][j] = r4[j];
-    }
+    // row u of P^T, this lane's tokens from u's block on (uniform over a quad position)
+    unroll16<0>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      ld_tri<(u >> 2)>(PT + 4 * h + u * LDT, pt[u]);
+    });
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = 0.f;
     // y_t = sum_{u<=t} P_tu D_tu w_u, Horner over u, for this lane's tokens t = 4 i + h >= u: every token of
