@@ -21,10 +21,10 @@
 // an exponential of a difference, so nothing overflows however small r is.
 //
 // The value channels are independent, so each (batch, head) chain runs as
-// two workgroups of 32 channels (192 workgroups for 96 chains: the chip's
-// CUs, not one chain's serial chain, would otherwise sit idle), the two kept
-// on one XCD so that the K and Q rows they both read are fetched once into its
-// L2.  Seven waves per workgroup:
+// two workgroups of 32 channels: with one workgroup per chain, 96 chains would
+// leave most of the 256 CUs idle.  The two are kept on one XCD so that the K
+// and Q rows they both read are fetched once into its L2.  Seven waves per
+// workgroup:
 //   state waves  (two, 16 channels each) S [64 x 16] in matrix-core
 //                accumulators (keys in the key_row order of gdn_pipe.hpp); per
 //                sub-chunk n they apply the update of sub-chunk n - 1, then
@@ -43,7 +43,9 @@
 // one wave, were issue-bound; four lanes per channel split each lane's share.
 // Tables read by a quad's own tokens are stored with each row's tokens in
 // "quad order" (token t at position 4 (t mod 4) + t / 4), so a lane reads its
-// four with one 16-byte load.
+// four with one 16-byte load; the triangular G and P tables put a lane's four
+// in reverse, so that the entries at or below the diagonal, the only ones a
+// row's readers use, are a prefix of the lane's 16 bytes (tri_pos).
 // Everything a role reads in step n was written in an earlier step; one
 // barrier per step.  The solver's substitution is the chain that carries the
 // state from sub-chunk to sub-chunk; the products that need only the old
@@ -75,8 +77,8 @@ struct Lay {
   static constexpr int szIn = iBq + 16 * 4;
   // per-parity ring (bytes): Y^T = (K S)^T, QS^T [NCH][LDT] fp32 (quad order); beta G^T [16][LDT] fp32
   // (column u of beta_t G_tu, t > u); P^T [16][LDT] fp32 (t >= u) -- both with the tokens of row u in
-  // quad order; C as bf16 A operands, 64 lanes x 8 bytes; (lambda w)^T [NCH][LDX] bf16; w^T [NCH][LDT]
-  // fp32; g_15 per channel [NCH] fp32
+  // triangular order (tri_pos); C as bf16 A operands, 64 lanes x 8 bytes; (lambda w)^T [NCH][LDX] bf16;
+  // w^T [NCH][LDT] fp32 (token order); g_15 per channel [NCH] fp32
   static constexpr int rY = 0, rQS = rY + NCH * LDT * 4, rG = rQS + NCH * LDT * 4, rP = rG + 16 * LDT * 4,
                        rC = rP + 16 * LDT * 4, rXL = rC + 64 * 8, rW = rXL + NCH * LDX * 2, rGE = rW + NCH * LDT * 4;
   static constexpr int szRing = rGE + NCH * 4;
