@@ -114,28 +114,35 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
 // the read through the conjugated key and query,
 //   e_j = v_j - sum_i conj(k_i) s_ij,   s_ij <- r_j s_ij + beta k_i e_j,
 //   o_j = sum_i conj(q_i) s_ij,
-// r real.  The columns are independent, so each chain runs as four waves of
-// 8 columns (one 64-thread workgroup each): lane l owns column 8 g + l / 8 of
-// its group g and rows 4 (l % 8) .. + 3, as (re, im) pairs; the column sums are
-// 4-term in-lane sums and an 8-lane DPP sum.  Each wave stages its inputs in
-// LDS a block of 8 tokens ahead (k and q rows, its columns of v and r, beta),
-// so the memory latency hides behind the previous block's steps.
+// r real.  The columns are independent, so each chain runs as eight waves of
+// 4 columns (one 64-thread workgroup each): lane l owns column 4 g + l / 16 of
+// its group g and rows 2 (l % 16) .. + 1, as (re, im) pairs; the column sums
+// are 2-term in-lane sums and a 16-lane DPP sum.  (A wave issues one vector
+// instruction per 4 cycles, so a token step costs about the instructions of
+// one lane: with 4 rows per lane, four waves per chain, it took twice as long.)
+// Each wave stages its inputs in LDS a block of 8 tokens ahead (k and q rows,
+// its columns of v and r, beta), so the memory latency hides behind the
+// previous block's steps.
 constexpr int DC = 32;
-constexpr int CG = 8;    // columns per wave
-constexpr int RC = 4;    // rows per lane
+constexpr int CG = 4;    // columns per wave
+constexpr int RC = 2;    // rows per lane
+constexpr int LPC = DC / RC;  // lanes per column
 constexpr int NGC = DC / CG;
 constexpr int BT = 8;    // tokens per staged block
+static_assert(LPC * CG == 64, "one column per 16-lane row");
 
-// Sum over the 8 consecutive lanes of a column: xor 1, xor 2 (quad_perm),
-// then the half-row mirror, which reads the xor-4 partner's value once the
-// quads agree.
+// Sum over the 16 lanes of a column (one DPP row): xor 1, xor 2 (quad_perm),
+// then the half-row mirror and the row mirror, each of which reads a partner
+// whose partial sum covers the other half once the smaller groups agree.
+// Every lane of the row ends with the same value.
 template <int ctrl> __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true));
 }
-__device__ __forceinline__ float sum8(float v) {
+__device__ __forceinline__ float sum16(float v) {
   v += dpp_mov<0xB1>(v);
   v += dpp_mov<0x4E>(v);
-  return v + dpp_mov<0x141>(v);
+  v += dpp_mov<0x141>(v);
+  return v + dpp_mov<0x140>(v);
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
   const int grp = bid % NGC, chain = bid / NGC, b = chain / H, h = chain % H;
-  const int cl = l >> 3, c = grp * CG + cl, i0 = RC * (l & 7);
+  const int cl = l / LPC, c = grp * CG + cl, i0 = RC * (l % LPC);
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
   float sr[RC], si[RC];
 #pragma unroll
@@ -172,11 +179,11 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
     si[ii] = S0 ? S0[2 * e + 1] : 0.f;
   }
   // A block's inputs in registers: k and q rows (512 floats each: 2 float4 per
-  // lane), v of the group's columns (128 floats: 2 per lane), r (64: 1 per
-  // lane), beta (lanes 0 .. 7).  Tokens past T read token T - 1 (never used).
+  // lane), v of the group's columns (64 floats: 1 per lane), r (32: lanes 0 ..
+  // 31), beta (lanes 0 .. 7).  Tokens past T read token T - 1 (never used).
   struct Regs {
     f4 k[2], q[2];
-    float v[2], r, be;
+    float v, r, be;
   };
   auto load_block = [&](int blk) {
     Regs x;
@@ -188,13 +195,12 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
       x.k[u] = *reinterpret_cast<const f4*>(k + rt * 2 * DC + e);
       x.q[u] = *reinterpret_cast<const f4*>(q + rt * 2 * DC + e);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int f = l + 64 * u, m = f / (2 * CG), e = f % (2 * CG);
-      x.v[u] = v[tok(min(t0 + m, T - 1)) * 2 * DC + 2 * grp * CG + e];
+    {
+      const int m = l / (2 * CG), e = l % (2 * CG);
+      x.v = v[tok(min(t0 + m, T - 1)) * 2 * DC + 2 * grp * CG + e];
     }
     {
-      const int m = l / CG, e = l % CG;
+      const int m = (l & 31) / CG, e = l % CG;
       x.r = r[tok(min(t0 + m, T - 1)) * DC + grp * CG + e];
     }
     x.be = beta[tok(min(t0 + (l & 7), T - 1))];
@@ -207,12 +213,8 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
       *reinterpret_cast<f4*>(&B.k[m][e]) = x.k[u];
       *reinterpret_cast<f4*>(&B.q[m][e]) = x.q[u];
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int f = l + 64 * u, m = f / (2 * CG), e = f % (2 * CG);
-      B.v[m][e] = x.v[u];
-    }
-    B.r[l / CG][l % CG] = x.r;
+    B.v[l / (2 * CG)][l % (2 * CG)] = x.v;
+    if (l < BT * CG) B.r[l / CG][l % CG] = x.r;
     if (l < BT) B.be[l] = x.be;
   };
   const int nblk = (T + BT - 1) / BT;
@@ -224,39 +226,47 @@ __global__ __launch_bounds__(64) void channel_decay_c64_kernel(const float* __re
       store_block(x, B);
       wave_sync();
       if (blk + 1 < nblk) x = load_block(blk + 1);
-      const int mend = min(BT, T - blk * BT);
+      // One token of the block.  Every lane of a column's 16 ends with the same sums (sum16), so all of
+      // them store them: no per-lane branch splits the unrolled block, and the compiler can issue a token's
+      // LDS reads during the previous token's arithmetic.
+      auto token = [&](int m) {
+        const f4 ka = *reinterpret_cast<const f4*>(&B.k[m][2 * i0]);
+        const f4 qa = *reinterpret_cast<const f4*>(&B.q[m][2 * i0]);
+        const float kr[RC] = {ka.x, ka.z}, ki[RC] = {ka.y, ka.w};
+        const float qr[RC] = {qa.x, qa.z}, qi[RC] = {qa.y, qa.w};
+        const float rr = B.r[m][cl], be = B.be[m];
+        const float vr = B.v[m][2 * cl], vi = B.v[m][2 * cl + 1];
+        float ur = 0.f, ui = 0.f;  // sum_i conj(k_i) s_i
 #pragma unroll
-      for (int m = 0; m < BT; ++m) {
-        if (m < mend) {
-          const f4 ka = *reinterpret_cast<const f4*>(&B.k[m][2 * i0]), kb = *reinterpret_cast<const f4*>(&B.k[m][2 * i0 + 4]);
-          const f4 qa = *reinterpret_cast<const f4*>(&B.q[m][2 * i0]), qb = *reinterpret_cast<const f4*>(&B.q[m][2 * i0 + 4]);
-          const float kr[RC] = {ka.x, ka.z, kb.x, kb.z}, ki[RC] = {ka.y, ka.w, kb.y, kb.w};
-          const float qr[RC] = {qa.x, qa.z, qb.x, qb.z}, qi[RC] = {qa.y, qa.w, qb.y, qb.w};
-          const float rr = B.r[m][cl], be = B.be[m];
-          const float vr = B.v[m][2 * cl], vi = B.v[m][2 * cl + 1];
-          float ur = 0.f, ui = 0.f;  // sum_i conj(k_i) s_i
-#pragma unroll
-          for (int ii = 0; ii < RC; ++ii) {
-            ur += kr[ii] * sr[ii] + ki[ii] * si[ii];
-            ui += kr[ii] * si[ii] - ki[ii] * sr[ii];
-          }
-          ur = sum8(ur);
-          ui = sum8(ui);
-          const float er = be * (vr - ur), ei = be * (vi - ui);  // beta e
-          float orr = 0.f, oi = 0.f;
-#pragma unroll
-          for (int ii = 0; ii < RC; ++ii) {
-            const float nr = rr * sr[ii] + (kr[ii] * er - ki[ii] * ei);
-            const float ni = rr * si[ii] + (kr[ii] * ei + ki[ii] * er);
-            sr[ii] = nr;
-            si[ii] = ni;
-            orr += qr[ii] * nr + qi[ii] * ni;  // conj(q) s
-            oi += qr[ii] * ni - qi[ii] * nr;
-          }
-          orr = sum8(orr);
-          oi = sum8(oi);
-          if ((l & 7) == 0) *reinterpret_cast<float2*>(out + (tok(blk * BT + m) * DC + c) * 2) = float2{orr, oi};
+        for (int ii = 0; ii < RC; ++ii) {
+          ur += kr[ii] * sr[ii] + ki[ii] * si[ii];
+          ui += kr[ii] * si[ii] - ki[ii] * sr[ii];
         }
+        ur = sum16(ur);
+        ui = sum16(ui);
+        const float er = be * (vr - ur), ei = be * (vi - ui);  // beta e
+        float orr = 0.f, oi = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < RC; ++ii) {
+          const float nr = rr * sr[ii] + (kr[ii] * er - ki[ii] * ei);
+          const float ni = rr * si[ii] + (kr[ii] * ei + ki[ii] * er);
+          sr[ii] = nr;
+          si[ii] = ni;
+          orr += qr[ii] * nr + qi[ii] * ni;  // conj(q) s
+          oi += qr[ii] * ni - qi[ii] * nr;
+        }
+        orr = sum16(orr);
+        oi = sum16(oi);
+        *reinterpret_cast<float2*>(out + (tok(blk * BT + m) * DC + c) * 2) = float2{orr, oi};
+      };
+      if ((blk + 1) * BT <= T) {
+#pragma unroll
+        for (int m = 0; m < BT; ++m) token(m);
+      } else {  // the ragged last block
+        const int mend = T - blk * BT;
+#pragma unroll
+        for (int m = 0; m < BT; ++m)
+          if (m < mend) token(m);
       }
     }
   }
