@@ -185,9 +185,9 @@ int gdn_chunk_fwd_prologue(const void *q, const void *k, const void *v, const fl
  * segment maps when it splits long sequences (as gdn_chunk_fwd_workspace_bytes
  * reports them).  fp32 (d = 64) and complex64 (d = 32): the forward state
  * every 8 tokens, B * H * ceil(T / 8) * d * d * e bytes (e = 4 or 8), plus the
- * shares of dq, dk, dalpha and dbeta from each of the d / 8 column groups,
- * (d / 8) * B * T * H * (2 * d * e + 8) bytes.  0 for an unsupported
- * combination.
+ * shares of dq, dk, dalpha and dbeta from each of the n column groups (n = 8:
+ * d / 8 for fp32, d / 4 for complex64), n * B * T * H * (2 * d * e + 8) bytes.
+ * 0 for an unsupported combination.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
 

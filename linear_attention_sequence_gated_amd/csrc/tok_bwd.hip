@@ -18,11 +18,15 @@
 //
 // The columns of S (value channels) evolve independently, in the forward and
 // in this reverse pass: only dq, dk, dalpha and dbeta sum over them, and they
-// are linear in those sums.  So each chain is split into D / 8 groups of 8
-// columns, one wave each (no workgroup barrier on the token chain).  Lane l
-// owns column 8 g + l / 8 of its group g and rows R (l % 8) .. + R - 1
-// (R = D / 8); column sums are 8-lane DPP sums, the row sums over the wave's
-// columns go through an LDS transpose within the wave.  Each wave writes its
+// are linear in those sums.  So each chain is split into groups of NCW
+// columns (8 for fp32, 4 for complex64), one wave each (no workgroup barrier
+// on the token chain).  Lane l owns column NCW g + l / L of its group g and
+// rows R (l % L) .. + R - 1 (L = 64 / NCW lanes per column, R = D / L);
+// column sums are L-lane DPP sums, the row sums over the wave's columns go
+// through an LDS transpose within the wave.  A wave issues one vector
+// instruction per 4 cycles, so a token step costs about one lane's
+// instructions: the complex chain runs as eight waves of 4 columns (2 rows
+// per lane), not four of 8.  Each wave writes its
 // group's share of dq, dk, dalpha and dbeta to the workspace, and a second
 // launch adds the groups' shares.  S_{t-1} is needed in reverse order: a first
 // pass runs the forward and checkpoints the group's columns every 8 tokens; the
@@ -39,7 +43,6 @@ namespace gdn {
 namespace tbwd {
 
 constexpr int SUB = 8;  // tokens per checkpoint block
-constexpr int NCW = 8;  // columns per wave
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // Real and complex scalars with the same operations (conj is the identity for real).
@@ -62,19 +65,23 @@ __device__ __forceinline__ cf mul(cf a, cf b) { return {a.x * b.x - a.y * b.y, a
 __device__ __forceinline__ cf mulc(cf a, cf b) { return {a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y}; }
 __device__ __forceinline__ float dotr(cf a, cf b) { return a.x * b.x + a.y * b.y; }
 
-// Sum over the 8 consecutive lanes of a column (xor 1, xor 2 by quad_perm,
-// then the half-row mirror, which reads the xor-4 partner's value once the
-// quads agree).
+// Sum over the L consecutive lanes of a column, L = 8 or 16: xor 1, xor 2 by
+// quad_perm, then the half-row mirror (and for 16 lanes the row mirror), each
+// reading a partner whose partial sum covers the other half once the smaller
+// groups agree; every lane of the column ends with the same value.
 template <int ctrl> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true));
 }
-__device__ __forceinline__ float sum8(float v) {
+template <int L> __device__ __forceinline__ float colsum(float v) {
+  static_assert(L == 8 || L == 16, "column width");
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
-  return v + dpp<0x141>(v);
+  v += dpp<0x141>(v);
+  if constexpr (L == 16) v += dpp<0x140>(v);
+  return v;
 }
-__device__ __forceinline__ rf sum8(rf a) { return {sum8(a.x)}; }
-__device__ __forceinline__ cf sum8(cf a) { return {sum8(a.x), sum8(a.y)}; }
+template <int L> __device__ __forceinline__ rf colsum(rf a) { return {colsum<L>(a.x)}; }
+template <int L> __device__ __forceinline__ cf colsum(cf a) { return {colsum<L>(a.x), colsum<L>(a.y)}; }
 __device__ __forceinline__ rf wsum(rf a) { return {lane::wave_sum(a.x)}; }
 __device__ __forceinline__ cf wsum(cf a) { return {lane::wave_sum(a.x), lane::wave_sum(a.y)}; }
 
@@ -88,7 +95,9 @@ __device__ __forceinline__ void wave_sync() {
 template <bool CX> struct Cfg {
   using S = typename std::conditional<CX, cf, rf>::type;
   static constexpr int D = CX ? 32 : 64;  // head dimension (d_k = d_v)
-  static constexpr int R = D / 8;         // rows per lane
+  static constexpr int NCW = CX ? 4 : 8;  // columns per wave
+  static constexpr int L = 64 / NCW;      // lanes per column
+  static constexpr int R = D / L;         // rows per lane
   static constexpr int NG = D / NCW;      // column groups (waves) per chain
   static constexpr int W = CX ? 2 : 1;    // floats per element
   static constexpr int P = 2 * D;         // partial elements per token: dq, dk
@@ -113,7 +122,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const float* base, s
 // One 8-token block of inputs staged in LDS: k and q rows, this group's
 // columns of v and dO, the gates.
 template <bool CX> struct Blk {
-  static constexpr int D = Cfg<CX>::D, W = Cfg<CX>::W;
+  static constexpr int D = Cfg<CX>::D, W = Cfg<CX>::W, NCW = Cfg<CX>::NCW;
   float k[SUB][D * W], q[SUB][D * W], v[SUB][NCW * W], dO[SUB][NCW * W], a[SUB], be[SUB];
 };
 
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(64) void tok_bwd_kernel(const float* __restrict__ q
                                                      float* __restrict__ ckpt, int T, int H) {
   using C = Cfg<CX>;
   using S = typename C::S;
-  constexpr int D = C::D, R = C::R, NG = C::NG, W = C::W;
+  constexpr int D = C::D, R = C::R, NG = C::NG, W = C::W, NCW = C::NCW, L = C::L;
   constexpr int KPL = SUB * D * W / 4 / 64;  // float4 of a k (or q) block per lane: 2
   constexpr int VPL = SUB * NCW * W / 64;    // floats of a v (or dO) block per lane: 1 or 2
   static_assert(KPL * 256 == SUB * D * W && VPL * 64 == SUB * NCW * W, "block shapes");
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(64) void tok_bwd_kernel(const float* __restrict__ q
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
   const int grp = bid % NG, chain = bid / NG, b = chain / H, h = chain % H;
-  const int cl = l >> 3, c = grp * NCW + cl, rq = l & 7, i0 = R * rq;
+  const int cl = l / L, c = grp * NCW + cl, rq = l % L, i0 = R * rq;
   const int nsub = (T + SUB - 1) / SUB;
   const size_t ntok = (size_t)(gridDim.x / NG) * T;
   // checkpoints of this group's columns: [nsub][NCW][D]
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(64) void tok_bwd_kernel(const float* __restrict__ q
     S u{};
 #pragma unroll
     for (int ii = 0; ii < R; ++ii) u = u + mulc(s[ii], kk[ii]);
-    u = sum8(u);
+    u = colsum<L>(u);
     const S y = be * ld<CX>(&B.v[m][cl * W]) - (a * be) * u;
 #pragma unroll
     for (int ii = 0; ii < R; ++ii) s[ii] = a * s[ii] + mul(kk[ii], y);
@@ -283,8 +292,8 @@ __global__ __launch_bounds__(64) void tok_bwd_kernel(const float* __restrict__ q
             wc = wc + mulc(g[ii], kk[ii]);
             dsp += dotr(g[ii], sp[m][ii]);
           }
-          u = sum8(u);
-          wc = sum8(wc);
+          u = colsum<L>(u);
+          wc = colsum<L>(wc);
           const S y = be * vc - ab * u;
           if (rq == 0) stv(dv + (r * D + c) * W, be * wc);
           const float lead = rq == 0 ? 1.f : 0.f;  // one copy of each per-column term
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(256) void tok_bwd_sum_kernel(const float* __restric
 template <bool CX> static size_t tok_bwd_bytes(int B, int T, int H, size_t* ck_bytes) {
   using C = tbwd::Cfg<CX>;
   const size_t chains = (size_t)B * H, nsub = (T + tbwd::SUB - 1) / tbwd::SUB;
-  const size_t ck = chains * C::NG * nsub * tbwd::NCW * C::D * C::W * 4;
+  const size_t ck = chains * C::NG * nsub * C::NCW * C::D * C::W * 4;
   const size_t ntok = (size_t)B * T * H;
   if (ck_bytes) *ck_bytes = ck;
   return ck + C::NG * ntok * (C::P * C::W + 2) * 4;

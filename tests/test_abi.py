@@ -224,9 +224,9 @@ def test_backward_empty_and_workspace_query():
         2 * 3 * 17 * 64 * 64 * 4 + 8 * (2 * 129 * 3) * (2 * 64 + 2) * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 0, 3, 64, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 128, 3, 64, 64, gdn.GDN_C64) == 0
-    # complex64 d = 32: the same in 4 column groups, complex values
+    # complex64 d = 32: the same in 8 column groups of 4 columns, complex values
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 129, 3, 32, 32, gdn.GDN_C64) == \
-        2 * 3 * 17 * 32 * 32 * 8 + 4 * (2 * 129 * 3) * (2 * 32 * 2 + 2) * 4
+        2 * 3 * 17 * 32 * 32 * 8 + 8 * (2 * 129 * 3) * (2 * 32 * 2 + 2) * 4
 
 
 def channel(**kw):
