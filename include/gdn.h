@@ -228,9 +228,9 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int dt
  * gradient carried from the last chunk to the first, then every chunk's
  * gradients at once), with bf16 operands and fp32 accumulation, like the
  * forward.  fp32 and complex64 inputs take a token-by-token reverse pass in
- * fp32 throughout (checkpoints every 8 tokens), split by groups of 8 state
- * columns (the columns evolve independently; a second launch adds the
- * groups' shares of dq, dk, dalpha and dbeta).  The forward is recomputed inside the call, so
+ * fp32 throughout (checkpoints every 8 tokens), split by groups of state
+ * columns, 8 for fp32 and 4 for complex64 (the columns evolve independently;
+ * a second launch adds the groups' shares of dq, dk, dalpha and dbeta).  The forward is recomputed inside the call, so
  * nothing from a forward call is needed.  Gradient outputs must not alias any
  * input.  alpha must be positive (the chunk form works with log alpha).
  * B * H == 0 is a no-op; T == 0 copies grad_S_final (or zeros) to grad_S0.

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64) void channel_decay_kernel(const IT* __restrict_
 // its group g and rows 2 (l % 16) .. + 1, as (re, im) pairs; the column sums
 // are 2-term in-lane sums and a 16-lane DPP sum.  (A wave issues one vector
 // instruction per 4 cycles, so a token step costs about the instructions of
-// one lane: with 4 rows per lane, four waves per chain, it took twice as long.)
+// one lane: with 4 rows per lane, four waves per chain, it took a third longer.)
 // Each wave stages its inputs in LDS a block of 8 tokens ahead (k and q rows,
 // its columns of v and r, beta), so the memory latency hides behind the
 // previous block's steps.
