@@ -125,8 +125,8 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *alph
  * Bytes of device workspace gdn_chunk_fwd_prologue needs for these sizes (0:
  * workspace may be NULL; 0 also for unsupported arguments).  bf16: 0 where
  * gdn_chunk_fwd needs no workspace; otherwise (the two-launch path) what
- * gdn_chunk_fwd needs plus B * H * ceil(T / 64) * 512 bytes, the inverse key
- * and query norms handed from the first launch to the second.  GDN_F32 and GDN_C64: the
+ * gdn_chunk_fwd needs plus B * H * ceil(T / 64) * 256 bytes, the inverse key
+ * norms handed from the first launch to the second.  GDN_F32 and GDN_C64: the
  * transformed q and k (B * T * H rows of 256 bytes each) and the two gates
  * (B * T * H floats each), each rounded up to 256 bytes, plus, for GDN_C64,
  * what gdn_chunk_fwd needs.  Ownership and sharing as for gdn_chunk_fwd.

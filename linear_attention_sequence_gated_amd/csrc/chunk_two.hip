@@ -105,16 +105,16 @@ struct FactorCfg {
 
 // PRO: the layer's input transforms are fused in.  k and q are raw: the
 // inverse row norms r = 1 / max(|k|, 1e-12) scale the Gram tiles (K^ K^^T =
-// diag(r) K K^T diag(r) for the normalised keys K^), and r and the queries'
-// p = 1 / max(|q|, 1e-12) go to rpw[chunk][2][64] for the state pass, which
-// folds them into its gates; alpha and beta hold the logits a and b,
+// diag(r) K K^T diag(r) for the normalised keys K^), and r goes to
+// rpw[chunk][64] for the state pass, which folds it into its gates (the
+// queries' norms are taken by the state pass's output wave, from the rows it
+// reads anyway); alpha and beta hold the logits a and b,
 // alpha = exp(-softplus(a)), beta = bscale * sigmoid(b).
 template <int DK, bool PRO>
 __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ kg, const float* __restrict__ alpha,
                                                     const float* __restrict__ beta, char* __restrict__ ws,
                                                     char* __restrict__ wsT, int T, int H, int nch, int total,
-                                                    float bscale, const __bf16* __restrict__ qg,
-                                                    float* __restrict__ rpw) {
+                                                    float bscale, float* __restrict__ rpw) {
   using Cf = FactorCfg<DK>;
   constexpr int NKP = Cf::NKP;
   __shared__ __attribute__((aligned(16))) float W[Cf::szW];
@@ -143,29 +143,20 @@ __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ k
   const bool live = t0 + l < T;
 
   if constexpr (PRO) {
-    // Inverse norms of the lane's four key rows 16 i + c and of the same
-    // query rows: its pieces 4p + g are summed over p here and over g across
-    // lanes (xor 16, xor 32).
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + tokbase * DK, span_bytes((size_t)T * H * DK * 2, (size_t)h * DK * 2));
-    float* const rp = rpw + ((size_t)chain * nch + n) * 128;
+    // Inverse norms of the lane's four key rows 16 i + c: its pieces 4p + g
+    // are summed over p here and over g across lanes (xor 16, xor 32).
+    float* const rp = rpw + ((size_t)chain * nch + n) * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float sk = 0.f, sq = 0.f;
+      float sk = 0.f;
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) {
-        sk += piece_sumsq(kr[i][p]);
-        sq += piece_sumsq(__builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * i + c) * rowK + 2 * (32 * p + 8 * g), t0 * rowK, 0)));
-      }
+      for (int p = 0; p < NKP; ++p) sk += piece_sumsq(kr[i][p]);
       sk += __shfl_xor(sk, 16);
-      sq += __shfl_xor(sq, 16);
       sk += __shfl_xor(sk, 32);
-      sq += __shfl_xor(sq, 32);
       const float r = inv_row_norm(sk);
       if (g == 0) {
         W[Cf::fR + 16 * i + c] = r;
         rp[16 * i + c] = r;
-        rp[64 + 16 * i + c] = inv_row_norm(sq);
       }
     }
   }
@@ -333,14 +324,15 @@ struct StateCfg {
   static constexpr int oK = 0, oQ = 64 * DK * 2, oV = 2 * 64 * DK * 2, oTb = oV + 64 * LDV * 2, oGt = oTb + 6 * 1024;
   // gate table (floats): gamma, lambda, g, fs (decay to the end of the
   // token's 16-block), ge[3][64] (decay from the end of block k to the
-  // token), gamma_C, gamma for the output, and g + log2 p and g - log2 r
-  // for the P tiles' diagonal blocks.  With the prologue fused in, the
-  // inverse row norms r of the keys and p of the queries (from the factor
-  // pass) are folded in here: the consumers' gamma and lambda, and fs, carry
-  // r, the output's gamma and ge carry p, so no wave of the step multiplies
-  // by them itself.
-  static constexpr int gGam = 0, gLam = 64, gG = 128, gFs = 192, gGe = 256, gGC = 448, gGO = 452, gGq = 516,
-                       gGk = 580, szG = 644;
+  // token), gamma_C, gamma for the output, and g - log2 r for the P tiles'
+  // diagonal blocks.  With the prologue fused in, the inverse row norms r of
+  // the keys (from the factor pass) are folded in here: the consumers' gamma
+  // and lambda, fs and the P tiles' key side carry r, so no wave of the step
+  // multiplies by them itself.  The queries' norms p scale whole output rows
+  // (o_t = p_t (gamma_t q_t S + (P Ut)_t) for raw q), so the output wave
+  // applies them last.
+  static constexpr int gGam = 0, gLam = 64, gG = 128, gFs = 192, gGe = 256, gGC = 448, gGO = 452, gGk = 516,
+                       szG = 580;
   static constexpr int szSlot = oGt + szG * 4;
   static constexpr int oP = 3 * szSlot, szP = 6 * 1024;  // P ring, two slots
   // hand-off to the output wave, two slots each: Ut (NC x 4 tiles) and the
@@ -365,7 +357,7 @@ struct StateArgs {
   float* seg_state;    // segmented scan: start states [chains][G][DK][DV] (output mode) or
                        // maps [chains][G][DK][DK + DV] (map mode)
   __bf16* Sck;         // output mode, or NULL: every chunk's start state, bf16 [chains][nch][DK][DV]
-  const float* rp;     // fused prologue: 1 / |k| and 1 / |q| per token, [chains][nch][2][64]
+  const float* rp;     // fused prologue: 1 / |k| per token, [chains][nch][64]
   int T, H, DV, nch;
   int G, SC;           // segments per chain and chunks per segment (G = 1: one segment)
   int nseg;            // segments per chain in this launch's grid (G, or G - 1 in map mode)
@@ -627,7 +619,7 @@ __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* 
       }
     float gr[4], ger[4][3];
     f32x4 gsv[4], fsv[4];
-    constexpr int oGr = PRO ? Cf::gGq : Cf::gG, oGs = PRO ? Cf::gGk : Cf::gG;
+    constexpr int oGr = Cf::gG, oGs = PRO ? Cf::gGk : Cf::gG;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gr[i] = Gt[oGr + 16 * i + c];
@@ -665,11 +657,28 @@ __device__ __forceinline__ void p_role(const StateArgs& a, const Seg& sg, char* 
   });
 }
 
+// Element c & 3 of v: lane (c / 4, c) holds diagonal entry c of a 16 x 16
+// accumulator tile there.
+__device__ __forceinline__ float diag_entry(const f32x4& v, int c) {
+  const int j = c & 3;
+  return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
+}
+
+// x of lane `src` (0..63), through the cross-lane permute.
+__device__ __forceinline__ float from_lane(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, x)));
+}
+
 // The output, transposed so that lane (g, c) holds token 16i + c and value
 // columns 16t + 4g .. + 3 of consumer tile t (one 8-byte store):
 //   O_i^T = (S^T Q_i^T) diag(gamma_i) + sum_{k <= i} Ut_k^T P_ik^T.
 // In step k it finishes chunk k - 1 (the P Ut term) and starts chunk k (the
-// Q S term, from the start state the consumers handed over).
+// Q S term, from the start state the consumers handed over).  With the
+// prologue fused in, q is raw and the P tiles are formed from it, so both
+// terms are scaled last by the row's inverse query norm p: |q|^2 is the
+// diagonal of Q_i Q_i^T, formed on the matrix cores from the Q operands the
+// wave holds (a vector-instruction sum of squares cost this wave more than
+// its slack).
 template <int DK, int NC, bool PRO>
 __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
   using Cf = StateCfg<DK, NC>;
@@ -685,6 +694,7 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
   const int rowO = H * DV * 2, vofO = c * rowO + 8 * g;
   const int tok0 = sg.n0 * 64;
   f32x4 o[4][NC];
+  float pn[4];  // fused prologue: 1 / |q| of the lane's four token rows, carried from start to finish
   auto start = [&](int k, const char* R) {
     const __bf16* const Rb = reinterpret_cast<const __bf16*>(R);
     const float* const Gt = reinterpret_cast<const float*>(R + Cf::oGt);
@@ -704,6 +714,15 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
       gm[i] = Gt[Cf::gGO + 16 * i + c];
     }
     issue_fence();
+    if constexpr (PRO) {  // |q|^2 of row 16i + c: lane (c / 4, c) of Q_i Q_i^T, read by every lane of row c
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 d = zero4();
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) d = mma32(qr[i][p], qr[i][p], d);
+        pn[i] = from_lane(inv_row_norm(diag_entry(d, c)), 16 * (c >> 2) + c);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -735,6 +754,10 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
       for (int i = 0; i < 4; ++i) {
         f32x4 r = mma32(x01, P[pblk(i, 0)], o[i][t]);
         if (i >= 2) r = mma32(x23, P[pblk(i, 1)], r);
+        if constexpr (PRO) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r[j] *= pn[i];
+        }
         __builtin_amdgcn_raw_buffer_store_b64(cvt4(r), ro, vofO + 32 * t, (tok0 + k * 64 + 16 * i) * rowO, 0);
       }
     }
@@ -832,11 +855,11 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
     }
     struct Set {
       u32x4 v[NVL], tb[6];
-      float gv, rk, pq;
+      float gv, rk;
     };
     // fused prologue: the factor pass's 1 / |k| and 1 / |q| per token of the segment's chunks
     const __amdgpu_buffer_rsrc_t rn =
-        make_rsrc(PRO ? a.rp + ((size_t)sg.chain * a.nch + sg.n0) * 128 : nullptr, PRO ? (uint32_t)nloc * 512 : 0u);
+        make_rsrc(PRO ? a.rp + ((size_t)sg.chain * a.nch + sg.n0) * 64 : nullptr, PRO ? (uint32_t)nloc * 256 : 0u);
     Set st[3];
     auto load = [&](auto sc, int m) {
       constexpr int s = decltype(sc)::value;
@@ -850,8 +873,7 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, kRecTb + e * 1024 + l * 16, m * kRecBytes, 0));
       st[s].gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, kRecG + 4 * l, m * kRecBytes, 0));
       if constexpr (PRO) {
-        st[s].rk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, 4 * l, m * 512, 0));
-        st[s].pq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, 256 + 4 * l, m * 512, 0));
+        st[s].rk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, 4 * l, m * 256, 0));
       }
     };
     load(ic<0>{}, clampc(0, nloc));
@@ -879,19 +901,16 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
         const int blk = l >> 4;
         const float gend = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gC;
         const float gam = __builtin_amdgcn_exp2f(gl);
-        const float rk = PRO ? st[ph].rk : 1.f, pq = PRO ? st[ph].pq : 1.f;
+        const float rk = PRO ? st[ph].rk : 1.f;
         Gt[Cf::gGam + l] = gam * rk;
         Gt[Cf::gLam + l] = __builtin_amdgcn_exp2f(gC - gl) * rk;
-        Gt[Cf::gGO + l] = gam * pq;
+        Gt[Cf::gGO + l] = gam;
         Gt[Cf::gG + l] = gl;
         Gt[Cf::gFs + l] = __builtin_amdgcn_exp2f(gend - gl) * rk;
-        if constexpr (PRO) {
-          Gt[Cf::gGq + l] = gl + __builtin_amdgcn_logf(pq);
-          Gt[Cf::gGk + l] = gl - __builtin_amdgcn_logf(rk);
-        }
-        Gt[Cf::gGe + l] = __builtin_amdgcn_exp2f(blk > 0 ? gl - e0 : -INFINITY) * pq;
-        Gt[Cf::gGe + 64 + l] = __builtin_amdgcn_exp2f(blk > 1 ? gl - e1 : -INFINITY) * pq;
-        Gt[Cf::gGe + 128 + l] = __builtin_amdgcn_exp2f(blk > 2 ? gl - e2 : -INFINITY) * pq;
+        if constexpr (PRO) Gt[Cf::gGk + l] = gl - __builtin_amdgcn_logf(rk);
+        Gt[Cf::gGe + l] = __builtin_amdgcn_exp2f(blk > 0 ? gl - e0 : -INFINITY);
+        Gt[Cf::gGe + 64 + l] = __builtin_amdgcn_exp2f(blk > 1 ? gl - e1 : -INFINITY);
+        Gt[Cf::gGe + 128 + l] = __builtin_amdgcn_exp2f(blk > 2 ? gl - e2 : -INFINITY);
         if (l == 63) Gt[Cf::gGC] = __builtin_amdgcn_exp2f(gC);
       }
       issue_fence();
@@ -1048,12 +1067,12 @@ size_t chunk_two_workspace_bytes(const ChunkArgs& a) {
 }
 
 size_t chunk_two_prologue_workspace_bytes(const ChunkArgs& a) {
-  return chunk_two_workspace_bytes(a) + (size_t)a.B * a.H * ((a.T + 63) / 64) * 2 * 64 * 4;
+  return chunk_two_workspace_bytes(a) + (size_t)a.B * a.H * ((a.T + 63) / 64) * 64 * 4;
 }
 
 template <int DK, int NC, bool PRO>
 static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, __bf16* Sck) {
-  // fused prologue: 1 / |k| and 1 / |q| per token after the records and segment maps
+  // fused prologue: 1 / |k| per token after the records and segment maps
   float* const rp = PRO ? reinterpret_cast<float*>(static_cast<char*>(workspace) + chunk_two_workspace_bytes(a))
                         : nullptr;
   using Cf = two::StateCfg<DK, NC>;
@@ -1065,7 +1084,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
   if (total > 0) {
     const hipError_t e = launch_kernel(two::factor_kernel<DK, PRO>, dim3((unsigned)total), dim3(64), st,
                                        static_cast<const __bf16*>(a.k), a.alpha, a.beta, ws, wsT, a.T, a.H, nch,
-                                       (int)total, a.beta_scale, static_cast<const __bf16*>(a.q), rp);
+                                       (int)total, a.beta_scale, rp);
     if (e != hipSuccess) return e;
   }
   two::StateArgs s{};

@@ -152,14 +152,14 @@ def test_prologue_argument_errors(kw, status):
 
 
 def test_prologue_workspace_sizes():
-    """bf16 needs what the plain forward needs, plus 1/|k| and 1/|q| per token (512 bytes per chunk) on the
+    """bf16 needs what the plain forward needs, plus 1/|k| per token (256 bytes per chunk) on the
     two-launch path;
     fp32 and complex64 hold the transformed q, k (256-byte rows) and the two gates, each rounded up to 256 bytes,
     and complex64 adds the forward's own workspace."""
     rows = 2 * 128 * 3
     rowpass = 2 * (rows * 256) + 2 * ((rows * 4 + 255) // 256 * 256)
     assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_BF16) == 0
-    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 128, 128, 64, gdn.GDN_BF16) == 2 * 3 * 2 * (6400 + 512)
+    assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 128, 128, 64, gdn.GDN_BF16) == 2 * 3 * 2 * (6400 + 256)
     assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_F32) == rowpass
     assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 32, 32, 64, gdn.GDN_C64) == rowpass + 2 * 3 * 2 * 57600
     assert gdn.gdn_chunk_fwd_prologue_workspace_bytes(2, 128, 3, 64, 64, 64, gdn.GDN_C64) == 0   # unsupported
