@@ -14,6 +14,10 @@ SMALL = [
     ("f32_tail_s0", "f32", 2, 200, 3, 64, dict(s0_var=0.1)),
     ("bf16_d64_tail", "bf16", 2, 300, 3, 64, {}),
     ("bf16_d64_s0", "bf16", 1, 129, 2, 64, dict(s0_var=0.01)),
+    # bf16 d64 grids of 16 and 192 workgroups, filled to 256 with cache warm-up
+    # workgroups (ragged tails: their loads past T must read nothing)
+    ("bf16_d64_warm_16", "bf16", 2, 1000, 4, 64, {}),
+    ("bf16_d64_warm_192", "bf16", 8, 333, 12, 64, dict(s0_var=0.01)),
     ("bf16_d128_s0", "bf16", 1, 200, 2, 128, dict(s0_var=0.01, alpha_mu=-5.0)),
     ("bf16_d128_tail", "bf16", 2, 77, 1, 128, {}),
     ("c64_tail", "c64", 2, 200, 2, 32, dict(beta_scale=2.0)),
