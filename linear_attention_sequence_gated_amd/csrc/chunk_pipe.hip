@@ -1119,12 +1119,18 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a) {
   if (a.dtype == kDtBF16 && a.dk == 64) {
     const int nslices = a.dv / pipe::Cfg<64>::NV;
     long nblk = (long)a.B * a.H * nslices;
-    // With at least four idle CUs per XCD and whole chains on every XCD, the
-    // grid is filled to the 256 CUs with cache warm-up workgroups.  Not with
-    // the prologue folded in: there they cost more than they saved (B8 T2048
-    // H12: 48.2 against 47.0 us, where the plain call gained 42.9 -> 41.7).
+    // On a whole device (256 CUs in 8 XCDs) with at least four idle CUs per
+    // XCD and whole chains on every XCD, the grid is filled to 256 workgroups
+    // with cache warm-up workgroups (on fewer CUs they would queue behind the
+    // chains and only add their paced loop).  Not with the prologue folded
+    // in: there they cost more than they saved (B8 T2048 H12: 48.2 against
+    // 47.0 us, where the plain call gained 42.9 -> 41.7).
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      ncu = 0;
     int nwarm = 0;
-    if (!a.prologue && nblk % 8 == 0 && nblk <= 224 && (nblk / 8) % nslices == 0) {
+    if (!a.prologue && ncu == 256 && nblk % 8 == 0 && nblk <= 224 && (nblk / 8) % nslices == 0) {
       nwarm = 32 - (int)(nblk / 8);
       nblk = 256;
     }
