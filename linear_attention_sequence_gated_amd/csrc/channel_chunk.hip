@@ -369,12 +369,19 @@ __device__ void solver_role(const Args& a, char* smem, int l, int sv) {
       xl[u] = lam * w[u];
       lam *= rr[u];
     }
+    // the lane's block 4 h .. 4 h + 3, picked by masked sums (a store per
+    // block under a lane condition compiles to branches on the execution
+    // mask, and a chain of selects to an indexed private array)
+    f32x4 xs, ws;
 #pragma unroll
-    for (int u = 0; u < SC; u += 4) {
-      if ((u >> 2) != h) continue;
-      *reinterpret_cast<u32x2*>(XLn + u) = cvt4(f32x4{xl[u], xl[u + 1], xl[u + 2], xl[u + 3]});
-      *reinterpret_cast<f32x4*>(Wn + u) = f32x4{w[u], w[u + 1], w[u + 2], w[u + 3]};
+    for (int j = 0; j < 4; ++j) {
+      xs[j] = (h == 0 ? xl[j] : 0.f) + (h == 1 ? xl[4 + j] : 0.f) + (h == 2 ? xl[8 + j] : 0.f) +
+              (h == 3 ? xl[12 + j] : 0.f);
+      ws[j] = (h == 0 ? w[j] : 0.f) + (h == 1 ? w[4 + j] : 0.f) + (h == 2 ? w[8 + j] : 0.f) +
+              (h == 3 ? w[12 + j] : 0.f);
     }
+    *reinterpret_cast<u32x2*>(XLn + 4 * h) = cvt4(xs);
+    *reinterpret_cast<f32x4*>(Wn + 4 * h) = ws;
     if (h == 0) reinterpret_cast<float*>(R + Lay::rGE)[ch] = lam;
     ge_prev = lam;
   });
@@ -422,7 +429,11 @@ __device__ void output_role(const Args& a, int b, int h_, int dv0, char* smem, i
     for (int t = 1; t < SC; ++t) gc[t] = gc[t - 1] * rr[t];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float gt = h == 0 ? gc[4 * i] : h == 1 ? gc[4 * i + 1] : h == 2 ? gc[4 * i + 2] : gc[4 * i + 3];
+      // g of the lane's token 4 i + h, the products of gc in the same order
+      // with factors of one past it (a select of gc entries on h compiles to
+      // branches on the execution mask, or to an indexed private array)
+      const float gt = gc[4 * i] * (h >= 1 ? rr[4 * i + 1] : 1.f) * (h >= 2 ? rr[4 * i + 2] : 1.f) *
+                       (h >= 3 ? rr[4 * i + 3] : 1.f);
       const float o = gt * qs[i] + y[i];
       const unsigned short ob = __builtin_bit_cast(unsigned short, __float2bfloat16(o));
       __builtin_amdgcn_raw_buffer_store_b16(ob, ro, 2 * ch + (4 * i + h) * rowO, m * SC * rowO, 0);
