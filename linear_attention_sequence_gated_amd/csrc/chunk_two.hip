@@ -773,8 +773,9 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
 // earlier, then reload that register set with chunk k + 5.  Loads are
 // unconditional (clamped chunk index; range-checked buffer loads read rows
 // past T as zero), so the loop has one load path and the compiler's wait
-// counts stay three steps deep.
-template <int DK, int NC, int ROLE, bool PRO>
+// counts stay three steps deep.  NOQ: the launch forms no output (map mode,
+// or the chunk states alone), so the Q rows are neither loaded nor staged.
+template <int DK, int NC, int ROLE, bool PRO, bool NOQ>
 __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
   using Cf = StateCfg<DK, NC>;
   const int H = a.H, T = a.T, DV = a.DV, nloc = sg.nloc;
@@ -783,7 +784,11 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
   // Role 0: K rows (and Q rows at d = 64).  Role 1 at d = 128: Q rows.  Last
   // role: V tile, Tb record and g, and the chunk's gate table.
   constexpr bool kRows = ROLE < Cf::NLOAD - 1;
-  constexpr int NROW = DK == 64 ? 2 : 1;  // row matrices per rows loader
+  if constexpr (NOQ && DK == 128 && ROLE == 1) {  // the Q rows loader has nothing to do
+    run_steps2(nloc, [](auto, int) {});
+    return;
+  }
+  constexpr int NROW = DK == 64 && !NOQ ? 2 : 1;  // row matrices per rows loader
   constexpr int NU = DK / 8;              // 16-byte pieces per row
   constexpr int NPL = 64 * NU / 64;       // pieces per lane per matrix
   constexpr int NVU = Cf::NV / 8;         // 16-byte units per V row
@@ -794,9 +799,11 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
     int ldst[NROW];
     if constexpr (DK == 64) {
       src[0] = a.k;
-      src[1] = a.q;
       ldst[0] = Cf::oK / 2;
-      ldst[1] = Cf::oQ / 2;
+      if constexpr (NROW > 1) {
+        src[1] = a.q;
+        ldst[1] = Cf::oQ / 2;
+      }
     } else {
       src[0] = ROLE == 0 ? a.k : a.q;
       ldst[0] = ROLE == 0 ? Cf::oK / 2 : Cf::oQ / 2;
@@ -919,7 +926,7 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
   }
 }
 
-template <int DK, int NC, bool PRO>
+template <int DK, int NC, bool PRO, bool NOQ>
 __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(StateArgs a) {
   using Cf = StateCfg<DK, NC>;
   __shared__ __attribute__((aligned(16))) char smem[Cf::bytes];
@@ -948,16 +955,19 @@ __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   if (w < NC)
     consumer_role<DK, NC>(a, sg, smem, w, l);
-  else if (w == Cf::wP)
-    p_role<DK, NC, PRO>(a, sg, smem, l);
-  else if (w == Cf::wO)
-    out_role<DK, NC, PRO>(a, sg, smem, l);
-  else if (w == Cf::wL)
-    load_role<DK, NC, 0, PRO>(a, sg, smem, l);
+  else if (w == Cf::wP || w == Cf::wO) {
+    if constexpr (NOQ)  // no output: the P and output waves only keep the barrier count
+      run_steps2(sg.nloc, [](auto, int) {});
+    else if (w == Cf::wP)
+      p_role<DK, NC, PRO>(a, sg, smem, l);
+    else
+      out_role<DK, NC, PRO>(a, sg, smem, l);
+  } else if (w == Cf::wL)
+    load_role<DK, NC, 0, PRO, NOQ>(a, sg, smem, l);
   else if (w == Cf::wL + 1)
-    load_role<DK, NC, 1, PRO>(a, sg, smem, l);
+    load_role<DK, NC, 1, PRO, NOQ>(a, sg, smem, l);
   else if constexpr (Cf::NLOAD > 2)
-    load_role<DK, NC, 2, PRO>(a, sg, smem, l);
+    load_role<DK, NC, 2, PRO, NOQ>(a, sg, smem, l);
 }
 
 // Start states of the segments: S_(s+1) = M_s S_s + B_s for s = 0 .. G - 2,
@@ -1110,7 +1120,7 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
     s.mode = two::kMap;
     s.nseg = G - 1;
     s.seg_state = maps;
-    hipError_t e = launch_kernel(two::state_kernel<DK, NC, PRO>, dim3((unsigned)(chains * (G - 1) * ((DK + a.dv) / Cf::NV))),
+    hipError_t e = launch_kernel(two::state_kernel<DK, NC, PRO, true>, dim3((unsigned)(chains * (G - 1) * ((DK + a.dv) / Cf::NV))),
                                  dim3(Cf::kThreads), st, s);
     if (e != hipSuccess) return e;
     e = launch_kernel(two::combine_kernel<DK>, dim3((unsigned)(chains * (a.dv / 16))), dim3(256), st,
@@ -1120,8 +1130,9 @@ static hipError_t launch_two_dk(const ChunkArgs& a, void* workspace, char* wsT, 
   }
   s.mode = two::kOut;
   s.nseg = G;
-  return launch_kernel(two::state_kernel<DK, NC, PRO>, dim3((unsigned)(chains * G * (a.dv / Cf::NV))),
-                       dim3(Cf::kThreads), st, s);
+  const dim3 grid((unsigned)(chains * G * (a.dv / Cf::NV)));
+  if (s.out == nullptr) return launch_kernel(two::state_kernel<DK, NC, PRO, true>, grid, dim3(Cf::kThreads), st, s);
+  return launch_kernel(two::state_kernel<DK, NC, PRO, false>, grid, dim3(Cf::kThreads), st, s);
 }
 
 hipError_t launch_chunk_two(const ChunkArgs& a, void* workspace) {
