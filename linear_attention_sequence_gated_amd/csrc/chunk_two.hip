@@ -848,8 +848,11 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
       load(ic<ph>{}, clampc(k + 5, nloc));
     });
   } else {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + tokbase * DV + sg.dv0,
-                                                span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2));
+    // The identity columns of a segment map take no V: an empty range makes
+    // their V loads return zero without reading memory.
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+        a.v + tokbase * DV + sg.dv0,
+        sg.mcol ? 0u : span_bytes((size_t)T * H * DV * 2, ((size_t)sg.h * DV + sg.dv0) * 2));
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.ws + ((size_t)sg.chain * a.nch + sg.n0) * kRecBytes,
                                                 (uint32_t)nloc * kRecBytes);
     const int rowV = H * DV * 2;
