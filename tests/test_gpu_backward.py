@@ -155,6 +155,28 @@ def test_backward_d128_long():
     assert_grads("bwd_d128_long", run_bwd(inp, "bf16", dO, dSf), oracle_bwd(inp, dO, dSf), "bf16")
 
 
+# Long single-chain sequences: the backward's forward state pass takes the two-level scan (segment maps,
+# their combine, then every segment's chunk states from its true start state), with ragged segment and
+# chunk tails.  (name, T, d): 65 chunks split into 4 segments (17, 17, 17, 14), 257 into 16 (15 of 17, one of 2).
+BWD_SEGMENTED = [("d64_T4100", 4100, 64), ("d128_T4100", 4100, 128), ("d64_T16400", 16400, 64)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,T,d", BWD_SEGMENTED, ids=[s[0] for s in BWD_SEGMENTED])
+def test_backward_segmented_scan(name, T, d):
+    torch_dev()
+    import linear_attention_sequence_gated_amd as gdn
+    nch = (T + 63) // 64
+    rec = 6400  # bytes of one chunk's factor record; more workspace than the records means segment maps
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, T, 1, d, d, 64, gdn.GDN_BF16) > nch * rec, \
+        "this shape must take the segmented scan"
+    inp = gen_chunk(1, T, 1, d, d, dtype="bf16", seed=40 + d, alpha_mu=-5.0, s0_var=0.1)
+    dO, dSf = gen_upstream_grads(1, T, 1, d, d, seed=40 + d, with_dS=True)
+    dO = bf16_round(dO)
+    note(f"backward segmented {name}")
+    assert_grads(f"bwd_segmented_{name}", run_bwd(inp, "bf16", dO, dSf), oracle_bwd(inp, dO, dSf), "bf16")
+
+
 # Complex data, d = 32 (the phasor memory): the token-by-token kernel in fp32, gradients dL/dRe + i dL/dIm.
 @pytest.mark.parametrize("B,T,H,s0,dS", [(1, 20, 2, False, False), (2, 77, 3, True, True), (1, 200, 2, True, False)])
 def test_backward_complex(B, T, H, s0, dS):
