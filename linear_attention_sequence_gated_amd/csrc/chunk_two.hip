@@ -311,7 +311,10 @@ __global__ __launch_bounds__(64) void factor_kernel(const __bf16* __restrict__ k
 }
 
 // -------------------------------------------------------------- state pass
-template <int DK, int NC>
+// NOQ: a pass that forms no output (segment maps, or the chunk states alone)
+// stages no Q rows and has no P ring or output hand-off, so at d = 64 two of
+// its workgroups fit a CU.
+template <int DK, int NC, bool NOQ = false>
 struct StateCfg {
   static constexpr int NV = 16 * NC;              // value columns per workgroup
   static constexpr int NDT = DK / 16, NKP = DK / 32;
@@ -321,7 +324,8 @@ struct StateCfg {
   static constexpr int NLOAD = DK == 64 ? 2 : 3;  // (K and Q rows | V, Tb, g) or (K | Q | V, Tb, g)
   static constexpr int kThreads = (NC + 2 + NLOAD) * 64;
   // stage slot (bytes): K rows, Q rows, V tile, Tb blocks, gate table
-  static constexpr int oK = 0, oQ = 64 * DK * 2, oV = 2 * 64 * DK * 2, oTb = oV + 64 * LDV * 2, oGt = oTb + 6 * 1024;
+  static constexpr int oK = 0, oQ = 64 * DK * 2, oV = (NOQ ? 1 : 2) * 64 * DK * 2, oTb = oV + 64 * LDV * 2,
+                       oGt = oTb + 6 * 1024;
   // gate table (floats): gamma, lambda, g, fs (decay to the end of the
   // token's 16-block), ge[3][64] (decay from the end of block k to the
   // token), gamma_C, gamma for the output, and g - log2 r for the P tiles'
@@ -334,14 +338,15 @@ struct StateCfg {
   static constexpr int gGam = 0, gLam = 64, gG = 128, gFs = 192, gGe = 256, gGC = 448, gGO = 452, gGk = 516,
                        szG = 580;
   static constexpr int szSlot = oGt + szG * 4;
-  static constexpr int oP = 3 * szSlot, szP = 6 * 1024;  // P ring, two slots
+  static constexpr int oP = 3 * szSlot, szP = NOQ ? 0 : 6 * 1024;  // P ring, two slots
   // hand-off to the output wave, two slots each: Ut (NC x 4 tiles) and the
   // start-of-chunk state (NC x NDT tiles), bf16 operands in lane order
-  static constexpr int szHU = NC * 4 * 64 * 8, szHS = NC * NDT * 64 * 8;
+  static constexpr int szHU = NOQ ? 0 : NC * 4 * 64 * 8, szHS = NOQ ? 0 : NC * NDT * 64 * 8;
   static constexpr int oHU = oP + 2 * szP, oHS = oHU + 2 * szHU;
   static constexpr int bytes = oHS + 2 * szHS;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(szSlot % 16 == 0 && oTb % 16 == 0 && oGt % 16 == 0, "16-byte alignment");
+  static constexpr int kPerCU = bytes <= 80 * 1024 ? 2 : 1;  // workgroups per CU the LDS allows
 };
 
 enum Mode { kOut = 0, kMap = 1 };
@@ -372,9 +377,9 @@ struct Seg {
   bool mcol;                       // map mode, identity columns (V reads as zero)
 };
 
-template <int DK, int NC>
+template <int DK, int NC, bool NOQ>
 struct Consumer2 {
-  using Cf = StateCfg<DK, NC>;
+  using Cf = StateCfg<DK, NC, NOQ>;
   static constexpr int NDT = Cf::NDT, NKP = Cf::NKP;
   f32x4 S[NDT];
   u32x2 sfr[NDT];
@@ -573,14 +578,14 @@ __device__ __forceinline__ void run_steps2(int nloc, Step&& step) {
 
 __device__ __forceinline__ int clampc(int m, int nloc) { return __builtin_amdgcn_readfirstlane(max(0, min(m, nloc - 1))); }
 
-template <int DK, int NC>
+template <int DK, int NC, bool NOQ>
 __device__ __forceinline__ void consumer_role(const StateArgs& a, const Seg& sg, char* smem, int w, int l) {
-  using Cf = StateCfg<DK, NC>;
-  Consumer2<DK, NC> cs;
+  using Cf = StateCfg<DK, NC, NOQ>;
+  Consumer2<DK, NC, NOQ> cs;
   cs.init(a, sg, w, l);
   // Output mode without an output array (the gradient pass's forward, which
   // keeps only the chunk states): nothing is handed to the output wave.
-  const bool out = a.mode == kOut, form = out && a.out;
+  const bool out = a.mode == kOut, form = !NOQ && out && a.out;
   run_steps2(sg.nloc, [&](auto pc, int k) {
     constexpr int slot = (decltype(pc)::value + 1) % 3;  // k % 3
     if (k == -1) cs.publish_state(form ? reinterpret_cast<unsigned*>(smem + Cf::oHS) : nullptr);  // chunk 0's start
@@ -777,7 +782,7 @@ __device__ __forceinline__ void out_role(const StateArgs& a, const Seg& sg, char
 // or the chunk states alone), so the Q rows are neither loaded nor staged.
 template <int DK, int NC, int ROLE, bool PRO, bool NOQ>
 __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, char* smem, int l) {
-  using Cf = StateCfg<DK, NC>;
+  using Cf = StateCfg<DK, NC, NOQ>;
   const int H = a.H, T = a.T, DV = a.DV, nloc = sg.nloc;
   const size_t tokbase = (size_t)sg.b * T * H + sg.h;
   const int tok0 = sg.n0 * 64;
@@ -930,8 +935,9 @@ __device__ __forceinline__ void load_role(const StateArgs& a, const Seg& sg, cha
 }
 
 template <int DK, int NC, bool PRO, bool NOQ>
-__global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(StateArgs a) {
-  using Cf = StateCfg<DK, NC>;
+__global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), (StateCfg<DK, NC, NOQ>::kPerCU)) void state_kernel(
+    StateArgs a) {
+  using Cf = StateCfg<DK, NC, NOQ>;
   __shared__ __attribute__((aligned(16))) char smem[Cf::bytes];
   // Block order: slices of one (chain, segment) are neighbours, kept on one
   // XCD (the hardware deals consecutive blocks to the eight XCDs in turn), so
@@ -957,7 +963,7 @@ __global__ __launch_bounds__((StateCfg<DK, NC>::kThreads), 1) void state_kernel(
   // instructions ignore the exec mask).
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   if (w < NC)
-    consumer_role<DK, NC>(a, sg, smem, w, l);
+    consumer_role<DK, NC, NOQ>(a, sg, smem, w, l);
   else if (w == Cf::wP || w == Cf::wO) {
     if constexpr (NOQ)  // no output: the P and output waves only keep the barrier count
       run_steps2(sg.nloc, [](auto, int) {});
@@ -1056,13 +1062,16 @@ int chunk_two_segments(const ChunkArgs& a) {
   constexpr long kCU = 256;
   auto rounds = [](long wg) { return (wg + kCU - 1) / kCU; };
   const long factor = a.dk == 64 ? chains * nch / 235 : 0;
+  // the map launch forms no output: at d = 64 two of its workgroups share a CU
+  const long map_per_cu = a.dk == 64 ? two::StateCfg<64, 2, true>::kPerCU : two::StateCfg<128, 1, true>::kPerCU;
   const long base = nch * rounds(chains * out_sl);
   long best_cost = base;
   int best = 1;
   for (int G = 2; G <= 16; ++G) {
     const long sc = (nch + G - 1) / G;
     if (sc < 16) break;
-    const long cost = sc * (rounds(chains * (G - 1) * map_sl) + rounds(chains * G * out_sl)) + G + factor;
+    const long cost = sc * (rounds((chains * (G - 1) * map_sl + map_per_cu - 1) / map_per_cu) + rounds(chains * G * out_sl)) +
+                      G + factor;
     if (cost < best_cost) {
       best_cost = cost;
       best = G;
